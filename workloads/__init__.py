@@ -1,0 +1,280 @@
+"""Seeded synthetic inputs for paged GQA decode attention.
+
+This module is the only code the CPU oracle and the HIP path share: it draws
+random numbers, rounds them to BF16 and lays them out in a page pool.  It holds
+none of the attention arithmetic.
+
+Shapes follow the Llama-3.2-1B layer the pages describe ("6 Hours of YouTube
+and 85 handtyped pages of notes on LLM Inference", features completed so far
+and current scope): 32 query heads sharing 8 KV heads of dimension 64, BF16
+K/V in a shared pool of 16-token pages reached through per-sequence block
+tables, a 2,048-token context and a 128 MiB default pool.
+
+Pool layout handed to both sides: ``[num_pages][16 slots][8 kv heads][64]``
+BF16 bits for K and, separately, for V.  Every pool byte that no sequence owns
+(unused pages, slots past a sequence's length in its last page, the slot a
+pending append will fill) holds the BF16 quiet NaN ``0x7FC0``, and every
+unused block-table entry holds ``-1``, so that a kernel reading anything
+outside the sequence shows it in the result.
+
+Random numbers come from NumPy's PCG64 ``default_rng``: standard normals drawn
+in float32, scaled, then rounded to BF16 with round-to-nearest-even.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+NUM_Q_HEADS = 32
+NUM_KV_HEADS = 8
+HEAD_DIM = 64
+PAGE_SIZE = 16
+MAX_CONTEXT = 2048
+MAX_BLOCKS = MAX_CONTEXT // PAGE_SIZE          # block-table row length (128)
+SCALE = 0.125                                   # 1/sqrt(64)
+BF16_NAN = 0x7FC0
+PAGE_BYTES_K = PAGE_SIZE * NUM_KV_HEADS * HEAD_DIM * 2   # 16 KiB of K per page
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to BF16 bit patterns, round-to-nearest-even.
+
+    Adds ``0x7FFF`` plus the lowest kept bit to the binary32 word and keeps the
+    upper 16 bits (the usual bias method).  Inputs here are finite normals.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass
+class DecodeBatch:
+    """One layer's decode-step inputs, as BF16 bit arrays and int32 metadata."""
+
+    name: str
+    q: np.ndarray               # uint16 [B][32][64]
+    k_pool: np.ndarray          # uint16 [num_pages][16][8][64]
+    v_pool: np.ndarray          # uint16 [num_pages][16][8][64]
+    block_tables: np.ndarray    # int32  [B][128]
+    seq_lens: np.ndarray        # int32  [B]
+    scale: float = SCALE
+    k_new: Optional[np.ndarray] = None   # uint16 [B][8][64] when the step appends
+    v_new: Optional[np.ndarray] = None
+    recipe: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.batch else 0
+
+
+def pages_for(seq_len: int) -> int:
+    return (int(seq_len) + PAGE_SIZE - 1) // PAGE_SIZE
+
+
+def make_batch(seq_lens, num_pages: int, seed, *, q_sigma: float = 1.0,
+               append: bool = False, placement: str = "random",
+               name: str = "custom", recipe: Optional[dict] = None) -> DecodeBatch:
+    """Build a poisoned page pool holding random BF16 K/V for ``seq_lens``.
+
+    ``placement`` is ``"random"`` (pages taken in the order of a seeded
+    permutation of the pool) or ``"identity"`` (pages 0, 1, 2, ... in order).
+    With ``append=True`` the pool holds tokens ``0 .. L-2`` of each sequence
+    and the last token is returned separately in ``k_new``/``v_new``; its slot
+    is poisoned until an append writes it.
+
+    Draw order (fixed, so a seed reproduces every byte): page permutation, q,
+    then for each sequence in batch order its K block then its V block.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = int(seq_lens.shape[0])
+    if np.any(seq_lens < 0) or np.any(seq_lens > MAX_CONTEXT):
+        raise ValueError("seq_lens must lie in [0, %d]" % MAX_CONTEXT)
+    rng = np.random.default_rng(seed)
+    n_pages = [pages_for(L) for L in seq_lens]
+    need = sum(n_pages)
+    if need > num_pages:
+        raise ValueError(f"pool of {num_pages} pages cannot hold {need} pages")
+    if placement == "random":
+        order = rng.permutation(num_pages).astype(np.int32)
+    elif placement == "identity":
+        order = np.arange(num_pages, dtype=np.int32)
+    else:
+        raise ValueError(placement)
+
+    block_tables = np.full((B, MAX_BLOCKS), -1, dtype=np.int32)
+    shape_pool = (num_pages, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
+    k_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
+    v_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
+    q = f32_to_bf16_bits(
+        rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM), dtype=np.float32) * np.float32(q_sigma))
+    k_new = np.full((B, NUM_KV_HEADS, HEAD_DIM), BF16_NAN, dtype=np.uint16) if append else None
+    v_new = np.full((B, NUM_KV_HEADS, HEAD_DIM), BF16_NAN, dtype=np.uint16) if append else None
+
+    cursor = 0
+    for b in range(B):
+        L, n = int(seq_lens[b]), n_pages[b]
+        pages = order[cursor:cursor + n]
+        cursor += n
+        block_tables[b, :n] = pages
+        if L == 0:
+            continue
+        tok_shape = (L, NUM_KV_HEADS, HEAD_DIM)
+        K = f32_to_bf16_bits(rng.standard_normal(tok_shape, dtype=np.float32))
+        V = f32_to_bf16_bits(rng.standard_normal(tok_shape, dtype=np.float32))
+        stored = L
+        if append:
+            k_new[b], v_new[b] = K[L - 1], V[L - 1]
+            stored = L - 1
+        _place(k_pool, pages, K[:stored])
+        _place(v_pool, pages, V[:stored])
+
+    rec = dict(recipe or {})
+    rec.update(num_pages=num_pages, placement=placement, q_sigma=q_sigma,
+               append=append, seed=_seed_repr(seed))
+    return DecodeBatch(name=name, q=q, k_pool=k_pool, v_pool=v_pool,
+                       block_tables=block_tables, seq_lens=seq_lens, scale=SCALE,
+                       k_new=k_new, v_new=v_new, recipe=rec)
+
+
+def pack_logical(q, k_rows, v_rows, num_pages: int, seed, *, capacity=None,
+                 placement: str = "random", name: str = "packed") -> DecodeBatch:
+    """Place caller-given logical K/V rows into a poisoned page pool.
+
+    ``k_rows[b]`` / ``v_rows[b]`` are uint16 ``[T_b][8][64]`` BF16 bits of
+    tokens ``0 .. T_b-1``.  ``capacity[b]`` (default ``T_b``) is the sequence
+    length to reserve pages for and to report in ``seq_lens``; it may exceed
+    ``T_b`` by one to leave the slot of a pending append poisoned.  Pages are
+    taken in the order of ``default_rng(seed).permutation(num_pages)`` (or
+    0, 1, 2, ... for ``"identity"``), sequence by sequence.
+    """
+    B = len(k_rows)
+    cap = [int(k.shape[0]) for k in k_rows] if capacity is None else [int(c) for c in capacity]
+    rng = np.random.default_rng(seed)
+    order = (rng.permutation(num_pages) if placement == "random"
+             else np.arange(num_pages)).astype(np.int32)
+    need = sum(pages_for(c) for c in cap)
+    if need > num_pages:
+        raise ValueError(f"pool of {num_pages} pages cannot hold {need} pages")
+    shape_pool = (num_pages, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
+    k_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
+    v_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
+    block_tables = np.full((B, MAX_BLOCKS), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        if not 0 <= k_rows[b].shape[0] <= cap[b] <= MAX_CONTEXT:
+            raise ValueError("rows must fit the reserved capacity")
+        n = pages_for(cap[b])
+        pages = order[cursor:cursor + n]
+        cursor += n
+        block_tables[b, :n] = pages
+        _place(k_pool, pages, np.asarray(k_rows[b], dtype=np.uint16))
+        _place(v_pool, pages, np.asarray(v_rows[b], dtype=np.uint16))
+    return DecodeBatch(name=name, q=np.asarray(q, dtype=np.uint16), k_pool=k_pool,
+                       v_pool=v_pool, block_tables=block_tables,
+                       seq_lens=np.asarray(cap, dtype=np.int32), scale=SCALE,
+                       recipe={"num_pages": num_pages, "placement": placement,
+                               "seed": _seed_repr(seed)})
+
+
+def random_rows(rng, T: int, sigma: float = 1.0) -> np.ndarray:
+    """``[T][8][64]`` BF16 bits of N(0, sigma^2) values."""
+    return f32_to_bf16_bits(
+        rng.standard_normal((T, NUM_KV_HEADS, HEAD_DIM), dtype=np.float32) * np.float32(sigma))
+
+
+def random_q(rng, B: int, sigma: float = 1.0) -> np.ndarray:
+    """``[B][32][64]`` BF16 bits of N(0, sigma^2) values."""
+    return f32_to_bf16_bits(
+        rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM), dtype=np.float32) * np.float32(sigma))
+
+
+def _place(pool: np.ndarray, pages: np.ndarray, rows: np.ndarray) -> None:
+    """Store token rows ``[T][8][64]`` into consecutive logical pages."""
+    T = rows.shape[0]
+    full = T // PAGE_SIZE
+    if full:
+        pool[pages[:full]] = rows[:full * PAGE_SIZE].reshape(full, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
+    tail = T - full * PAGE_SIZE
+    if tail:
+        pool[pages[full], :tail] = rows[full * PAGE_SIZE:]
+
+
+def _seed_repr(seed):
+    return list(seed) if isinstance(seed, (list, tuple)) else seed
+
+
+# ---------------------------------------------------------------------------
+# The five workloads: Llama-3.2-1B decode-step shapes (synthetic stand-ins; the
+# pages name no public benchmark or dataset)
+# ---------------------------------------------------------------------------
+WORKLOADS = {
+    1: "single sequence, seq_len 37 (pages 16+16+5), 64-page pool",
+    2: "batch 8, seq_len uniform in [1, 2048], 4096-page (128 MiB) pool",
+    3: "16 layers, batch 64, seq_len uniform in [16, 2048], q sigma 0.5, append then attend per layer",
+    4: "batch 256, every seq_len 2048 (1 GiB of K/V), pool of exactly 32768 pages",
+    5: "batch 512, seq_len Zipf(1.1) clipped to [1, 2048], append then attend, 10% poison slack",
+}
+NUM_LAYERS_W3 = 16
+POOL_PAGES_W3 = 8192
+
+
+def workload_seq_lens(index: int, seed: Optional[int] = None) -> np.ndarray:
+    """Sequence lengths of workload ``index`` (drawn from their own stream)."""
+    seed = index if seed is None else seed
+    rng = np.random.default_rng([seed, 0])
+    if index == 1:
+        return np.array([37], dtype=np.int32)
+    if index == 2:
+        return rng.integers(1, MAX_CONTEXT + 1, size=8).astype(np.int32)
+    if index == 3:
+        return rng.integers(16, MAX_CONTEXT + 1, size=64).astype(np.int32)
+    if index == 4:
+        return np.full(256, MAX_CONTEXT, dtype=np.int32)
+    if index == 5:
+        return np.clip(rng.zipf(1.1, size=512), 1, MAX_CONTEXT).astype(np.int32)
+    raise ValueError(index)
+
+
+def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
+                  placement: str = "random") -> DecodeBatch:
+    """Inputs of workload ``index`` (for workload 3: of layer ``layer``)."""
+    seed = index if seed is None else seed
+    lens = workload_seq_lens(index, seed)
+    name = f"w{index}"
+    recipe = {"workload": WORKLOADS[index]}
+    if index == 1:
+        return make_batch(lens, 64, [seed, 1], name=name, recipe=recipe, placement=placement)
+    if index == 2:
+        return make_batch(lens, 4096, [seed, 1], name=name, recipe=recipe, placement=placement)
+    if index == 3:
+        if not 0 <= layer < NUM_LAYERS_W3:
+            raise ValueError(layer)
+        return make_batch(lens, POOL_PAGES_W3, [seed, 1, layer], q_sigma=0.5, append=True,
+                          name=f"{name}_layer{layer}", recipe=dict(recipe, layer=layer),
+                          placement=placement)
+    if index == 4:
+        return make_batch(lens, 256 * MAX_BLOCKS, [seed, 1], name=name, recipe=recipe,
+                          placement=placement)
+    if index == 5:
+        need = int(sum(pages_for(L) for L in lens))
+        pool = need + (need + 9) // 10
+        return make_batch(lens, pool, [seed, 1], append=True, name=name, recipe=recipe,
+                          placement=placement)
+    raise ValueError(index)
+
+
+def poison_summary(batch: DecodeBatch) -> dict:
+    """Counts of poisoned pool rows and block-table entries (for reports)."""
+    nan_rows = int(np.count_nonzero(batch.k_pool[..., 0, 0] == BF16_NAN))
+    return {"nan_slots": nan_rows, "unused_bt": int(np.count_nonzero(batch.block_tables < 0))}
