@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA decode hot path on one MI355X.
+
+One step = one layer's decode step of the full-context batch: the one-token
+page append of every sequence, then paged GQA decode attention (32 query
+heads over 8 KV heads, head_dim 64, BF16 K/V in 16-token pages, FP32 online
+softmax) including the split merge.  Workload: batch 256, every sequence
+2,048 tokens after the append (128 pages each, 1 GiB of K/V), pages at
+seeded-random places in a pool of exactly 32,768 pages; synthetic BF16
+N(0, 1) data.
+
+Timing: the inputs are resident in HBM before the timed region.  Before each
+step a 512 MiB buffer is overwritten so the step starts with cold L2 and
+Infinity Cache (the flush is outside the per-step events); HIP events on the
+stream the kernels run on bracket the append, the main attention kernel and
+the merge kernel of every step.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention KV-read GB/s (% of MI355X HBM peak) + sequences/s per layer"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic_b256_l2048.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc", n)
+                  for n in ("pa_kernels.h", "pa_decode.hip")]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_units_bytes: int):
+    """HBM bytes per launch of the main kernel from committed rocprofv3 counters.
+
+    The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+    main kernel and of a device copy of known size, taken on the same kernel
+    source; None when absent or when the kernel has changed since.
+    """
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return int(round(t["hbm_bytes_per_launch"]))
+
+
+def cpu_baseline(batch, gpu_out, seconds: float):
+    """The oracle, as it stands, on the first sequences of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new,
+                                        batch.block_tables, batch.seq_lens)
+        done, t0 = [], time.perf_counter()
+        worst = 0.0
+        while len(done) < batch.batch:
+            b = len(done)
+            ref = oracle.decode_attention(batch.q, k_ref, v_ref, batch.block_tables,
+                                          batch.seq_lens, batch.scale, sequences=[b])
+            worst = max(worst, float(np.max(np.abs(ref[b] - gpu_out[b]))))
+            done.append(b)
+            if time.perf_counter() - t0 >= seconds and len(done) >= 2:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    tokens = int(sum(int(batch.seq_lens[b]) for b in done))
+    kv = tokens * 2048
+    return {
+        "value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"first {len(done)} of {batch.batch} sequences ({tokens} tokens, "
+                   f"{kv / 2**20:.0f} MiB of K/V), float64 NumPy, 1 BLAS thread, "
+                   f"{dt:.1f} s"),
+        "seq_per_s": round(len(done) / dt, 3),
+        "host_cpus": os.cpu_count(),
+        "max_abs_vs_gpu_on_sample": worst,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--pages-per-split", type=int, default=0, help="0 = library plan")
+    ap.add_argument("--placement", choices=["random", "identity"], default="random")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X "
+              "and has no multi-GPU mode (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_decode_07_amd import accounting as A
+    from paged_kv_decode_07_amd import binding as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+
+    t0 = time.perf_counter()
+    batch = W.make_workload(4, placement=args.placement, append=True)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s "
+        f"({batch.batch} sequences, {batch.num_pages} pages)")
+
+    def up16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    q, k_pool, v_pool = up16(batch.q), up16(batch.k_pool), up16(batch.v_pool)
+    k_new, v_new = up16(batch.k_new), up16(batch.v_new)
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    lens = torch.from_numpy(batch.seq_lens).to(dev)
+    B, msl = batch.batch, batch.max_seq_len
+    ps, ns = pa.decode_plan(B, msl, batch.num_pages, 128, args.pages_per_split)
+    ws_bytes = pa.decode_workspace_bytes(B, msl, batch.num_pages, 128, ps)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 32, 64), dtype=torch.float32, device=dev)
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"plan: {ps} pages per split, {ns} splits; workspace {ws_bytes} B")
+
+    K, Wm = args.steps, args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for row in ev:                      # create the HIP events before the timed region
+        row[2].record(stream)
+    scratch_mid = torch.cuda.Event(enable_timing=True)
+    scratch_mid.record(stream)
+
+    def step(marks=None):
+        if marks:
+            marks[0].record(stream)
+        pa.append_kv(k_new, v_new, k_pool, v_pool, bt, lens, stream=stream)
+        if marks:
+            marks[1].record(stream)
+        pa.decode_attention(q, k_pool, v_pool, bt, lens, msl, scale=batch.scale, out=out,
+                            pages_per_split=ps, workspace=workspace, stream=stream,
+                            event_after_main=marks[2] if marks else scratch_mid)
+        if marks:
+            marks[3].record(stream)
+
+    for i in range(Wm):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        step()
+    torch.cuda.synchronize()
+    log(f"{Wm} warmup steps done")
+
+    wall0 = time.perf_counter()
+    for i in range(K):
+        if not args.no_flush:
+            flush.fill_((i + 7) & 0xFF)
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    log(f"{K} timed steps done in {wall:.3f} s wall (flushes included)")
+
+    t_app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_main = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e-3
+    by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
+    kv = by["kv"]
+    mean_step = float(t_step.mean())
+    value = kv / mean_step / 1e9
+    achieved = kv / float(t_main.mean()) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(mean_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "paged GQA decode, 1 layer, batch 256 x 2048 tokens (1 GiB BF16 K/V), "
+                        "append + attention",
+            "global_batch": B, "seq_len": msl, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
+            "page_tokens": 16, "num_pages": batch.num_pages, "placement": args.placement,
+            "pages_per_split": ps, "splits": ns, "out_dtype": "f32",
+            "cache_flush_between_steps": not args.no_flush,
+        },
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "seq_per_s_per_layer": round(B / mean_step, 1),
+        "kv_gbps_attention_only": round(kv / float((t_main + t_merge).mean()) / 1e9, 2),
+        "algorithmic_bytes_per_step": by,
+        "times_us": {
+            "append": round(float(t_app.mean()) * 1e6, 2),
+            "attention_main": round(float(t_main.mean()) * 1e6, 2),
+            "merge": round(float(t_merge.mean()) * 1e6, 2),
+            "step": round(mean_step * 1e6, 2),
+            "step_min": round(float(t_step.min()) * 1e6, 2),
+            "step_median": round(float(np.median(t_step)) * 1e6, 2),
+            "wall_per_step_incl_flush": round(wall / K * 1e6, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa::decode_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(kv),
+            "algorithmic_bytes_per_launch": kv,
+            "avg_launch_us": round(float(t_main.mean()) * 1e6, 2),
+        },
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(batch, out.cpu().numpy().astype(np.float64),
+                                            args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

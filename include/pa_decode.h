@@ -1,0 +1,192 @@
+/*
+ * pa_decode.h -- C ABI of the MI355X (gfx950) paged GQA decode library.
+ *
+ * Operations (defined by the pages of the subject, cited by title/section):
+ *
+ *  - pa_append_kv: decode writes each sequence's new K/V row into its page
+ *    slot at the token's absolute position ("6 Hours of YouTube and 85
+ *    handtyped pages of notes on LLM Inference - Start here", samir-vllm
+ *    README, features completed so far: shared BF16 KV page pool, a block
+ *    table per sequence and layer, 16 tokens of K and V per physical page).
+ *
+ *  - pa_decode_attention: each active sequence's new query, 32 query heads
+ *    over 8 KV heads of dimension 64, attends that sequence's cached tokens
+ *    through its block table and attention length, with an FP32 online
+ *    softmax, never gathering a contiguous prefix and never storing scores
+ *    (same page, same section: direct paged decode attention; batched decode
+ *    with a page map and attention length per sequence).  The result is the
+ *    textbook single-query attention: scores q.K^T scaled by `scale`,
+ *    max-subtracted softmax over the sequence, weighted sum of V
+ *    ("Building an LLM inference engine from scratch: KV cache, operator
+ *    fusion and quantisation practice", section 3.2).
+ *
+ * Memory and ownership (same README: preallocated device buffers, reused;
+ * request count never grows the pool): every buffer is allocated and owned
+ * by the caller.  The library allocates no device memory and keeps no
+ * mutable global state besides a per-device cache of the compute-unit
+ * count.  All device pointers are HIP device addresses.  Calls only enqueue
+ * work on `stream` (a hipStream_t; NULL means the default stream) and
+ * return without synchronising, except pa_validate_metadata.
+ *
+ * Errors (same README, current scope: impossible requests get an explicit
+ * error, never a silent one): every call returns PA_OK or a negative
+ * pa_status before it launches anything.  Host-checkable mistakes are
+ * reported: NULL pointers, unsupported shapes, misaligned pointers, an
+ * undersized workspace, out-of-range sizes.  Device-resident metadata
+ * (page ids, lengths) cannot be checked without a synchronisation; the
+ * kernels never read or write outside the pool for any metadata value: a
+ * sequence whose block-table entries fall outside [0, num_pages) or whose
+ * length exceeds the capacity gets NaN in every output element, and an
+ * append with such metadata writes nothing.  pa_validate_metadata checks
+ * metadata explicitly.
+ *
+ * Supported shape: num_q_heads 32, num_kv_heads 8, head_dim 64, page_size
+ * 16 (anything else returns PA_ERR_SHAPE).
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  PA_ERR_SHAPE = -2,     /* head counts / head_dim / page_size not supported    */
+  PA_ERR_ALIGN = -3,     /* a pointer is not aligned as documented              */
+  PA_ERR_WORKSPACE = -4, /* workspace missing or smaller than required          */
+  PA_ERR_LAUNCH = -5,    /* HIP reported an error when launching                */
+  PA_ERR_VALUE = -6,     /* a size or scalar argument is out of range           */
+  PA_ERR_METADATA = -7,  /* pa_validate_metadata found a bad table or length    */
+  PA_ERR_DEVICE = -8     /* HIP device query failed                             */
+} pa_status;
+
+typedef enum pa_out_dtype {
+  PA_OUT_F32 = 0,        /* float32 output (the default for parity)             */
+  PA_OUT_BF16 = 1        /* BF16 output, round-to-nearest-even                  */
+} pa_out_dtype;
+
+/* Geometry of one layer's pool region.  Passed by pointer, read only. */
+typedef struct pa_shape {
+  int32_t num_q_heads;        /* Hq = 32                                        */
+  int32_t num_kv_heads;       /* Hkv = 8; query head h reads KV head h / 4      */
+  int32_t head_dim;           /* D = 64                                         */
+  int32_t page_size;          /* P = 16 tokens per page                         */
+  int32_t num_pages;          /* pages in the region k_pool / v_pool point at   */
+  int32_t max_blocks_per_seq; /* row length (stride) of block_tables, >= 1;
+                                 capacity of a sequence = 16 * this             */
+} pa_shape;
+
+/*
+ * Layouts (all row-major, no padding):
+ *   q             BF16  [batch][Hq][D]                 16-byte aligned
+ *   k_pool/v_pool BF16  [num_pages][P][Hkv][D]         16-byte aligned
+ *                 token t of sequence b lives in page block_tables[b][t/16],
+ *                 slot t%16; one page = 16 KiB of K plus 16 KiB of V
+ *   k_new/v_new   BF16  [batch][Hkv][D]                16-byte aligned
+ *   block_tables  int32 [batch][max_blocks_per_seq]    4-byte aligned;
+ *                 entries past ceil(seq_len/16) are never read
+ *   seq_lens      int32 [batch]                        4-byte aligned;
+ *                 length AFTER the append; 0 marks an idle batch slot
+ *   out           [batch][Hq][D], float32 or BF16      16-byte aligned
+ */
+
+/*
+ * Append one token per sequence: for every b with L = seq_lens[b] >= 1,
+ * copy k_new[b] (8 x 64 BF16, 1 KiB) to k_pool[block_tables[b][(L-1)/16]]
+ * [(L-1)%16] and v_new[b] likewise.  Bit-exact copy; nothing else in the
+ * pools changes.  Idle slots (L == 0) and sequences whose target page id or
+ * length is out of range write nothing.  Two sequences must not target the
+ * same slot in one call.  batch == 0 is a no-op returning PA_OK.
+ */
+int pa_append_kv(const pa_shape* shape, int32_t batch,
+                 const void* k_new, const void* v_new,
+                 void* k_pool, void* v_pool,
+                 const int32_t* block_tables, const int32_t* seq_lens,
+                 void* stream);
+
+/*
+ * Workspace needed by pa_decode_attention for these arguments, in bytes
+ * (0 when every sequence fits one split).  pages_per_split is 0 to let the
+ * library plan (the plan then depends on the current device's compute-unit
+ * count) or a fixed split size in pages, 1 .. max_blocks_per_seq.
+ * Returns PA_OK and stores the size in *bytes.
+ */
+int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch,
+                              int32_t max_seq_len, int32_t pages_per_split,
+                              size_t* bytes);
+
+/*
+ * Split size (pages per work-group) the library would use for these
+ * arguments; with pages_per_split != 0 it is returned unchanged after
+ * validation.  Stores it in *pages_out and the number of splits of the
+ * longest sequence in *splits_out (either may be NULL).
+ */
+int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_len,
+                   int32_t pages_per_split, int32_t* pages_out,
+                   int32_t* splits_out);
+
+/*
+ * Paged GQA decode attention for one layer.
+ *   out[b][h][:] = sum_t w_t V_b[t][h/4][:],  w = softmax_t(scale * q[b][h] . K_b[t][h/4])
+ * over tokens t in [0, seq_lens[b]); rows with seq_lens[b] == 0 are zero.
+ * max_seq_len is a host-side upper bound of seq_lens (0 .. 16 *
+ * max_blocks_per_seq); a sequence longer than it gets NaN outputs.
+ * scale must be finite (1/8 for head_dim 64).  out_dtype is a pa_out_dtype.
+ * Sequences longer than one split write FP32 partial results (running max,
+ * sum, unnormalised output) to the workspace and a second kernel merges them
+ * in split order; results are deterministic run to run and do not depend on
+ * where pages sit in the pool.  `out` must not alias any input.
+ */
+int pa_decode_attention(const pa_shape* shape, int32_t batch,
+                        const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        int32_t max_seq_len, float scale,
+                        void* out, int32_t out_dtype,
+                        int32_t pages_per_split,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * pa_decode_attention plus a timing hook: when event_after_main (a
+ * hipEvent_t created by the caller) is not NULL it is recorded on `stream`
+ * right after the main attention kernel is enqueued and before the split
+ * merge kernel, so that a caller's events before and after the call time the
+ * two kernels separately.  Same arguments, checks and results otherwise.
+ */
+int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 int32_t max_seq_len, float scale,
+                                 void* out, int32_t out_dtype,
+                                 int32_t pages_per_split,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream, void* event_after_main);
+
+/*
+ * Debug check of device-resident metadata: copies block_tables and
+ * seq_lens to the host (synchronising `stream`) and checks that every
+ * length lies in [0, max_seq_len], every used block-table entry lies in
+ * [0, num_pages) and no page is used twice.  Returns PA_OK or
+ * PA_ERR_METADATA and stores the first offending batch index in
+ * *bad_index (or -1); bad_index may be NULL.
+ */
+int pa_validate_metadata(const pa_shape* shape, int32_t batch,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         int32_t max_seq_len, void* stream, int64_t* bad_index);
+
+/* Static, human-readable name of a pa_status value. */
+const char* pa_status_string(int status);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,209 @@
+"""ctypes binding of libpa_decode.so: argument marshalling only.
+
+Every step of the decode path runs in the HIP library; this module checks
+tensor dtypes, shapes, devices and contiguity, passes raw device pointers and
+torch's current HIP stream, and turns a non-zero status into an exception.
+PyTorch provides the device memory and the stream, nothing else.  If the
+library is missing the functions raise: there is no other implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+_lock = threading.Lock()
+_lib = None
+
+PA_OUT_F32, PA_OUT_BF16 = 0, 1
+HQ, HKV, D, PAGE = 32, 8, 64, 16
+
+# names declared in include/pa_decode.h
+EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
+           "pa_decode_attention", "pa_decode_attention_profiled",
+           "pa_validate_metadata", "pa_status_string", "pa_abi_version")
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+def make_shape(num_pages: int, max_blocks: int, num_q_heads: int = HQ,
+               num_kv_heads: int = HKV, head_dim: int = D, page_size: int = PAGE) -> PaShape:
+    return PaShape(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, max_blocks)
+
+
+def load_library(path: str | None = None):
+    """Open the built library (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        path = path or _build.LIB
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library not built: {path} is missing "
+                "(run `python -m paged_kv_decode_07_amd.build`)")
+        lib = ctypes.CDLL(path)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        SP = ctypes.POINTER(PaShape)
+        lib.pa_append_kv.argtypes = [SP, I32, P, P, P, P, P, P, P]
+        lib.pa_decode_workspace_bytes.argtypes = [SP, I32, I32, I32, ctypes.POINTER(SZ)]
+        lib.pa_decode_plan.argtypes = [SP, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        lib.pa_decode_attention.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float,
+                                            P, I32, I32, P, SZ, P]
+        lib.pa_decode_attention_profiled.argtypes = lib.pa_decode_attention.argtypes + [P]
+        lib.pa_validate_metadata.argtypes = [SP, I32, P, P, I32, P, ctypes.POINTER(ctypes.c_int64)]
+        lib.pa_status_string.argtypes = [ctypes.c_int]
+        lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_abi_version.argtypes = []
+        for name in ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
+                     "pa_decode_attention", "pa_decode_attention_profiled",
+                     "pa_validate_metadata", "pa_abi_version"):
+            getattr(lib, name).restype = ctypes.c_int
+        if path == _build.LIB:
+            _lib = lib
+        return lib
+
+
+def status_string(rc: int) -> str:
+    return load_library().pa_status_string(int(rc)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what}: {status_string(rc)} (status {rc})")
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bits16(t: torch.Tensor, name: str, shape_tail) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bfloat16 (or its 16-bit patterns), got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if tuple(t.shape[-len(shape_tail):]) != tuple(shape_tail):
+        raise ValueError(f"{name}: trailing shape {tuple(t.shape)} != {tuple(shape_tail)}")
+    return t
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous int32 device tensor")
+    return t
+
+
+def append_kv(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, stream=None) -> None:
+    """Write each sequence's new K/V row (``[B][8][64]``) into its page slot."""
+    B = int(seq_lens.shape[0])
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    shape = make_shape(int(k_pool.shape[0]), int(block_tables.shape[1]))
+    rc = load_library().pa_append_kv(ctypes.byref(shape), B, _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                     _ptr(seq_lens), _stream_ptr(stream))
+    _check(rc, "pa_append_kv")
+
+
+def decode_plan(batch: int, max_seq_len: int, num_pages: int, max_blocks: int = 128,
+                pages_per_split: int = 0):
+    """(pages per split, splits of the longest sequence) the library uses."""
+    shape = make_shape(num_pages, max_blocks)
+    ps, ns = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = load_library().pa_decode_plan(ctypes.byref(shape), batch, max_seq_len,
+                                       pages_per_split, ctypes.byref(ps), ctypes.byref(ns))
+    _check(rc, "pa_decode_plan")
+    return ps.value, ns.value
+
+
+def decode_workspace_bytes(batch: int, max_seq_len: int, num_pages: int,
+                           max_blocks: int = 128, pages_per_split: int = 0) -> int:
+    shape = make_shape(num_pages, max_blocks)
+    n = ctypes.c_size_t(0)
+    rc = load_library().pa_decode_workspace_bytes(ctypes.byref(shape), batch, max_seq_len,
+                                                  pages_per_split, ctypes.byref(n))
+    _check(rc, "pa_decode_workspace_bytes")
+    return n.value
+
+
+def decode_attention(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int,
+                     scale: float = 0.125, out=None, out_dtype=torch.float32,
+                     pages_per_split: int = 0, workspace=None, stream=None,
+                     event_after_main=None):
+    """Paged GQA decode attention; returns ``out`` ``[B][32][64]``.
+
+    ``workspace`` may be passed (a uint8 device tensor of at least
+    ``decode_workspace_bytes(...)`` bytes) to keep the call free of torch
+    allocations; otherwise one is allocated here when the plan needs it.
+    """
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if q.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    num_pages, max_blocks = int(k_pool.shape[0]), int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][32][64] tensor of out_dtype")
+    need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    shape = make_shape(num_pages, max_blocks)
+    args = [ctypes.byref(shape), B, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            _ptr(seq_lens), int(max_seq_len), float(scale), _ptr(out), code,
+            int(pages_per_split), _ptr(workspace), ws_bytes, _stream_ptr(stream)]
+    lib = load_library()
+    if event_after_main is None:
+        rc = lib.pa_decode_attention(*args)
+    else:
+        # a torch.cuda.Event: its HIP event exists once it has been recorded
+        handle = event_after_main.cuda_event
+        if not handle:
+            raise ValueError("record event_after_main once before passing it")
+        rc = lib.pa_decode_attention_profiled(*args, ctypes.c_void_p(handle))
+    _check(rc, "pa_decode_attention")
+    return out
+
+
+def validate_metadata(block_tables, seq_lens, max_seq_len: int, num_pages: int, stream=None):
+    """Host check of device metadata; returns (ok, first bad batch index or -1)."""
+    B = int(seq_lens.shape[0])
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    shape = make_shape(num_pages, int(block_tables.shape[1]))
+    bad = ctypes.c_int64(-1)
+    rc = load_library().pa_validate_metadata(ctypes.byref(shape), B, _ptr(block_tables),
+                                             _ptr(seq_lens), int(max_seq_len),
+                                             _stream_ptr(stream), ctypes.byref(bad))
+    if rc not in (0, -7):
+        _check(rc, "pa_validate_metadata")
+    return rc == 0, bad.value

@@ -1,0 +1,58 @@
+"""Build the HIP library in-tree with hipcc for gfx950.
+
+``python -m paged_kv_decode_07_amd.build`` compiles
+``csrc/pa_decode.hip`` (with ``csrc/pa_kernels.h``) and the header in
+``include/`` into ``paged_kv_decode_07_amd/_lib/libpa_decode.so``.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "pa_decode.hip")
+OUT_DIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(OUT_DIR, "libpa_decode.so")
+ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-fvisibility=hidden",
+    # packed FP32 instructions stay off: plain FP32 VALU only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS,
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+           SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = ("packed-fp32-ops", "--hip-link")
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
+            if ln.strip() and not any(n in ln for n in noise)]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

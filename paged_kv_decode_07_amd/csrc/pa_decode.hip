@@ -1,0 +1,270 @@
+// Host side of the paged GQA decode library: argument checks, split planning
+// and kernel launches behind the C ABI declared in include/pa_decode.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "pa_decode.h"
+#include "pa_kernels.h"
+
+#define PA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+// Compute units of the current device, queried once per device.
+int current_cu_count(int* cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_DEVICE;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    g_cu_count[dev] = n;
+  });
+  if (g_cu_count[dev] <= 0) return PA_ERR_DEVICE;
+  *cu = g_cu_count[dev];
+  return PA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const pa_shape* s) {
+  if (!s) return PA_ERR_NULL;
+  if (s->num_q_heads != pa::kHq || s->num_kv_heads != pa::kHkv || s->head_dim != pa::kD ||
+      s->page_size != pa::kPage)
+    return PA_ERR_SHAPE;
+  if (s->num_pages < 0 || s->max_blocks_per_seq < 1) return PA_ERR_VALUE;
+  // page offsets are formed in 64-bit; the block table row stride in 32-bit
+  if ((int64_t)s->max_blocks_per_seq * pa::kPage > INT32_MAX) return PA_ERR_VALUE;
+  return PA_OK;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Split size in pages.  With `fixed` != 0 that size is used as given.
+// Otherwise: enough work-groups to give every compute unit about two
+// (sequences x splits >= 2 x CUs), but never splits shorter than 8 pages
+// (128 tokens), so the partial results stay a small fraction of the bytes.
+int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pages, int* splits) {
+  const int max_pages = ceil_div(max_seq_len, pa::kPage);
+  int ps;
+  if (fixed != 0) {
+    if (fixed < 1 || fixed > s->max_blocks_per_seq) return PA_ERR_VALUE;
+    ps = fixed;
+  } else {
+    if (max_pages <= 8 || batch <= 0) {
+      ps = max_pages > 0 ? max_pages : 1;
+    } else {
+      int cu = 0;
+      const int rc = current_cu_count(&cu);
+      if (rc != PA_OK) return rc;
+      const int want = ceil_div(2 * cu, batch);               // splits per sequence wanted
+      const int cap = ceil_div(max_pages, 8);                 // >= 8 pages per split
+      const int ns = want < 1 ? 1 : (want > cap ? cap : want);
+      ps = ceil_div(max_pages, ns);
+    }
+  }
+  *pages = ps;
+  *splits = max_pages > 0 ? ceil_div(max_pages, ps) : 1;
+  return PA_OK;
+}
+
+size_t workspace_for(int batch, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)batch * splits * pa::kHq;
+  size_t acc = rows * pa::kD * sizeof(float);
+  acc = (acc + 255) & ~(size_t)255;
+  return acc + rows * 2 * sizeof(float);
+}
+
+int check_decode_sizes(const pa_shape* shape, int32_t batch, int32_t max_seq_len) {
+  int rc = check_shape(shape);
+  if (rc != PA_OK) return rc;
+  if (batch < 0) return PA_ERR_VALUE;
+  if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)shape->max_blocks_per_seq * pa::kPage)
+    return PA_ERR_VALUE;
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_API int pa_abi_version(void) { return 1; }
+
+PA_API const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: only 32 query heads, 8 KV heads, head_dim 64, 16-token pages";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: pointer not aligned (16 B for tensors, 4 B for metadata)";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP kernel launch failed";
+    case PA_ERR_VALUE: return "PA_ERR_VALUE: size or scalar argument out of range";
+    case PA_ERR_METADATA: return "PA_ERR_METADATA: block table or sequence length invalid";
+    case PA_ERR_DEVICE: return "PA_ERR_DEVICE: HIP device query failed";
+    default: return "unknown pa_status";
+  }
+}
+
+PA_API int pa_append_kv(const pa_shape* shape, int32_t batch, const void* k_new,
+                        const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* block_tables, const int32_t* seq_lens, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != PA_OK) return rc;
+  if (batch < 0) return PA_ERR_VALUE;
+  if (batch == 0) return PA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens) return PA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  if (shape->num_pages < 1) return PA_ERR_VALUE;
+  hipLaunchKernelGGL(pa::append_kernel, dim3(batch), dim3(64), 0, (hipStream_t)stream,
+                     (const uint4*)k_new, (const uint4*)v_new, (uint4*)k_pool, (uint4*)v_pool,
+                     block_tables, seq_lens, shape->max_blocks_per_seq, shape->num_pages);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+PA_API int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_len,
+                          int32_t pages_per_split, int32_t* pages_out, int32_t* splits_out) {
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  int ps = 0, ns = 0;
+  rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
+  if (rc != PA_OK) return rc;
+  if (pages_out) *pages_out = ps;
+  if (splits_out) *splits_out = ns;
+  return PA_OK;
+}
+
+PA_API int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch, int32_t max_seq_len,
+                                     int32_t pages_per_split, size_t* bytes) {
+  if (!bytes) return PA_ERR_NULL;
+  int ps = 0, ns = 0;
+  const int rc = pa_decode_plan(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
+  if (rc != PA_OK) return rc;
+  *bytes = workspace_for(batch, ns);
+  return PA_OK;
+}
+
+namespace {
+int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_pool,
+                const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
+                int32_t pages_per_split, void* workspace, size_t workspace_bytes,
+                void* stream, void* event_after_main) {
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  if (out_dtype != PA_OUT_F32 && out_dtype != PA_OUT_BF16) return PA_ERR_VALUE;
+  if (!std::isfinite(scale)) return PA_ERR_VALUE;
+  if (batch == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  if (shape->num_pages < 1 && max_seq_len > 0) return PA_ERR_VALUE;
+  int ps = 0, ns = 0;
+  rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
+  if (rc != PA_OK) return rc;
+  const size_t need = workspace_for(batch, ns);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PA_ERR_ALIGN;
+  }
+  if ((int64_t)batch * ns > INT32_MAX || ns > 65535 || batch > 65535 * 64) return PA_ERR_VALUE;
+
+  pa::DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.k_pool = (const uint16_t*)k_pool;
+  a.v_pool = (const uint16_t*)v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_acc = (float*)workspace;
+  const size_t rows = (size_t)batch * ns * pa::kHq;
+  const size_t acc_bytes = (rows * pa::kD * sizeof(float) + 255) & ~(size_t)255;
+  a.part_ml = need ? (float*)((char*)workspace + acc_bytes) : nullptr;
+  a.xscale = scale * pa::kLog2e;
+  a.num_pages = shape->num_pages;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.pages_per_split = ps;
+  a.num_splits = ns;
+
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid(ns, batch);
+  if (out_dtype == PA_OUT_BF16)
+    hipLaunchKernelGGL(pa::decode_kernel<true>, grid, dim3(pa::kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(pa::decode_kernel<false>, grid, dim3(pa::kThreads), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  if (event_after_main && hipEventRecord((hipEvent_t)event_after_main, st) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  if (ns > 1) {
+    if (out_dtype == PA_OUT_BF16)
+      hipLaunchKernelGGL(pa::merge_kernel<true>, dim3(batch), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(pa::merge_kernel<false>, dim3(batch), dim3(256), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+}  // namespace
+
+PA_API int pa_decode_attention(const pa_shape* shape, int32_t batch, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
+                               int32_t pages_per_split, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return decode_impl(shape, batch, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
+                     scale, out, out_dtype, pages_per_split, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, const void* q,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, const int32_t* seq_lens,
+                                        int32_t max_seq_len, float scale, void* out,
+                                        int32_t out_dtype, int32_t pages_per_split,
+                                        void* workspace, size_t workspace_bytes, void* stream,
+                                        void* event_after_main) {
+  return decode_impl(shape, batch, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
+                     scale, out, out_dtype, pages_per_split, workspace, workspace_bytes, stream,
+                     event_after_main);
+}
+
+PA_API int pa_validate_metadata(const pa_shape* shape, int32_t batch,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t max_seq_len, void* stream, int64_t* bad_index) {
+  if (bad_index) *bad_index = -1;
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  if (batch == 0) return PA_OK;
+  if (!block_tables || !seq_lens) return PA_ERR_NULL;
+  const int mb = shape->max_blocks_per_seq;
+  std::vector<int32_t> bt((size_t)batch * mb), lens(batch);
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  std::vector<int32_t> owner(shape->num_pages > 0 ? shape->num_pages : 0, -1);
+  for (int b = 0; b < batch; ++b) {
+    const int L = lens[b];
+    if (L < 0 || L > max_seq_len) { if (bad_index) *bad_index = b; return PA_ERR_METADATA; }
+    const int n = ceil_div(L, pa::kPage);
+    for (int i = 0; i < n; ++i) {
+      const int id = bt[(size_t)b * mb + i];
+      if (id < 0 || id >= shape->num_pages || owner[id] != -1) {
+        if (bad_index) *bad_index = b;
+        return PA_ERR_METADATA;
+      }
+      owner[id] = b;
+    }
+  }
+  return PA_OK;
+}

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports what its header declares, and rejects bad
+arguments on the host before any launch (no GPU needed: none of these calls
+reaches the device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_decode_07_amd import binding as pa
+from paged_kv_decode_07_amd import build as pb
+
+HEADER = os.path.join(pb.ROOT, "include", "pa_decode.h")
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pb.LIB):
+        pb.build()
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(pa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert "pa_append_kv" in names and "pa_decode_attention" in names
+    assert set(names) == set(pa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.pa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for rc in range(0, -9, -1):
+        s = pa.status_string(rc)
+        assert s.startswith("PA_")
+    assert "unknown" in pa.status_string(42)
+
+
+def shape(**kw):
+    s = pa.make_shape(64, 128)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def decode(lib, s, batch=1, max_seq_len=37, ptrs=None, scale=0.125, out_dtype=0, ps=1,
+           ws=FAKE, ws_bytes=1 << 30, align_off=0):
+    # every case here must be rejected (or be a batch-0 no-op) before a launch:
+    # the pointers are fake.  With ps=1 the 37-token sequence needs 3 splits,
+    # so a workspace is required and FAKE with ws_bytes=1<<30 is never reached
+    # unless an earlier check fails first.
+    p = ptrs or [ctypes.c_void_p(0x10000 + align_off)] * 6
+    rc = lib.pa_decode_attention(ctypes.byref(s) if s is not None else None, batch,
+                                   p[0], p[1], p[2], p[3], p[4], max_seq_len, scale, p[5],
+                                   out_dtype, ps, ws, ws_bytes, None)
+    assert rc < 0 or batch == 0, "a fake-pointer call was not rejected on the host"
+    return rc
+
+
+def test_decode_argument_errors(lib):
+    assert decode(lib, None) == -1                                         # NULL shape
+    assert decode(lib, shape(num_q_heads=16)) == -2                         # shape
+    assert decode(lib, shape(head_dim=128)) == -2
+    assert decode(lib, shape(page_size=32)) == -2
+    assert decode(lib, shape(), batch=-1) == -6                             # value
+    assert decode(lib, shape(), max_seq_len=2049) == -6
+    assert decode(lib, shape(), scale=float("inf")) == -6
+    assert decode(lib, shape(), out_dtype=7) == -6
+    assert decode(lib, shape(), ps=129) == -6
+    assert decode(lib, shape(), batch=0) == 0                               # no-op
+    assert decode(lib, shape(), ptrs=[None] * 6) == -1                      # NULL tensors
+    assert decode(lib, shape(), align_off=4) == -3                          # misaligned
+    assert decode(lib, shape(), ws=None, ws_bytes=0) == -4                  # 3 splits need space
+    assert decode(lib, shape(), ws_bytes=100) == -4
+
+
+def test_workspace_sizes(lib):
+    n = ctypes.c_size_t(0)
+    s = shape()
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(s), 8, 2048, 128, ctypes.byref(n)) == 0
+    assert n.value == 0                                                     # one split
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(s), 8, 2048, 16, ctypes.byref(n)) == 0
+    rows = 8 * 8 * 32                                                       # B x splits x heads
+    assert n.value == ((rows * 64 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    ps, ns = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.pa_decode_plan(ctypes.byref(s), 8, 37, 2, ctypes.byref(ps), ctypes.byref(ns)) == 0
+    assert (ps.value, ns.value) == (2, 2)
+
+
+def test_append_argument_errors(lib):
+    s = shape()
+    F = FAKE
+    assert lib.pa_append_kv(None, 1, F, F, F, F, F, F, None) == -1
+    assert lib.pa_append_kv(ctypes.byref(shape(num_kv_heads=4)), 1, F, F, F, F, F, F, None) == -2
+    assert lib.pa_append_kv(ctypes.byref(s), -2, F, F, F, F, F, F, None) == -6
+    assert lib.pa_append_kv(ctypes.byref(s), 0, None, None, None, None, None, None, None) == 0
+    assert lib.pa_append_kv(ctypes.byref(s), 1, None, F, F, F, F, F, None) == -1
+    bad = ctypes.c_void_p(0x10008)
+    assert lib.pa_append_kv(ctypes.byref(s), 1, bad, F, F, F, F, F, None) == -3
+    assert lib.pa_append_kv(ctypes.byref(shape(num_pages=0)), 1, F, F, F, F, F, F, None) == -6
+
+
+def test_validate_metadata_argument_errors(lib):
+    s = shape()
+    bad = ctypes.c_int64(0)
+    assert lib.pa_validate_metadata(ctypes.byref(s), 0, None, None, 0, None,
+                                    ctypes.byref(bad)) == 0
+    assert lib.pa_validate_metadata(ctypes.byref(s), 2, None, None, 16, None,
+                                    ctypes.byref(bad)) == -1
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        pa.load_library(str(tmp_path / "nope.so"))

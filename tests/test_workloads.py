@@ -55,3 +55,15 @@ def test_small_workload_layout():
     assert list(w.block_tables[0, :3] >= 0) == [True] * 3 and w.block_tables[0, 3] == -1
     last = w.block_tables[0, 2]
     assert np.all(w.k_pool[last, 5:] == W.BF16_NAN) and not np.any(w.k_pool[last, :5] == W.BF16_NAN)
+
+
+def test_placement_does_not_change_the_logical_cache():
+    import oracle
+    a = W.make_workload(2)
+    b = W.make_workload(2, placement="identity")
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.seq_lens, b.seq_lens)
+    assert not np.array_equal(a.block_tables, b.block_tables)
+    for i in range(a.batch):
+        L = int(a.seq_lens[i])
+        assert np.array_equal(oracle.gather_sequence(a.k_pool, a.block_tables[i], L),
+                              oracle.gather_sequence(b.k_pool, b.block_tables[i], L))

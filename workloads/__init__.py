@@ -105,8 +105,11 @@ def make_batch(seq_lens, num_pages: int, seed, *, q_sigma: float = 1.0,
     need = sum(n_pages)
     if need > num_pages:
         raise ValueError(f"pool of {num_pages} pages cannot hold {need} pages")
+    # the permutation is always drawn, so the values that follow do not depend
+    # on the placement: "identity" and "random" hold the same logical cache
+    perm = rng.permutation(num_pages).astype(np.int32)
     if placement == "random":
-        order = rng.permutation(num_pages).astype(np.int32)
+        order = perm
     elif placement == "identity":
         order = np.arange(num_pages, dtype=np.int32)
     else:
@@ -247,8 +250,12 @@ def workload_seq_lens(index: int, seed: Optional[int] = None) -> np.ndarray:
 
 
 def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
-                  placement: str = "random") -> DecodeBatch:
-    """Inputs of workload ``index`` (for workload 3: of layer ``layer``)."""
+                  placement: str = "random", append: Optional[bool] = None) -> DecodeBatch:
+    """Inputs of workload ``index`` (for workload 3: of layer ``layer``).
+
+    ``append`` overrides whether the last token of every sequence is held
+    back for an append (default: workloads 3 and 5 append, the others not).
+    """
     seed = index if seed is None else seed
     lens = workload_seq_lens(index, seed)
     name = f"w{index}"
@@ -265,7 +272,7 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
                           placement=placement)
     if index == 4:
         return make_batch(lens, 256 * MAX_BLOCKS, [seed, 1], name=name, recipe=recipe,
-                          placement=placement)
+                          placement=placement, append=bool(append))
     if index == 5:
         need = int(sum(pages_for(L) for L in lens))
         pool = need + (need + 9) // 10
