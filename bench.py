@@ -10,10 +10,12 @@ seeded-random places in a pool of exactly 32,768 pages; synthetic BF16
 N(0, 1) data.
 
 Timing: the inputs are resident in HBM before the timed region.  Before each
-step a 512 MiB buffer is overwritten so the step starts with cold L2 and
-Infinity Cache (the flush is outside the per-step events); HIP events on the
-stream the kernels run on bracket the append, the main attention kernel and
-the merge kernel of every step.  Prints one JSON line.
+step a separate 1 GiB buffer is read (a reduction), so the step starts with
+L2 and Infinity Cache holding none of its inputs; the flush only reads, so it
+leaves no dirty lines whose write-back would land inside the next step.  HIP
+events on the stream the kernels run on bracket the append, the main
+attention kernel and the merge kernel of every step (the flush is outside
+them).  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -78,10 +80,12 @@ def cpu_baseline(batch, gpu_out, seconds: float):
     try:
         k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new,
                                         batch.block_tables, batch.seq_lens)
+        # sequences in batch order, cycling over the batch until the time
+        # budget is spent (the whole batch takes well under a second)
         done, t0 = [], time.perf_counter()
         worst = 0.0
-        while len(done) < batch.batch:
-            b = len(done)
+        while True:
+            b = len(done) % batch.batch
             ref = oracle.decode_attention(batch.q, k_ref, v_ref, batch.block_tables,
                                           batch.seq_lens, batch.scale, sequences=[b])
             worst = max(worst, float(np.max(np.abs(ref[b] - gpu_out[b]))))
@@ -96,9 +100,9 @@ def cpu_baseline(batch, gpu_out, seconds: float):
     kv = tokens * 2048
     return {
         "value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"first {len(done)} of {batch.batch} sequences ({tokens} tokens, "
-                   f"{kv / 2**20:.0f} MiB of K/V), float64 NumPy, 1 BLAS thread, "
-                   f"{dt:.1f} s"),
+        "sample": (f"{len(done)} sequence decodes cycling over the {batch.batch} sequences "
+                   f"({tokens} tokens, {kv / 2**20:.0f} MiB of K/V), float64 NumPy, "
+                   f"1 BLAS thread, {dt:.1f} s"),
         "seq_per_s": round(len(done) / dt, 3),
         "host_cpus": os.cpu_count(),
         "max_abs_vs_gpu_on_sample": worst,
@@ -115,6 +119,9 @@ def main() -> int:
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a 256 MiB device copy per step (outside the timed events), "
+                         "the known-size reference for hardware byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -151,49 +158,72 @@ def main() -> int:
     ws_bytes = pa.decode_workspace_bytes(B, msl, batch.num_pages, 128, ps)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, 32, 64), dtype=torch.float32, device=dev)
-    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(2**28, dtype=torch.int32, device=dev)       # 1 GiB, read only
+    flush_out = torch.empty((), dtype=torch.int32, device=dev)
+
+    def flush():
+        torch.amax(flush_buf, dim=None, out=flush_out)
     stream = torch.cuda.current_stream()
     log(f"plan: {ps} pages per split, {ns} splits; workspace {ws_bytes} B")
+    if args.calibration_copy:
+        copy_src = torch.ones(2**26, dtype=torch.int32, device=dev)     # 256 MiB
+        copy_dst = torch.empty_like(copy_src)
 
     K, Wm = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for row in ev:                      # create the HIP events before the timed region
-        row[2].record(stream)
-    scratch_mid = torch.cuda.Event(enable_timing=True)
-    scratch_mid.record(stream)
 
     def step(marks=None):
-        if marks:
-            marks[0].record(stream)
         pa.append_kv(k_new, v_new, k_pool, v_pool, bt, lens, stream=stream)
         if marks:
-            marks[1].record(stream)
+            marks[0].record(stream)
         pa.decode_attention(q, k_pool, v_pool, bt, lens, msl, scale=batch.scale, out=out,
                             pages_per_split=ps, workspace=workspace, stream=stream,
-                            event_after_main=marks[2] if marks else scratch_mid)
-        if marks:
-            marks[3].record(stream)
+                            event_before_main=marks[1] if marks else None,
+                            event_after_main=marks[2] if marks else None)
+
+    def pre_step():
+        if args.calibration_copy:
+            copy_dst.copy_(copy_src)
+        if not args.no_flush:
+            flush()
 
     for i in range(Wm):
-        if not args.no_flush:
-            flush.fill_(i & 0xFF)
+        pre_step()
         step()
     torch.cuda.synchronize()
     log(f"{Wm} warmup steps done")
 
+    # pass A (the timed K steps): one event pair around each whole step
+    evA = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
-        if not args.no_flush:
-            flush.fill_((i + 7) & 0xFF)
-        step(ev[i])
+        pre_step()
+        evA[i][0].record(stream)
+        step()
+        evA[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    log(f"{K} timed steps done in {wall:.3f} s wall (flushes included)")
+    log(f"{K} timed steps done in {wall:.3f} s wall (cache flushes included)")
 
-    t_app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    t_main = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
-    t_step = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e-3
+    # pass B (K more steps, per-kernel breakdown): [0] start, [1] after append,
+    # [2]/[3] recorded by the library right before / after the main kernel,
+    # [4] end (after the merge kernel, if any)
+    evB = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    for row in evB:                     # create the HIP events before use
+        row[2].record(stream)
+        row[3].record(stream)
+    for i in range(K):
+        pre_step()
+        evB[i][0].record(stream)
+        step(marks=[evB[i][1], evB[i][2], evB[i][3]])
+        evB[i][4].record(stream)
+    torch.cuda.synchronize()
+    log(f"{K} breakdown steps done")
+
+    t_step = np.array([e[0].elapsed_time(e[1]) for e in evA]) * 1e-3
+    t_app = np.array([e[0].elapsed_time(e[1]) for e in evB]) * 1e-3
+    t_main = np.array([e[2].elapsed_time(e[3]) for e in evB]) * 1e-3
+    t_merge = np.array([e[3].elapsed_time(e[4]) for e in evB]) * 1e-3
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
     mean_step = float(t_step.mean())
@@ -223,16 +253,17 @@ def main() -> int:
         },
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "seq_per_s_per_layer": round(B / mean_step, 1),
-        "kv_gbps_attention_only": round(kv / float((t_main + t_merge).mean()) / 1e9, 2),
+        "kv_gbps_main_kernel": round(kv / float(t_main.mean()) / 1e9, 2),
         "algorithmic_bytes_per_step": by,
         "times_us": {
-            "append": round(float(t_app.mean()) * 1e6, 2),
-            "attention_main": round(float(t_main.mean()) * 1e6, 2),
-            "merge": round(float(t_merge.mean()) * 1e6, 2),
             "step": round(mean_step * 1e6, 2),
             "step_min": round(float(t_step.min()) * 1e6, 2),
             "step_median": round(float(np.median(t_step)) * 1e6, 2),
             "wall_per_step_incl_flush": round(wall / K * 1e6, 2),
+            "breakdown_append": round(float(t_app.mean()) * 1e6, 2),
+            "breakdown_attention_main": round(float(t_main.mean()) * 1e6, 2),
+            "breakdown_merge": round(float(t_merge.mean()) * 1e6, 2),
+            "breakdown_note": "second pass with events between kernels; each event adds a few us",
         },
         "roofline": {
             "bound": "hbm",

@@ -113,7 +113,7 @@ int pa_append_kv(const pa_shape* shape, int32_t batch,
  * Workspace needed by pa_decode_attention for these arguments, in bytes
  * (0 when every sequence fits one split).  pages_per_split is 0 to let the
  * library plan (the plan then depends on the current device's compute-unit
- * count) or a fixed split size in pages, 1 .. max_blocks_per_seq.
+ * count) or a fixed split size in pages, 1 .. min(max_blocks_per_seq, 256).
  * Returns PA_OK and stores the size in *bytes.
  */
 int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch,
@@ -152,11 +152,12 @@ int pa_decode_attention(const pa_shape* shape, int32_t batch,
                         void* stream);
 
 /*
- * pa_decode_attention plus a timing hook: when event_after_main (a
- * hipEvent_t created by the caller) is not NULL it is recorded on `stream`
- * right after the main attention kernel is enqueued and before the split
- * merge kernel, so that a caller's events before and after the call time the
- * two kernels separately.  Same arguments, checks and results otherwise.
+ * pa_decode_attention plus timing hooks: event_before_main and
+ * event_after_main (hipEvent_t handles created by the caller; either may be
+ * NULL) are recorded on `stream` immediately before and after the main
+ * attention kernel is enqueued, i.e. before the split merge kernel, so the
+ * pair times the main kernel alone and an event after the call times the
+ * merge.  Same arguments, checks and results otherwise.
  */
 int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
                                  const void* q, const void* k_pool, const void* v_pool,
@@ -165,7 +166,8 @@ int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
                                  void* out, int32_t out_dtype,
                                  int32_t pages_per_split,
                                  void* workspace, size_t workspace_bytes,
-                                 void* stream, void* event_after_main);
+                                 void* stream, void* event_before_main,
+                                 void* event_after_main);
 
 /*
  * Debug check of device-resident metadata: copies block_tables and

@@ -59,7 +59,7 @@ def load_library(path: str | None = None):
         lib.pa_decode_plan.argtypes = [SP, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         lib.pa_decode_attention.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float,
                                             P, I32, I32, P, SZ, P]
-        lib.pa_decode_attention_profiled.argtypes = lib.pa_decode_attention.argtypes + [P]
+        lib.pa_decode_attention_profiled.argtypes = lib.pa_decode_attention.argtypes + [P, P]
         lib.pa_validate_metadata.argtypes = [SP, I32, P, P, I32, P, ctypes.POINTER(ctypes.c_int64)]
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
@@ -151,7 +151,7 @@ def decode_workspace_bytes(batch: int, max_seq_len: int, num_pages: int,
 def decode_attention(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int,
                      scale: float = 0.125, out=None, out_dtype=torch.float32,
                      pages_per_split: int = 0, workspace=None, stream=None,
-                     event_after_main=None):
+                     event_before_main=None, event_after_main=None):
     """Paged GQA decode attention; returns ``out`` ``[B][32][64]``.
 
     ``workspace`` may be passed (a uint8 device tensor of at least
@@ -183,14 +183,17 @@ def decode_attention(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int
             _ptr(seq_lens), int(max_seq_len), float(scale), _ptr(out), code,
             int(pages_per_split), _ptr(workspace), ws_bytes, _stream_ptr(stream)]
     lib = load_library()
-    if event_after_main is None:
+    if event_before_main is None and event_after_main is None:
         rc = lib.pa_decode_attention(*args)
     else:
-        # a torch.cuda.Event: its HIP event exists once it has been recorded
-        handle = event_after_main.cuda_event
-        if not handle:
-            raise ValueError("record event_after_main once before passing it")
-        rc = lib.pa_decode_attention_profiled(*args, ctypes.c_void_p(handle))
+        # torch.cuda.Event objects: a HIP event exists once it has been recorded
+        handles = []
+        for ev in (event_before_main, event_after_main):
+            h = ev.cuda_event if ev is not None else 0
+            if ev is not None and not h:
+                raise ValueError("record each timing event once before passing it")
+            handles.append(ctypes.c_void_p(h or None))
+        rc = lib.pa_decode_attention_profiled(*args, *handles)
     _check(rc, "pa_decode_attention")
     return out
 

@@ -47,14 +47,16 @@ int check_shape(const pa_shape* s) {
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Split size in pages.  With `fixed` != 0 that size is used as given.
-// Otherwise: enough work-groups to give every compute unit about two
-// (sequences x splits >= 2 x CUs), but never splits shorter than 8 pages
-// (128 tokens), so the partial results stay a small fraction of the bytes.
+// Otherwise: at least one work-group per compute unit (sequences x splits >=
+// CUs; a work-group holds a whole CU's worth of waves and LDS ring), but
+// never splits shorter than 8 pages (128 tokens), so the partial results stay
+// a small fraction of the bytes.
 int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pages, int* splits) {
   const int max_pages = ceil_div(max_seq_len, pa::kPage);
   int ps;
   if (fixed != 0) {
-    if (fixed < 1 || fixed > s->max_blocks_per_seq) return PA_ERR_VALUE;
+    if (fixed < 1 || fixed > s->max_blocks_per_seq || fixed > pa::kMaxSplitPages)
+      return PA_ERR_VALUE;
     ps = fixed;
   } else {
     if (max_pages <= 8 || batch <= 0) {
@@ -63,11 +65,12 @@ int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pa
       int cu = 0;
       const int rc = current_cu_count(&cu);
       if (rc != PA_OK) return rc;
-      const int want = ceil_div(2 * cu, batch);               // splits per sequence wanted
+      const int want = ceil_div(cu, batch);                   // splits per sequence wanted
       const int cap = ceil_div(max_pages, 8);                 // >= 8 pages per split
       const int ns = want < 1 ? 1 : (want > cap ? cap : want);
       ps = ceil_div(max_pages, ns);
     }
+    if (ps > pa::kMaxSplitPages) ps = pa::kMaxSplitPages;
   }
   *pages = ps;
   *splits = max_pages > 0 ? ceil_div(max_pages, ps) : 1;
@@ -155,7 +158,7 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
                 const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                 int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
                 int32_t pages_per_split, void* workspace, size_t workspace_bytes,
-                void* stream, void* event_after_main) {
+                void* stream, void* event_before_main, void* event_after_main) {
   int rc = check_decode_sizes(shape, batch, max_seq_len);
   if (rc != PA_OK) return rc;
   if (out_dtype != PA_OUT_F32 && out_dtype != PA_OUT_BF16) return PA_ERR_VALUE;
@@ -196,6 +199,8 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
 
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid(ns, batch);
+  if (event_before_main && hipEventRecord((hipEvent_t)event_before_main, st) != hipSuccess)
+    return PA_ERR_LAUNCH;
   if (out_dtype == PA_OUT_BF16)
     hipLaunchKernelGGL(pa::decode_kernel<true>, grid, dim3(pa::kThreads), 0, st, a);
   else
@@ -222,7 +227,7 @@ PA_API int pa_decode_attention(const pa_shape* shape, int32_t batch, const void*
                                void* stream) {
   return decode_impl(shape, batch, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
                      scale, out, out_dtype, pages_per_split, workspace, workspace_bytes, stream,
-                     nullptr);
+                     nullptr, nullptr);
 }
 
 PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, const void* q,
@@ -231,10 +236,10 @@ PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, co
                                         int32_t max_seq_len, float scale, void* out,
                                         int32_t out_dtype, int32_t pages_per_split,
                                         void* workspace, size_t workspace_bytes, void* stream,
-                                        void* event_after_main) {
+                                        void* event_before_main, void* event_after_main) {
   return decode_impl(shape, batch, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
                      scale, out, out_dtype, pages_per_split, workspace, workspace_bytes, stream,
-                     event_after_main);
+                     event_before_main, event_after_main);
 }
 
 PA_API int pa_validate_metadata(const pa_shape* shape, int32_t batch,

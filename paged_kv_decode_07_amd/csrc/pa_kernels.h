@@ -6,20 +6,37 @@
 //   * 8 wavefronts per work-group, wavefront g serves KV head g and its 4
 //     query heads 4g .. 4g+3 (grouped-query attention: 32 query heads share
 //     8 KV heads);
-//   * inside a wavefront, lane = 4 * token + part: `token` (0..15) is the
+//   * inside a wavefront, lane = 16 * part + token: `token` (0..15) is the
 //     page slot the lane owns, `part` (0..3) selects 16 of the 64 head dims,
 //     {8 part .. 8 part + 7} and {32 + 8 part .. 32 + 8 part + 7}.  One load
-//     instruction of a wavefront therefore reads, for 16 tokens, 64
-//     contiguous bytes of the 128-byte row of its KV head, and the 8
-//     wavefronts of a work-group together read every byte of each 16 KiB K
-//     page and 16 KiB V page.
+//     instruction of a wavefront reads, for 16 tokens, 64 contiguous bytes
+//     of the 128-byte row of its KV head, and the 8 wavefronts of a
+//     work-group together read every byte of each 16 KiB K page and 16 KiB
+//     V page.
+//
+// Page stream: each wavefront keeps a ring of kRing page slots in LDS (4 KiB
+// each: its 2 KiB slice of the K page and of the V page).  Pages are fetched
+// with gfx950's direct-to-LDS loads (global_load_lds_dwordx4: every lane's
+// 16 bytes land at lane*16 of a 1 KiB LDS row, without passing through
+// VGPRs); a slot is refilled as soon as its page has been copied to
+// registers, so while a page is being used the next kRing pages are in
+// flight: kRing x 32 KiB of HBM reads per work-group at a register cost of
+// one page.  A wavefront only ever reads its own ring, so no barrier is needed:
+// explicit vmcnt waits mark a slot as landed and the LDS reads are issued one
+// page ahead of their use.
 //
 // Arithmetic (the FP32 online softmax of the samir-vllm README's paged
 // decode attention, written here for this lane layout):
-//   * scores: q.k over the lane's 16 dims with v_dot2_f32_bf16 (BF16 products
-//     are exact in FP32), summed over the 4 parts of a token with two DPP
-//     quad permutes; x = score * scale * log2(e) so that exp2 is the
-//     hardware v_exp_f32;
+//   * scores: two v_mfma_f32_16x16x32_bf16 per page compute Q' K^T, where
+//     the 16 rows of Q' are the 4 query heads of the group repeated 4 times
+//     and K^T is the page (16 tokens x 64 dims).  With the matrix-core lane
+//     layout (lane l holds row l%16 of the A operand's 8-wide k slice
+//     8*(l/16), column l%16 of B, and rows 4*(l/16)..+3 of column l%16 of
+//     the result) every lane receives the 4 heads' scores of its own token,
+//     which is exactly what its part of P.V needs: no cross-lane reduction.
+//     3/4 of the matrix work is the repetition; the matrix core has the room
+//     and the VALU does not.  BF16 products are exact in FP32.
+//     x = score * scale * log2(e) so that exp2 is the hardware v_exp_f32;
 //   * each lane keeps its own running maximum m, sum l and unnormalised
 //     output acc[4 heads][16 dims] for the tokens of its slot (the online
 //     normaliser of Milakov and Gimelshein, 2018).  The running maximum is
@@ -27,8 +44,9 @@
 //     units); weights are then at most 2^kTau and the rescale of acc is
 //     almost never executed after the first page;
 //   * at the end of the split the 16 token slots are merged with the same
-//     rule (max, rescale, add) across lanes; a single-split sequence writes
-//     acc / l, a longer one writes (m, l, acc) for the merge kernel.
+//     rule (common maximum, rescale, add) by DPP row reductions; a
+//     single-split sequence writes acc / l, a longer one writes (m, l, acc)
+//     for the merge kernel.
 //
 // Masking: slots past the sequence length in its last page (and anything a
 // block table points at beyond the used pages) may hold any bits, NaN
@@ -38,6 +56,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace pa {
 
@@ -52,24 +72,22 @@ constexpr int kWaves = kHkv;                    // one wavefront per KV head
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;                    // lazy-rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef PA_RING_DEPTH
+#define PA_RING_DEPTH 2
+#endif
+#ifndef PA_WG_PER_CU
+#define PA_WG_PER_CU 1
+#endif
+constexpr int kRing = PA_RING_DEPTH;            // LDS page slots per wavefront
+constexpr int kWgPerCu = PA_WG_PER_CU;          // work-groups resident per compute unit
+constexpr int kMaxSplitPages = 256;             // longest split (4096 tokens)
+static_assert(kRing >= 2 && kWgPerCu * kRing * kWaves * 4 * 1024 <= 160 * 1024,
+              "LDS ring too large for the resident work-groups");
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Sum over the 4 lanes of a quad (the 4 dim-parts of one token), result in all 4.
-__device__ __forceinline__ float quad_allsum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
-                                                          0xB1, 0xF, 0xF, true));  // [1,0,3,2]
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
-                                                          0x4E, 0xF, 0xF, true));  // [2,3,0,1]
-  return x;
-}
 
 // Round-to-nearest-even FP32 -> BF16 bits (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -79,9 +97,41 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 struct PageRegs {
-  uint4 k0, k1, v0, v1;
+  u32x4 k0, k1, v0, v1;
 };
+
+// Byte address of an LDS object (what ds_read and M0 expect).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Wait until at most N vector-memory operations of this wavefront are still
+// outstanding (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The four 16-byte LDS rows of one page slot (K lo/hi, V lo/hi) of this lane.
+// Issued without waiting; the registers are valid after lds_page_ready().
+__device__ __forceinline__ void lds_page_issue(PageRegs& r, uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072"
+      : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v0), "=&v"(r.v1)
+      : "v"(addr)
+      : "memory");
+}
+// Wait for the LDS reads (and scalar loads) of this wavefront; ties the
+// registers to the wait so no use is scheduled before it.
+__device__ __forceinline__ void lds_page_ready(PageRegs& r) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.k0), "+v"(r.k1), "+v"(r.v0), "+v"(r.v1)::"memory");
+}
 
 // Running state of one lane: 4 query heads x 16 dims.
 struct LaneState {
@@ -90,33 +140,18 @@ struct LaneState {
   float acc[kGroup][16];
 };
 
-__device__ __forceinline__ PageRegs load_page(const uint16_t* __restrict__ k_pool,
-                                              const uint16_t* __restrict__ v_pool,
-                                              int64_t phys, int lane_off) {
-  const int64_t base = phys * kPageElems + lane_off;
-  PageRegs r;
-  r.k0 = *reinterpret_cast<const uint4*>(k_pool + base);
-  r.k1 = *reinterpret_cast<const uint4*>(k_pool + base + 32);
-  r.v0 = *reinterpret_cast<const uint4*>(v_pool + base);
-  r.v1 = *reinterpret_cast<const uint4*>(v_pool + base + 32);
-  return r;
-}
-
 // One page for one lane.  MASK: tokens at slot >= `valid` are not part of
-// the sequence.
+// the sequence.  qlo/qhi: this lane's rows of Q' (head token%4, dims of part).
 template <bool MASK>
-__device__ __forceinline__ void consume_page(LaneState& st, const PageRegs& r,
-                                             const uint32_t (&q)[kGroup][8], float xscale,
-                                             int token, int valid) {
-  const uint32_t kw[8] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w, r.k1.x, r.k1.y, r.k1.z, r.k1.w};
+__device__ __forceinline__ void consume_page(LaneState& st, const PageRegs& r, bf16x8_t qlo,
+                                             bf16x8_t qhi, float xscale, int token, int valid) {
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo, __builtin_bit_cast(bf16x8_t, r.k0),
+                                                       zero, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi, __builtin_bit_cast(bf16x8_t, r.k1), sc, 0, 0, 0);
   float x[kGroup];
 #pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) s = dot2_bf16(q[j][w], kw[w], s);
-    x[j] = quad_allsum(s) * xscale;
-  }
+  for (int j = 0; j < kGroup; ++j) x[j] = sc[j] * xscale;
   const bool live = !MASK || token < valid;
   bool raise = false;
 #pragma unroll
@@ -154,23 +189,41 @@ __device__ __forceinline__ void consume_page(LaneState& st, const PageRegs& r,
   }
 }
 
-// Merge lane state with the lane `mask` away (xor); symmetric, so both lanes
-// of a pair end with the same sums.
-__device__ __forceinline__ void merge_lanes(LaneState& st, int mask) {
+// All-reduce over the 16 lanes of a row (the 16 token slots of one dim
+// part) with DPP: quad permutes, then rotations by 4 and 8 within the row.
+// Pure VALU; every lane of the row ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_allsum(float x) {
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x124>(x);   // row_ror:4
+  x += dpp_mov<0x128>(x);   // row_ror:8
+  return x;
+}
+__device__ __forceinline__ float row_allmax(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x124>(x));
+  x = fmaxf(x, dpp_mov<0x128>(x));
+  return x;
+}
+
+// Combine the 16 token slots of a row: rescale every slot to the row's
+// largest running maximum, then sum l and acc over the row (the same merge
+// rule as for split partials, applied 16 ways at once).
+__device__ __forceinline__ void merge_token_slots(LaneState& st) {
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) {
-    const float mo = __shfl_xor(st.m[j], mask);
-    const float lo = __shfl_xor(st.l[j], mask);
-    const float mn = fmaxf(st.m[j], mo);
-    const float fa = (st.m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m[j] - mn);
-    const float fb = (mo == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
-    st.l[j] = fa * st.l[j] + fb * lo;
+    const float M = row_allmax(st.m[j]);
+    const float f = (st.m[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m[j] - M);
+    st.l[j] = row_allsum(st.l[j] * f);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float ao = __shfl_xor(st.acc[j][e], mask);
-      st.acc[j][e] = fa * st.acc[j][e] + fb * ao;
-    }
-    st.m[j] = mn;
+    for (int e = 0; e < 16; ++e) st.acc[j][e] = row_allsum(st.acc[j][e] * f);
+    st.m[j] = M;
   }
 }
 
@@ -224,13 +277,14 @@ struct DecodeArgs {
 };
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+// second bound: minimum waves per SIMD (a work-group puts 2 on each SIMD)
+__global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeArgs a) {
   const int s = blockIdx.x;
   const int b = blockIdx.y;
-  const int g = threadIdx.x >> 6;      // KV head of this wavefront
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wavefront
   const int lane = threadIdx.x & 63;
-  const int token = lane >> 2;
-  const int part = lane & 3;
+  const int token = lane & 15;
+  const int part = lane >> 4;
 
   const int L = a.seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
@@ -255,15 +309,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int tail_valid = L - last * kPage;           // 1..16 tokens valid in page `last`
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
 
-  // query rows of the 4 heads of this group, this lane's 16 dims, as BF16 pairs
-  uint32_t q[kGroup][8];
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + j) * kD + 8 * part;
-    const uint4 lo = *reinterpret_cast<const uint4*>(qr);
-    const uint4 hi = *reinterpret_cast<const uint4*>(qr + 32);
-    q[j][0] = lo.x; q[j][1] = lo.y; q[j][2] = lo.z; q[j][3] = lo.w;
-    q[j][4] = hi.x; q[j][5] = hi.y; q[j][6] = hi.z; q[j][7] = hi.w;
+  // this lane's rows of Q': head 4g + token%4, dims {8 part..+7} and {32 + 8 part..+7}
+  bf16x8_t qlo, qhi;
+  {
+    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (token & 3)) * kD + 8 * part;
+    qlo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr));
+    qhi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr + 32));
   }
 
   LaneState st;
@@ -276,36 +327,71 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   const int lane_off = token * kRowElems + g * kD + 8 * part;
+  // The split's block-table entries (at most kMaxSplitPages) are loaded once
+  // into VGPRs, entry j of the split in lane j%64 of ent[j/64], and picked
+  // with v_readlane: no memory access for page ids inside the page stream.
+  int ent[kMaxSplitPages / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
+    const int j = p0 + c * 64 + lane;
+    ent[c] = (c * 64 < p1 - p0 && j <= last) ? bt[j] : 0;
+  }
   bool bad_page = false;
-  auto page_id = [&](int i) -> int64_t {
-    const int id = bt[i];
+  auto page_id = [&](int i) -> int64_t {          // i: logical page, p0 <= i <= last
+    const int j = i - p0;
+    int id = __builtin_amdgcn_readlane(ent[0], j & 63);
+#pragma unroll
+    for (int c = 1; c < kMaxSplitPages / 64; ++c)
+      if ((j >> 6) == c) id = __builtin_amdgcn_readlane(ent[c], j & 63);
     const bool ok = (unsigned)id < (unsigned)a.num_pages;
     bad_page |= !ok;
     return ok ? id : 0;
   };
 
-  // double-buffered page stream: page i+1 is in flight while page i is used
-  PageRegs A = load_page(a.k_pool, a.v_pool, page_id(p0), lane_off);
-  for (int i = p0;; i += 2) {
-    PageRegs B = load_page(a.k_pool, a.v_pool, page_id(min(i + 1, last)), lane_off);
-    if (i == last && tail_valid < kPage)
-      consume_page<true>(st, A, q, a.xscale, token, tail_valid);
-    else
-      consume_page<false>(st, A, q, a.xscale, token, kPage);
-    if (i + 1 > last) break;
-    A = load_page(a.k_pool, a.v_pool, page_id(min(i + 2, last)), lane_off);
-    if (i + 1 == last && tail_valid < kPage)
-      consume_page<true>(st, B, q, a.xscale, token, tail_valid);
-    else
-      consume_page<false>(st, B, q, a.xscale, token, kPage);
-    if (i + 2 > last) break;
-  }
+  // LDS ring: slot r of wavefront g holds rows [K lo, K hi, V lo, V hi] x 64 lanes x 16 B
+  __shared__ uint4 ring[kRing][kWaves][4][64];
+  const uint32_t lane_bytes = 2u * lane_off;         // byte offset of this lane in a page
+  const char* k_base = reinterpret_cast<const char*>(a.k_pool);
+  const char* v_base = reinterpret_cast<const char*>(a.v_pool);
+  auto fetch = [&](int page, int slot) {            // 4 direct-to-LDS loads
+    const int64_t off = page_id(page) * (int64_t)(kPageElems * 2);   // uniform
+    const char* kp = k_base + off;
+    const char* vp = v_base + off;
+    __builtin_amdgcn_global_load_lds(kp + lane_bytes, &ring[slot][g][0][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kp + lane_bytes + 64, &ring[slot][g][1][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + lane_bytes, &ring[slot][g][2][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + lane_bytes + 64, &ring[slot][g][3][0], 16, 0, 0);
+  };
+  const uint32_t my_row = lds_address(&ring[0][g][0][lane]);
+  constexpr uint32_t kSlotBytes = kWaves * 4 * 64 * 16;
 
-  // merge the 16 token slots (lane bits 2..5)
-  merge_lanes(st, 4);
-  merge_lanes(st, 8);
-  merge_lanes(st, 16);
-  merge_lanes(st, 32);
+  // One page of the stream: wait for page i, copy it from its slot to
+  // registers, refill that slot with page i+kRing right away (so kRing pages
+  // stay in flight while page i is used), then use it.
+  auto step = [&](int i, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    const int slot = (i - p0) % kRing;
+    wait_vmem<4 * (kRing - 1)>();                   // page i has landed
+    PageRegs cur;
+    lds_page_issue(cur, my_row + slot * kSlotBytes);
+    lds_page_ready(cur);
+    fetch(min(i + kRing, last), slot);
+    consume_page<MASK>(st, cur, qlo, qhi, a.xscale, token, MASK ? tail_valid : kPage);
+  };
+
+  // prologue: pages p0 .. p0+kRing-1 in flight (clamped to the split's last
+  // page, so the count of outstanding loads is the same on every path)
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) fetch(min(p0 + r, last), r);
+  // full pages in the loop, a partial last page peeled off after it, so the
+  // loop body has a single path and its accumulators stay in place
+  const int full_end = (tail_valid < kPage) ? last : last + 1;
+  for (int i = p0; i < full_end; ++i) step(i, std::false_type{});
+  if (full_end == last) step(last, std::true_type{});
+  wait_vmem<0>();                                   // drain the clamped extra fetches
+
+  // merge the 16 token slots (lane bits 0..3: one DPP row)
+  merge_token_slots(st);
 
   if (bad_page) {
     // a block-table entry outside the pool: nothing was read from it; the
