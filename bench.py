@@ -2,20 +2,23 @@
 """Benchmark of the paged GQA decode hot path on one MI355X.
 
 One step = one layer's decode step of the full-context batch: the one-token
-page append of every sequence, then paged GQA decode attention (32 query
-heads over 8 KV heads, head_dim 64, BF16 K/V in 16-token pages, FP32 online
-softmax) including the split merge.  Workload: batch 256, every sequence
-2,048 tokens after the append (128 pages each, 1 GiB of K/V), pages at
-seeded-random places in a pool of exactly 32,768 pages; synthetic BF16
-N(0, 1) data.
+page append of every sequence and paged GQA decode attention (32 query heads
+over 8 KV heads, head_dim 64, BF16 K/V in 16-token pages, FP32 online
+softmax), including the split merge when the plan has one.  The step is the
+library's fused single-launch call (pa_append_decode_attention); the same
+step as two calls (pa_append_kv then pa_decode_attention) is timed as well.
+Workload: batch 256, every sequence 2,048 tokens after the append (128 pages
+each, 1 GiB of K/V), pages at seeded-random places in a pool of exactly
+32,768 pages; synthetic BF16 N(0, 1) data.
 
 Timing: the inputs are resident in HBM before the timed region.  Before each
 step a separate 1 GiB buffer is read (a reduction), so the step starts with
 L2 and Infinity Cache holding none of its inputs; the flush only reads, so it
-leaves no dirty lines whose write-back would land inside the next step.  HIP
-events on the stream the kernels run on bracket the append, the main
-attention kernel and the merge kernel of every step (the flush is outside
-them).  Prints one JSON line.
+leaves no dirty lines whose write-back would land inside the next step.
+Pass A times the K steps with one event pair around each step; pass B
+repeats them with the library recording events right around its main
+kernel (the roofline figure); pass C times the two-call form.  The flush is
+outside every event pair.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -172,13 +175,16 @@ def main() -> int:
     K, Wm = args.steps, args.warmup
 
     def step(marks=None):
+        pa.append_decode_attention(q, k_new, v_new, k_pool, v_pool, bt, lens, msl,
+                                   scale=batch.scale, out=out, pages_per_split=ps,
+                                   workspace=workspace, stream=stream,
+                                   event_before_main=marks[0] if marks else None,
+                                   event_after_main=marks[1] if marks else None)
+
+    def two_call_step():
         pa.append_kv(k_new, v_new, k_pool, v_pool, bt, lens, stream=stream)
-        if marks:
-            marks[0].record(stream)
         pa.decode_attention(q, k_pool, v_pool, bt, lens, msl, scale=batch.scale, out=out,
-                            pages_per_split=ps, workspace=workspace, stream=stream,
-                            event_before_main=marks[1] if marks else None,
-                            event_after_main=marks[2] if marks else None)
+                            pages_per_split=ps, workspace=workspace, stream=stream)
 
     def pre_step():
         if args.calibration_copy:
@@ -189,41 +195,41 @@ def main() -> int:
     for i in range(Wm):
         pre_step()
         step()
+        pre_step()
+        two_call_step()
     torch.cuda.synchronize()
     log(f"{Wm} warmup steps done")
 
-    # pass A (the timed K steps): one event pair around each whole step
-    evA = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    def timed(fn, n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(n):
+            pre_step()
+            evs[i][0].record(stream)
+            fn()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+
+    # pass A (the timed K steps)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(K):
-        pre_step()
-        evA[i][0].record(stream)
-        step()
-        evA[i][1].record(stream)
-    torch.cuda.synchronize()
+    t_step = timed(step, K)
     wall = time.perf_counter() - wall0
     log(f"{K} timed steps done in {wall:.3f} s wall (cache flushes included)")
 
-    # pass B (K more steps, per-kernel breakdown): [0] start, [1] after append,
-    # [2]/[3] recorded by the library right before / after the main kernel,
-    # [4] end (after the merge kernel, if any)
-    evB = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    # pass B: events recorded by the library right before / after its main kernel
+    evB = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for row in evB:                     # create the HIP events before use
-        row[2].record(stream)
-        row[3].record(stream)
+        row[0].record(stream)
+        row[1].record(stream)
     for i in range(K):
         pre_step()
-        evB[i][0].record(stream)
-        step(marks=[evB[i][1], evB[i][2], evB[i][3]])
-        evB[i][4].record(stream)
+        step(marks=evB[i])
     torch.cuda.synchronize()
-    log(f"{K} breakdown steps done")
-
-    t_step = np.array([e[0].elapsed_time(e[1]) for e in evA]) * 1e-3
-    t_app = np.array([e[0].elapsed_time(e[1]) for e in evB]) * 1e-3
-    t_main = np.array([e[2].elapsed_time(e[3]) for e in evB]) * 1e-3
-    t_merge = np.array([e[3].elapsed_time(e[4]) for e in evB]) * 1e-3
+    t_main = np.array([e[0].elapsed_time(e[1]) for e in evB]) * 1e-3
+    # pass C: the same step as two calls
+    t_two = timed(two_call_step, K)
+    log(f"{K} breakdown steps and {K} two-call steps done")
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
     mean_step = float(t_step.mean())
@@ -245,7 +251,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "paged GQA decode, 1 layer, batch 256 x 2048 tokens (1 GiB BF16 K/V), "
-                        "append + attention",
+                        "fused append + attention",
             "global_batch": B, "seq_len": msl, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
             "page_tokens": 16, "num_pages": batch.num_pages, "placement": args.placement,
             "pages_per_split": ps, "splits": ns, "out_dtype": "f32",
@@ -260,14 +266,13 @@ def main() -> int:
             "step_min": round(float(t_step.min()) * 1e6, 2),
             "step_median": round(float(np.median(t_step)) * 1e6, 2),
             "wall_per_step_incl_flush": round(wall / K * 1e6, 2),
-            "breakdown_append": round(float(t_app.mean()) * 1e6, 2),
-            "breakdown_attention_main": round(float(t_main.mean()) * 1e6, 2),
-            "breakdown_merge": round(float(t_merge.mean()) * 1e6, 2),
-            "breakdown_note": "second pass with events between kernels; each event adds a few us",
+            "main_kernel": round(float(t_main.mean()) * 1e6, 2),
+            "two_call_step": round(float(t_two.mean()) * 1e6, 2),
         },
+        "two_call_kv_gbps": round(kv / float(t_two.mean()) / 1e9, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa::decode_kernel",
+            "kernel": "pa::decode_kernel (append fused)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

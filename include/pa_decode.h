@@ -152,15 +152,37 @@ int pa_decode_attention(const pa_shape* shape, int32_t batch,
                         void* stream);
 
 /*
- * pa_decode_attention plus timing hooks: event_before_main and
- * event_after_main (hipEvent_t handles created by the caller; either may be
- * NULL) are recorded on `stream` immediately before and after the main
- * attention kernel is enqueued, i.e. before the split merge kernel, so the
- * pair times the main kernel alone and an event after the call times the
- * merge.  Same arguments, checks and results otherwise.
+ * Fused decode step: the effect of pa_append_kv followed by
+ * pa_decode_attention with the same arguments, in one launch (plus the split
+ * merge when the plan has several splits).  The work-group that owns each
+ * sequence's last page writes the new K/V row (k_new[b], v_new[b]) into slot
+ * (L-1)%16 of page block_tables[b][(L-1)/16] and takes that token's K/V from
+ * registers.  Pools end bit-identical to the two-call sequence and outputs
+ * are identical too.  Same layouts, alignment and error rules as the two
+ * calls; k_new and v_new are required when batch > 0.
+ */
+int pa_append_decode_attention(const pa_shape* shape, int32_t batch,
+                               const void* q, const void* k_new, const void* v_new,
+                               void* k_pool, void* v_pool,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t max_seq_len, float scale,
+                               void* out, int32_t out_dtype,
+                               int32_t pages_per_split,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * pa_decode_attention (k_new = v_new = NULL) or pa_append_decode_attention
+ * (both non-NULL) plus timing hooks: event_before_main and event_after_main
+ * (hipEvent_t handles created by the caller; either may be NULL) are
+ * recorded on `stream` immediately before and after the main kernel is
+ * enqueued, i.e. before the split merge kernel, so the pair times the main
+ * kernel alone and an event after the call times the merge.  Same
+ * arguments, checks and results otherwise.
  */
 int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
-                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 void* k_pool, void* v_pool,
                                  const int32_t* block_tables, const int32_t* seq_lens,
                                  int32_t max_seq_len, float scale,
                                  void* out, int32_t out_dtype,

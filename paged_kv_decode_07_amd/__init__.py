@@ -6,7 +6,7 @@ Importing the package loads nothing; the library is opened on first use and a
 missing library raises instead of falling back to anything else.
 """
 
-__all__ = ["append_kv", "decode_attention", "decode_workspace_bytes",
+__all__ = ["append_kv", "decode_attention", "append_decode_attention", "decode_workspace_bytes",
            "validate_metadata", "status_string", "load_library"]
 
 

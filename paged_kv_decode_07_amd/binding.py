@@ -25,7 +25,7 @@ HQ, HKV, D, PAGE = 32, 8, 64, 16
 
 # names declared in include/pa_decode.h
 EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
-           "pa_decode_attention", "pa_decode_attention_profiled",
+           "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
            "pa_validate_metadata", "pa_status_string", "pa_abi_version")
 
 
@@ -59,14 +59,17 @@ def load_library(path: str | None = None):
         lib.pa_decode_plan.argtypes = [SP, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         lib.pa_decode_attention.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float,
                                             P, I32, I32, P, SZ, P]
-        lib.pa_decode_attention_profiled.argtypes = lib.pa_decode_attention.argtypes + [P, P]
+        lib.pa_decode_attention_profiled.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
+                                                     ctypes.c_float, P, I32, I32, P, SZ, P, P, P]
+        lib.pa_append_decode_attention.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
+                                                   ctypes.c_float, P, I32, I32, P, SZ, P]
         lib.pa_validate_metadata.argtypes = [SP, I32, P, P, I32, P, ctypes.POINTER(ctypes.c_int64)]
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_abi_version.argtypes = []
         for name in ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
                      "pa_decode_attention", "pa_decode_attention_profiled",
-                     "pa_validate_metadata", "pa_abi_version"):
+                     "pa_append_decode_attention", "pa_validate_metadata", "pa_abi_version"):
             getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
@@ -86,6 +89,20 @@ def _stream_ptr(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _event_handles(*events):
+    """HIP event handles of torch.cuda.Event objects (None passes NULL).
+
+    A torch event owns a HIP event only once it has been recorded.
+    """
+    handles = []
+    for ev in events:
+        h = ev.cuda_event if ev is not None else 0
+        if ev is not None and not h:
+            raise ValueError("record each timing event once before passing it")
+        handles.append(ctypes.c_void_p(h or None))
+    return handles
 
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
@@ -186,15 +203,54 @@ def decode_attention(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int
     if event_before_main is None and event_after_main is None:
         rc = lib.pa_decode_attention(*args)
     else:
-        # torch.cuda.Event objects: a HIP event exists once it has been recorded
-        handles = []
-        for ev in (event_before_main, event_after_main):
-            h = ev.cuda_event if ev is not None else 0
-            if ev is not None and not h:
-                raise ValueError("record each timing event once before passing it")
-            handles.append(ctypes.c_void_p(h or None))
-        rc = lib.pa_decode_attention_profiled(*args, *handles)
+        rc = lib.pa_decode_attention_profiled(*args[:3], None, None, *args[3:],
+                                              *_event_handles(event_before_main,
+                                                              event_after_main))
     _check(rc, "pa_decode_attention")
+    return out
+
+
+def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                            max_seq_len: int, scale: float = 0.125, out=None,
+                            out_dtype=torch.float32, pages_per_split: int = 0, workspace=None,
+                            stream=None, event_before_main=None, event_after_main=None):
+    """One decode step in one launch: append each sequence's new K/V row, then attend.
+
+    Same result as ``append_kv`` followed by ``decode_attention``; returns ``out``.
+    """
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if q.shape[0] != B or block_tables.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    num_pages, max_blocks = int(k_pool.shape[0]), int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][32][64] tensor of out_dtype")
+    need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    shape = make_shape(num_pages, max_blocks)
+    args = [ctypes.byref(shape), B, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+            _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), float(scale),
+            _ptr(out), code, int(pages_per_split), _ptr(workspace), ws_bytes,
+            _stream_ptr(stream)]
+    lib = load_library()
+    if event_before_main is None and event_after_main is None:
+        rc = lib.pa_append_decode_attention(*args)
+    else:
+        rc = lib.pa_decode_attention_profiled(*args, *_event_handles(event_before_main,
+                                                                      event_after_main))
+    _check(rc, "pa_append_decode_attention")
     return out
 
 

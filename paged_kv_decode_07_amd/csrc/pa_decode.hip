@@ -154,7 +154,9 @@ PA_API int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch, int32
 }
 
 namespace {
-int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_pool,
+// k_new/v_new non-NULL: the one-token append is fused into the main kernel
+int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_new,
+                const void* v_new, const void* k_pool,
                 const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                 int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
                 int32_t pages_per_split, void* workspace, size_t workspace_bytes,
@@ -165,8 +167,11 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   if (!std::isfinite(scale)) return PA_ERR_VALUE;
   if (batch == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_ERR_NULL;
+  const bool fused = k_new != nullptr || v_new != nullptr;
+  if (fused && (!k_new || !v_new)) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) ||
+      (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))))
     return PA_ERR_ALIGN;
   if (shape->num_pages < 1 && max_seq_len > 0) return PA_ERR_VALUE;
   int ps = 0, ns = 0;
@@ -183,6 +188,10 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.q = (const uint16_t*)q;
   a.k_pool = (const uint16_t*)k_pool;
   a.v_pool = (const uint16_t*)v_pool;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_pool_w = (uint16_t*)k_pool;
+  a.v_pool_w = (uint16_t*)v_pool;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = out;
@@ -201,10 +210,14 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   const dim3 grid(ns, batch);
   if (event_before_main && hipEventRecord((hipEvent_t)event_before_main, st) != hipSuccess)
     return PA_ERR_LAUNCH;
-  if (out_dtype == PA_OUT_BF16)
-    hipLaunchKernelGGL(pa::decode_kernel<true>, grid, dim3(pa::kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(pa::decode_kernel<false>, grid, dim3(pa::kThreads), 0, st, a);
+  const dim3 block(pa::kThreads);
+  if (out_dtype == PA_OUT_BF16) {
+    if (fused) hipLaunchKernelGGL((pa::decode_kernel<true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((pa::decode_kernel<true, false>), grid, block, 0, st, a);
+  } else {
+    if (fused) hipLaunchKernelGGL((pa::decode_kernel<false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((pa::decode_kernel<false, false>), grid, block, 0, st, a);
+  }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   if (event_after_main && hipEventRecord((hipEvent_t)event_after_main, st) != hipSuccess)
     return PA_ERR_LAUNCH;
@@ -225,21 +238,34 @@ PA_API int pa_decode_attention(const pa_shape* shape, int32_t batch, const void*
                                int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
                                int32_t pages_per_split, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  return decode_impl(shape, batch, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
-                     scale, out, out_dtype, pages_per_split, workspace, workspace_bytes, stream,
-                     nullptr, nullptr);
+  return decode_impl(shape, batch, q, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens,
+                     max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+                     workspace_bytes, stream, nullptr, nullptr);
+}
+
+PA_API int pa_append_decode_attention(const pa_shape* shape, int32_t batch, const void* q,
+                                      const void* k_new, const void* v_new, void* k_pool,
+                                      void* v_pool, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                      void* out, int32_t out_dtype, int32_t pages_per_split,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
+  return decode_impl(shape, batch, q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                     max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+                     workspace_bytes, stream, nullptr, nullptr);
 }
 
 PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, const void* q,
-                                        const void* k_pool, const void* v_pool,
+                                        const void* k_new, const void* v_new,
+                                        void* k_pool, void* v_pool,
                                         const int32_t* block_tables, const int32_t* seq_lens,
                                         int32_t max_seq_len, float scale, void* out,
                                         int32_t out_dtype, int32_t pages_per_split,
                                         void* workspace, size_t workspace_bytes, void* stream,
                                         void* event_before_main, void* event_after_main) {
-  return decode_impl(shape, batch, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
-                     scale, out, out_dtype, pages_per_split, workspace, workspace_bytes, stream,
-                     event_before_main, event_after_main);
+  return decode_impl(shape, batch, q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                     max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+                     workspace_bytes, stream, event_before_main, event_after_main);
 }
 
 PA_API int pa_validate_metadata(const pa_shape* shape, int32_t batch,

@@ -263,6 +263,10 @@ struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k_pool;
   const uint16_t* v_pool;
+  const uint16_t* k_new;   // fused append: [B][Hkv][D] new-token rows (else unused)
+  const uint16_t* v_new;
+  uint16_t* k_pool_w;      // fused append: the same pools, written at slot L-1
+  uint16_t* v_pool_w;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
@@ -276,7 +280,11 @@ struct DecodeArgs {
   int32_t num_splits;  // S: splits per sequence in the grid
 };
 
-template <bool OUT_BF16>
+// APPEND: the one-token append is fused in.  The work-group whose split
+// holds the sequence's last page writes the new K/V row (token L-1) into its
+// page slot and uses the same values, from registers, in place of what the
+// page stream read for that slot; no other work-group reads that page.
+template <bool OUT_BF16, bool APPEND>
 // second bound: minimum waves per SIMD (a work-group puts 2 on each SIMD)
 __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeArgs a) {
   const int s = blockIdx.x;
@@ -317,6 +325,18 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
     qhi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr + 32));
   }
 
+  // fused append: this lane's 16 + 16 dims of the new K and V row of head g
+  const bool app_here = APPEND && p1 == n_pages;     // this split holds token L-1
+  const int app_slot = (L - 1) % kPage;
+  PageRegs nw = {};
+  if (app_here) {
+    const int64_t row = ((int64_t)b * kHkv + g) * kD + 8 * part;
+    nw.k0 = *reinterpret_cast<const u32x4*>(a.k_new + row);
+    nw.k1 = *reinterpret_cast<const u32x4*>(a.k_new + row + 32);
+    nw.v0 = *reinterpret_cast<const u32x4*>(a.v_new + row);
+    nw.v1 = *reinterpret_cast<const u32x4*>(a.v_new + row + 32);
+  }
+
   LaneState st;
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) {
@@ -337,12 +357,16 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
     ent[c] = (c * 64 < p1 - p0 && j <= last) ? bt[j] : 0;
   }
   bool bad_page = false;
-  auto page_id = [&](int i) -> int64_t {          // i: logical page, p0 <= i <= last
+  auto raw_page_id = [&](int i) -> int {          // i: logical page, p0 <= i <= last
     const int j = i - p0;
     int id = __builtin_amdgcn_readlane(ent[0], j & 63);
 #pragma unroll
     for (int c = 1; c < kMaxSplitPages / 64; ++c)
       if ((j >> 6) == c) id = __builtin_amdgcn_readlane(ent[c], j & 63);
+    return id;
+  };
+  auto page_id = [&](int i) -> int64_t {          // validated; out-of-range -> flagged, 0
+    const int id = raw_page_id(i);
     const bool ok = (unsigned)id < (unsigned)a.num_pages;
     bad_page |= !ok;
     return ok ? id : 0;
@@ -376,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
     lds_page_issue(cur, my_row + slot * kSlotBytes);
     lds_page_ready(cur);
     fetch(min(i + kRing, last), slot);
+    if (MASK && app_here && token == app_slot) cur = nw;   // the appended token
     consume_page<MASK>(st, cur, qlo, qhi, a.xscale, token, MASK ? tail_valid : kPage);
   };
 
@@ -383,12 +408,23 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
   // page, so the count of outstanding loads is the same on every path)
 #pragma unroll
   for (int r = 0; r < kRing; ++r) fetch(min(p0 + r, last), r);
-  // full pages in the loop, a partial last page peeled off after it, so the
-  // loop body has a single path and its accumulators stay in place
-  const int full_end = (tail_valid < kPage) ? last : last + 1;
-  for (int i = p0; i < full_end; ++i) step(i, std::false_type{});
-  if (full_end == last) step(last, std::true_type{});
+  // pages p0 .. last-1 in the loop; the split's last page is peeled off
+  // after it (masked when partial, and the place of the appended token), so
+  // the loop body has a single path and its accumulators stay in place
+  for (int i = p0; i < last; ++i) step(i, std::false_type{});
+  step(last, std::true_type{});
   wait_vmem<0>();                                   // drain the clamped extra fetches
+  if (app_here && token == app_slot) {
+    // write the new row: 4 lanes per wavefront x (16 + 16) B of K and of V
+    const int id = raw_page_id(last);
+    if ((unsigned)id < (unsigned)a.num_pages) {
+      const int64_t off = (int64_t)id * kPageElems + app_slot * kRowElems + g * kD + 8 * part;
+      *reinterpret_cast<u32x4*>(a.k_pool_w + off) = nw.k0;
+      *reinterpret_cast<u32x4*>(a.k_pool_w + off + 32) = nw.k1;
+      *reinterpret_cast<u32x4*>(a.v_pool_w + off) = nw.v0;
+      *reinterpret_cast<u32x4*>(a.v_pool_w + off + 32) = nw.v1;
+    }
+  }
 
   // merge the 16 token slots (lane bits 0..3: one DPP row)
   merge_token_slots(st);

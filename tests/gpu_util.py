@@ -75,3 +75,13 @@ def assert_close(got: np.ndarray, ref: np.ndarray, bf16_out=False, where=""):
     if not bf16_out:
         assert rel.max() <= RTOL_REPORT, f"{where}: max-rel {rel.max():.3e}"
     return float(err.max()), float(rel.max())
+
+
+def gpu_fused(db: DeviceBatch, pages_per_split=0, out_dtype=torch.float32):
+    """Fused append + decode in one call; pools of ``db`` are updated in place."""
+    from paged_kv_decode_07_amd import binding as pa
+    out = pa.append_decode_attention(db.q, db.k_new, db.v_new, db.k_pool, db.v_pool, db.bt,
+                                     db.lens, db.h.max_seq_len, scale=db.h.scale,
+                                     out_dtype=out_dtype, pages_per_split=pages_per_split)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,107 @@
+"""Fused append + decode (one launch) against the two-call sequence and the oracle.
+
+The fused call must leave the pools bit-identical to pa_append_kv and return
+outputs bit-identical to pa_decode_attention run after it (same arithmetic,
+the new token taken from registers instead of the pool), and within the
+attention tolerance of the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import DeviceBatch, assert_close, gpu_append, gpu_decode, gpu_fused, host16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from paged_kv_decode_07_amd import binding
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _two_call_vs_fused(batch, ps):
+    a = DeviceBatch(batch)
+    gpu_append(a)
+    two = gpu_decode(a, pages_per_split=ps)
+    f = DeviceBatch(batch)
+    fused = gpu_fused(f, pages_per_split=ps)
+    assert np.array_equal(host16(f.k_pool), host16(a.k_pool)), "K pool differs"
+    assert np.array_equal(host16(f.v_pool), host16(a.v_pool)), "V pool differs"
+    assert np.array_equal(fused, two), "fused output differs from append + decode"
+    return fused
+
+
+@pytest.mark.parametrize("pages_per_split", [0, 1, 3, 16, 128])
+def test_fused_edge_lengths(pages_per_split):
+    lens = [1, 2, 15, 16, 17, 32, 33, 100, 2047, 2048, 0]
+    w = W.make_batch(lens, sum(W.pages_for(L) for L in lens) + 9, seed=71, append=True)
+    got = _two_call_vs_fused(w, pages_per_split)
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got, ref, where=f"fused edge ps={pages_per_split}")
+    assert np.all(got[-1] == 0.0)
+
+
+def test_fused_seq_len_one_returns_the_new_v_row():
+    w = W.make_batch([1] * 5, 8, seed=72, append=True)
+    got = gpu_fused(DeviceBatch(w))
+    for b in range(5):
+        vnew = oracle.bf16_bits_to_f64(w.v_new[b])
+        for h in range(32):
+            assert np.array_equal(got[b, h], vnew[h // 4])
+
+
+def test_fused_full_batch512_zipf():
+    w = W.make_workload(5)
+    got = _two_call_vs_fused(w, 0)
+    seqs = sorted(set([int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 3, 100, 511]))
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale,
+                                  sequences=seqs)
+    assert_close(got[seqs], ref[seqs], where="fused batch512 sampled")
+
+
+def test_fused_full_batch256_len2048_bench_configuration():
+    w = W.make_workload(4, append=True)
+    got = _two_call_vs_fused(w, 0)
+    seqs = [0, 77, 255]
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale,
+                                  sequences=seqs)
+    assert_close(got[seqs], ref[seqs], where="fused batch256 sampled")
+
+
+def test_fused_16_layer_workload_first_and_last_layer():
+    for layer in (0, W.NUM_LAYERS_W3 - 1):
+        w = W.make_workload(3, layer=layer)
+        got = _two_call_vs_fused(w, 0)
+        assert np.all(np.isfinite(got))
+
+
+def test_fused_bad_last_page_writes_nothing_and_gives_nan():
+    w = W.make_batch([20, 40, 5], 16, seed=73, append=True)
+    bt = w.block_tables.copy()
+    bt[1, (40 - 1) // 16] = 999                       # the page the append would write
+    db = DeviceBatch(w)
+    from gpu_util import dev32
+    db.bt = dev32(bt)
+    got = gpu_fused(db)
+    assert np.all(np.isnan(got[1]))
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new[[0, 2]], w.v_new[[0, 2]],
+                                    bt[[0, 2]], w.seq_lens[[0, 2]])
+    assert np.array_equal(host16(db.k_pool), k_ref)
+    assert np.array_equal(host16(db.v_pool), v_ref)
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got[[0, 2]], ref[[0, 2]], where="fused others")
