@@ -131,6 +131,20 @@ int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_len,
                    int32_t* splits_out);
 
 /*
+ * Split size for a batch whose lengths the caller knows on the host (a
+ * scheduler does): seq_lens_host is a HOST array of `batch` lengths.  The
+ * library simulates how its work-groups would be spread over num_cus
+ * compute units (0: the current device's count) for each candidate split
+ * size (8 .. 256 pages) and returns the fastest by its cost model; pass the
+ * result as pages_per_split.  Useful for skewed batches, where the
+ * size-only plan is blind.  Reads nothing on the device; with num_cus > 0
+ * it makes no HIP call at all.
+ */
+int pa_decode_plan_lengths(const pa_shape* shape, int32_t batch,
+                           const int32_t* seq_lens_host, int32_t max_seq_len,
+                           int32_t num_cus, int32_t* pages_out, int32_t* splits_out);
+
+/*
  * Paged GQA decode attention for one layer.
  *   out[b][h][:] = sum_t w_t V_b[t][h/4][:],  w = softmax_t(scale * q[b][h] . K_b[t][h/4])
  * over tokens t in [0, seq_lens[b]); rows with seq_lens[b] == 0 are zero.

@@ -24,7 +24,7 @@ PA_OUT_F32, PA_OUT_BF16 = 0, 1
 HQ, HKV, D, PAGE = 32, 8, 64, 16
 
 # names declared in include/pa_decode.h
-EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
+EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_decode_plan_lengths",
            "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
            "pa_validate_metadata", "pa_status_string", "pa_abi_version")
 
@@ -57,6 +57,8 @@ def load_library(path: str | None = None):
         lib.pa_append_kv.argtypes = [SP, I32, P, P, P, P, P, P, P]
         lib.pa_decode_workspace_bytes.argtypes = [SP, I32, I32, I32, ctypes.POINTER(SZ)]
         lib.pa_decode_plan.argtypes = [SP, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        lib.pa_decode_plan_lengths.argtypes = [SP, I32, P, I32, I32, ctypes.POINTER(I32),
+                                               ctypes.POINTER(I32)]
         lib.pa_decode_attention.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float,
                                             P, I32, I32, P, SZ, P]
         lib.pa_decode_attention_profiled.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
@@ -68,6 +70,7 @@ def load_library(path: str | None = None):
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_abi_version.argtypes = []
         for name in ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
+                     "pa_decode_plan_lengths",
                      "pa_decode_attention", "pa_decode_attention_profiled",
                      "pa_append_decode_attention", "pa_validate_metadata", "pa_abi_version"):
             getattr(lib, name).restype = ctypes.c_int
@@ -152,6 +155,25 @@ def decode_plan(batch: int, max_seq_len: int, num_pages: int, max_blocks: int = 
     rc = load_library().pa_decode_plan(ctypes.byref(shape), batch, max_seq_len,
                                        pages_per_split, ctypes.byref(ps), ctypes.byref(ns))
     _check(rc, "pa_decode_plan")
+    return ps.value, ns.value
+
+
+def decode_plan_lengths(seq_lens_host, num_pages: int, max_blocks: int = 128,
+                        max_seq_len: int | None = None, num_cus: int = 0):
+    """Split plan for lengths known on the host: (pages per split, splits).
+
+    ``num_cus`` 0 plans for the current device; a positive count plans
+    without touching any device.
+    """
+    import numpy as np
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    msl = int(lens.max()) if max_seq_len is None and lens.size else int(max_seq_len or 0)
+    shape = make_shape(num_pages, max_blocks)
+    ps, ns = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = load_library().pa_decode_plan_lengths(ctypes.byref(shape), int(lens.size),
+                                               lens.ctypes.data_as(ctypes.c_void_p), msl,
+                                               int(num_cus), ctypes.byref(ps), ctypes.byref(ns))
+    _check(rc, "pa_decode_plan_lengths")
     return ps.value, ns.value
 
 

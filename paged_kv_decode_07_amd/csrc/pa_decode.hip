@@ -2,8 +2,11 @@
 // and kernel launches behind the C ABI declared in include/pa_decode.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <queue>
+#include <utility>
 #include <vector>
 
 #include "pa_decode.h"
@@ -77,6 +80,124 @@ int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pa
   return PA_OK;
 }
 
+// Split size for known sequence lengths (host copy).  For each candidate
+// size the host simulates one launch: work-groups are dealt round-robin to
+// the XCDs (work-group i to XCD i mod 8) and each XCD starts its next one
+// when one of its CUs frees up (one resident work-group per CU); a
+// work-group spends group_us on fixed costs, then streams its pages, all
+// streaming work-groups sharing the HBM bandwidth equally but none faster
+// than one CU alone (page_us per page); empty grid slots cost empty_us; a
+// multi-split plan adds the merge (merge_us plus its partial traffic).  The
+// constants were fitted to measurements of this kernel on MI355X over batch
+// 8 .. 512 and split sizes 8 .. 128.  The largest size predicted within 3%
+// of the fastest is returned (the model's error is about that size).
+struct PlanModel {
+  double page_us = 0.85, group_us = 6.0, empty_us = 0.5, merge_us = 8.0;
+  double hbm_bytes_per_us = 6.1e6;
+};
+
+double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,
+                     const PlanModel& m) {
+  const int max_pages = ceil_div(max_seq_len, pa::kPage);
+  const int S = ceil_div(max_pages, ps);
+  const double page_bytes = 2.0 * pa::kPageElems * 2;            // K + V page, bytes
+  const double chip_rate = m.hbm_bytes_per_us / page_bytes;      // pages/us, whole chip
+  const double cu_rate = 1.0 / m.page_us;                        // pages/us, one CU alone
+  const int per_xcd = cu / xcds > 0 ? cu / xcds : 1;
+  struct Item { double fixed, pages; };
+  std::vector<Item> items;
+  items.reserve((size_t)batch * S);
+  double partial_rows = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int L = lens[b] < 0 ? 0 : (lens[b] > max_seq_len ? max_seq_len : lens[b]);
+    const int n = ceil_div(L, pa::kPage);
+    const int nsb = n > 0 ? ceil_div(n, ps) : 1;
+    if (nsb > 1) partial_rows += nsb;
+    for (int k = 0; k < S; ++k) {
+      if (k < nsb) items.push_back({m.group_us, (double)((k + 1) * ps <= n ? ps : n - k * ps)});
+      else items.push_back({m.empty_us, 0.0});
+    }
+  }
+  // Streaming progress is tracked in virtual pages V (every streaming
+  // work-group advances by the same rate), so a work-group that starts
+  // streaming r pages at V0 ends when V reaches V0 + r.
+  typedef std::pair<double, int> Ev;   // (time or V, xcd); payload index in pages_of
+  std::priority_queue<std::pair<double, std::pair<int, double>>,
+                      std::vector<std::pair<double, std::pair<int, double>>>,
+                      std::greater<std::pair<double, std::pair<int, double>>>> fixed_end;
+  std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> stream_end;
+  std::vector<size_t> next(xcds);
+  std::vector<int> busy(xcds, 0);
+  for (int x = 0; x < xcds; ++x) next[x] = (size_t)x;
+  double t = 0, V = 0;
+  auto fill = [&](int x) {
+    while (busy[x] < per_xcd && next[x] < items.size()) {
+      const Item& it = items[next[x]];
+      next[x] += (size_t)xcds;
+      ++busy[x];
+      fixed_end.push({t + it.fixed, {x, it.pages}});
+    }
+  };
+  for (int x = 0; x < xcds; ++x) fill(x);
+  while (!fixed_end.empty() || !stream_end.empty()) {
+    const int ns = (int)stream_end.size();
+    const double r = ns > 0 ? std::min(cu_rate, chip_rate / ns) : cu_rate;
+    const double dt_fixed = fixed_end.empty() ? 1e300 : fixed_end.top().first - t;
+    const double dt_stream = stream_end.empty() ? 1e300 : (stream_end.top().first - V) / r;
+    if (dt_fixed <= dt_stream) {
+      t += dt_fixed;
+      V += r * dt_fixed * (ns > 0);
+      const auto e = fixed_end.top();
+      fixed_end.pop();
+      if (e.second.second > 0) {
+        stream_end.push({V + e.second.second, e.second.first});
+      } else {
+        --busy[e.second.first];
+        fill(e.second.first);
+      }
+    } else {
+      t += dt_stream;
+      V = stream_end.top().first;
+      const int x = stream_end.top().second;
+      stream_end.pop();
+      --busy[x];
+      fill(x);
+    }
+  }
+  if (partial_rows > 0)
+    t += m.merge_us + 2.0 * partial_rows * pa::kHq * (pa::kD + 2) * 4.0 / m.hbm_bytes_per_us;
+  return t;
+}
+
+int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int max_seq_len,
+                       int num_cus, int* pages, int* splits) {
+  int cu = num_cus;
+  if (cu <= 0) {
+    const int rc = current_cu_count(&cu);
+    if (rc != PA_OK) return rc;
+  }
+  const int max_pages = ceil_div(max_seq_len, pa::kPage);
+  if (max_pages <= 0) { *pages = 1; *splits = 1; return PA_OK; }
+  const int xcds = (cu % 8 == 0) ? 8 : 1;         // MI300-class parts: 8 XCDs
+  const PlanModel model;
+  std::vector<std::pair<int, double>> cands;
+  for (int ps : {8, 16, 32, 64, 128, 256}) {
+    const int cand = ps < max_pages ? ps : max_pages;
+    if (cand > s->max_blocks_per_seq || cand > pa::kMaxSplitPages) break;
+    cands.push_back({cand, simulate_plan(lens, batch, max_seq_len, cand, cu, xcds, model)});
+    if (cand == max_pages) break;
+  }
+  if (cands.empty()) { *pages = 1; *splits = max_pages; return PA_OK; }
+  double best = 1e300;
+  for (auto& c : cands) best = std::min(best, c.second);
+  int ps = cands.front().first;
+  for (auto& c : cands)
+    if (c.second <= best * 1.03) ps = std::max(ps, c.first);
+  *pages = ps;
+  *splits = ceil_div(max_pages, ps);
+  return PA_OK;
+}
+
 size_t workspace_for(int batch, int splits) {
   if (splits <= 1) return 0;
   const size_t rows = (size_t)batch * splits * pa::kHq;
@@ -138,6 +259,23 @@ PA_API int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_
   int ps = 0, ns = 0;
   rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
   if (rc != PA_OK) return rc;
+  if (pages_out) *pages_out = ps;
+  if (splits_out) *splits_out = ns;
+  return PA_OK;
+}
+
+PA_API int pa_decode_plan_lengths(const pa_shape* shape, int32_t batch,
+                                  const int32_t* seq_lens_host, int32_t max_seq_len,
+                                  int32_t num_cus, int32_t* pages_out, int32_t* splits_out) {
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  if (batch > 0 && !seq_lens_host) return PA_ERR_NULL;
+  if (num_cus < 0) return PA_ERR_VALUE;
+  int ps = 1, ns = 1;
+  if (batch > 0) {
+    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, &ps, &ns);
+    if (rc != PA_OK) return rc;
+  }
   if (pages_out) *pages_out = ps;
   if (splits_out) *splits_out = ns;
   return PA_OK;

@@ -325,16 +325,16 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
     qhi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr + 32));
   }
 
-  // fused append: this lane's 16 + 16 dims of the new K and V row of head g
+  // fused append: the new K and V row of head g (128 + 128 bytes) is parked
+  // in LDS for the page stream's last page (keeps 16 VGPRs free in the loop):
+  // lanes 0..15 each copy 16 bytes, K row then V row.
   const bool app_here = APPEND && p1 == n_pages;     // this split holds token L-1
   const int app_slot = (L - 1) % kPage;
-  PageRegs nw = {};
-  if (app_here) {
-    const int64_t row = ((int64_t)b * kHkv + g) * kD + 8 * part;
-    nw.k0 = *reinterpret_cast<const u32x4*>(a.k_new + row);
-    nw.k1 = *reinterpret_cast<const u32x4*>(a.k_new + row + 32);
-    nw.v0 = *reinterpret_cast<const u32x4*>(a.v_new + row);
-    nw.v1 = *reinterpret_cast<const u32x4*>(a.v_new + row + 32);
+  __shared__ uint4 new_rows[APPEND ? kWaves : 1][16];
+  if (app_here && lane < 16) {
+    const uint16_t* src = (lane < 8 ? a.k_new : a.v_new) +
+                          ((int64_t)b * kHkv + g) * kD + 8 * (lane & 7);
+    new_rows[g][lane] = *reinterpret_cast<const uint4*>(src);
   }
 
   LaneState st;
@@ -400,7 +400,13 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
     lds_page_issue(cur, my_row + slot * kSlotBytes);
     lds_page_ready(cur);
     fetch(min(i + kRing, last), slot);
-    if (MASK && app_here && token == app_slot) cur = nw;   // the appended token
+    if (MASK && app_here && token == app_slot) {           // the appended token
+      const u32x4* nr = reinterpret_cast<const u32x4*>(&new_rows[APPEND ? g : 0][0]);
+      cur.k0 = nr[part];
+      cur.k1 = nr[4 + part];
+      cur.v0 = nr[8 + part];
+      cur.v1 = nr[12 + part];
+    }
     consume_page<MASK>(st, cur, qlo, qhi, a.xscale, token, MASK ? tail_valid : kPage);
   };
 
@@ -414,15 +420,13 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
   for (int i = p0; i < last; ++i) step(i, std::false_type{});
   step(last, std::true_type{});
   wait_vmem<0>();                                   // drain the clamped extra fetches
-  if (app_here && token == app_slot) {
-    // write the new row: 4 lanes per wavefront x (16 + 16) B of K and of V
+  if (app_here && lane < 16) {
+    // write the new row into its slot: lanes 0..15 each store 16 bytes
     const int id = raw_page_id(last);
     if ((unsigned)id < (unsigned)a.num_pages) {
-      const int64_t off = (int64_t)id * kPageElems + app_slot * kRowElems + g * kD + 8 * part;
-      *reinterpret_cast<u32x4*>(a.k_pool_w + off) = nw.k0;
-      *reinterpret_cast<u32x4*>(a.k_pool_w + off + 32) = nw.k1;
-      *reinterpret_cast<u32x4*>(a.v_pool_w + off) = nw.v0;
-      *reinterpret_cast<u32x4*>(a.v_pool_w + off + 32) = nw.v1;
+      const int64_t off = (int64_t)id * kPageElems + app_slot * kRowElems + g * kD + 8 * (lane & 7);
+      uint16_t* dst = (lane < 8 ? a.k_pool_w : a.v_pool_w) + off;
+      *reinterpret_cast<uint4*>(dst) = new_rows[APPEND ? g : 0][lane];
     }
   }
 
@@ -470,6 +474,10 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
 
 // Log-sum-exp merge of the splits of each multi-split sequence, in split
 // order.  One work-group of 256 threads per sequence: thread = (head, 8 dims).
+// Splits are read 8 at a time with all loads issued before any use, so the
+// loop costs one memory latency per 8 splits rather than one per split.
+constexpr int kMergeBatch = 8;
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const int b = blockIdx.x;
@@ -483,18 +491,40 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const int h = threadIdx.x >> 3;
   const int d0 = (threadIdx.x & 7) * 8;
   const int64_t row0 = (int64_t)b * a.num_splits * kHq + h;   // split s at row0 + s*kHq
+  // pass 1: the largest running maximum over the splits
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(row0 + (int64_t)s * kHq) * 2]);
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float m[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      m[k] = (s0 + k < ns) ? a.part_ml[(row0 + (int64_t)(s0 + k) * kHq) * 2] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, m[k]);
+  }
+  // pass 2: weights 2^(m_s - M), sums in split order
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const int64_t row = row0 + (int64_t)s * kHq;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[row * 2] - M);
-    den += w * a.part_ml[row * 2 + 1];
-    const float4* src = reinterpret_cast<const float4*>(a.part_acc + row * kD + d0);
-    const float4 x0 = src[0], x1 = src[1];
-    num[0] += w * x0.x; num[1] += w * x0.y; num[2] += w * x0.z; num[3] += w * x0.w;
-    num[4] += w * x1.x; num[5] += w * x1.y; num[6] += w * x1.z; num[7] += w * x1.w;
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch];
+    float4 x0[kMergeBatch], x1[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const bool in = s0 + k < ns;
+      const int64_t row = row0 + (int64_t)(in ? s0 + k : 0) * kHq;
+      const float4* src = reinterpret_cast<const float4*>(a.part_acc + row * kD + d0);
+      m[k] = in ? a.part_ml[row * 2] : -INFINITY;
+      l[k] = a.part_ml[row * 2 + 1];
+      x0[k] = src[0];
+      x1[k] = src[1];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (s0 + k >= ns) break;
+      const float w = __builtin_amdgcn_exp2f(m[k] - M);
+      den += w * l[k];
+      num[0] += w * x0[k].x; num[1] += w * x0[k].y; num[2] += w * x0[k].z; num[3] += w * x0[k].w;
+      num[4] += w * x1[k].x; num[5] += w * x1[k].y; num[6] += w * x1[k].z; num[7] += w * x1[k].w;
+    }
   }
   const float inv = 1.f / den;
   const int64_t orow = (int64_t)b * kHq + h;

@@ -122,3 +122,29 @@ def test_validate_metadata_argument_errors(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         pa.load_library(str(tmp_path / "nope.so"))
+
+
+def test_host_length_planner_choices():
+    """The split plan for known lengths, for a 256-CU part, on the five workloads.
+
+    Expected sizes are the fastest measured on MI355X for each workload
+    (single sequence: one split of its 3 pages).
+    """
+    import numpy as np
+    import workloads as W
+    expect = {1: 3, 2: 8, 3: 32, 4: 128, 5: 64}
+    for i, ps_best in expect.items():
+        lens = W.workload_seq_lens(i)
+        ps, ns = pa.decode_plan_lengths(lens, 40000, num_cus=256)
+        assert ps == ps_best, (i, ps)
+        assert ns == -(-W.pages_for(int(lens.max())) // ps)
+    # degenerate inputs
+    assert pa.decode_plan_lengths(np.zeros(4, np.int32), 16, num_cus=256, max_seq_len=0) == (1, 1)
+    s = pa.make_shape(64, 128)
+    ps, ns = ctypes.c_int32(0), ctypes.c_int32(0)
+    lib = pa.load_library()
+    assert lib.pa_decode_plan_lengths(ctypes.byref(s), 3, None, 16, 256, ctypes.byref(ps),
+                                      ctypes.byref(ns)) == -1
+    lens = (ctypes.c_int32 * 3)(1, 2, 3)
+    assert lib.pa_decode_plan_lengths(ctypes.byref(s), 3, lens, 16, -1, ctypes.byref(ps),
+                                      ctypes.byref(ns)) == -6

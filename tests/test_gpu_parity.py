@@ -286,3 +286,18 @@ def test_full_16_layers_append_then_decode():
         assert_close(got[seqs], ref[seqs], where=f"16-layer layer {layer}")
         del db
         torch.cuda.empty_cache()
+
+
+def test_plan_from_host_lengths_is_valid_and_correct():
+    from paged_kv_decode_07_amd import binding as pa
+    for wi in (2, 5):
+        w = W.make_workload(wi, append=False)
+        ps, ns = pa.decode_plan_lengths(w.seq_lens, w.num_pages)
+        assert 1 <= ps <= 256 and ns == -(-W.pages_for(w.max_seq_len) // ps)
+        got = gpu_decode(DeviceBatch(w), pages_per_split=ps)
+        seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 0]
+        ref = oracle_decode(w, sequences=seqs)
+        assert_close(got[seqs], ref[seqs], where=f"host-length plan w{wi} ps={ps}")
+    # uniform full-length batch covering the CUs: one split per sequence
+    ps, ns = pa.decode_plan_lengths(np.full(256, 2048, np.int32), 32768)
+    assert (ps, ns) == (128, 1)

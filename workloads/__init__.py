@@ -260,23 +260,26 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
     lens = workload_seq_lens(index, seed)
     name = f"w{index}"
     recipe = {"workload": WORKLOADS[index]}
+    app = (index in (3, 5)) if append is None else bool(append)
     if index == 1:
-        return make_batch(lens, 64, [seed, 1], name=name, recipe=recipe, placement=placement)
+        return make_batch(lens, 64, [seed, 1], name=name, recipe=recipe, placement=placement,
+                          append=app)
     if index == 2:
-        return make_batch(lens, 4096, [seed, 1], name=name, recipe=recipe, placement=placement)
+        return make_batch(lens, 4096, [seed, 1], name=name, recipe=recipe, placement=placement,
+                          append=app)
     if index == 3:
         if not 0 <= layer < NUM_LAYERS_W3:
             raise ValueError(layer)
-        return make_batch(lens, POOL_PAGES_W3, [seed, 1, layer], q_sigma=0.5, append=True,
+        return make_batch(lens, POOL_PAGES_W3, [seed, 1, layer], q_sigma=0.5, append=app,
                           name=f"{name}_layer{layer}", recipe=dict(recipe, layer=layer),
                           placement=placement)
     if index == 4:
         return make_batch(lens, 256 * MAX_BLOCKS, [seed, 1], name=name, recipe=recipe,
-                          placement=placement, append=bool(append))
+                          placement=placement, append=app)
     if index == 5:
         need = int(sum(pages_for(L) for L in lens))
         pool = need + (need + 9) // 10
-        return make_batch(lens, pool, [seed, 1], append=True, name=name, recipe=recipe,
+        return make_batch(lens, pool, [seed, 1], append=app, name=name, recipe=recipe,
                           placement=placement)
     raise ValueError(index)
 
