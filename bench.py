@@ -229,7 +229,18 @@ def main() -> int:
     t_main = np.array([e[0].elapsed_time(e[1]) for e in evB]) * 1e-3
     # pass C: the same step as two calls
     t_two = timed(two_call_step, K)
-    log(f"{K} breakdown steps and {K} two-call steps done")
+    # pass D: the fused step with the rotary embedding of the new q/k fused in
+    cos_np, sin_np = W.rope_table(W.MAX_CONTEXT)
+    rope_cos = torch.from_numpy(cos_np).to(dev)
+    rope_sin = torch.from_numpy(sin_np).to(dev)
+
+    def rope_step():
+        pa.append_decode_attention_rope(q, k_new, v_new, rope_cos, rope_sin, k_pool, v_pool,
+                                        bt, lens, msl, scale=batch.scale, out=out,
+                                        pages_per_split=ps, workspace=workspace, stream=stream)
+    rope_step()
+    t_rope = timed(rope_step, K)
+    log(f"{K} breakdown, {K} two-call and {K} RoPE steps done")
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
     mean_step = float(t_step.mean())
@@ -268,6 +279,7 @@ def main() -> int:
             "wall_per_step_incl_flush": round(wall / K * 1e6, 2),
             "main_kernel": round(float(t_main.mean()) * 1e6, 2),
             "two_call_step": round(float(t_two.mean()) * 1e6, 2),
+            "rope_fused_step": round(float(t_rope.mean()) * 1e6, 2),
         },
         "two_call_kv_gbps": round(kv / float(t_two.mean()) / 1e9, 2),
         "roofline": {

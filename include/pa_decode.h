@@ -186,6 +186,53 @@ int pa_append_decode_attention(const pa_shape* shape, int32_t batch,
                                void* stream);
 
 /*
+ * Rotary position embedding of the new token (the step before the append in
+ * the model: the new K is stored at its absolute RoPE position).  Rotate-half
+ * pairing: dims i and i+32 rotate by the angle of position L-1 and frequency
+ * i, out[i] = x[i] c - x[i+32] s, out[i+32] = x[i+32] c + x[i] s, each
+ * product and sum rounded to FP32 on its own, the result rounded to BF16
+ * (RNE).  The angles come as caller tables, so the frequency schedule is the
+ * caller's choice.
+ */
+typedef struct pa_rope {
+  const float* cos;    /* device, float32 [positions][head_dim/2], 4-byte aligned */
+  const float* sin;    /* device, float32 [positions][head_dim/2]                 */
+  int32_t positions;   /* rows of each table; must cover every position used       */
+} pa_rope;
+
+/*
+ * Append with RoPE: for each b with L = seq_lens[b] >= 1, q_out[b] = RoPE(q[b])
+ * and the page slot of token L-1 receives RoPE(k_new[b]) and v_new[b].  Idle
+ * slots and out-of-range metadata write no pool bytes and copy q[b] to
+ * q_out[b].  q, q_out: BF16 [batch][32][64], 16-byte aligned; the tables
+ * must cover 16 * max_blocks_per_seq positions.
+ */
+int pa_append_kv_rope(const pa_shape* shape, int32_t batch,
+                      const void* q, const void* k_new, const void* v_new,
+                      const pa_rope* rope, void* q_out,
+                      void* k_pool, void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens,
+                      void* stream);
+
+/*
+ * Fused decode step with RoPE: the effect of pa_append_kv_rope followed by
+ * pa_decode_attention on its q_out, in one launch (plus the split merge).
+ * Every work-group rotates its own query rows; the one holding the last
+ * page rotates and writes the new key.  Outputs and pools are identical to
+ * the two-call form.  The tables must cover max_seq_len positions.
+ */
+int pa_append_decode_attention_rope(const pa_shape* shape, int32_t batch,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    const pa_rope* rope,
+                                    void* k_pool, void* v_pool,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    int32_t max_seq_len, float scale,
+                                    void* out, int32_t out_dtype,
+                                    int32_t pages_per_split,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * pa_decode_attention (k_new = v_new = NULL) or pa_append_decode_attention
  * (both non-NULL) plus timing hooks: event_before_main and event_after_main
  * (hipEvent_t handles created by the caller; either may be NULL) are

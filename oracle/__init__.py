@@ -35,3 +35,4 @@ from .paged_decode import (  # noqa: F401
     append_kv,
     kv_head_of,
 )
+from . import rope  # noqa: F401,E402

@@ -26,6 +26,7 @@ HQ, HKV, D, PAGE = 32, 8, 64, 16
 # names declared in include/pa_decode.h
 EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_decode_plan_lengths",
            "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
+           "pa_append_kv_rope", "pa_append_decode_attention_rope",
            "pa_validate_metadata", "pa_status_string", "pa_abi_version")
 
 
@@ -33,6 +34,10 @@ class PaShape(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+class PaRope(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("positions", ctypes.c_int32)]
 
 
 def make_shape(num_pages: int, max_blocks: int, num_q_heads: int = HQ,
@@ -65,6 +70,10 @@ def load_library(path: str | None = None):
                                                      ctypes.c_float, P, I32, I32, P, SZ, P, P, P]
         lib.pa_append_decode_attention.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
                                                    ctypes.c_float, P, I32, I32, P, SZ, P]
+        RP = ctypes.POINTER(PaRope)
+        lib.pa_append_kv_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P, P]
+        lib.pa_append_decode_attention_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, I32,
+                                                        ctypes.c_float, P, I32, I32, P, SZ, P]
         lib.pa_validate_metadata.argtypes = [SP, I32, P, P, I32, P, ctypes.POINTER(ctypes.c_int64)]
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
@@ -72,7 +81,9 @@ def load_library(path: str | None = None):
         for name in ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
                      "pa_decode_plan_lengths",
                      "pa_decode_attention", "pa_decode_attention_profiled",
-                     "pa_append_decode_attention", "pa_validate_metadata", "pa_abi_version"):
+                     "pa_append_decode_attention", "pa_append_kv_rope",
+                     "pa_append_decode_attention_rope", "pa_validate_metadata",
+                     "pa_abi_version"):
             getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
@@ -273,6 +284,71 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, seq_l
         rc = lib.pa_decode_attention_profiled(*args, *_event_handles(event_before_main,
                                                                       event_after_main))
     _check(rc, "pa_append_decode_attention")
+    return out
+
+
+def _rope(cos, sin) -> PaRope:
+    for name, t in (("rope_cos", cos), ("rope_sin", sin)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2 \
+                or t.shape[1] != D // 2:
+            raise ValueError(f"{name}: must be a contiguous float32 [positions][32] device tensor")
+    if cos.shape != sin.shape:
+        raise ValueError("rope_cos and rope_sin differ in shape")
+    return PaRope(cos.data_ptr(), sin.data_ptr(), int(cos.shape[0]))
+
+
+def append_kv_rope(q, k_new, v_new, rope_cos, rope_sin, k_pool, v_pool, block_tables,
+                   seq_lens, q_out=None, stream=None):
+    """Rotate the new q/k at position L-1 (RoPE), append K/V; returns ``q_out``."""
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if q.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _bits16(q_out, "q_out", (HQ, D))
+    rope = _rope(rope_cos, rope_sin)
+    shape = make_shape(int(k_pool.shape[0]), int(block_tables.shape[1]))
+    rc = load_library().pa_append_kv_rope(
+        ctypes.byref(shape), B, _ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(rope),
+        _ptr(q_out), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens),
+        _stream_ptr(stream))
+    _check(rc, "pa_append_kv_rope")
+    return q_out
+
+
+def append_decode_attention_rope(q, k_new, v_new, rope_cos, rope_sin, k_pool, v_pool,
+                                 block_tables, seq_lens, max_seq_len: int, scale: float = 0.125,
+                                 out=None, out_dtype=torch.float32, pages_per_split: int = 0,
+                                 workspace=None, stream=None):
+    """Fused step with RoPE: rotate q/k at L-1, append, attend; returns ``out``."""
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if q.shape[0] != B or block_tables.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    num_pages, max_blocks = int(k_pool.shape[0]), int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rope = _rope(rope_cos, rope_sin)
+    shape = make_shape(num_pages, max_blocks)
+    rc = load_library().pa_append_decode_attention_rope(
+        ctypes.byref(shape), B, _ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(rope),
+        _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), int(max_seq_len),
+        float(scale), _ptr(out), code, int(pages_per_split), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check(rc, "pa_append_decode_attention_rope")
     return out
 
 

@@ -215,6 +215,13 @@ int check_decode_sizes(const pa_shape* shape, int32_t batch, int32_t max_seq_len
   return PA_OK;
 }
 
+int check_rope(const pa_rope* rope, int64_t needed_positions) {
+  if (!rope->cos || !rope->sin) return PA_ERR_NULL;
+  if (!aligned(rope->cos, 4) || !aligned(rope->sin, 4)) return PA_ERR_ALIGN;
+  if (rope->positions < 1 || rope->positions < needed_positions) return PA_ERR_VALUE;
+  return PA_OK;
+}
+
 }  // namespace
 
 PA_API int pa_abi_version(void) { return 1; }
@@ -294,7 +301,7 @@ PA_API int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch, int32
 namespace {
 // k_new/v_new non-NULL: the one-token append is fused into the main kernel
 int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_new,
-                const void* v_new, const void* k_pool,
+                const void* v_new, const pa_rope* rope, const void* k_pool,
                 const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                 int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
                 int32_t pages_per_split, void* workspace, size_t workspace_bytes,
@@ -311,6 +318,11 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
       !aligned(block_tables, 4) || !aligned(seq_lens, 4) ||
       (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))))
     return PA_ERR_ALIGN;
+  if (rope) {
+    if (!fused) return PA_ERR_VALUE;
+    rc = check_rope(rope, max_seq_len);
+    if (rc != PA_OK) return rc;
+  }
   if (shape->num_pages < 1 && max_seq_len > 0) return PA_ERR_VALUE;
   int ps = 0, ns = 0;
   rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
@@ -330,6 +342,8 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.v_new = (const uint16_t*)v_new;
   a.k_pool_w = (uint16_t*)k_pool;
   a.v_pool_w = (uint16_t*)v_pool;
+  a.rope_cos = rope ? rope->cos : nullptr;
+  a.rope_sin = rope ? rope->sin : nullptr;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = out;
@@ -350,10 +364,12 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
     return PA_ERR_LAUNCH;
   const dim3 block(pa::kThreads);
   if (out_dtype == PA_OUT_BF16) {
-    if (fused) hipLaunchKernelGGL((pa::decode_kernel<true, true>), grid, block, 0, st, a);
+    if (rope) hipLaunchKernelGGL((pa::decode_kernel<true, true, true>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((pa::decode_kernel<true, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((pa::decode_kernel<true, false>), grid, block, 0, st, a);
   } else {
-    if (fused) hipLaunchKernelGGL((pa::decode_kernel<false, true>), grid, block, 0, st, a);
+    if (rope) hipLaunchKernelGGL((pa::decode_kernel<false, true, true>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((pa::decode_kernel<false, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((pa::decode_kernel<false, false>), grid, block, 0, st, a);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
@@ -376,8 +392,8 @@ PA_API int pa_decode_attention(const pa_shape* shape, int32_t batch, const void*
                                int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
                                int32_t pages_per_split, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  return decode_impl(shape, batch, q, nullptr, nullptr, k_pool, v_pool, block_tables, seq_lens,
-                     max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+  return decode_impl(shape, batch, q, nullptr, nullptr, nullptr, k_pool, v_pool, block_tables,
+                     seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
                      workspace_bytes, stream, nullptr, nullptr);
 }
 
@@ -388,9 +404,50 @@ PA_API int pa_append_decode_attention(const pa_shape* shape, int32_t batch, cons
                                       void* out, int32_t out_dtype, int32_t pages_per_split,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   if (batch > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
-  return decode_impl(shape, batch, q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+  return decode_impl(shape, batch, q, k_new, v_new, nullptr, k_pool, v_pool, block_tables,
+                     seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+                     workspace_bytes, stream, nullptr, nullptr);
+}
+
+PA_API int pa_append_decode_attention_rope(const pa_shape* shape, int32_t batch, const void* q,
+                                           const void* k_new, const void* v_new,
+                                           const pa_rope* rope, void* k_pool, void* v_pool,
+                                           const int32_t* block_tables, const int32_t* seq_lens,
+                                           int32_t max_seq_len, float scale, void* out,
+                                           int32_t out_dtype, int32_t pages_per_split,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (batch > 0 && (!k_new || !v_new || !rope)) return PA_ERR_NULL;
+  return decode_impl(shape, batch, q, k_new, v_new, rope, k_pool, v_pool, block_tables, seq_lens,
                      max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
                      workspace_bytes, stream, nullptr, nullptr);
+}
+
+PA_API int pa_append_kv_rope(const pa_shape* shape, int32_t batch, const void* q,
+                             const void* k_new, const void* v_new, const pa_rope* rope,
+                             void* q_out, void* k_pool, void* v_pool,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             void* stream) {
+  int rc = check_shape(shape);
+  if (rc != PA_OK) return rc;
+  if (batch < 0) return PA_ERR_VALUE;
+  if (batch == 0) return PA_OK;
+  if (!q || !k_new || !v_new || !rope || !q_out || !k_pool || !v_pool || !block_tables ||
+      !seq_lens)
+    return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q_out, 16) ||
+      !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_tables, 4) ||
+      !aligned(seq_lens, 4))
+    return PA_ERR_ALIGN;
+  if (shape->num_pages < 1) return PA_ERR_VALUE;
+  rc = check_rope(rope, (int64_t)shape->max_blocks_per_seq * pa::kPage);
+  if (rc != PA_OK) return rc;
+  hipLaunchKernelGGL(pa::append_rope_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new,
+                     rope->cos, rope->sin, (uint16_t*)q_out, (uint16_t*)k_pool,
+                     (uint16_t*)v_pool, block_tables, seq_lens, shape->max_blocks_per_seq,
+                     shape->num_pages);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, const void* q,
@@ -401,8 +458,8 @@ PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, co
                                         int32_t out_dtype, int32_t pages_per_split,
                                         void* workspace, size_t workspace_bytes, void* stream,
                                         void* event_before_main, void* event_after_main) {
-  return decode_impl(shape, batch, q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
-                     max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+  return decode_impl(shape, batch, q, k_new, v_new, nullptr, k_pool, v_pool, block_tables,
+                     seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
                      workspace_bytes, stream, event_before_main, event_after_main);
 }
 

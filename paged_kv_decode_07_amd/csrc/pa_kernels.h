@@ -97,6 +97,44 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Rotary embedding of rotate-half pairs (x[i], x[i+32]).  Each product and
+// the sum are rounded to FP32 on their own: contraction into a fused
+// multiply-add is switched off here (only here), because the result is then
+// rounded to BF16 and a one-ulp FP32 difference flips ties of that rounding.
+// rope_pairs8: lo holds x[8c .. 8c+7], hi holds x[32+8c .. 32+8c+7] (BF16),
+// cs/sn the cos/sin of their angles; the result is rounded to BF16 (RNE).
+__device__ __forceinline__ float rope_first(float x1, float x2, float c, float s) {
+#pragma clang fp contract(off)
+  return x1 * c - x2 * s;                 // two rounded products, one rounded difference
+}
+__device__ __forceinline__ float rope_second(float x1, float x2, float c, float s) {
+#pragma clang fp contract(off)
+  return x2 * c + x1 * s;
+}
+
+__device__ __forceinline__ void rope_pairs8(uint4& lo, uint4& hi, const float* cs,
+                                            const float* sn) {
+  uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w}, h[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t ol = 0, oh = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = 2 * w + k;
+      const float x1 = k ? bf16_hi(l[w]) : bf16_lo(l[w]);
+      const float x2 = k ? bf16_hi(h[w]) : bf16_lo(h[w]);
+      const float y1 = rope_first(x1, x2, cs[e], sn[e]);
+      const float y2 = rope_second(x1, x2, cs[e], sn[e]);
+      ol |= f32_to_bf16_rne(y1) << (16 * k);
+      oh |= f32_to_bf16_rne(y2) << (16 * k);
+    }
+    l[w] = ol;
+    h[w] = oh;
+  }
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct PageRegs {
@@ -267,6 +305,8 @@ struct DecodeArgs {
   const uint16_t* v_new;
   uint16_t* k_pool_w;      // fused append: the same pools, written at slot L-1
   uint16_t* v_pool_w;
+  const float* rope_cos;   // fused RoPE: [positions][32] cos / sin of the rotation angles
+  const float* rope_sin;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
@@ -284,9 +324,13 @@ struct DecodeArgs {
 // holds the sequence's last page writes the new K/V row (token L-1) into its
 // page slot and uses the same values, from registers, in place of what the
 // page stream read for that slot; no other work-group reads that page.
-template <bool OUT_BF16, bool APPEND>
+// ROPE (with APPEND): the new query and key are rotated at their absolute
+// position L-1 first; every work-group of the sequence rotates its own q
+// rows (lane-local: a lane holds both halves of each rotate-half pair).
+template <bool OUT_BF16, bool APPEND, bool ROPE = false>
 // second bound: minimum waves per SIMD (a work-group puts 2 on each SIMD)
 __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeArgs a) {
+  static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   const int s = blockIdx.x;
   const int b = blockIdx.y;
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wavefront
@@ -321,20 +365,36 @@ __global__ __launch_bounds__(kThreads, 2 * kWgPerCu) void decode_kernel(DecodeAr
   bf16x8_t qlo, qhi;
   {
     const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (token & 3)) * kD + 8 * part;
-    qlo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr));
-    qhi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr + 32));
+    uint4 lo = *reinterpret_cast<const uint4*>(qr);
+    uint4 hi = *reinterpret_cast<const uint4*>(qr + 32);
+    if (ROPE) {
+      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * part;
+      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+    }
+    qlo = __builtin_bit_cast(bf16x8_t, lo);
+    qhi = __builtin_bit_cast(bf16x8_t, hi);
   }
 
   // fused append: the new K and V row of head g (128 + 128 bytes) is parked
   // in LDS for the page stream's last page (keeps 16 VGPRs free in the loop):
-  // lanes 0..15 each copy 16 bytes, K row then V row.
+  // slots 0..7 hold K dims 8j..8j+7, slots 8..15 the V ones.  Lane c < 4
+  // takes K dims {8c..} and {32+8c..} (one set of rotate-half pairs, rotated
+  // here with RoPE), lane 4 + c the same V dims.
   const bool app_here = APPEND && p1 == n_pages;     // this split holds token L-1
   const int app_slot = (L - 1) % kPage;
   __shared__ uint4 new_rows[APPEND ? kWaves : 1][16];
-  if (app_here && lane < 16) {
-    const uint16_t* src = (lane < 8 ? a.k_new : a.v_new) +
-                          ((int64_t)b * kHkv + g) * kD + 8 * (lane & 7);
-    new_rows[g][lane] = *reinterpret_cast<const uint4*>(src);
+  if (app_here && lane < 8) {
+    const int c = lane & 3;
+    const bool is_k = lane < 4;
+    const uint16_t* src = (is_k ? a.k_new : a.v_new) + ((int64_t)b * kHkv + g) * kD + 8 * c;
+    uint4 lo = *reinterpret_cast<const uint4*>(src);
+    uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
+    if (ROPE && is_k) {
+      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * c;
+      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+    }
+    new_rows[g][(is_k ? 0 : 8) + c] = lo;
+    new_rows[g][(is_k ? 0 : 8) + 4 + c] = hi;
   }
 
   LaneState st;
@@ -562,6 +622,59 @@ __global__ __launch_bounds__(64) void append_kernel(const uint4* __restrict__ k_
   const int64_t row = (int64_t)id * kPage + (pos % kPage);   // 1 KiB rows = 64 x uint4
   k_pool[row * 64 + lane] = k_new[(int64_t)b * 64 + lane];
   v_pool[row * 64 + lane] = v_new[(int64_t)b * 64 + lane];
+}
+
+// One-token append with RoPE: one work-group of 256 threads per sequence
+// rotates the new query (32 heads x 32 pairs, into q_out) and key (8 x 32
+// pairs) at position L-1 and writes the rotated key and the value into the
+// page slot.  Idle slots and out-of-range metadata write no pool bytes; their
+// q_out row is a copy of q.
+__global__ __launch_bounds__(256) void append_rope_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
+    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    int32_t max_blocks, int32_t num_pages) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int L = seq_lens[b];
+  const bool live = L >= 1 && L <= max_blocks * kPage;
+  const int pos = live ? L - 1 : 0;
+  const int64_t cs_row = (int64_t)pos * (kD / 2);
+  // query: thread t rotates pairs j = t, t+256, t+512, t+768 (head j/32, dim j%32)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = t + 256 * r;
+    const int64_t base = ((int64_t)b * kHq + (j >> 5)) * kD + (j & 31);
+    const uint16_t x1b = q[base], x2b = q[base + 32];
+    uint16_t y1b = x1b, y2b = x2b;
+    if (live) {
+      const float x1 = __uint_as_float((uint32_t)x1b << 16);
+      const float x2 = __uint_as_float((uint32_t)x2b << 16);
+      const float c = rope_cos[cs_row + (j & 31)], sn = rope_sin[cs_row + (j & 31)];
+      y1b = (uint16_t)f32_to_bf16_rne(rope_first(x1, x2, c, sn));
+      y2b = (uint16_t)f32_to_bf16_rne(rope_second(x1, x2, c, sn));
+    }
+    q_out[base] = y1b;
+    q_out[base + 32] = y2b;
+  }
+  if (!live) return;
+  const int id = block_tables[(int64_t)b * max_blocks + pos / kPage];
+  if ((unsigned)id >= (unsigned)num_pages) return;
+  const int64_t row = ((int64_t)id * kPage + (pos % kPage)) * kRowElems;   // token row
+  {  // key: thread t rotates pair (head t/32, dim t%32)
+    const int64_t src = (int64_t)b * kRowElems + (t >> 5) * kD + (t & 31);
+    const float x1 = __uint_as_float((uint32_t)k_new[src] << 16);
+    const float x2 = __uint_as_float((uint32_t)k_new[src + 32] << 16);
+    const float c = rope_cos[cs_row + (t & 31)], sn = rope_sin[cs_row + (t & 31)];
+    const int64_t dst = row + (t >> 5) * kD + (t & 31);
+    k_pool[dst] = (uint16_t)f32_to_bf16_rne(rope_first(x1, x2, c, sn));
+    k_pool[dst + 32] = (uint16_t)f32_to_bf16_rne(rope_second(x1, x2, c, sn));
+  }
+  if (t < 64)  // value: 64 x 16 bytes
+    reinterpret_cast<uint4*>(v_pool + row)[t] =
+        reinterpret_cast<const uint4*>(v_new + (int64_t)b * kRowElems)[t];
 }
 
 }  // namespace pa

@@ -288,3 +288,16 @@ def poison_summary(batch: DecodeBatch) -> dict:
     """Counts of poisoned pool rows and block-table entries (for reports)."""
     nan_rows = int(np.count_nonzero(batch.k_pool[..., 0, 0] == BF16_NAN))
     return {"nan_slots": nan_rows, "unused_bt": int(np.count_nonzero(batch.block_tables < 0))}
+
+
+def rope_table(max_pos: int = MAX_CONTEXT, head_dim: int = HEAD_DIM, base: float = 500000.0):
+    """Float32 cos and sin ``[max_pos][head_dim/2]`` for rotary embeddings.
+
+    Frequency ``i`` is ``base ** (-2 i / head_dim)`` (500000 is the Llama-3
+    base); angles are formed and evaluated in float64, then rounded to float32.
+    Callers that use another frequency schedule pass their own table.
+    """
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * i / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
