@@ -241,6 +241,42 @@ def main() -> int:
     rope_step()
     t_rope = timed(rope_step, K)
     log(f"{K} breakdown, {K} two-call and {K} RoPE steps done")
+
+    # prefill page fill of one 2048-token prompt (2 x 2 MiB moved, read + write),
+    # into a scratch pool of its own so the measured cache stays untouched
+    fill_rows = torch.from_numpy(np.ascontiguousarray(
+        W.random_rows(np.random.default_rng(9), W.MAX_CONTEXT)).view(np.int16)).to(dev)
+    fill_bt = torch.arange(W.MAX_BLOCKS, dtype=torch.int32, device=dev)
+    fill_k = torch.empty((W.MAX_BLOCKS, 16, 8, 64), dtype=torch.int16, device=dev)
+    fill_v = torch.empty_like(fill_k)
+
+    def fill_step():
+        pa.fill_kv(fill_rows, fill_rows, fill_bt, 0, fill_k, fill_v, stream=stream)
+    fill_step()
+    t_fill = timed(fill_step, K)
+    fill_bytes = 2 * 2 * W.MAX_CONTEXT * 1024
+
+    # host page allocator: one decode step of the batch (grow every sequence by
+    # a token, mark the step), 16 layers, sequences crossing page boundaries
+    alloc = pa.KVPool(2 * B * 16 * 128, 16, 16, W.MAX_CONTEXT)
+    for rid in range(B):
+        alloc.submit(rid, 1000, 1000)
+    alloc.admit(capacity=B)
+    for rid in range(B):
+        alloc.grow(rid, 1000)
+    t0 = time.perf_counter()
+    n_steps = 64
+    for s_i in range(n_steps):
+        for rid in range(B):
+            alloc.grow(rid, 1001 + s_i)
+        alloc.step()
+    alloc_step_us = (time.perf_counter() - t0) / n_steps * 1e6
+    alloc.close()
+
+    # the RoPE pass left rotated keys in the appended slots and its own output:
+    # one more plain step restores the state the oracle recomputes
+    step()
+    torch.cuda.synchronize()
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
     mean_step = float(t_step.mean())
@@ -280,7 +316,10 @@ def main() -> int:
             "main_kernel": round(float(t_main.mean()) * 1e6, 2),
             "two_call_step": round(float(t_two.mean()) * 1e6, 2),
             "rope_fused_step": round(float(t_rope.mean()) * 1e6, 2),
+            "prefill_fill_2048_tokens": round(float(t_fill.mean()) * 1e6, 2),
         },
+        "prefill_fill_gbps": round(fill_bytes / float(t_fill.mean()) / 1e9, 1),
+        "allocator_us_per_decode_step": round(alloc_step_us, 1),
         "two_call_kv_gbps": round(kv / float(t_two.mean()) / 1e9, 2),
         "roofline": {
             "bound": "hbm",

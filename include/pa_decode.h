@@ -110,6 +110,19 @@ int pa_append_kv(const pa_shape* shape, int32_t batch,
                  void* stream);
 
 /*
+ * Prefill page fill: write tokens start .. start+num_tokens-1 of one
+ * sequence into its pages (the prompt's K/V, one prompt at a time, as the
+ * engine prefills), token t into page block_table_row[t/16], slot t%16.
+ * k_rows, v_rows: BF16 [num_tokens][8][64] (16-byte aligned);
+ * block_table_row: int32 device row of that sequence (4-byte aligned).
+ * Bit-exact copy; tokens whose page id is outside [0, num_pages) are
+ * skipped.  start + num_tokens must not exceed 16 * max_blocks_per_seq.
+ */
+int pa_fill_kv(const pa_shape* shape, const void* k_rows, const void* v_rows,
+               int32_t num_tokens, int32_t start, const int32_t* block_table_row,
+               void* k_pool, void* v_pool, void* stream);
+
+/*
  * Workspace needed by pa_decode_attention for these arguments, in bytes
  * (0 when every sequence fits one split).  pages_per_split is 0 to let the
  * library plan (the plan then depends on the current device's compute-unit

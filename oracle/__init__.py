@@ -33,6 +33,7 @@ from .paged_decode import (  # noqa: F401
     attention_one_query,
     decode_attention,
     append_kv,
+    fill_kv,
     kv_head_of,
 )
-from . import rope  # noqa: F401,E402
+from . import admission, rope  # noqa: F401,E402

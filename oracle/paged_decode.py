@@ -182,3 +182,22 @@ def append_kv(k_pool_bits, v_pool_bits, k_new_bits, v_new_bits, block_tables, se
         k_out[physical, slot] = k_new_bits[b]
         v_out[physical, slot] = v_new_bits[b]
     return k_out, v_out
+
+
+def fill_kv(k_pool_bits, v_pool_bits, k_rows_bits, v_rows_bits, block_table_row, start: int):
+    """Write tokens ``start .. start+T-1`` of one sequence into its pages; return new pools.
+
+    The prefill fills the prompt's pages ("6 Hours of YouTube ...", features
+    completed so far: prefill fills the prompt pages, decode appends one
+    token); token t goes to page ``block_table_row[t // P]``, slot ``t % P``.
+    ``k_rows_bits``/``v_rows_bits``: ``[T][Hkv][D]``.  Integer copy only.
+    """
+    k_out = np.array(k_pool_bits, copy=True)
+    v_out = np.array(v_pool_bits, copy=True)
+    page_size = k_out.shape[1]
+    for j in range(len(k_rows_bits)):
+        t = start + j
+        physical = int(block_table_row[t // page_size])
+        k_out[physical, t % page_size] = k_rows_bits[j]
+        v_out[physical, t % page_size] = v_rows_bits[j]
+    return k_out, v_out

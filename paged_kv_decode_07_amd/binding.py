@@ -23,17 +23,26 @@ _lib = None
 PA_OUT_F32, PA_OUT_BF16 = 0, 1
 HQ, HKV, D, PAGE = 32, 8, 64, 16
 
-# names declared in include/pa_decode.h
+# names declared in include/pa_decode.h and include/pa_kvpool.h
 EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_decode_plan_lengths",
            "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
-           "pa_append_kv_rope", "pa_append_decode_attention_rope",
-           "pa_validate_metadata", "pa_status_string", "pa_abi_version")
+           "pa_append_kv_rope", "pa_append_decode_attention_rope", "pa_fill_kv",
+           "pa_validate_metadata", "pa_status_string", "pa_abi_version",
+           # include/pa_kvpool.h
+           "pa_kvpool_create", "pa_kvpool_destroy", "pa_kvpool_credit", "pa_kvpool_submit",
+           "pa_kvpool_admit", "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
+           "pa_kvpool_block_table", "pa_kvpool_request_info", "pa_kvpool_get_stats")
 
 
 class PaShape(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+class KVPoolStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("pool_pages", "peak_active", "max_batch",
+                                              "peak_allocated", "admission_waits", "free_pages")]
 
 
 class PaRope(ctypes.Structure):
@@ -74,6 +83,22 @@ def load_library(path: str | None = None):
         lib.pa_append_kv_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P, P]
         lib.pa_append_decode_attention_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, I32,
                                                         ctypes.c_float, P, I32, I32, P, SZ, P]
+        lib.pa_fill_kv.argtypes = [SP, P, P, I32, I32, P, P, P, P]
+        I64 = ctypes.c_int64
+        PP = ctypes.POINTER(ctypes.c_void_p)
+        lib.pa_kvpool_create.argtypes = [I32, I32, I32, I32, I32, PP]
+        lib.pa_kvpool_destroy.argtypes = [P]
+        lib.pa_kvpool_credit.argtypes = [P, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)]
+        lib.pa_kvpool_submit.argtypes = [P, I64, I32, I32, ctypes.POINTER(I32)]
+        lib.pa_kvpool_admit.argtypes = [P, ctypes.POINTER(I64), I32, ctypes.POINTER(I32)]
+        lib.pa_kvpool_grow.argtypes = [P, I64, I32]
+        lib.pa_kvpool_step.argtypes = [P]
+        lib.pa_kvpool_finish.argtypes = [P, I64]
+        lib.pa_kvpool_block_table.argtypes = [P, I64, I32, ctypes.POINTER(I32), I32,
+                                              ctypes.POINTER(I32)]
+        lib.pa_kvpool_request_info.argtypes = [P, I64, ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                               ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        lib.pa_kvpool_get_stats.argtypes = [P, ctypes.POINTER(KVPoolStats)]
         lib.pa_validate_metadata.argtypes = [SP, I32, P, P, I32, P, ctypes.POINTER(ctypes.c_int64)]
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
@@ -83,7 +108,11 @@ def load_library(path: str | None = None):
                      "pa_decode_attention", "pa_decode_attention_profiled",
                      "pa_append_decode_attention", "pa_append_kv_rope",
                      "pa_append_decode_attention_rope", "pa_validate_metadata",
-                     "pa_abi_version"):
+                     "pa_abi_version", "pa_fill_kv", "pa_kvpool_create", "pa_kvpool_destroy",
+                     "pa_kvpool_credit", "pa_kvpool_submit", "pa_kvpool_admit",
+                     "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
+                     "pa_kvpool_block_table", "pa_kvpool_request_info",
+                     "pa_kvpool_get_stats"):
             getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
@@ -350,6 +379,95 @@ def append_decode_attention_rope(q, k_new, v_new, rope_cos, rope_sin, k_pool, v_
         workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check(rc, "pa_append_decode_attention_rope")
     return out
+
+
+def fill_kv(k_rows, v_rows, block_table_row, start: int, k_pool, v_pool, stream=None) -> None:
+    """Prefill page fill: tokens ``start .. start+T-1`` of one sequence into its pages."""
+    _bits16(k_rows, "k_rows", (HKV, D)); _bits16(v_rows, "v_rows", (HKV, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_table_row, "block_table_row")
+    if k_rows.shape != v_rows.shape:
+        raise ValueError("k_rows and v_rows differ in shape")
+    shape = make_shape(int(k_pool.shape[0]), int(block_table_row.shape[-1]))
+    rc = load_library().pa_fill_kv(ctypes.byref(shape), _ptr(k_rows), _ptr(v_rows),
+                                   int(k_rows.shape[0]), int(start), _ptr(block_table_row),
+                                   _ptr(k_pool), _ptr(v_pool), _stream_ptr(stream))
+    _check(rc, "pa_fill_kv")
+
+
+class KVPool:
+    """Host page allocator and admission control (``include/pa_kvpool.h``)."""
+
+    WAIT, REJECT = "wait", "reject"
+
+    def __init__(self, num_pages: int, num_layers: int = 16, page_tokens: int = PAGE,
+                 context: int = 2048, static: bool = False):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_kvpool_create(num_pages, num_layers, page_tokens, context,
+                                          int(static), ctypes.byref(h)), "pa_kvpool_create")
+        self._h = h
+        self.num_pages, self.layers = num_pages, num_layers
+
+    def close(self):
+        if self._h:
+            self._lib.pa_kvpool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def credit_for(self, prompt: int, max_new: int):
+        a, c = ctypes.c_int32(), ctypes.c_int64()
+        _check(self._lib.pa_kvpool_credit(self._h, prompt, max_new, ctypes.byref(a),
+                                          ctypes.byref(c)), "pa_kvpool_credit")
+        return a.value, c.value
+
+    def submit(self, rid: int, prompt: int, max_new: int) -> str:
+        r = ctypes.c_int32()
+        _check(self._lib.pa_kvpool_submit(self._h, rid, prompt, max_new, ctypes.byref(r)),
+               "pa_kvpool_submit")
+        return self.WAIT if r.value == 1 else self.REJECT
+
+    def admit(self, capacity: int = 65536):
+        arr = (ctypes.c_int64 * capacity)()
+        n = ctypes.c_int32()
+        _check(self._lib.pa_kvpool_admit(self._h, arr, capacity, ctypes.byref(n)),
+               "pa_kvpool_admit")
+        return [arr[i] for i in range(n.value)]
+
+    def grow(self, rid: int, length: int) -> None:
+        _check(self._lib.pa_kvpool_grow(self._h, rid, length), "pa_kvpool_grow")
+
+    def step(self) -> None:
+        _check(self._lib.pa_kvpool_step(self._h), "pa_kvpool_step")
+
+    def finish(self, rid: int) -> None:
+        _check(self._lib.pa_kvpool_finish(self._h, rid), "pa_kvpool_finish")
+
+    def block_table(self, rid: int, layer: int, capacity: int = 128):
+        row = (ctypes.c_int32 * capacity)()
+        n = ctypes.c_int32()
+        _check(self._lib.pa_kvpool_block_table(self._h, rid, layer, row, capacity,
+                                               ctypes.byref(n)), "pa_kvpool_block_table")
+        return [row[i] for i in range(n.value)]
+
+    def info(self, rid: int):
+        a, c, L, act = (ctypes.c_int32() for _ in range(4))
+        _check(self._lib.pa_kvpool_request_info(self._h, rid, ctypes.byref(a), ctypes.byref(c),
+                                                ctypes.byref(L), ctypes.byref(act)),
+               "pa_kvpool_request_info")
+        return {"allowed_new": a.value, "credit": c.value, "length": L.value,
+                "active": bool(act.value)}
+
+    @property
+    def stats(self):
+        st = KVPoolStats()
+        _check(self._lib.pa_kvpool_get_stats(self._h, ctypes.byref(st)), "pa_kvpool_get_stats")
+        return {n: getattr(st, n) for n, _ in KVPoolStats._fields_}
 
 
 def validate_metadata(block_tables, seq_lens, max_seq_len: int, num_pages: int, stream=None):

@@ -1,8 +1,9 @@
 """Build the HIP library in-tree with hipcc for gfx950.
 
-``python -m paged_kv_decode_07_amd.build`` compiles
-``csrc/pa_decode.hip`` (with ``csrc/pa_kernels.h``) and the header in
-``include/`` into ``paged_kv_decode_07_amd/_lib/libpa_decode.so``.
+``python -m paged_kv_decode_07_amd.build`` compiles ``csrc/pa_decode.hip``
+(device kernels in ``csrc/pa_kernels.h``) and ``csrc/pa_kvpool.cpp`` (host
+page allocator), against the headers in ``include/``, into
+``paged_kv_decode_07_amd/_lib/libpa_decode.so``.
 """
 
 from __future__ import annotations
@@ -14,7 +15,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "pa_decode.hip")
+SRCS = [os.path.join(PKG, "csrc", "pa_decode.hip"), os.path.join(PKG, "csrc", "pa_kvpool.cpp")]
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libpa_decode.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
@@ -39,7 +40,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS,
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           SRC, "-o", tmp]
+           *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

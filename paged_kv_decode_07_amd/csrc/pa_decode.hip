@@ -259,6 +259,26 @@ PA_API int pa_append_kv(const pa_shape* shape, int32_t batch, const void* k_new,
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+PA_API int pa_fill_kv(const pa_shape* shape, const void* k_rows, const void* v_rows,
+                      int32_t num_tokens, int32_t start, const int32_t* block_table_row,
+                      void* k_pool, void* v_pool, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0 || start < 0 ||
+      (int64_t)start + num_tokens > (int64_t)shape->max_blocks_per_seq * pa::kPage)
+    return PA_ERR_VALUE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_rows || !v_rows || !block_table_row || !k_pool || !v_pool) return PA_ERR_NULL;
+  if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(k_pool, 16) ||
+      !aligned(v_pool, 16) || !aligned(block_table_row, 4))
+    return PA_ERR_ALIGN;
+  if (shape->num_pages < 1) return PA_ERR_VALUE;
+  hipLaunchKernelGGL(pa::fill_kernel, dim3(ceil_div(num_tokens, 4)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint4*)k_rows, (const uint4*)v_rows, num_tokens,
+                     start, block_table_row, (uint4*)k_pool, (uint4*)v_pool, shape->num_pages);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 PA_API int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_len,
                           int32_t pages_per_split, int32_t* pages_out, int32_t* splits_out) {
   int rc = check_decode_sizes(shape, batch, max_seq_len);

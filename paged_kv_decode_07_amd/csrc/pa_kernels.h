@@ -624,6 +624,28 @@ __global__ __launch_bounds__(64) void append_kernel(const uint4* __restrict__ k_
   v_pool[row * 64 + lane] = v_new[(int64_t)b * 64 + lane];
 }
 
+// Prefill page fill: tokens start .. start+T-1 of one sequence (K and V
+// rows of 1 KiB each) into their page slots; 4 tokens per work-group, one
+// wavefront per token, 16 bytes per lane.  Tokens whose page id is out of
+// range are skipped.
+__global__ __launch_bounds__(256) void fill_kernel(const uint4* __restrict__ k_rows,
+                                                   const uint4* __restrict__ v_rows,
+                                                   int32_t num_tokens, int32_t start,
+                                                   const int32_t* __restrict__ bt_row,
+                                                   uint4* __restrict__ k_pool,
+                                                   uint4* __restrict__ v_pool,
+                                                   int32_t num_pages) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= num_tokens) return;
+  const int t = start + tok;
+  const int id = bt_row[t / kPage];
+  if ((unsigned)id >= (unsigned)num_pages) return;
+  const int64_t row = (int64_t)id * kPage + (t % kPage);
+  k_pool[row * 64 + lane] = k_rows[(int64_t)tok * 64 + lane];
+  v_pool[row * 64 + lane] = v_rows[(int64_t)tok * 64 + lane];
+}
+
 // One-token append with RoPE: one work-group of 256 threads per sequence
 // rotates the new query (32 heads x 32 pairs, into q_out) and key (8 x 32
 // pairs) at position L-1 and writes the rotated key and the value into the
