@@ -38,7 +38,7 @@ METRIC = "decode-attention KV-read GB/s (% of MI355X HBM peak) + sequences/s per
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic_b256_l2048.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc", n)
-                  for n in ("pa_kernels.h", "pa_decode.hip")]
+                  for n in ("pa_kernels.h", "pa_decode.hip", "pa_host.h")]
 
 
 def log(msg: str) -> None:

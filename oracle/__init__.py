@@ -36,4 +36,4 @@ from .paged_decode import (  # noqa: F401
     fill_kv,
     kv_head_of,
 )
-from . import admission, rope  # noqa: F401,E402
+from . import admission, kvquant, rope  # noqa: F401,E402

@@ -10,11 +10,12 @@
 #include <vector>
 
 #include "pa_decode.h"
+#include "pa_host.h"
 #include "pa_kernels.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
-namespace {
+namespace pa_host {
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
@@ -91,17 +92,11 @@ int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pa
 // constants were fitted to measurements of this kernel on MI355X over batch
 // 8 .. 512 and split sizes 8 .. 128.  The largest size predicted within 3%
 // of the fastest is returned (the model's error is about that size).
-struct PlanModel {
-  double page_us = 0.85, group_us = 6.0, empty_us = 0.5, merge_us = 8.0;
-  double hbm_bytes_per_us = 6.1e6;
-};
-
 double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,
                      const PlanModel& m) {
   const int max_pages = ceil_div(max_seq_len, pa::kPage);
   const int S = ceil_div(max_pages, ps);
-  const double page_bytes = 2.0 * pa::kPageElems * 2;            // K + V page, bytes
-  const double chip_rate = m.hbm_bytes_per_us / page_bytes;      // pages/us, whole chip
+  const double chip_rate = m.hbm_bytes_per_us / m.page_bytes;    // pages/us, whole chip
   const double cu_rate = 1.0 / m.page_us;                        // pages/us, one CU alone
   const int per_xcd = cu / xcds > 0 ? cu / xcds : 1;
   struct Item { double fixed, pages; };
@@ -170,7 +165,7 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
 }
 
 int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int max_seq_len,
-                       int num_cus, int* pages, int* splits) {
+                       int num_cus, const PlanModel& model, int* pages, int* splits) {
   int cu = num_cus;
   if (cu <= 0) {
     const int rc = current_cu_count(&cu);
@@ -179,7 +174,6 @@ int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int ma
   const int max_pages = ceil_div(max_seq_len, pa::kPage);
   if (max_pages <= 0) { *pages = 1; *splits = 1; return PA_OK; }
   const int xcds = (cu % 8 == 0) ? 8 : 1;         // MI300-class parts: 8 XCDs
-  const PlanModel model;
   std::vector<std::pair<int, double>> cands;
   for (int ps : {8, 16, 32, 64, 128, 256}) {
     const int cand = ps < max_pages ? ps : max_pages;
@@ -222,7 +216,9 @@ int check_rope(const pa_rope* rope, int64_t needed_positions) {
   return PA_OK;
 }
 
-}  // namespace
+}  // namespace pa_host
+
+using namespace pa_host;
 
 PA_API int pa_abi_version(void) { return 1; }
 
@@ -300,7 +296,8 @@ PA_API int pa_decode_plan_lengths(const pa_shape* shape, int32_t batch,
   if (num_cus < 0) return PA_ERR_VALUE;
   int ps = 1, ns = 1;
   if (batch > 0) {
-    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, &ps, &ns);
+    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, PlanModel(), &ps,
+                            &ns);
     if (rc != PA_OK) return rc;
   }
   if (pages_out) *pages_out = ps;

@@ -1,0 +1,43 @@
+// Host-side helpers shared by the library's entry points (argument checks,
+// device queries, split planning).  Internal to the shared library: nothing
+// here is exported.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa_decode.h"
+
+namespace pa_host {
+
+bool aligned(const void* p, size_t a);
+int ceil_div(int a, int b);
+// Compute units of the current device (queried once per device).
+int current_cu_count(int* cu);
+// Fixed geometry: 32 query heads, 8 KV heads, head_dim 64, 16-token pages.
+int check_shape(const pa_shape* s);
+int check_decode_sizes(const pa_shape* shape, int32_t batch, int32_t max_seq_len);
+int check_rope(const pa_rope* rope, int64_t needed_positions);
+// Split size without sequence lengths (fixed != 0: that size, validated).
+int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pages, int* splits);
+
+// Cost model of one decode launch, used to pick the split size from host
+// sequence lengths: a work-group spends group_us on fixed costs, then
+// streams its pages, all streaming work-groups sharing the HBM bandwidth
+// equally but none faster than one CU alone (page_us per page of page_bytes
+// bytes); empty grid slots cost empty_us; a multi-split plan adds the merge.
+// The defaults were fitted to the BF16 kernel on MI355X over batch 8 .. 512
+// and split sizes 8 .. 128.
+struct PlanModel {
+  double page_us = 0.85, group_us = 6.0, empty_us = 0.5, merge_us = 8.0;
+  double hbm_bytes_per_us = 6.1e6;
+  double page_bytes = 2.0 * 16 * 8 * 64 * 2;   // one K page and one V page, BF16
+};
+double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,
+                     const PlanModel& m);
+int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int max_seq_len,
+                       int num_cus, const PlanModel& model, int* pages, int* splits);
+// Bytes of split partials for `splits` splits per sequence (0 for one split).
+size_t workspace_for(int batch, int splits);
+
+}  // namespace pa_host
