@@ -23,11 +23,15 @@ _lib = None
 PA_OUT_F32, PA_OUT_BF16 = 0, 1
 HQ, HKV, D, PAGE = 32, 8, 64, 16
 
-# names declared in include/pa_decode.h and include/pa_kvpool.h
+# names declared in include/pa_decode.h, include/pa_decode_q8.h and include/pa_kvpool.h
 EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_decode_plan_lengths",
            "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
            "pa_append_kv_rope", "pa_append_decode_attention_rope", "pa_fill_kv",
            "pa_validate_metadata", "pa_status_string", "pa_abi_version",
+           # include/pa_decode_q8.h
+           "pa_append_kv_q8", "pa_append_kv_rope_q8", "pa_fill_kv_q8", "pa_decode_attention_q8",
+           "pa_append_decode_attention_q8", "pa_append_decode_attention_rope_q8",
+           "pa_decode_plan_lengths_q8",
            # include/pa_kvpool.h
            "pa_kvpool_create", "pa_kvpool_destroy", "pa_kvpool_credit", "pa_kvpool_submit",
            "pa_kvpool_admit", "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
@@ -84,6 +88,18 @@ def load_library(path: str | None = None):
         lib.pa_append_decode_attention_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, I32,
                                                         ctypes.c_float, P, I32, I32, P, SZ, P]
         lib.pa_fill_kv.argtypes = [SP, P, P, I32, I32, P, P, P, P]
+        lib.pa_append_kv_q8.argtypes = [SP, I32, P, P, P, P, P, P, P, P]
+        lib.pa_append_kv_rope_q8.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P, P, P]
+        lib.pa_fill_kv_q8.argtypes = [SP, P, P, I32, I32, P, P, P, P, P]
+        lib.pa_decode_attention_q8.argtypes = [SP, I32, P, P, P, P, P, P, I32, ctypes.c_float,
+                                               P, I32, I32, P, SZ, P]
+        lib.pa_append_decode_attention_q8.argtypes = [SP, I32, P, P, P, P, P, P, P, P, I32,
+                                                      ctypes.c_float, P, I32, I32, P, SZ, P]
+        lib.pa_append_decode_attention_rope_q8.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P,
+                                                           I32, ctypes.c_float, P, I32, I32, P,
+                                                           SZ, P]
+        lib.pa_decode_plan_lengths_q8.argtypes = [SP, I32, P, I32, I32, ctypes.POINTER(I32),
+                                                  ctypes.POINTER(I32)]
         I64 = ctypes.c_int64
         PP = ctypes.POINTER(ctypes.c_void_p)
         lib.pa_kvpool_create.argtypes = [I32, I32, I32, I32, I32, PP]
@@ -112,7 +128,9 @@ def load_library(path: str | None = None):
                      "pa_kvpool_credit", "pa_kvpool_submit", "pa_kvpool_admit",
                      "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
                      "pa_kvpool_block_table", "pa_kvpool_request_info",
-                     "pa_kvpool_get_stats"):
+                     "pa_kvpool_get_stats", "pa_append_kv_q8", "pa_append_kv_rope_q8",
+                     "pa_fill_kv_q8", "pa_decode_attention_q8", "pa_append_decode_attention_q8",
+                     "pa_append_decode_attention_rope_q8", "pa_decode_plan_lengths_q8"):
             getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
@@ -393,6 +411,162 @@ def fill_kv(k_rows, v_rows, block_table_row, start: int, k_pool, v_pool, stream=
                                    int(k_rows.shape[0]), int(start), _ptr(block_table_row),
                                    _ptr(k_pool), _ptr(v_pool), _stream_ptr(stream))
     _check(rc, "pa_fill_kv")
+
+
+# ---------------------------------------------------------------------------
+# INT8 K/V pages (include/pa_decode_q8.h)
+# ---------------------------------------------------------------------------
+def new_q8_pools(num_pages: int, device="cuda"):
+    """Zeroed INT8 pools: K codes, V codes (int8 ``[pages][16][8][64]``) and scales
+    (float32 ``[pages][8][2][16]``)."""
+    codes = (num_pages, PAGE, HKV, D)
+    return (torch.zeros(codes, dtype=torch.int8, device=device),
+            torch.zeros(codes, dtype=torch.int8, device=device),
+            torch.zeros((num_pages, HKV, 2, PAGE), dtype=torch.float32, device=device))
+
+
+def _q8_pools(k_codes, v_codes, kv_scales) -> int:
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() or \
+                tuple(t.shape[1:]) != (PAGE, HKV, D):
+            raise ValueError(f"{name}: must be a contiguous int8 [pages][16][8][64] device tensor")
+    if k_codes.shape != v_codes.shape:
+        raise ValueError("k_codes and v_codes differ in shape")
+    n = int(k_codes.shape[0])
+    if kv_scales.dtype != torch.float32 or not kv_scales.is_cuda or \
+            not kv_scales.is_contiguous() or tuple(kv_scales.shape) != (n, HKV, 2, PAGE):
+        raise ValueError("kv_scales: must be a contiguous float32 [pages][8][2][16] device tensor")
+    return n
+
+
+def append_kv_q8(k_new, v_new, k_codes, v_codes, kv_scales, block_tables, seq_lens,
+                 stream=None) -> None:
+    """Quantise each sequence's new K/V row (``[B][8][64]`` BF16) into its page slot."""
+    B = int(seq_lens.shape[0])
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales), int(block_tables.shape[1]))
+    rc = load_library().pa_append_kv_q8(
+        ctypes.byref(shape), B, _ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(v_codes),
+        _ptr(kv_scales), _ptr(block_tables), _ptr(seq_lens), _stream_ptr(stream))
+    _check(rc, "pa_append_kv_q8")
+
+
+def append_kv_rope_q8(q, k_new, v_new, rope_cos, rope_sin, k_codes, v_codes, kv_scales,
+                      block_tables, seq_lens, q_out=None, stream=None):
+    """Rotate the new q/k at position L-1, quantise K/V into the slot; returns ``q_out``."""
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if q.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _bits16(q_out, "q_out", (HQ, D))
+    rope = _rope(rope_cos, rope_sin)
+    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales), int(block_tables.shape[1]))
+    rc = load_library().pa_append_kv_rope_q8(
+        ctypes.byref(shape), B, _ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(rope),
+        _ptr(q_out), _ptr(k_codes), _ptr(v_codes), _ptr(kv_scales), _ptr(block_tables),
+        _ptr(seq_lens), _stream_ptr(stream))
+    _check(rc, "pa_append_kv_rope_q8")
+    return q_out
+
+
+def fill_kv_q8(k_rows, v_rows, block_table_row, start: int, k_codes, v_codes, kv_scales,
+               stream=None) -> None:
+    """Quantised prefill fill: tokens ``start .. start+T-1`` of one sequence."""
+    _bits16(k_rows, "k_rows", (HKV, D)); _bits16(v_rows, "v_rows", (HKV, D))
+    _i32(block_table_row, "block_table_row")
+    if k_rows.shape != v_rows.shape:
+        raise ValueError("k_rows and v_rows differ in shape")
+    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales), int(block_table_row.shape[-1]))
+    rc = load_library().pa_fill_kv_q8(ctypes.byref(shape), _ptr(k_rows), _ptr(v_rows),
+                                      int(k_rows.shape[0]), int(start), _ptr(block_table_row),
+                                      _ptr(k_codes), _ptr(v_codes), _ptr(kv_scales),
+                                      _stream_ptr(stream))
+    _check(rc, "pa_fill_kv_q8")
+
+
+def decode_plan_lengths_q8(seq_lens_host, num_pages: int, max_blocks: int = 128,
+                           max_seq_len: int | None = None, num_cus: int = 0):
+    """(pages_per_split, splits) for INT8 pages from host sequence lengths."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    if max_seq_len is None:
+        max_seq_len = int(lens.max()) if lens.size else 0
+    shape = make_shape(num_pages, max_blocks)
+    ps, ns = ctypes.c_int32(), ctypes.c_int32()
+    rc = load_library().pa_decode_plan_lengths_q8(
+        ctypes.byref(shape), int(lens.size), lens.ctypes.data_as(ctypes.c_void_p),
+        int(max_seq_len), int(num_cus), ctypes.byref(ps), ctypes.byref(ns))
+    _check(rc, "pa_decode_plan_lengths_q8")
+    return ps.value, ns.value
+
+
+def _decode_q8(fn, q, k_new, v_new, rope, k_codes, v_codes, kv_scales, block_tables, seq_lens,
+               max_seq_len, scale, out, out_dtype, pages_per_split, workspace, stream):
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    if k_new is not None:
+        _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+        if k_new.shape[0] != B or v_new.shape[0] != B:
+            raise ValueError("batch dimension mismatch")
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    if q.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch dimension mismatch")
+    num_pages = _q8_pools(k_codes, v_codes, kv_scales)
+    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    max_blocks = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][32][64] tensor of out_dtype")
+    need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    shape = make_shape(num_pages, max_blocks)
+    args = [ctypes.byref(shape), B, _ptr(q)]
+    if k_new is not None:
+        args += [_ptr(k_new), _ptr(v_new)]
+    if rope is not None:
+        args += [ctypes.byref(rope)]
+    args += [_ptr(k_codes), _ptr(v_codes), _ptr(kv_scales), _ptr(block_tables), _ptr(seq_lens),
+             int(max_seq_len), float(scale), _ptr(out), code, int(pages_per_split),
+             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(stream)]
+    _check(getattr(load_library(), fn)(*args), fn)
+    return out
+
+
+def decode_attention_q8(q, k_codes, v_codes, kv_scales, block_tables, seq_lens, max_seq_len: int,
+                        scale: float = 0.125, out=None, out_dtype=torch.float32,
+                        pages_per_split: int = 0, workspace=None, stream=None):
+    """Decode attention over INT8 pages; returns ``out`` ``[B][32][64]``."""
+    return _decode_q8("pa_decode_attention_q8", q, None, None, None, k_codes, v_codes, kv_scales,
+                      block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
+                      pages_per_split, workspace, stream)
+
+
+def append_decode_attention_q8(q, k_new, v_new, k_codes, v_codes, kv_scales, block_tables,
+                               seq_lens, max_seq_len: int, scale: float = 0.125, out=None,
+                               out_dtype=torch.float32, pages_per_split: int = 0,
+                               workspace=None, stream=None, rope_cos=None, rope_sin=None):
+    """Fused quantised decode step (optionally with RoPE of the new q/k); returns ``out``."""
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("give both rope_cos and rope_sin, or neither")
+    if rope_cos is None:
+        return _decode_q8("pa_append_decode_attention_q8", q, k_new, v_new, None, k_codes,
+                          v_codes, kv_scales, block_tables, seq_lens, max_seq_len, scale, out,
+                          out_dtype, pages_per_split, workspace, stream)
+    return _decode_q8("pa_append_decode_attention_rope_q8", q, k_new, v_new,
+                      _rope(rope_cos, rope_sin), k_codes, v_codes, kv_scales, block_tables,
+                      seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+                      stream)
 
 
 class KVPool:

@@ -15,6 +15,108 @@
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
+// Kernels launched only from this file (the shared decode and merge kernel
+// templates are in pa_kernels.h).
+namespace pa {
+
+// One-token append: one wavefront per sequence, each lane copies 16 bytes of
+// the 1 KiB K row and 16 bytes of the V row.
+__global__ __launch_bounds__(64) void append_kernel(const uint4* __restrict__ k_new,
+                                                    const uint4* __restrict__ v_new,
+                                                    uint4* __restrict__ k_pool,
+                                                    uint4* __restrict__ v_pool,
+                                                    const int32_t* __restrict__ block_tables,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int32_t max_blocks, int32_t num_pages) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int L = seq_lens[b];
+  if (L <= 0 || L > max_blocks * kPage) return;
+  const int pos = L - 1;
+  const int id = block_tables[(int64_t)b * max_blocks + pos / kPage];
+  if ((unsigned)id >= (unsigned)num_pages) return;
+  const int64_t row = (int64_t)id * kPage + (pos % kPage);   // 1 KiB rows = 64 x uint4
+  k_pool[row * 64 + lane] = k_new[(int64_t)b * 64 + lane];
+  v_pool[row * 64 + lane] = v_new[(int64_t)b * 64 + lane];
+}
+
+// Prefill page fill: tokens start .. start+T-1 of one sequence (K and V
+// rows of 1 KiB each) into their page slots; 4 tokens per work-group, one
+// wavefront per token, 16 bytes per lane.  Tokens whose page id is out of
+// range are skipped.
+__global__ __launch_bounds__(256) void fill_kernel(const uint4* __restrict__ k_rows,
+                                                   const uint4* __restrict__ v_rows,
+                                                   int32_t num_tokens, int32_t start,
+                                                   const int32_t* __restrict__ bt_row,
+                                                   uint4* __restrict__ k_pool,
+                                                   uint4* __restrict__ v_pool,
+                                                   int32_t num_pages) {
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= num_tokens) return;
+  const int t = start + tok;
+  const int id = bt_row[t / kPage];
+  if ((unsigned)id >= (unsigned)num_pages) return;
+  const int64_t row = (int64_t)id * kPage + (t % kPage);
+  k_pool[row * 64 + lane] = k_rows[(int64_t)tok * 64 + lane];
+  v_pool[row * 64 + lane] = v_rows[(int64_t)tok * 64 + lane];
+}
+
+// One-token append with RoPE: one work-group of 256 threads per sequence
+// rotates the new query (32 heads x 32 pairs, into q_out) and key (8 x 32
+// pairs) at position L-1 and writes the rotated key and the value into the
+// page slot.  Idle slots and out-of-range metadata write no pool bytes; their
+// q_out row is a copy of q.
+__global__ __launch_bounds__(256) void append_rope_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
+    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    int32_t max_blocks, int32_t num_pages) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int L = seq_lens[b];
+  const bool live = L >= 1 && L <= max_blocks * kPage;
+  const int pos = live ? L - 1 : 0;
+  const int64_t cs_row = (int64_t)pos * (kD / 2);
+  // query: thread t rotates pairs j = t, t+256, t+512, t+768 (head j/32, dim j%32)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = t + 256 * r;
+    const int64_t base = ((int64_t)b * kHq + (j >> 5)) * kD + (j & 31);
+    const uint16_t x1b = q[base], x2b = q[base + 32];
+    uint16_t y1b = x1b, y2b = x2b;
+    if (live) {
+      const float x1 = __uint_as_float((uint32_t)x1b << 16);
+      const float x2 = __uint_as_float((uint32_t)x2b << 16);
+      const float c = rope_cos[cs_row + (j & 31)], sn = rope_sin[cs_row + (j & 31)];
+      y1b = (uint16_t)f32_to_bf16_rne(rope_first(x1, x2, c, sn));
+      y2b = (uint16_t)f32_to_bf16_rne(rope_second(x1, x2, c, sn));
+    }
+    q_out[base] = y1b;
+    q_out[base + 32] = y2b;
+  }
+  if (!live) return;
+  const int id = block_tables[(int64_t)b * max_blocks + pos / kPage];
+  if ((unsigned)id >= (unsigned)num_pages) return;
+  const int64_t row = ((int64_t)id * kPage + (pos % kPage)) * kRowElems;   // token row
+  {  // key: thread t rotates pair (head t/32, dim t%32)
+    const int64_t src = (int64_t)b * kRowElems + (t >> 5) * kD + (t & 31);
+    const float x1 = __uint_as_float((uint32_t)k_new[src] << 16);
+    const float x2 = __uint_as_float((uint32_t)k_new[src + 32] << 16);
+    const float c = rope_cos[cs_row + (t & 31)], sn = rope_sin[cs_row + (t & 31)];
+    const int64_t dst = row + (t >> 5) * kD + (t & 31);
+    k_pool[dst] = (uint16_t)f32_to_bf16_rne(rope_first(x1, x2, c, sn));
+    k_pool[dst + 32] = (uint16_t)f32_to_bf16_rne(rope_second(x1, x2, c, sn));
+  }
+  if (t < 64)  // value: 64 x 16 bytes
+    reinterpret_cast<uint4*>(v_pool + row)[t] =
+        reinterpret_cast<const uint4*>(v_new + (int64_t)b * kRowElems)[t];
+}
+
+}  // namespace pa
+
 namespace pa_host {
 
 constexpr int kMaxDevices = 64;

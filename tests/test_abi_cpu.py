@@ -153,3 +153,75 @@ def test_host_length_planner_choices():
     lens = (ctypes.c_int32 * 3)(1, 2, 3)
     assert lib.pa_decode_plan_lengths(ctypes.byref(s), 3, lens, 16, -1, ctypes.byref(ps),
                                       ctypes.byref(ns)) == -6
+
+
+def decode_q8(lib, s, batch=1, max_seq_len=37, ptrs=None, scale=0.125, out_dtype=0, ps=1,
+              ws=FAKE, ws_bytes=1 << 30, align_off=0, fused=False):
+    # as decode(): every case must be rejected before a launch (fake pointers)
+    n = 9 if fused else 7
+    p = ptrs or [ctypes.c_void_p(0x10000 + align_off)] * n
+    sp = ctypes.byref(s) if s is not None else None
+    if fused:
+        rc = lib.pa_append_decode_attention_q8(sp, batch, *p[:8], max_seq_len, scale, p[8],
+                                               out_dtype, ps, ws, ws_bytes, None)
+    else:
+        rc = lib.pa_decode_attention_q8(sp, batch, *p[:6], max_seq_len, scale, p[6], out_dtype,
+                                        ps, ws, ws_bytes, None)
+    assert rc < 0 or batch == 0, "a fake-pointer call was not rejected on the host"
+    return rc
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_q8_decode_argument_errors(lib, fused):
+    d = lambda *a, **k: decode_q8(lib, *a, fused=fused, **k)
+    n = 9 if fused else 7
+    assert d(None) == -1
+    assert d(shape(num_kv_heads=4)) == -2
+    assert d(shape(), batch=-1) == -6
+    assert d(shape(), max_seq_len=2049) == -6
+    assert d(shape(), scale=float("nan")) == -6
+    assert d(shape(), out_dtype=3) == -6
+    assert d(shape(), batch=0) == 0
+    assert d(shape(), ptrs=[None] * n) == -1
+    assert d(shape(), align_off=8) == -3
+    assert d(shape(), ws=None, ws_bytes=0) == -4
+    # the scale pool alone missing or misaligned
+    p = [FAKE] * n
+    p[(5 if fused else 3)] = None
+    assert d(shape(), ptrs=p) == -1
+    p[(5 if fused else 3)] = ctypes.c_void_p(0x10004)
+    assert d(shape(), ptrs=p) == -3
+
+
+def test_q8_append_and_fill_argument_errors(lib):
+    s, F = shape(), FAKE
+    bad = ctypes.c_void_p(0x10008)
+    assert lib.pa_append_kv_q8(None, 1, F, F, F, F, F, F, F, None) == -1
+    assert lib.pa_append_kv_q8(ctypes.byref(shape(head_dim=32)), 1, F, F, F, F, F, F, F, None) == -2
+    assert lib.pa_append_kv_q8(ctypes.byref(s), -1, F, F, F, F, F, F, F, None) == -6
+    assert lib.pa_append_kv_q8(ctypes.byref(s), 0, None, None, None, None, None, None, None,
+                               None) == 0
+    assert lib.pa_append_kv_q8(ctypes.byref(s), 1, F, F, F, F, None, F, F, None) == -1
+    assert lib.pa_append_kv_q8(ctypes.byref(s), 1, F, F, bad, F, F, F, F, None) == -3
+    assert lib.pa_append_kv_q8(ctypes.byref(shape(num_pages=0)), 1, F, F, F, F, F, F, F,
+                               None) == -6
+    # RoPE variant: the tables are required
+    assert lib.pa_append_kv_rope_q8(ctypes.byref(s), 1, F, F, F, None, F, F, F, F, F, F,
+                                    None) == -1
+    # fill
+    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, -1, 0, F, F, F, F, None) == -6
+    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 10, 2040, F, F, F, F, None) == -6
+    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 0, 0, None, None, None, None, None) == 0
+    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 4, 0, F, F, F, None, None) == -1
+    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 4, 0, F, F, bad, F, None) == -3
+
+
+def test_q8_planner_prefers_longer_splits_for_smaller_pages():
+    """The INT8 cost model (17 KiB pages) never picks a shorter split than BF16's."""
+    import workloads as W
+    for i in (2, 3, 4, 5):
+        lens = W.workload_seq_lens(i)
+        ps8, ns8 = pa.decode_plan_lengths_q8(lens, 40000, num_cus=256)
+        ps16, _ = pa.decode_plan_lengths(lens, 40000, num_cus=256)
+        assert ps8 >= 8 and ns8 == -(-W.pages_for(int(lens.max())) // ps8)
+        assert ps8 >= ps16 or ps8 == W.pages_for(int(lens.max())), (i, ps8, ps16)

@@ -284,6 +284,113 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
     raise ValueError(index)
 
 
+@dataclass
+class Q8Batch:
+    """One layer's decode-step inputs over INT8 pages.
+
+    Codes are int8 in the BF16 pool's layout, scales float32
+    ``[num_pages][8][2][16]`` (per page and KV head: 16 K scales, 16 V scales).
+    """
+
+    name: str
+    q: np.ndarray               # uint16 [B][32][64]
+    k_codes: np.ndarray         # int8   [num_pages][16][8][64]
+    v_codes: np.ndarray
+    kv_scales: np.ndarray       # float32 [num_pages][8][2][16]
+    block_tables: np.ndarray    # int32  [B][128]
+    seq_lens: np.ndarray        # int32  [B]
+    scale: float = SCALE
+    k_new: Optional[np.ndarray] = None   # uint16 [B][8][64] BF16 rows when the step appends
+    v_new: Optional[np.ndarray] = None
+    recipe: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_codes.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.batch else 0
+
+
+Q8_CODE_SIGMA = 45.0            # codes of N(0, 1) rows of 64 values: amax ~ 2.8 -> 127
+Q8_SCALE_RANGE = (0.018, 0.028)
+
+
+def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
+                  placement: str = "random", name: str = "q8") -> Q8Batch:
+    """Random INT8 pages for ``seq_lens``, shaped like quantised N(0, 1) rows.
+
+    Every stored (token, head) row gets codes round(N(0, 45)) clipped to
+    [-127, 127] with one code set to +-127 (its largest magnitude), and a
+    scale uniform in [0.018, 0.028].  Slots that hold no token have random
+    codes and a NaN scale (poison).  With ``append=True`` the slot of token
+    L-1 stays poisoned and BF16 N(0, 1) rows for it come in ``k_new``/``v_new``.
+
+    Draw order: page permutation, q, poison codes, then per sequence its K
+    codes, V codes, K scales, V scales (and, appending, its new K and V rows).
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = int(seq_lens.shape[0])
+    if np.any(seq_lens < 0) or np.any(seq_lens > MAX_CONTEXT):
+        raise ValueError("seq_lens must lie in [0, %d]" % MAX_CONTEXT)
+    rng = np.random.default_rng(seed)
+    n_pages = [pages_for(L) for L in seq_lens]
+    if sum(n_pages) > num_pages:
+        raise ValueError(f"pool of {num_pages} pages cannot hold {sum(n_pages)} pages")
+    perm = rng.permutation(num_pages).astype(np.int32)
+    order = perm if placement == "random" else np.arange(num_pages, dtype=np.int32)
+    if placement not in ("random", "identity"):
+        raise ValueError(placement)
+    q = f32_to_bf16_bits(rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM), dtype=np.float32))
+    shape = (num_pages, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
+    k_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
+    v_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
+    kv_scales = np.full((num_pages, NUM_KV_HEADS, 2, PAGE_SIZE), np.nan, dtype=np.float32)
+    k_new = np.zeros((B, NUM_KV_HEADS, HEAD_DIM), np.uint16) if append else None
+    v_new = np.zeros((B, NUM_KV_HEADS, HEAD_DIM), np.uint16) if append else None
+    block_tables = np.full((B, MAX_BLOCKS), -1, dtype=np.int32)
+
+    def codes(T):
+        c = np.clip(np.rint(rng.standard_normal((T, NUM_KV_HEADS, HEAD_DIM), dtype=np.float32)
+                            * np.float32(Q8_CODE_SIGMA)), -127, 127).astype(np.int8)
+        pick = rng.integers(0, HEAD_DIM, size=(T, NUM_KV_HEADS))
+        sign = rng.choice(np.array([-127, 127], np.int8), size=(T, NUM_KV_HEADS))
+        np.put_along_axis(c, pick[..., None], sign[..., None], axis=-1)
+        return c
+
+    cursor = 0
+    for b in range(B):
+        L, n = int(seq_lens[b]), n_pages[b]
+        pages = order[cursor:cursor + n]
+        cursor += n
+        block_tables[b, :n] = pages
+        if L == 0:
+            continue
+        kc, vc = codes(L), codes(L)
+        ks = rng.uniform(*Q8_SCALE_RANGE, size=(L, NUM_KV_HEADS)).astype(np.float32)
+        vs = rng.uniform(*Q8_SCALE_RANGE, size=(L, NUM_KV_HEADS)).astype(np.float32)
+        stored = L - 1 if append else L
+        for t in range(stored):
+            page, slot = pages[t // PAGE_SIZE], t % PAGE_SIZE
+            k_codes[page, slot] = kc[t]
+            v_codes[page, slot] = vc[t]
+            kv_scales[page, :, 0, slot] = ks[t]
+            kv_scales[page, :, 1, slot] = vs[t]
+        if append:
+            k_new[b] = f32_to_bf16_bits(rng.standard_normal((NUM_KV_HEADS, HEAD_DIM), dtype=np.float32))
+            v_new[b] = f32_to_bf16_bits(rng.standard_normal((NUM_KV_HEADS, HEAD_DIM), dtype=np.float32))
+    recipe = dict(num_pages=num_pages, placement=placement, append=append, seed=_seed_repr(seed),
+                  code_sigma=Q8_CODE_SIGMA, scale_range=Q8_SCALE_RANGE)
+    return Q8Batch(name=name, q=q, k_codes=k_codes, v_codes=v_codes, kv_scales=kv_scales,
+                   block_tables=block_tables, seq_lens=seq_lens, k_new=k_new, v_new=v_new,
+                   recipe=recipe)
+
+
 def poison_summary(batch: DecodeBatch) -> dict:
     """Counts of poisoned pool rows and block-table entries (for reports)."""
     nan_rows = int(np.count_nonzero(batch.k_pool[..., 0, 0] == BF16_NAN))
