@@ -17,8 +17,10 @@ L2 and Infinity Cache holding none of its inputs; the flush only reads, so it
 leaves no dirty lines whose write-back would land inside the next step.
 Pass A times the K steps with one event pair around each step; pass B
 repeats them with the library recording events right around its main
-kernel (the roofline figure); pass C times the two-call form.  The flush is
-outside every event pair.  Prints one JSON line.
+kernel (the roofline figure); pass C times the two-call form; pass D the
+fused step with RoPE; pass E the fused step over INT8 pages (the BF16 cache
+quantised on the GPU first).  The flush is outside every event pair.  Prints
+one JSON line.
 """
 
 from __future__ import annotations
@@ -37,34 +39,37 @@ if ROOT not in sys.path:
 METRIC = "decode-attention KV-read GB/s (% of MI355X HBM peak) + sequences/s per layer"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic_b256_l2048.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc", n)
-                  for n in ("pa_kernels.h", "pa_decode.hip", "pa_host.h")]
+TRAFFIC_FILE_Q8 = os.path.join(ROOT, "profiles", "decode_q8_kernel_traffic_b256_l2048.json")
+_CSRC = os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in ("pa_kernels.h", "pa_decode.hip", "pa_host.h")]
+KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n)
+                     for n in ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_q8.hip", "pa_host.h")]
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_units_bytes: int):
-    """HBM bytes per launch of the main kernel from committed rocprofv3 counters.
+def measured_traffic(path: str = TRAFFIC_FILE, sources=None):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counters.
 
     The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
-    main kernel and of a device copy of known size, taken on the same kernel
+    kernel and of a device copy of known size, taken on the same kernel
     source; None when absent or when the kernel has changed since.
     """
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_hash():
+    if t.get("kernel_source_sha") != kernel_source_hash(sources):
         return None
     return int(round(t["hbm_bytes_per_launch"]))
 
@@ -277,8 +282,29 @@ def main() -> int:
     # one more plain step restores the state the oracle recomputes
     step()
     torch.cuda.synchronize()
+
+    # pass E: the same step over INT8 pages.  The BF16 cache is quantised on
+    # the GPU page by page (every slot of every page, as one sequence over an
+    # identity table), then the fused quantise-append + decode is timed.
+    q8_k, q8_v, q8_s = pa.new_q8_pools(batch.num_pages, device=dev)
+    npg = batch.num_pages
+    ident = torch.arange(npg, dtype=torch.int32, device=dev)
+    pa.fill_kv_q8(k_pool.view(npg * 16, 8, 64), v_pool.view(npg * 16, 8, 64), ident, 0,
+                  q8_k, q8_v, q8_s, stream=stream)
+    out_q8 = torch.empty_like(out)
+
+    def q8_step():
+        pa.append_decode_attention_q8(q, k_new, v_new, q8_k, q8_v, q8_s, bt, lens, msl,
+                                      scale=batch.scale, out=out_q8, pages_per_split=ps,
+                                      workspace=workspace, stream=stream)
+    for _ in range(Wm):
+        pre_step()
+        q8_step()
+    t_q8 = timed(q8_step, K)
+    log(f"{K} INT8-page steps done")
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
+    by_q8 = A.step_bytes_q8(batch.seq_lens)["kv"]
     mean_step = float(t_step.mean())
     value = kv / mean_step / 1e9
     achieved = kv / float(t_main.mean()) / 1e9
@@ -321,6 +347,18 @@ def main() -> int:
         "prefill_fill_gbps": round(fill_bytes / float(t_fill.mean()) / 1e9, 1),
         "allocator_us_per_decode_step": round(alloc_step_us, 1),
         "two_call_kv_gbps": round(kv / float(t_two.mean()) / 1e9, 2),
+        "int8_pages": {
+            "step_us": round(float(t_q8.mean()) * 1e6, 2),
+            "step_min_us": round(float(t_q8.min()) * 1e6, 2),
+            "kv_bytes": by_q8,
+            "kv_gbps": round(by_q8 / float(t_q8.mean()) / 1e9, 2),
+            "hbm_peak_frac": round(by_q8 / float(t_q8.mean()) / 1e9 / HBM_PEAK_GBPS, 4),
+            "speedup_vs_bf16_step": round(mean_step / float(t_q8.mean()), 3),
+            "seq_per_s_per_layer": round(B / float(t_q8.mean()), 1),
+            "format": "int8 codes + one FP32 scale per (token, KV head) row, K and V",
+            "traffic": measured_traffic(TRAFFIC_FILE_Q8, KERNEL_SOURCES_Q8),
+            "kernel_source_sha": kernel_source_hash(KERNEL_SOURCES_Q8),
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": "pa::decode_kernel (append fused)",
@@ -328,7 +366,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(kv),
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": kv,
             "avg_launch_us": round(float(t_main.mean()) * 1e6, 2),
         },

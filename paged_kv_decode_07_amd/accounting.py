@@ -51,3 +51,23 @@ def step_flops(seq_lens) -> int:
     """Multiply-adds of q.K^T and p.V, two flops each: 4 flops per KV byte."""
     lens = np.asarray(seq_lens, dtype=np.int64)
     return int(lens.sum()) * Q_HEADS * HEAD_DIM * 2 * 2
+
+
+# INT8 pages: one byte per value plus one FP32 scale per (token, KV head) row,
+# for K and for V (the INT8 cache of the same section 5.1, with the symmetric
+# quantiser of section 3.4 applied row by row)
+Q8_TOKEN_BYTES = 2 * KV_HEADS * (HEAD_DIM + 4)                       # 1088 per layer
+Q8_PAGE_BYTES = PAGE * Q8_TOKEN_BYTES                                # 17 KiB (K+V+scales)
+
+
+def step_bytes_q8(seq_lens, out_bytes: int = 4, append: bool = False) -> dict:
+    """As ``step_bytes`` for INT8 pages: ``kv`` counts 1088 bytes per valid token;
+    the append reads a BF16 row pair and writes its codes and scales."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    base = step_bytes(lens, out_bytes=out_bytes, append=False)
+    active = int(np.count_nonzero(lens))
+    kv = int(lens.sum()) * Q8_TOKEN_BYTES
+    app = active * (KV_TOKEN_BYTES + Q8_TOKEN_BYTES + 8) if append else 0
+    out = dict(base, kv=kv, app=app)
+    out["total"] = kv + base["q"] + base["out"] + base["meta"] + app
+    return out

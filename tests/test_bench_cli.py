@@ -20,8 +20,13 @@ def test_traffic_is_dropped_when_the_kernel_changed(tmp_path, monkeypatch):
     import bench
     f = tmp_path / "t.json"
     f.write_text(json.dumps({"kernel_source_sha": "0" * 16, "hbm_bytes_per_launch": 1.0}))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic(1) is None
+    assert bench.measured_traffic(str(f)) is None
     f.write_text(json.dumps({"kernel_source_sha": bench.kernel_source_hash(),
                              "hbm_bytes_per_launch": 123.0}))
-    assert bench.measured_traffic(1) == 123
+    assert bench.measured_traffic(str(f)) == 123
+    # the INT8 kernel's figure is keyed to the INT8 sources
+    assert bench.measured_traffic(str(f), bench.KERNEL_SOURCES_Q8) is None
+    f.write_text(json.dumps({"kernel_source_sha": bench.kernel_source_hash(bench.KERNEL_SOURCES_Q8),
+                             "hbm_bytes_per_launch": 7.0}))
+    assert bench.measured_traffic(str(f), bench.KERNEL_SOURCES_Q8) == 7
+
