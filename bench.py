@@ -41,9 +41,9 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic_b256_l2048.json")
 TRAFFIC_FILE_Q8 = os.path.join(ROOT, "profiles", "decode_q8_kernel_traffic_b256_l2048.json")
 _CSRC = os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc")
-KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in ("pa_kernels.h", "pa_decode.hip", "pa_host.h")]
-KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n)
-                     for n in ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_q8.hip", "pa_host.h")]
+_DEVICE = ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_kernel.h", "pa_host.h")
+KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode.hip",)]
+KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_q8.hip",)]
 
 
 def log(msg: str) -> None:

@@ -15,8 +15,9 @@
  * stores scale 0 and codes 0.  Inputs must be finite.
  *
  * Layouts (row-major, no padding; 16-byte aligned unless stated):
- *   k_codes/v_codes  int8    [num_pages][16 slots][8 KV heads][64]
- *                    (the BF16 pool's layout, one byte per value)
+ *   k_codes/v_codes  int8    [num_pages][8 KV heads][16 slots][64]
+ *                    (within a page, each head's 16 code rows are one
+ *                    contiguous 1 KiB block)
  *   kv_scales        float32 [num_pages][8 KV heads][2][16 slots]
  *                    ([..][0][s]: K scale of slot s, [..][1][s]: V scale)
  *   one page = 8 KiB of K codes + 8 KiB of V codes + 1 KiB of scales
@@ -42,7 +43,7 @@ extern "C" {
 /*
  * Quantised one-token append: for every b with L = seq_lens[b] >= 1, the K
  * row k_new[b] (8 heads x 64 BF16) is quantised head by head into
- * k_codes[page][(L-1)%16] and its 8 scales into kv_scales[page][h][0][(L-1)%16],
+ * k_codes[page][h][(L-1)%16] and its 8 scales into kv_scales[page][h][0][(L-1)%16],
  * page = block_tables[b][(L-1)/16]; v_new[b] likewise with [..][1][..].
  * Deterministic (the codes and scales are a function of the row alone);
  * nothing else changes.  Idle slots and out-of-range metadata write nothing.

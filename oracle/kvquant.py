@@ -35,8 +35,8 @@ the design notes of the repository):
 
 Layout (the library's format, which these functions also define):
 
-* ``k_codes``, ``v_codes``: int8 ``[num_pages][P][Hkv][D]`` (the BF16 pool's
-  layout, one byte per value);
+* ``k_codes``, ``v_codes``: int8 ``[num_pages][Hkv][P][D]``: within a page,
+  each KV head's 16 token rows of 64 codes are one contiguous 1 KiB block;
 * ``scales``: float32 ``[num_pages][Hkv][2][P]``: for page ``p`` and KV head
   ``g``, the 16 K scales of the page's slots, then the 16 V scales.
 
@@ -88,8 +88,8 @@ def dequantize(codes, scale) -> np.ndarray:
 def _write_token(k_codes, v_codes, scales, physical, slot, k_row_bits, v_row_bits):
     kc, ks = quantize_rows(k_row_bits)            # [Hkv][D], [Hkv]
     vc, vs = quantize_rows(v_row_bits)
-    k_codes[physical, slot] = kc
-    v_codes[physical, slot] = vc
+    k_codes[physical, :, slot] = kc
+    v_codes[physical, :, slot] = vc
     scales[physical, :, 0, slot] = ks
     scales[physical, :, 1, slot] = vs
 
@@ -102,7 +102,7 @@ def append_kv_q8(k_codes, v_codes, scales, k_new_bits, v_new_bits, block_tables,
     row stored as its codes and its scale.
     """
     kc, vc, sc = (np.array(a, copy=True) for a in (k_codes, v_codes, scales))
-    page_size = kc.shape[1]
+    page_size = kc.shape[2]
     for b in range(len(seq_lens)):
         L = int(seq_lens[b])
         if L == 0:
@@ -116,7 +116,7 @@ def append_kv_q8(k_codes, v_codes, scales, k_new_bits, v_new_bits, block_tables,
 def fill_kv_q8(k_codes, v_codes, scales, k_rows_bits, v_rows_bits, block_table_row, start: int):
     """Quantise tokens ``start .. start+T-1`` of one sequence into their pages."""
     kc, vc, sc = (np.array(a, copy=True) for a in (k_codes, v_codes, scales))
-    page_size = kc.shape[1]
+    page_size = kc.shape[2]
     for j in range(len(k_rows_bits)):
         t = start + j
         physical = int(block_table_row[t // page_size])
@@ -130,12 +130,12 @@ def fill_kv_q8(k_codes, v_codes, scales, k_rows_bits, v_rows_bits, block_table_r
 def gather_sequence_q8(codes, scales, which: int, block_table_row, seq_len: int) -> np.ndarray:
     """Dequantised ``[L][Hkv][D]`` float64 rows of one sequence (which: 0 = K, 1 = V)."""
     codes = np.asarray(codes)
-    page_size, hkv, d = codes.shape[1:]
+    hkv, page_size, d = codes.shape[1:]
     rows = []
     for t in range(seq_len):
         physical = int(block_table_row[t // page_size])
         slot = t % page_size
-        rows.append(dequantize(codes[physical, slot], scales[physical, :, which, slot]))
+        rows.append(dequantize(codes[physical, :, slot], scales[physical, :, which, slot]))
     if not rows:
         return np.zeros((0, hkv, d), dtype=np.float64)
     return np.stack(rows)
@@ -151,7 +151,7 @@ def decode_attention_q8(q_bits, k_codes, v_codes, scales, block_tables, seq_lens
     """
     q_all = np.asarray(q_bits)
     B, Hq, D = q_all.shape
-    Hkv = np.asarray(k_codes).shape[2]
+    Hkv = np.asarray(k_codes).shape[1]
     out = np.zeros((B, Hq, D), dtype=np.float64)
     todo = range(B) if sequences is None else sequences
     for b in todo:

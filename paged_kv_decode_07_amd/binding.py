@@ -417,9 +417,9 @@ def fill_kv(k_rows, v_rows, block_table_row, start: int, k_pool, v_pool, stream=
 # INT8 K/V pages (include/pa_decode_q8.h)
 # ---------------------------------------------------------------------------
 def new_q8_pools(num_pages: int, device="cuda"):
-    """Zeroed INT8 pools: K codes, V codes (int8 ``[pages][16][8][64]``) and scales
-    (float32 ``[pages][8][2][16]``)."""
-    codes = (num_pages, PAGE, HKV, D)
+    """Zeroed INT8 pools: K codes, V codes (int8 ``[pages][8][16][64]``, head-major
+    within a page) and scales (float32 ``[pages][8][2][16]``)."""
+    codes = (num_pages, HKV, PAGE, D)
     return (torch.zeros(codes, dtype=torch.int8, device=device),
             torch.zeros(codes, dtype=torch.int8, device=device),
             torch.zeros((num_pages, HKV, 2, PAGE), dtype=torch.float32, device=device))
@@ -428,8 +428,8 @@ def new_q8_pools(num_pages: int, device="cuda"):
 def _q8_pools(k_codes, v_codes, kv_scales) -> int:
     for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
         if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() or \
-                tuple(t.shape[1:]) != (PAGE, HKV, D):
-            raise ValueError(f"{name}: must be a contiguous int8 [pages][16][8][64] device tensor")
+                tuple(t.shape[1:]) != (HKV, PAGE, D):
+            raise ValueError(f"{name}: must be a contiguous int8 [pages][8][16][64] device tensor")
     if k_codes.shape != v_codes.shape:
         raise ValueError("k_codes and v_codes differ in shape")
     n = int(k_codes.shape[0])

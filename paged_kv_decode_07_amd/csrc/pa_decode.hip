@@ -11,7 +11,7 @@
 
 #include "pa_decode.h"
 #include "pa_host.h"
-#include "pa_kernels.h"
+#include "pa_decode_kernel.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
@@ -453,14 +453,14 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   }
   if ((int64_t)batch * ns > INT32_MAX || ns > 65535 || batch > 65535 * 64) return PA_ERR_VALUE;
 
-  pa::DecodeArgs a;
+  pa::DecodeArgs a = {};
   a.q = (const uint16_t*)q;
-  a.k_pool = (const uint16_t*)k_pool;
-  a.v_pool = (const uint16_t*)v_pool;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
   a.k_new = (const uint16_t*)k_new;
   a.v_new = (const uint16_t*)v_new;
-  a.k_pool_w = (uint16_t*)k_pool;
-  a.v_pool_w = (uint16_t*)v_pool;
+  a.k_pool_w = const_cast<void*>(k_pool);
+  a.v_pool_w = const_cast<void*>(v_pool);
   a.rope_cos = rope ? rope->cos : nullptr;
   a.rope_sin = rope ? rope->sin : nullptr;
   a.block_tables = block_tables;
@@ -476,32 +476,11 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.max_seq_len = max_seq_len;
   a.pages_per_split = ps;
   a.num_splits = ns;
-
-  hipStream_t st = (hipStream_t)stream;
-  const dim3 grid(ns, batch);
-  if (event_before_main && hipEventRecord((hipEvent_t)event_before_main, st) != hipSuccess)
-    return PA_ERR_LAUNCH;
-  const dim3 block(pa::kThreads);
-  if (out_dtype == PA_OUT_BF16) {
-    if (rope) hipLaunchKernelGGL((pa::decode_kernel<true, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((pa::decode_kernel<true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((pa::decode_kernel<true, false>), grid, block, 0, st, a);
-  } else {
-    if (rope) hipLaunchKernelGGL((pa::decode_kernel<false, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((pa::decode_kernel<false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((pa::decode_kernel<false, false>), grid, block, 0, st, a);
-  }
-  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  if (event_after_main && hipEventRecord((hipEvent_t)event_after_main, st) != hipSuccess)
-    return PA_ERR_LAUNCH;
-  if (ns > 1) {
-    if (out_dtype == PA_OUT_BF16)
-      hipLaunchKernelGGL(pa::merge_kernel<true>, dim3(batch), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(pa::merge_kernel<false>, dim3(batch), dim3(256), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  }
-  return PA_OK;
+  const hipError_t e = pa::launch_decode<false>(a, batch, out_dtype == PA_OUT_BF16, fused,
+                                                rope != nullptr, (hipStream_t)stream,
+                                                (hipEvent_t)event_before_main,
+                                                (hipEvent_t)event_after_main);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 }  // namespace
 

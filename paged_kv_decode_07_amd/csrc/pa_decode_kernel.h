@@ -1,0 +1,615 @@
+// Decode kernel of the paged GQA decode library for gfx950 (CDNA4, wave64),
+// for BF16 pages and INT8 pages.
+//
+// Work decomposition: one work-group per (sequence b, split s); a split is a
+// run of at most `pages_per_split` consecutive logical pages of sequence b.
+// The 8 wavefronts of a work-group serve the 8 KV heads: wavefront g streams
+// its head's slice of every page of the split (grouped-query attention: 32
+// query heads share 8 KV heads; query heads 4g .. 4g+3 read KV head g).
+//
+// Page stream: each wavefront keeps a ring of page slots in LDS, filled with
+// gfx950's direct-to-LDS loads (every lane's 4 or 16 bytes land at lane*size
+// of the destination, without passing through VGPRs).  A slot is refilled as
+// soon as its page has been read into registers, so while a page is used the
+// next ring-depth pages are in flight.  A wavefront only ever reads its own
+// slots, so explicit vmcnt waits are the only synchronisation.  The split's
+// block-table entries are preloaded into VGPRs and picked with v_readlane.
+//
+// Arithmetic (the FP32 online softmax of the samir-vllm README's paged
+// decode attention, on the matrix cores):
+//
+//   * scores are computed transposed, S^T = K Q^T, with one
+//     v_mfma_f32_16x16x32_bf16 per 32 dims: the A operand is the page's K
+//     (row = token, 8 dims per lane), the B operand is Q^T with the 4 query
+//     heads repeated over the 16 columns.  Lane l = 16 G + n receives the
+//     scores of tokens 4G .. 4G+3 for head slot n (query head 4g + n % 4),
+//     scaled by scale * log2(e) so that exp2 is the hardware v_exp_f32;
+//   * that is exactly the A-operand layout of v_mfma_f32_16x16x16_bf16 with
+//     k = tokens: row n, tokens 4G .. 4G+3.  So P V runs on the matrix cores
+//     with no data movement between the two products: rows 0..3 carry the
+//     weights of heads 0..3 rounded to BF16, rows 4..7 the remainders
+//     (weight - its BF16 value, rounded again), rows 8..15 zero; one
+//     product per 16 output dims accumulates both parts, summed at the end
+//     (each weight is carried to about 2^-16 relative);
+//   * V reaches the B operand (column = dim, k = 4 tokens per lane) through
+//     gfx950's transposing LDS read ds_read_b64_tr_b16: within each group of
+//     16 lanes, output lane i takes element i % 4 of the 4-element chunks
+//     addressed by lanes 4c + i/4, c = 0..3; pointing lane 4c + q at dims
+//     4q .. 4q+3 of token 4G + c gives lane i the 4 tokens of dim i.  For
+//     INT8 codes the 16-bit unit is a pair of dims, so one read gives a lane
+//     4 tokens of an even and an odd dim (two products per 32 dims);
+//   * the online softmax keeps one running maximum per head, equal in every
+//     lane of that head (the product sums over tokens, so a page's weights
+//     share it); it is raised only when a score exceeds it by more than
+//     kTau (a wave-wide vote; the page maximum is then reduced across the
+//     four token groups).  Weights are then at most 2^kTau and the rescale
+//     of the accumulators is almost never executed after the first page.  The
+//     normaliser is a per-lane partial sum, reduced at the end;
+//   * the accumulator is 4 products x 4 floats per lane (16 VGPRs), and the
+//     VALU carries no multiply-add of P V.
+//
+// INT8 pages: K codes are widened to BF16 exactly for the score product and
+// the K scale of each token joins the score multiplier; V codes are widened
+// to BF16 exactly and the V scale joins the weight (w * v_scale), while the
+// normaliser sums w alone.
+//
+// Masking: slots past the sequence in its last page may hold any bits.  Their
+// scores are selected to -inf, their weights to 0, and for BF16 pages their V
+// values are replaced by zeros before the product (0 * NaN would be NaN).
+// A sequence whose block-table entry falls outside the pool reads nothing
+// from it and gets NaN outputs; so does a length beyond the declared bound.
+#pragma once
+
+#include "pa_kernels_q8.h"
+
+namespace pa {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Arguments of the decode kernel (either page format).
+struct DecodeArgs {
+  const uint16_t* q;
+  const void* k_pool;          // BF16 [pages][16][8][64] or int8 codes [pages][8][16][64]
+  const void* v_pool;
+  const float* kv_scales;      // INT8 only: [pages][8][2][16]
+  const uint16_t* k_new;       // fused append: [B][8][64] BF16 rows
+  const uint16_t* v_new;
+  void* k_pool_w;              // fused append: the same pools, written at slot L-1
+  void* v_pool_w;
+  float* kv_scales_w;
+  const float* rope_cos;
+  const float* rope_sin;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;
+  float* part_acc;
+  float* part_ml;
+  float xscale;
+  int32_t num_pages;
+  int32_t max_blocks;
+  int32_t max_seq_len;
+  int32_t pages_per_split;
+  int32_t num_splits;
+};
+
+// Page-format constants of the LDS ring (per wavefront slot).
+template <bool Q8>
+struct PageFormat;
+template <>
+struct PageFormat<false> {
+  static constexpr int kRingDepth = kRing;      // 2 slots of 4 KiB
+  static constexpr int kSlot = 4096;            // [K lo | K hi | V lo | V hi] x [16 part + token] x 16 B
+  static constexpr int kLoads = 4;              // direct-to-LDS loads per page
+};
+template <>
+struct PageFormat<true> {
+  static constexpr int kRingDepth = kRingQ8;    // 4 slots of 2304 B
+  static constexpr int kSlot = kSlotQ8;         // [K codes 16 x 64 B | V codes 16 x 64 B | scales]
+  static constexpr int kLoads = 3;
+};
+
+// Registers of one page for one lane.
+struct PageBF16 {
+  u32x4 k0, k1;       // K[token][8G..8G+7], K[token][32+8G..32+8G+7]
+  u32x2 v[4];         // V, 4 tokens x 16-dim block b (transposed read)
+};
+struct PageQ8 {
+  u32x2 k0, k1;       // K codes, 8 dims each
+  u32x2 v[2];         // V codes: 4 tokens x (even, odd) dim pairs, dims 0..31 and 32..63
+  u32x4 ks, vs;       // K and V scales of tokens 4G .. 4G+3
+};
+
+// kaddr: this lane's 16-byte row of the slot; vaddr: its transposed-read
+// chunk of V block 0 (blocks 1..3 at +512, +1024, +1536).
+__device__ __forceinline__ void lds_page_issue(PageBF16& r, uint32_t kaddr, uint32_t vaddr) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %7\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:512\n\t"
+      "ds_read_b64_tr_b16 %4, %7 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %5, %7 offset:1536"
+      : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.v[2]), "=&v"(r.v[3])
+      : "v"(kaddr), "v"(vaddr)
+      : "memory");
+}
+__device__ __forceinline__ void lds_page_ready(PageBF16& r) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r.k0), "+v"(r.k1), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.v[2]), "+v"(r.v[3])::"memory");
+}
+// kaddr: K codes of (token, 8G); vaddr: V chunk of this lane; saddr: scales + 16 G.
+__device__ __forceinline__ void lds_page_issue(PageQ8& r, uint32_t kaddr, uint32_t vaddr,
+                                         uint32_t saddr) {
+  asm volatile(
+      "ds_read_b64 %0, %6\n\t"
+      "ds_read_b64 %1, %6 offset:32\n\t"
+      "ds_read_b64_tr_b16 %2, %7\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:32\n\t"
+      "ds_read_b128 %4, %8\n\t"
+      "ds_read_b128 %5, %8 offset:64"
+      : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.ks), "=&v"(r.vs)
+      : "v"(kaddr), "v"(vaddr), "v"(saddr)
+      : "memory");
+}
+__device__ __forceinline__ void lds_page_ready(PageQ8& r) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r.k0), "+v"(r.k1), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ks), "+v"(r.vs)::"memory");
+}
+
+// 4 INT8 codes (bytes b0..b3 of w) -> BF16 pairs (b0, b2) and (b1, b3): the
+// even-dim and odd-dim values of two tokens when w holds (t, even), (t, odd),
+// (t+1, even), (t+1, odd).
+__device__ __forceinline__ void codes_even_odd(uint32_t w, uint32_t& even, uint32_t& odd) {
+  even = bf16_pair_trunc(code_f32<0>(w), code_f32<2>(w));
+  odd = bf16_pair_trunc(code_f32<1>(w), code_f32<3>(w));
+}
+
+// Running state of one lane: the accumulators of the P V products (4 tiles
+// of 16 x 16, this lane's rows 4G .. 4G+3 of column n), the head's running
+// maximum m (log2 units, same in all lanes of the head) and this lane's
+// partial normaliser l.
+struct LaneState {
+  f32x4_t acc[4];
+  float m;
+  float l;
+};
+
+template <bool Q8, bool MASK, typename Page>
+__device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t qlo, bf16x8_t qhi,
+                                           float xscale, int lane, int valid) {
+  const int G = lane >> 4;            // token group: tokens 4G .. 4G+3
+  const int n = lane & 15;            // head slot (query head 4g + n%4); P row
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t s;
+  if constexpr (Q8) {
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k0), qlo, zero, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k1), qhi, s, 0, 0, 0);
+  } else {
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k0), qlo, zero, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k1), qhi, s, 0, 0, 0);
+  }
+  float x[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float xs = xscale;
+    if constexpr (Q8) xs = xscale * __uint_as_float(r.ks[c]);
+    x[c] = s[c] * xs;
+    if (MASK) x[c] = (4 * G + c < valid) ? x[c] : -INFINITY;
+  }
+  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau)) {
+    // rare: raise the maximum of every head whose page maximum passed it
+    float pm = mx;
+    pm = fmaxf(pm, __shfl_xor(pm, 16));
+    pm = fmaxf(pm, __shfl_xor(pm, 32));
+    const float mn = (pm > st.m + kTau) ? pm : st.m;
+    const float a = __builtin_amdgcn_exp2f(st.m - mn);    // m = -inf -> 0
+    st.m = mn;
+    st.l *= a;
+    // rows 4G + r of this lane's tiles belong to head r (rows 0..7)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float ar = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), rr));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) st.acc[b][rr] *= ar;
+    }
+  }
+  float p[4], w[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    p[c] = __builtin_amdgcn_exp2f(x[c] - st.m);           // masked: exp2(-inf) = 0
+    w[c] = p[c];
+    if constexpr (Q8) {
+      w[c] = p[c] * __uint_as_float(r.vs[c]);
+      if (MASK) w[c] = (4 * G + c < valid) ? w[c] : 0.f;  // scale bits of a dead slot
+    }
+  }
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  // A operand: rows 0..3 the BF16 weights, rows 4..7 their remainders
+  const uint32_t h01 = f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16);
+  const uint32_t h23 = f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16);
+  u32x2 pa;
+  if (n < 4) {
+    pa = u32x2{h01, h23};
+  } else if (n < 8) {
+    const float r0 = w[0] - __uint_as_float(h01 << 16), r1 = w[1] - __uint_as_float(h01 & 0xffff0000u);
+    const float r2 = w[2] - __uint_as_float(h23 << 16), r3 = w[3] - __uint_as_float(h23 & 0xffff0000u);
+    pa = u32x2{f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16),
+               f32_to_bf16_rne(r2) | (f32_to_bf16_rne(r3) << 16)};
+  } else {
+    pa = u32x2{0u, 0u};
+  }
+  const bf16x4_t A = __builtin_bit_cast(bf16x4_t, pa);
+  if constexpr (Q8) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t e0, o0, e1, o1;
+      codes_even_odd(r.v[h].x, e0, o0);                    // tokens 4G, 4G+1
+      codes_even_odd(r.v[h].y, e1, o1);                    // tokens 4G+2, 4G+3
+      st.acc[2 * h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          A, __builtin_bit_cast(bf16x4_t, u32x2{e0, e1}), st.acc[2 * h], 0, 0, 0);
+      st.acc[2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          A, __builtin_bit_cast(bf16x4_t, u32x2{o0, o1}), st.acc[2 * h + 1], 0, 0, 0);
+    }
+  } else {
+    if (MASK) {
+      // tokens 4G .. 4G+3 sit in (lo, hi) halves of the two words
+      const uint32_t m0 = (4 * G < valid ? 0x0000ffffu : 0u) | (4 * G + 1 < valid ? 0xffff0000u : 0u);
+      const uint32_t m1 = (4 * G + 2 < valid ? 0x0000ffffu : 0u) | (4 * G + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) r.v[b] = u32x2{r.v[b].x & m0, r.v[b].y & m1};
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, r.v[b]),
+                                                            st.acc[b], 0, 0, 0);
+  }
+}
+
+// Output dim of column n of tile b: BF16 pages, tile b = dims 16b .. 16b+15;
+// INT8 pages, tile 2h + e = dims 32h + 8(n/4) + 2(n%4) + e.
+template <bool Q8>
+__device__ __forceinline__ int out_dim(int b, int n) {
+  if constexpr (Q8) return 32 * (b >> 1) + 8 * (n >> 2) + 2 * (n & 3) + (b & 1);
+  return 16 * b + n;
+}
+
+// Cache-policy bits of the page-stream loads (every page is read once).
+#ifndef PA_STREAM_CPOL
+#define PA_STREAM_CPOL 0
+#endif
+constexpr int kStreamCpol = PA_STREAM_CPOL;
+
+template <bool Q8, bool OUT_BF16, bool APPEND, bool ROPE = false>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+  static_assert(!ROPE || APPEND, "RoPE is fused with the append");
+  using F = PageFormat<Q8>;
+  const int s = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4;
+  const int n = lane & 15;
+
+  const int L = a.seq_lens[b];
+  const int n_pages = (L + kPage - 1) / kPage;
+  const bool bad_len = L < 0 || L > a.max_seq_len || n_pages > a.max_blocks ||
+                       n_pages > a.pages_per_split * a.num_splits;
+  const int n_splits_b = bad_len ? 1 : (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  if (s >= (n_splits_b > 0 ? n_splits_b : 1)) return;
+
+  if (L == 0 || bad_len) {
+    float res[16];
+    const float fill = bad_len ? __builtin_nanf("") : 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) res[e] = fill;
+    if (n < kGroup) store_row16<OUT_BF16>(a.out, (int64_t)b * kHq + kGroup * g + n, G, res);
+    return;
+  }
+
+  const int p0 = s * a.pages_per_split;
+  const int p1 = min(p0 + a.pages_per_split, n_pages);
+  const int last = p1 - 1;
+  const int tail_valid = L - last * kPage;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+
+  // B operand of the score product: column n = query head 4g + n%4, this
+  // lane's 8 dims {8G..} (qlo) and {32+8G..} (qhi)
+  bf16x8_t qlo, qhi;
+  {
+    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (n & 3)) * kD + 8 * G;
+    uint4 lo = *reinterpret_cast<const uint4*>(qr);
+    uint4 hi = *reinterpret_cast<const uint4*>(qr + 32);
+    if (ROPE) {
+      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * G;
+      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+    }
+    qlo = __builtin_bit_cast(bf16x8_t, lo);
+    qhi = __builtin_bit_cast(bf16x8_t, hi);
+  }
+
+  // fused append: lanes 0..3 build the new K row of head g (lane c: dims
+  // {8c..} and {32+8c..}, rotated first with RoPE), lanes 4..7 the V row;
+  // BF16 pages park the rows, INT8 pages their codes and scales, in LDS
+  const bool app_here = APPEND && p1 == n_pages;
+  const int app_slot = (L - 1) % kPage;
+  __shared__ u32x4 new_rows[APPEND ? kWaves : 1][Q8 ? 8 : 16];   // 16-byte chunks
+  __shared__ float new_scales[APPEND && Q8 ? kWaves : 1][2];
+  if (app_here && lane < 8) {
+    const int c = lane & 3;
+    const bool is_k = lane < 4;
+    const uint16_t* src = (is_k ? a.k_new : a.v_new) + ((int64_t)b * kHkv + g) * kD + 8 * c;
+    uint4 lo = *reinterpret_cast<const uint4*>(src);
+    uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
+    if (ROPE && is_k) {
+      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * c;
+      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+    }
+    const int slot = APPEND ? g : 0;
+    if constexpr (Q8) {
+      u32x2 clo, chi;
+      const float sc = quantize_quad_row(lo, hi, clo, chi);
+      new_rows[slot][lane] = u32x4{clo.x, clo.y, chi.x, chi.y};
+      if (c == 0) new_scales[APPEND && Q8 ? g : 0][is_k ? 0 : 1] = sc;
+    } else {
+      // [K lo parts 0..3 | K hi parts | V lo | V hi] in 16 chunks: 2 per lane
+      reinterpret_cast<u32x4*>(&new_rows[slot][0])[(is_k ? 0 : 8) + c] = u32x4{lo.x, lo.y, lo.z, lo.w};
+      reinterpret_cast<u32x4*>(&new_rows[slot][0])[(is_k ? 0 : 8) + 4 + c] = u32x4{hi.x, hi.y, hi.z, hi.w};
+    }
+  }
+
+  LaneState st;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  int ent[kMaxSplitPages / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
+    const int j = p0 + c * 64 + lane;
+    ent[c] = (c * 64 < p1 - p0 && j <= last) ? bt[j] : 0;
+  }
+  bool bad_page = false;
+  auto raw_page_id = [&](int i) -> int {
+    const int j = i - p0;
+    int id = __builtin_amdgcn_readlane(ent[0], j & 63);
+#pragma unroll
+    for (int c = 1; c < kMaxSplitPages / 64; ++c)
+      if ((j >> 6) == c) id = __builtin_amdgcn_readlane(ent[c], j & 63);
+    return id;
+  };
+  auto page_id = [&](int i) -> int64_t {
+    const int id = raw_page_id(i);
+    const bool ok = (unsigned)id < (unsigned)a.num_pages;
+    bad_page |= !ok;
+    return ok ? id : 0;
+  };
+
+  __shared__ __attribute__((aligned(16))) char ring[F::kRingDepth][kWaves][F::kSlot];
+  const char* k_base = reinterpret_cast<const char*>(a.k_pool);
+  const char* v_base = reinterpret_cast<const char*>(a.v_pool);
+  const char* s_base = reinterpret_cast<const char*>(a.kv_scales);
+  // DMA lane offsets (bytes within a page): INT8 lane l takes bytes 16 l of
+  // the head's code block (token l/4, dims 16 (l%4) ..) and float l%32 of its
+  // scale line; BF16 lane 16 G + n takes token n, dims 8G.. (+32 for the
+  // second load)
+  uint32_t dma_k, dma_s = 0;
+  if constexpr (Q8) {
+    dma_k = (uint32_t)(g * kHeadCodes + 16 * lane);                 // the head's 1 KiB block
+    dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
+  } else {
+    dma_k = 2u * (uint32_t)(n * kRowElems + g * kD + 8 * G);    // token n, dims 8G..
+  }
+  auto fetch = [&](int page, int slot) {
+    const int64_t id = page_id(page);
+    char* dst = &ring[slot][g][0];
+    if constexpr (Q8) {
+      const int64_t off = id * (int64_t)kPageCodes;
+      __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
+      __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 1024, 16, 0, kStreamCpol);
+      __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + dma_s,
+                                       dst + 2048, 4, 0, kStreamCpol);
+    } else {
+      const int64_t off = id * (int64_t)(kPageElems * 2);
+      __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
+      __builtin_amdgcn_global_load_lds(k_base + off + dma_k + 64, dst + 1024, 16, 0, kStreamCpol);
+      __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 2048, 16, 0, kStreamCpol);
+      __builtin_amdgcn_global_load_lds(v_base + off + dma_k + 64, dst + 3072, 16, 0, kStreamCpol);
+    }
+  };
+  // LDS read addresses of this lane in slot 0 of its wavefront
+  const uint32_t slot0 = lds_address(&ring[0][g][0]);
+  constexpr uint32_t kRingSlotBytes = kWaves * F::kSlot;
+  const int jq = n >> 2, jr = n & 3;              // transposed-read chunk: token 4G + jq
+  uint32_t ka, va, sa = 0;
+  if constexpr (Q8) {
+    ka = slot0 + 64 * n + 8 * G;
+    va = slot0 + 1024 + 64 * (4 * G + jq) + 8 * jr;
+    sa = slot0 + 2048 + 16 * G;
+  } else {
+    ka = slot0 + 16 * lane;
+    // V block 0 = dims 0..15: dims 4 jr .. 4 jr + 3 live in part jr/2 of the
+    // lo half, at byte 8 (jr % 2) of that part's 16-byte row of the token
+    va = slot0 + 2048 + 16 * (16 * (jr >> 1) + 4 * G + jq) + 8 * (jr & 1);
+  }
+
+  auto park_new_row = [&](uint32_t slot_base) {
+    // overwrite the appended token's slot in the ring with the new row
+    const int sl = APPEND ? g : 0;
+    if constexpr (Q8) {
+      if (lane < 8) {
+        const u32x4 w = new_rows[sl][lane];
+        const int c = lane & 3;
+        char* base = &ring[0][g][0] + (slot_base - slot0) + (lane < 4 ? 0 : 1024) + 64 * app_slot + 8 * c;
+        *reinterpret_cast<u32x2*>(base) = u32x2{w.x, w.y};
+        *reinterpret_cast<u32x2*>(base + 32) = u32x2{w.z, w.w};
+      }
+      if (lane < 2) {
+        float* sp = reinterpret_cast<float*>(&ring[0][g][0] + (slot_base - slot0) + 2048);
+        sp[lane * 16 + app_slot] = new_scales[APPEND && Q8 ? g : 0][lane];
+      }
+    } else {
+      if (lane < 16) {
+        // chunk lane: row lane/4 (K lo, K hi, V lo, V hi), part lane%4
+        const u32x4 w = reinterpret_cast<const u32x4*>(&new_rows[sl][0])[lane];
+        char* base = &ring[0][g][0] + (slot_base - slot0) + 1024 * (lane >> 2) +
+                     16 * (16 * (lane & 3) + app_slot);
+        *reinterpret_cast<u32x4*>(base) = w;
+      }
+    }
+  };
+
+  auto step = [&](int i, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    const int slot = (i - p0) % F::kRingDepth;
+    const uint32_t off = slot * kRingSlotBytes;
+    wait_vmem<F::kLoads * (F::kRingDepth - 1)>();          // page i has landed
+    if (MASK && app_here) park_new_row(slot0 + off);
+    if constexpr (Q8) {
+      PageQ8 cur;
+      lds_page_issue(cur, ka + off, va + off, sa + off);
+      lds_page_ready(cur);
+      fetch(min(i + F::kRingDepth, last), slot);
+      consume_page<true, MASK>(st, cur, qlo, qhi, a.xscale, lane, MASK ? tail_valid : kPage);
+    } else {
+      PageBF16 cur;
+      lds_page_issue(cur, ka + off, va + off);
+      lds_page_ready(cur);
+      fetch(min(i + F::kRingDepth, last), slot);
+      consume_page<false, MASK>(st, cur, qlo, qhi, a.xscale, lane, MASK ? tail_valid : kPage);
+    }
+  };
+
+#pragma unroll
+  for (int r = 0; r < F::kRingDepth; ++r) fetch(min(p0 + r, last), r);
+  for (int i = p0; i < last; ++i) step(i, std::false_type{});
+  step(last, std::true_type{});
+  wait_vmem<0>();
+
+  if (app_here && lane < (Q8 ? 8 : 16)) {
+    const int id = raw_page_id(last);
+    if ((unsigned)id < (unsigned)a.num_pages) {
+      const int sl = APPEND ? g : 0;
+      if constexpr (Q8) {
+        const int c = lane & 3;
+        const bool is_k = lane < 4;
+        const u32x4 w = new_rows[sl][lane];
+        int8_t* dst = reinterpret_cast<int8_t*>(is_k ? a.k_pool_w : a.v_pool_w) +
+                      (int64_t)id * kPageCodes + g * kHeadCodes + app_slot * kD + 8 * c;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w.x, w.y};
+        *reinterpret_cast<u32x2*>(dst + 32) = u32x2{w.z, w.w};
+        if (c == 0)
+          a.kv_scales_w[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + app_slot] =
+              new_scales[APPEND && Q8 ? g : 0][is_k ? 0 : 1];
+      } else {
+        // chunk lane: K (lanes 0..7) or V (8..15); dims 8 (lane%4) (+32 for the hi parts)
+        const u32x4 w = reinterpret_cast<const u32x4*>(&new_rows[sl][0])[lane];
+        const int row = lane >> 2;                 // 0 K lo, 1 K hi, 2 V lo, 3 V hi
+        uint16_t* dst = reinterpret_cast<uint16_t*>(row < 2 ? a.k_pool_w : a.v_pool_w) +
+                        (int64_t)id * kPageElems + app_slot * kRowElems + g * kD +
+                        32 * (row & 1) + 8 * (lane & 3);
+        *reinterpret_cast<u32x4*>(dst) = w;
+      }
+    }
+  }
+
+  // finish: the normaliser over the 4 token groups; the BF16 and remainder
+  // rows of each head added (lane n of group 0 gets lane n of group 1)
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  float o[4][4];                                 // [tile][row = head]
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) o[t][rr] = st.acc[t][rr] + __shfl_down(st.acc[t][rr], 16);
+
+  float m_out = st.m, l_out = st.l;
+  if (bad_page) {
+    m_out = __builtin_nanf("");
+    l_out = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) o[t][rr] = __builtin_nanf("");
+  }
+  // head r's m and l live in lanes with n % 4 == r; lane n (group 0) needs all 4
+  float mh[4], lh[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    mh[rr] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_out), rr));
+    lh[rr] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_out), rr));
+  }
+  if (G == 0) {
+    if (n_splits_b == 1) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float inv = 1.f / lh[rr];
+        const int64_t orow = ((int64_t)b * kHq + kGroup * g + rr) * kD;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int d = out_dim<Q8>(t, n);
+          if (OUT_BF16)
+            reinterpret_cast<uint16_t*>(a.out)[orow + d] = (uint16_t)f32_to_bf16_rne(o[t][rr] * inv);
+          else
+            reinterpret_cast<float*>(a.out)[orow + d] = o[t][rr] * inv;
+        }
+      }
+    } else {
+      const int64_t prow = ((int64_t)b * a.num_splits + s) * kHq + kGroup * g;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a.part_acc[(prow + rr) * kD + out_dim<Q8>(t, n)] = o[t][rr];
+        if (n == 0) {
+          a.part_ml[(prow + rr) * 2 + 0] = mh[rr];
+          a.part_ml[(prow + rr) * 2 + 1] = lh[rr];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace pa
+
+namespace pa {
+
+// Host: enqueue the decode kernel for page format Q8 (plus the split merge
+// when the plan has more than one split).  event_before/after (may be NULL)
+// are recorded right around the decode kernel.  Returns a hipError_t.
+template <bool Q8>
+inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
+                                bool rope, hipStream_t st, hipEvent_t event_before,
+                                hipEvent_t event_after) {
+  const dim3 grid(a.num_splits, batch), block(kThreads);
+  hipError_t e = hipSuccess;
+  if (event_before && (e = hipEventRecord(event_before, st)) != hipSuccess) return e;
+  if (out_bf16) {
+    if (rope) hipLaunchKernelGGL((decode_kernel<Q8, true, true, true>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<Q8, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<Q8, true, false>), grid, block, 0, st, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((decode_kernel<Q8, false, true, true>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<Q8, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<Q8, false, false>), grid, block, 0, st, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (event_after && (e = hipEventRecord(event_after, st)) != hipSuccess) return e;
+  if (a.num_splits > 1) {
+    MergeArgs m;
+    m.seq_lens = a.seq_lens;
+    m.out = a.out;
+    m.part_acc = a.part_acc;
+    m.part_ml = a.part_ml;
+    m.max_blocks = a.max_blocks;
+    m.max_seq_len = a.max_seq_len;
+    m.pages_per_split = a.pages_per_split;
+    m.num_splits = a.num_splits;
+    if (out_bf16) hipLaunchKernelGGL(merge_kernel<true>, dim3(batch), dim3(256), 0, st, m);
+    else hipLaunchKernelGGL(merge_kernel<false>, dim3(batch), dim3(256), 0, st, m);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pa

@@ -7,7 +7,7 @@
 #include "pa_decode.h"
 #include "pa_decode_q8.h"
 #include "pa_host.h"
-#include "pa_kernels_q8.h"
+#include "pa_decode_kernel.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(ROPE ? 256 : 64) void append_q8_kernel(
   u32x2 clo, chi;
   const float sc = quantize_quad_row(lo, hi, clo, chi);
   const int slot = pos % kPage;
-  int8_t* dst = (is_k ? k_codes : v_codes) + (int64_t)id * kPageCodes + slot * kRowCodes + g * kD + 8 * c;
+  int8_t* dst = (is_k ? k_codes : v_codes) + (int64_t)id * kPageCodes + g * kHeadCodes + slot * kD + 8 * c;
   *reinterpret_cast<u32x2*>(dst) = clo;
   *reinterpret_cast<u32x2*>(dst + 32) = chi;
   if (c == 0) kv_scales[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + slot] = sc;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void fill_q8_kernel(const uint16_t* __restrict
   u32x2 clo, chi;
   const float sc = quantize_quad_row(lo, hi, clo, chi);
   const int slot = t % kPage;
-  int8_t* dst = (is_k ? k_codes : v_codes) + (int64_t)id * kPageCodes + slot * kRowCodes + g * kD + 8 * c;
+  int8_t* dst = (is_k ? k_codes : v_codes) + (int64_t)id * kPageCodes + g * kHeadCodes + slot * kD + 8 * c;
   *reinterpret_cast<u32x2*>(dst) = clo;
   *reinterpret_cast<u32x2*>(dst + 32) = chi;
   if (c == 0) kv_scales[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + slot] = sc;
@@ -198,16 +198,16 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
   }
   if ((int64_t)batch * ns > INT32_MAX || ns > 65535 || batch > 65535 * 64) return PA_ERR_VALUE;
 
-  pa::DecodeArgsQ8 a;
+  pa::DecodeArgs a = {};
   a.q = (const uint16_t*)q;
-  a.k_codes = (const int8_t*)k_codes;
-  a.v_codes = (const int8_t*)v_codes;
+  a.k_pool = k_codes;
+  a.v_pool = v_codes;
   a.kv_scales = (const float*)kv_scales;
   a.k_new = (const uint16_t*)k_new;
   a.v_new = (const uint16_t*)v_new;
-  a.k_codes_w = (int8_t*)k_codes;
-  a.v_codes_w = (int8_t*)v_codes;
-  a.kv_scales_w = (float*)kv_scales;
+  a.k_pool_w = const_cast<void*>(k_codes);
+  a.v_pool_w = const_cast<void*>(v_codes);
+  a.kv_scales_w = (float*)const_cast<void*>(kv_scales);
   a.rope_cos = rope ? rope->cos : nullptr;
   a.rope_sin = rope ? rope->sin : nullptr;
   a.block_tables = block_tables;
@@ -223,37 +223,10 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
   a.max_seq_len = max_seq_len;
   a.pages_per_split = ps;
   a.num_splits = ns;
-
-  hipStream_t st = (hipStream_t)stream;
-  const dim3 grid(ns, batch), block(pa::kThreads);
-  if (out_dtype == PA_OUT_BF16) {
-    if (rope) hipLaunchKernelGGL((pa::decode_q8_kernel<true, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((pa::decode_q8_kernel<true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((pa::decode_q8_kernel<true, false>), grid, block, 0, st, a);
-  } else {
-    if (rope) hipLaunchKernelGGL((pa::decode_q8_kernel<false, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((pa::decode_q8_kernel<false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((pa::decode_q8_kernel<false, false>), grid, block, 0, st, a);
-  }
-  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  if (ns > 1) {
-    // the split merge is format-independent: it reads the partials only
-    pa::DecodeArgs m = {};
-    m.seq_lens = seq_lens;
-    m.out = out;
-    m.part_acc = a.part_acc;
-    m.part_ml = a.part_ml;
-    m.max_blocks = a.max_blocks;
-    m.max_seq_len = max_seq_len;
-    m.pages_per_split = ps;
-    m.num_splits = ns;
-    if (out_dtype == PA_OUT_BF16)
-      hipLaunchKernelGGL(pa::merge_kernel<true>, dim3(batch), dim3(256), 0, st, m);
-    else
-      hipLaunchKernelGGL(pa::merge_kernel<false>, dim3(batch), dim3(256), 0, st, m);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  }
-  return PA_OK;
+  const hipError_t e = pa::launch_decode<true>(a, batch, out_dtype == PA_OUT_BF16, fused,
+                                               rope != nullptr, (hipStream_t)stream, nullptr,
+                                               nullptr);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // namespace

@@ -37,7 +37,7 @@ def _bits(vals):
 
 
 def empty_q8_pools(pages):
-    return (np.zeros((pages, P, HKV, D), np.int8), np.zeros((pages, P, HKV, D), np.int8),
+    return (np.zeros((pages, HKV, P, D), np.int8), np.zeros((pages, HKV, P, D), np.int8),
             np.zeros((pages, HKV, 2, P), np.float32))
 
 
@@ -121,20 +121,21 @@ def pin_q8_append_touches_one_slot(kq):
     lens = np.array([17, 0, 48], np.int32)                  # slot 0 of page 2; idle; slot 15 of page 6
     kn, vn = W.random_rows(rng, 3), W.random_rows(rng, 3)
     k2, v2, s2 = kq.append_kv_q8(kc, vc, sc, kn, vn, bt, lens)
-    changed = {(int(p), int(t)) for p, t in zip(*np.nonzero(np.any(k2 != kc, axis=(2, 3))))}
+    changed = {(int(p), int(t)) for p, t in zip(*np.nonzero(np.any(k2 != kc, axis=(1, 3))))}
     assert changed <= {(2, 0), (6, 15)}
     for b, (page, slot) in ((0, (2, 0)), (2, (6, 15))):
         ck, skk = kq.quantize_rows(kn[b])
         cv, svv = kq.quantize_rows(vn[b])
-        assert np.array_equal(k2[page, slot], ck) and np.array_equal(v2[page, slot], cv)
+        assert np.array_equal(k2[page, :, slot], ck) and np.array_equal(v2[page, :, slot], cv)
         assert np.array_equal(s2[page, :, 0, slot], skk) and np.array_equal(s2[page, :, 1, slot], svv)
     mask = np.ones(sc.shape, bool)
     mask[2, :, :, 0] = False
     mask[6, :, :, 15] = False
     assert np.array_equal(s2[mask], sc[mask])
-    vmask = np.ones(vc.shape[:2], bool)
+    vmask = np.ones((pages, P), bool)
     vmask[2, 0] = vmask[6, 15] = False
-    assert np.array_equal(v2[vmask], vc[vmask])
+    v2t, vct = np.swapaxes(v2, 1, 2), np.swapaxes(vc, 1, 2)          # [page][slot][head][dim]
+    assert np.array_equal(v2t[vmask], vct[vmask])
 
 
 def pin_q8_fill_equals_appends(kq):

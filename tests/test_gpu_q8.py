@@ -123,8 +123,8 @@ def test_q8_fill_bitexact(start, count):
     pa = _pa()
     rng = np.random.default_rng(start * 13 + count)
     pages = 200
-    kc, vc, sc = (rng.integers(-128, 128, (pages, P, HKV, D), dtype=np.int8),
-                  rng.integers(-128, 128, (pages, P, HKV, D), dtype=np.int8),
+    kc, vc, sc = (rng.integers(-128, 128, (pages, HKV, P, D), dtype=np.int8),
+                  rng.integers(-128, 128, (pages, HKV, P, D), dtype=np.int8),
                   np.full((pages, HKV, 2, P), np.nan, np.float32))
     row = np.full(128, -1, np.int32)
     n = W.pages_for(start + count)
@@ -277,7 +277,8 @@ def test_q8_full_batch256_len2048_bench_configuration():
         kq, ks = kvquant.quantize_rows(kr)
         vq, vs = kvquant.quantize_rows(vr)
         # the pages on the GPU hold exactly the oracle's codes and scales
-        gk = kc[torch.from_numpy(pages).long().cuda()].cpu().numpy().reshape(-1, HKV, D)[:L]
+        gk = np.swapaxes(kc[torch.from_numpy(pages).long().cuda()].cpu().numpy(), 1, 2)
+        gk = gk.reshape(-1, HKV, D)[:L]                                    # [token][head][dim]
         gs = sc[torch.from_numpy(pages).long().cuda()].cpu().numpy()       # [n][8][2][16]
         assert np.array_equal(gk, kq)
         gks = np.transpose(gs[:, :, 0, :], (0, 2, 1)).reshape(-1, HKV)[:L]

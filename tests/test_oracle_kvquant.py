@@ -28,8 +28,9 @@ MUTANTS = {
     "multiply_by_scale": ("ratio = (x / safe[..., None])", "ratio = (x * safe[..., None])"),
     "v_scale_into_k_slot": ("scales[physical, :, 1, slot] = vs", "scales[physical, :, 0, slot] = vs"),
     "scale_slot_wrong": ("scales[physical, :, 0, slot] = ks", "scales[physical, :, 0, 0] = ks"),
-    "gather_k_scale_for_v": ("dequantize(codes[physical, slot], scales[physical, :, which, slot])",
-                             "dequantize(codes[physical, slot], scales[physical, :, 0, slot])"),
+    "k_codes_not_written": ("    k_codes[physical, :, slot] = kc\n", "    pass\n"),
+    "gather_k_scale_for_v": ("dequantize(codes[physical, :, slot], scales[physical, :, which, slot])",
+                             "dequantize(codes[physical, :, slot], scales[physical, :, 0, slot])"),
     "dequantize_without_scale": ("return np.asarray(codes, np.float64) * np.asarray(scale, np.float64)[..., None]",
                                  "return np.asarray(codes, np.float64)"),
     "append_slot_off_by_one": ("_write_token(kc, vc, sc, physical, pos % page_size,",

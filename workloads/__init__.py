@@ -288,13 +288,14 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
 class Q8Batch:
     """One layer's decode-step inputs over INT8 pages.
 
-    Codes are int8 in the BF16 pool's layout, scales float32
-    ``[num_pages][8][2][16]`` (per page and KV head: 16 K scales, 16 V scales).
+    Codes are int8 ``[num_pages][8][16][64]`` (per page, each KV head's 16
+    token rows contiguous), scales float32 ``[num_pages][8][2][16]`` (per page
+    and KV head: 16 K scales, 16 V scales).
     """
 
     name: str
     q: np.ndarray               # uint16 [B][32][64]
-    k_codes: np.ndarray         # int8   [num_pages][16][8][64]
+    k_codes: np.ndarray         # int8   [num_pages][8][16][64]
     v_codes: np.ndarray
     kv_scales: np.ndarray       # float32 [num_pages][8][2][16]
     block_tables: np.ndarray    # int32  [B][128]
@@ -347,7 +348,7 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
     if placement not in ("random", "identity"):
         raise ValueError(placement)
     q = f32_to_bf16_bits(rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM), dtype=np.float32))
-    shape = (num_pages, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
+    shape = (num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM)
     k_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
     v_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
     kv_scales = np.full((num_pages, NUM_KV_HEADS, 2, PAGE_SIZE), np.nan, dtype=np.float32)
@@ -377,8 +378,8 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
         stored = L - 1 if append else L
         for t in range(stored):
             page, slot = pages[t // PAGE_SIZE], t % PAGE_SIZE
-            k_codes[page, slot] = kc[t]
-            v_codes[page, slot] = vc[t]
+            k_codes[page, :, slot] = kc[t]
+            v_codes[page, :, slot] = vc[t]
             kv_scales[page, :, 0, slot] = ks[t]
             kv_scales[page, :, 1, slot] = vs[t]
         if append:
