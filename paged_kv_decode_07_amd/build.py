@@ -52,8 +52,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+    missing = undefined_kernel_stubs(tmp)
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs left undefined (a kernel template was not "
+                           "instantiated on the host side):\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
+
+
+def undefined_kernel_stubs(lib_path: str) -> list:
+    """Host launch stubs referenced by the library but not defined in it."""
+    nm = next((c for c in ("/opt/rocm/llvm/bin/llvm-nm", shutil.which("nm")) if c and os.path.exists(c)),
+              None)
+    if nm is None:
+        return []
+    out = subprocess.run([nm, "--undefined-only", lib_path], capture_output=True, text=True).stdout
+    return [ln.split()[-1] for ln in out.splitlines() if "__device_stub__" in ln]
 
 
 if __name__ == "__main__":
