@@ -19,8 +19,11 @@ Pass A times the K steps with one event pair around each step; pass B
 repeats them with the library recording events right around its main
 kernel (the roofline figure); pass C times the two-call form; pass D the
 fused step with RoPE; pass E the fused step over INT8 pages (the BF16 cache
-quantised on the GPU first).  The flush is outside every event pair.  Prints
-one JSON line.
+quantised on the GPU first).  Two diagnostics follow: the same step with the
+pages in identity order, and a plain streaming read of 1 GiB (the achievable
+read bandwidth, beside the published peak).  The flush is outside every event
+pair.  The oracle baseline runs on one core and on a pool of worker processes
+forked before the GPU is initialised.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -74,47 +77,92 @@ def measured_traffic(path: str = TRAFFIC_FILE, sources=None):
     return int(round(t["hbm_bytes_per_launch"]))
 
 
-def cpu_baseline(batch, gpu_out, seconds: float):
-    """The oracle, as it stands, on the first sequences of the same workload."""
-    import numpy as np
-    import oracle
+_CPU_STATE = None          # (batch, k_ref, v_ref): set before the pool forks
+
+
+def _blas_one_thread():
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx is not None:
-        ctx.__enter__()
-    try:
-        k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new,
-                                        batch.block_tables, batch.seq_lens)
-        # sequences in batch order, cycling over the batch until the time
-        # budget is spent (the whole batch takes well under a second)
-        done, t0 = [], time.perf_counter()
-        worst = 0.0
-        while True:
-            b = len(done) % batch.batch
-            ref = oracle.decode_attention(batch.q, k_ref, v_ref, batch.block_tables,
-                                          batch.seq_lens, batch.scale, sequences=[b])
+        pass
+
+
+def _oracle_decodes(first: int, stride: int, seconds: float, gpu_out=None):
+    """Decode sequences first, first+stride, ... (cycling) with the oracle for ``seconds``."""
+    import numpy as np
+    import oracle
+    batch, k_ref, v_ref = _CPU_STATE
+    done, worst, t0 = [], 0.0, time.perf_counter()
+    while True:
+        b = (first + stride * len(done)) % batch.batch
+        ref = oracle.decode_attention(batch.q, k_ref, v_ref, batch.block_tables,
+                                      batch.seq_lens, batch.scale, sequences=[b])
+        if gpu_out is not None:
             worst = max(worst, float(np.max(np.abs(ref[b] - gpu_out[b]))))
-            done.append(b)
-            if time.perf_counter() - t0 >= seconds and len(done) >= 2:
-                break
-        dt = time.perf_counter() - t0
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
+        done.append(b)
+        if time.perf_counter() - t0 >= seconds and len(done) >= 2:
+            break
+    return done, time.perf_counter() - t0, worst
+
+
+def _pool_leg(args):
+    first, stride, seconds = args
+    done, dt, _ = _oracle_decodes(first, stride, seconds)
+    return done, dt
+
+
+def prepare_cpu_baseline(batch, pool_workers: int):
+    """Append on the host and fork the worker pool, before the GPU is initialised
+    (the workers inherit the inputs and never touch the GPU)."""
+    global _CPU_STATE
+    import multiprocessing as mp
+    import oracle
+    k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new,
+                                    batch.block_tables, batch.seq_lens)
+    _CPU_STATE = (batch, k_ref, v_ref)
+    if pool_workers <= 1:
+        return None
+    return mp.get_context("fork").Pool(pool_workers, initializer=_blas_one_thread)
+
+
+def cpu_baseline(gpu_out, seconds: float, pool=None, pool_workers: int = 0):
+    """The oracle, as it stands, over the same workload: one core, then a process pool."""
+    import contextlib
+    batch = _CPU_STATE[0]
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        limit = contextlib.nullcontext()
+    with limit:
+        done, dt, worst = _oracle_decodes(0, 1, seconds, gpu_out)
     tokens = int(sum(int(batch.seq_lens[b]) for b in done))
     kv = tokens * 2048
-    return {
+    res = {
         "value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": (f"{len(done)} sequence decodes cycling over the {batch.batch} sequences "
                    f"({tokens} tokens, {kv / 2**20:.0f} MiB of K/V), float64 NumPy, "
                    f"1 BLAS thread, {dt:.1f} s"),
         "seq_per_s": round(len(done) / dt, 3),
         "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "blas_threads": 1,
         "max_abs_vs_gpu_on_sample": worst,
     }
+    if pool is not None:
+        t0 = time.perf_counter()
+        legs = pool.map(_pool_leg, [(w, pool_workers, seconds) for w in range(pool_workers)])
+        wall = time.perf_counter() - t0
+        n = sum(len(d) for d, _ in legs)
+        ptok = sum(int(batch.seq_lens[b]) for d, _ in legs for b in d)
+        res["pool"] = {
+            "value": round(ptok * 2048 / wall / 1e9, 4), "unit": "GB/s", "cores": pool_workers,
+            "sample": (f"{n} sequence decodes over {pool_workers} worker processes "
+                       f"(1 BLAS thread each), {wall:.1f} s wall"),
+            "seq_per_s": round(n / wall, 3),
+        }
+    return res
 
 
 def main() -> int:
@@ -126,6 +174,8 @@ def main() -> int:
     ap.add_argument("--placement", choices=["random", "identity"], default="random")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle process-pool size (0 = the CPUs this process may use, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 256 MiB device copy per step (outside the timed events), "
@@ -145,14 +195,20 @@ def main() -> int:
     from paged_kv_decode_07_amd import accounting as A
     from paged_kv_decode_07_amd import binding as pa
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    pa.load_library()
 
     t0 = time.perf_counter()
     batch = W.make_workload(4, placement=args.placement, append=True)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s "
         f"({batch.batch} sequences, {batch.num_pages} pages)")
+    pool, pool_workers = None, 0
+    if not args.no_cpu_baseline:
+        pool_workers = args.cpu_workers or min(len(os.sched_getaffinity(0)), 16)
+        pool = prepare_cpu_baseline(batch, pool_workers)
+
+    # the GPU is first touched here, after the oracle's worker processes were forked
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
 
     def up16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
@@ -302,6 +358,29 @@ def main() -> int:
         q8_step()
     t_q8 = timed(q8_step, K)
     log(f"{K} INT8-page steps done")
+    del q8_k, q8_v, q8_s
+
+    # diagnostic: the same step with the pages in identity order (each
+    # sequence's pages consecutive in the pool)
+    order = bt.reshape(-1).long()
+    k_id, v_id = k_pool[order].contiguous(), v_pool[order].contiguous()
+    bt_id = torch.arange(B * W.MAX_BLOCKS, dtype=torch.int32, device=dev).reshape(B, W.MAX_BLOCKS)
+    out_id = torch.empty_like(out)
+
+    def identity_step():
+        pa.append_decode_attention(q, k_new, v_new, k_id, v_id, bt_id, lens, msl,
+                                   scale=batch.scale, out=out_id, pages_per_split=ps,
+                                   workspace=workspace, stream=stream)
+    identity_step()
+    t_identity = timed(identity_step, K)
+    del k_id, v_id
+
+    # what a plain streaming read of 1 GiB achieves on this device
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    pa.stream_read(flush_buf, sink, stream=stream)
+    t_read = timed(lambda: pa.stream_read(flush_buf, sink, stream=stream), K)
+    read_gbps = flush_buf.numel() * 4 / float(np.median(t_read)) / 1e9
+    log(f"{K} identity-placement steps and {K} streaming reads done")
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
     by_q8 = A.step_bytes_q8(batch.seq_lens)["kv"]
@@ -347,6 +426,13 @@ def main() -> int:
         "prefill_fill_gbps": round(fill_bytes / float(t_fill.mean()) / 1e9, 1),
         "allocator_us_per_decode_step": round(alloc_step_us, 1),
         "two_call_kv_gbps": round(kv / float(t_two.mean()) / 1e9, 2),
+        "achievable_read": {
+            "kernel": "pa_stream_read over a 1 GiB buffer (median of the timed reads)",
+            "gbps": round(read_gbps, 1),
+            "frac_of_peak": round(read_gbps / HBM_PEAK_GBPS, 4),
+            "step_value_frac_of_achievable": round(value / read_gbps, 4),
+        },
+        "identity_placement_step_us": round(float(t_identity.mean()) * 1e6, 2),
         "int8_pages": {
             "step_us": round(float(t_q8.mean()) * 1e6, 2),
             "step_min_us": round(float(t_q8.min()) * 1e6, 2),
@@ -373,9 +459,13 @@ def main() -> int:
         "kernel_source_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(batch, out.cpu().numpy().astype(np.float64),
-                                            args.cpu_seconds)
+        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s on one core, then "
+            f"{args.cpu_seconds:.0f} s on {pool_workers} processes")
+        line["cpu_baseline"] = cpu_baseline(out.cpu().numpy().astype(np.float64),
+                                            args.cpu_seconds, pool, pool_workers)
+        if pool is not None:
+            pool.close()
+            pool.join()
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

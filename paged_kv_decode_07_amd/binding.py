@@ -32,6 +32,8 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_append_kv_q8", "pa_append_kv_rope_q8", "pa_fill_kv_q8", "pa_decode_attention_q8",
            "pa_append_decode_attention_q8", "pa_append_decode_attention_rope_q8",
            "pa_decode_plan_lengths_q8",
+           # include/pa_measure.h
+           "pa_stream_read",
            # include/pa_kvpool.h
            "pa_kvpool_create", "pa_kvpool_destroy", "pa_kvpool_credit", "pa_kvpool_submit",
            "pa_kvpool_admit", "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
@@ -100,6 +102,7 @@ def load_library(path: str | None = None):
                                                            SZ, P]
         lib.pa_decode_plan_lengths_q8.argtypes = [SP, I32, P, I32, I32, ctypes.POINTER(I32),
                                                   ctypes.POINTER(I32)]
+        lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
         I64 = ctypes.c_int64
         PP = ctypes.POINTER(ctypes.c_void_p)
         lib.pa_kvpool_create.argtypes = [I32, I32, I32, I32, I32, PP]
@@ -130,7 +133,8 @@ def load_library(path: str | None = None):
                      "pa_kvpool_block_table", "pa_kvpool_request_info",
                      "pa_kvpool_get_stats", "pa_append_kv_q8", "pa_append_kv_rope_q8",
                      "pa_fill_kv_q8", "pa_decode_attention_q8", "pa_append_decode_attention_q8",
-                     "pa_append_decode_attention_rope_q8", "pa_decode_plan_lengths_q8"):
+                     "pa_append_decode_attention_rope_q8", "pa_decode_plan_lengths_q8",
+                     "pa_stream_read"):
             getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
@@ -567,6 +571,18 @@ def append_decode_attention_q8(q, k_new, v_new, k_codes, v_codes, kv_scales, blo
                       _rope(rope_cos, rope_sin), k_codes, v_codes, kv_scales, block_tables,
                       seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
                       stream)
+
+
+def stream_read(buf, sink, groups: int = 0, stream=None) -> None:
+    """Read every byte of ``buf`` once (``include/pa_measure.h``); ``sink`` holds a
+    uint32 word per work-group."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda or sink.dtype != torch.int32:
+        raise ValueError("stream_read: contiguous device buffer and int32 device sink required")
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < (groups if groups > 0 else 65536):
+        raise ValueError("stream_read: sink smaller than the number of work-groups")
+    _check(load_library().pa_stream_read(_ptr(buf), nbytes, _ptr(sink), int(groups),
+                                         _stream_ptr(stream)), "pa_stream_read")
 
 
 class KVPool:

@@ -225,3 +225,14 @@ def test_q8_planner_prefers_longer_splits_for_smaller_pages():
         ps16, _ = pa.decode_plan_lengths(lens, 40000, num_cus=256)
         assert ps8 >= 8 and ns8 == -(-W.pages_for(int(lens.max())) // ps8)
         assert ps8 >= ps16 or ps8 == W.pages_for(int(lens.max())), (i, ps8, ps16)
+
+
+def test_stream_read_argument_errors(lib):
+    F, sink = FAKE, ctypes.c_void_p(0x20000)
+    assert lib.pa_stream_read(None, 1024, sink, 0, None) == -1
+    assert lib.pa_stream_read(F, 1024, None, 0, None) == -1
+    assert lib.pa_stream_read(ctypes.c_void_p(0x10008), 1024, sink, 0, None) == -3
+    assert lib.pa_stream_read(F, 1000, sink, 0, None) == -6          # not a multiple of 16
+    assert lib.pa_stream_read(F, 0, sink, 0, None) == -6
+    assert lib.pa_stream_read(F, 1024, sink, -1, None) == -6
+    assert lib.pa_stream_read(F, 1024, sink, 65537, None) == -6
