@@ -111,12 +111,16 @@ using namespace pa_host;
 namespace {
 
 // Planner cost model for INT8 pages: 17 KiB per page (8 KiB of K codes,
-// 8 KiB of V codes, 1 KiB of scales); the per-page time of one CU alone and
-// the fixed cost per work-group were fitted to this kernel on MI355X.
+// 8 KiB of V codes, 1 KiB of scales).  The per-page time of one CU alone, the
+// fixed cost per work-group and per empty grid slot were fitted to this
+// kernel's measured times on MI355X over batches of 8 to 512 sequences
+// (uniform and Zipf lengths) and split sizes 8 .. 128 pages.
 PlanModel q8_model() {
   PlanModel m;
   m.page_bytes = 2.0 * pa::kPageCodes + pa::kScalePageFloats * 4.0;
-  m.page_us = 0.5;
+  m.page_us = 0.8;
+  m.group_us = 2.0;
+  m.empty_us = 1.0;
   return m;
 }
 
