@@ -1,0 +1,131 @@
+"""The fused decode step captured in a HIP graph and replayed as a serving loop would.
+
+The library enqueues kernels on the caller's stream and allocates nothing, so
+the step can be captured once (launch shape fixed by the declared capacity)
+and replayed with new inputs written into the same buffers.  Every replay is
+checked bit for bit against the same step run eagerly on a twin set of
+buffers, with eager work and synchronisations between the replays; the last
+step is also checked against the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import assert_close, dev16, dev32
+from oracle import kvquant
+
+pytestmark = pytest.mark.gpu
+
+CAP = 400                     # declared capacity: the launch shape of the captured step
+STEPS = 6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from paged_kv_decode_07_amd import binding
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _state(q8: bool, seed: int):
+    lens0 = np.array([5, 100, 250, 31, 0, 390 - STEPS], np.int32)
+    pages = len(lens0) * W.pages_for(CAP) + 4
+    if q8:
+        w = W.make_q8_batch(lens0, pages, seed)
+        pools = [torch.from_numpy(a.copy()).cuda() for a in (w.k_codes, w.v_codes, w.kv_scales)]
+    else:
+        w = W.make_batch(lens0, pages, seed)
+        pools = [dev16(w.k_pool), dev16(w.v_pool)]
+    # every sequence owns pages for CAP tokens (its table row extended from the free pages)
+    bt = np.full((len(lens0), W.MAX_BLOCKS), -1, np.int32)
+    used = {int(p) for p in w.block_tables.ravel() if p >= 0}
+    free = [p for p in range(pages) if p not in used]
+    for b in range(len(lens0)):
+        n = W.pages_for(int(lens0[b]))
+        bt[b, :n] = w.block_tables[b, :n]
+        extra = W.pages_for(CAP) - n
+        bt[b, n:n + extra] = free[:extra]
+        free = free[extra:]
+    return w, pools, bt, lens0
+
+
+def _run(q8, pools, q, kn, vn, bt, lens, out, ws):
+    from paged_kv_decode_07_amd import binding as pa
+    if q8:
+        pa.append_decode_attention_q8(q, kn, vn, *pools, bt, lens, CAP, out=out,
+                                      pages_per_split=8, workspace=ws)
+    else:
+        pa.append_decode_attention(q, kn, vn, *pools, bt, lens, CAP, out=out,
+                                   pages_per_split=8, workspace=ws)
+
+
+@pytest.mark.parametrize("q8", [False, True], ids=["bf16", "int8"])
+def test_graph_replays_match_eager_steps(q8):
+    from paged_kv_decode_07_amd import binding as pa
+    w, pools_g, bt_h, lens0 = _state(q8, 1300 + q8)
+    pools_e = [p.clone() for p in pools_g]
+    B = len(lens0)
+    bt = dev32(bt_h)
+    rng = np.random.default_rng(1400 + q8)
+    q_s = torch.zeros((B, 32, 64), dtype=torch.int16, device="cuda")
+    kn_s = torch.zeros((B, 8, 64), dtype=torch.int16, device="cuda")
+    vn_s = torch.zeros_like(kn_s)
+    lens_s = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out_g = torch.empty((B, 32, 64), dtype=torch.float32, device="cuda")
+    out_e = torch.empty_like(out_g)
+    need = pa.decode_workspace_bytes(B, CAP, pools_g[0].shape[0], W.MAX_BLOCKS, 8)
+    ws_g = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws_g)
+
+    def inputs(step):
+        lens = np.where(lens0 > 0, lens0 + step + 1, 0).astype(np.int32)
+        return (W.random_q(rng, B), W.random_rows(rng, B), W.random_rows(rng, B), lens)
+
+    # warm-up outside the capture (device queries, first launches), on throw-away copies
+    scratch = [p.clone() for p in pools_g]
+    _run(q8, scratch, q_s, kn_s, vn_s, bt, lens_s, out_g, ws_g)
+    torch.cuda.synchronize()
+    del scratch
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            _run(q8, pools_g, q_s, kn_s, vn_s, bt, lens_s, out_g, ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    last = None
+    for step in range(STEPS):
+        qh, knh, vnh, lens = inputs(step)
+        q_s.copy_(dev16(qh)); kn_s.copy_(dev16(knh)); vn_s.copy_(dev16(vnh))
+        lens_s.copy_(dev32(lens))
+        graph.replay()
+        torch.cuda.synchronize()
+        # the same step, eagerly, on the twin buffers
+        _run(q8, pools_e, dev16(qh), dev16(knh), dev16(vnh), bt, dev32(lens), out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {step}: output differs from the eager step"
+        for pg, pe in zip(pools_g, pools_e):
+            # bit patterns: the INT8 scale pool keeps NaN poison in its unused slots
+            bits = (lambda t: t.view(torch.int32)) if pg.dtype == torch.float32 else (lambda t: t)
+            assert torch.equal(bits(pg), bits(pe)), f"replay {step}: pools differ from the eager step"
+        last = (qh, lens)
+
+    # the final state against the oracle (the cache holds every appended token)
+    qh, lens = last
+    if q8:
+        kc, vc, sc = (p.cpu().numpy() for p in pools_g)
+        ref = kvquant.decode_attention_q8(qh, kc, vc, sc, bt_h, lens, W.SCALE)
+    else:
+        kp, vp = (p.cpu().numpy().view(np.uint16) for p in pools_g)
+        ref = oracle.decode_attention(qh, kp, vp, bt_h, lens, W.SCALE)
+    assert_close(out_g.cpu().numpy().astype(np.float64), ref, where=f"graph final ({'int8' if q8 else 'bf16'})")
