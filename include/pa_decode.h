@@ -266,6 +266,47 @@ int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
                                  void* event_after_main);
 
 /*
+ * Work list for known sequence lengths (host copy): the (sequence, split)
+ * work items of one decode launch, ordered by their page count, largest
+ * first, so that long items start first and short ones fill in behind them
+ * (the longest-processing-time-first rule).  Items without pages are left
+ * out, except split 0 of a sequence without pages (its output row is still
+ * written: zeros, or NaN for a length beyond max_seq_len).
+ *   pages_per_split: the split size, or 0 to plan it from the lengths (the
+ *     cost model of pa_decode_plan_lengths, or of pa_decode_plan_lengths_q8
+ *     when page_format is 1 (INT8 pages); 0 = BF16 pages);
+ *   num_cus: compute units assumed by the planner (0 = current device);
+ *   work: host int32 [2 * capacity]; item k is sequence work[2k], split
+ *     work[2k+1]; *count receives the number of items (PA_ERR_VALUE when it
+ *     exceeds capacity; batch * splits always suffices);
+ *   pages_out, splits_out (may be NULL): the split size and the splits per
+ *     sequence of the plan, to be passed with the list.
+ */
+int pa_decode_worklist(const pa_shape* shape, int32_t batch, const int32_t* seq_lens_host,
+                       int32_t max_seq_len, int32_t pages_per_split, int32_t page_format,
+                       int32_t num_cus, int32_t* work, int32_t capacity, int32_t* count,
+                       int32_t* pages_out, int32_t* splits_out);
+
+/*
+ * Decode step launched from a work list (a copy of pa_decode_worklist's
+ * output in device memory, 4-byte aligned; num_work items): one work-group
+ * per item, in list order.  k_new and v_new are both given (the fused
+ * append, as pa_append_decode_attention) or both NULL (decode only, as
+ * pa_decode_attention).  pages_per_split must be the split size the list was
+ * built for (0 is refused).  Results are bitwise those of the grid launch.
+ * The list must hold every item of the plan exactly once; entries naming a
+ * sequence outside [0, batch) or a split outside the plan are skipped.
+ */
+int pa_append_decode_attention_worklist(const pa_shape* shape, int32_t batch,
+                                        const void* q, const void* k_new, const void* v_new,
+                                        void* k_pool, void* v_pool,
+                                        const int32_t* block_tables, const int32_t* seq_lens,
+                                        int32_t max_seq_len, float scale,
+                                        void* out, int32_t out_dtype, int32_t pages_per_split,
+                                        const int32_t* work, int32_t num_work,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Debug check of device-resident metadata: copies block_tables and
  * seq_lens to the host (synchronising `stream`) and checks that every
  * length lies in [0, max_seq_len], every used block-table entry lies in

@@ -121,6 +121,21 @@ int pa_append_decode_attention_rope_q8(const pa_shape* shape, int32_t batch, con
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * INT8-page decode step launched from a work list (pa_decode_worklist with
+ * page_format 1): as pa_append_decode_attention_worklist, with the pools of
+ * this header; k_new/v_new both NULL for decode only.
+ */
+int pa_append_decode_attention_worklist_q8(const pa_shape* shape, int32_t batch, const void* q,
+                                           const void* k_new, const void* v_new,
+                                           void* k_codes, void* v_codes, void* kv_scales,
+                                           const int32_t* block_tables, const int32_t* seq_lens,
+                                           int32_t max_seq_len, float scale,
+                                           void* out, int32_t out_dtype, int32_t pages_per_split,
+                                           const int32_t* work, int32_t num_work,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/*
  * Split size for INT8 pages from host sequence lengths: pa_decode_plan_lengths
  * with the planner's cost model set for 17 KiB pages.
  */

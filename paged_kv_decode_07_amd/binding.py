@@ -28,10 +28,11 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
            "pa_append_kv_rope", "pa_append_decode_attention_rope", "pa_fill_kv",
            "pa_validate_metadata", "pa_status_string", "pa_abi_version",
+           "pa_decode_worklist", "pa_append_decode_attention_worklist",
            # include/pa_decode_q8.h
            "pa_append_kv_q8", "pa_append_kv_rope_q8", "pa_fill_kv_q8", "pa_decode_attention_q8",
            "pa_append_decode_attention_q8", "pa_append_decode_attention_rope_q8",
-           "pa_decode_plan_lengths_q8",
+           "pa_decode_plan_lengths_q8", "pa_append_decode_attention_worklist_q8",
            # include/pa_measure.h
            "pa_stream_read",
            # include/pa_kvpool.h
@@ -103,6 +104,15 @@ def load_library(path: str | None = None):
         lib.pa_decode_plan_lengths_q8.argtypes = [SP, I32, P, I32, I32, ctypes.POINTER(I32),
                                                   ctypes.POINTER(I32)]
         lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
+        lib.pa_decode_worklist.argtypes = [SP, I32, P, I32, I32, I32, I32, P, I32,
+                                           ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                           ctypes.POINTER(I32)]
+        lib.pa_append_decode_attention_worklist.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
+                                                            ctypes.c_float, P, I32, I32, P, I32,
+                                                            P, SZ, P]
+        lib.pa_append_decode_attention_worklist_q8.argtypes = [SP, I32, P, P, P, P, P, P, P, P,
+                                                               I32, ctypes.c_float, P, I32, I32,
+                                                               P, I32, P, SZ, P]
         I64 = ctypes.c_int64
         PP = ctypes.POINTER(ctypes.c_void_p)
         lib.pa_kvpool_create.argtypes = [I32, I32, I32, I32, I32, PP]
@@ -134,7 +144,9 @@ def load_library(path: str | None = None):
                      "pa_kvpool_get_stats", "pa_append_kv_q8", "pa_append_kv_rope_q8",
                      "pa_fill_kv_q8", "pa_decode_attention_q8", "pa_append_decode_attention_q8",
                      "pa_append_decode_attention_rope_q8", "pa_decode_plan_lengths_q8",
-                     "pa_stream_read"):
+                     "pa_stream_read", "pa_decode_worklist",
+                     "pa_append_decode_attention_worklist",
+                     "pa_append_decode_attention_worklist_q8"):
             getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
@@ -571,6 +583,70 @@ def append_decode_attention_q8(q, k_new, v_new, k_codes, v_codes, kv_scales, blo
                       _rope(rope_cos, rope_sin), k_codes, v_codes, kv_scales, block_tables,
                       seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
                       stream)
+
+
+def decode_worklist(seq_lens_host, num_pages: int, max_blocks: int = 128,
+                    max_seq_len: int | None = None, pages_per_split: int = 0,
+                    int8: bool = False, num_cus: int = 0):
+    """Longest-first work list for host lengths: (work int32 [n][2], pages_per_split, splits)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    if max_seq_len is None:
+        max_seq_len = int(lens.max()) if lens.size else 0
+    shape = make_shape(num_pages, max_blocks)
+    cap = max(1, int(lens.size) * max(1, -(-max_seq_len // PAGE)))
+    work = np.zeros((cap, 2), dtype=np.int32)
+    count, ps, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = load_library().pa_decode_worklist(
+        ctypes.byref(shape), int(lens.size), lens.ctypes.data_as(ctypes.c_void_p),
+        int(max_seq_len), int(pages_per_split), 1 if int8 else 0, int(num_cus),
+        work.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(count), ctypes.byref(ps),
+        ctypes.byref(ns))
+    _check(rc, "pa_decode_worklist")
+    return work[:count.value].copy(), ps.value, ns.value
+
+
+def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                                     max_seq_len: int, work, pages_per_split: int,
+                                     scale: float = 0.125, out=None, out_dtype=torch.float32,
+                                     workspace=None, stream=None, kv_scales=None):
+    """Decode step over a device work list (``decode_worklist``); k_new/v_new may be None
+    (decode only).  With ``kv_scales`` the pools are INT8 code pools."""
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    _i32(work, "work")
+    if work.dim() != 2 or work.shape[1] != 2 or work.shape[0] < 1:
+        raise ValueError("work: int32 [n][2] device tensor with n >= 1")
+    q8 = kv_scales is not None
+    num_pages = _q8_pools(k_pool, v_pool, kv_scales) if q8 else int(k_pool.shape[0])
+    if not q8:
+        _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    max_blocks = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    shape = make_shape(num_pages, max_blocks)
+    nk = _ptr(k_new) if k_new is not None else None
+    nv = _ptr(v_new) if v_new is not None else None
+    pools = [_ptr(k_pool), _ptr(v_pool)] + ([_ptr(kv_scales)] if q8 else [])
+    fn = "pa_append_decode_attention_worklist_q8" if q8 else "pa_append_decode_attention_worklist"
+    rc = getattr(load_library(), fn)(
+        ctypes.byref(shape), B, _ptr(q), nk, nv, *pools, _ptr(block_tables), _ptr(seq_lens),
+        int(max_seq_len), float(scale), _ptr(out), code, int(pages_per_split), _ptr(work),
+        int(work.shape[0]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream))
+    _check(rc, fn)
+    return out
 
 
 def stream_read(buf, sink, groups: int = 0, stream=None) -> None:

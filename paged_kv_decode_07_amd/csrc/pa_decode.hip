@@ -195,7 +195,7 @@ int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pa
 // 8 .. 512 and split sizes 8 .. 128.  The largest size predicted within 3%
 // of the fastest is returned (the model's error is about that size).
 double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,
-                     const PlanModel& m) {
+                     const PlanModel& m, bool worklist) {
   const int max_pages = ceil_div(max_seq_len, pa::kPage);
   const int S = ceil_div(max_pages, ps);
   const double chip_rate = m.hbm_bytes_per_us / m.page_bytes;    // pages/us, whole chip
@@ -212,9 +212,12 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
     if (nsb > 1) partial_rows += nsb;
     for (int k = 0; k < S; ++k) {
       if (k < nsb) items.push_back({m.group_us, (double)((k + 1) * ps <= n ? ps : n - k * ps)});
-      else items.push_back({m.empty_us, 0.0});
+      else if (!worklist) items.push_back({m.empty_us, 0.0});
     }
   }
+  if (worklist)
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& x, const Item& y) { return x.pages > y.pages; });
   // Streaming progress is tracked in virtual pages V (every streaming
   // work-group advances by the same rate), so a work-group that starts
   // streaming r pages at V0 ends when V reaches V0 + r.
@@ -267,7 +270,8 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
 }
 
 int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int max_seq_len,
-                       int num_cus, const PlanModel& model, int* pages, int* splits) {
+                       int num_cus, const PlanModel& model, int* pages, int* splits,
+                       bool worklist) {
   int cu = num_cus;
   if (cu <= 0) {
     const int rc = current_cu_count(&cu);
@@ -277,10 +281,22 @@ int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int ma
   if (max_pages <= 0) { *pages = 1; *splits = 1; return PA_OK; }
   const int xcds = (cu % 8 == 0) ? 8 : 1;         // MI300-class parts: 8 XCDs
   std::vector<std::pair<int, double>> cands;
+  // A work list balances items of different sizes but needs many of them: at
+  // 128-page splits the Zipf batch of 512 measured 7% slower than at 32-64.
+  // Work-list plans stop at 64 pages unless the lengths are even (the
+  // shortest at least half the longest) and there is a sequence per CU.
+  int min_pages = max_pages;
+  for (int b = 0; b < batch; ++b) {
+    const int L = lens[b] < 0 ? 0 : (lens[b] > max_seq_len ? max_seq_len : lens[b]);
+    min_pages = std::min(min_pages, ceil_div(L, pa::kPage));
+  }
+  const bool long_splits = !worklist || (batch >= cu && 2 * min_pages >= max_pages);
   for (int ps : {8, 16, 32, 64, 128, 256}) {
+    if (!long_splits && ps > 64) break;
     const int cand = ps < max_pages ? ps : max_pages;
     if (cand > s->max_blocks_per_seq || cand > pa::kMaxSplitPages) break;
-    cands.push_back({cand, simulate_plan(lens, batch, max_seq_len, cand, cu, xcds, model)});
+    cands.push_back({cand, simulate_plan(lens, batch, max_seq_len, cand, cu, xcds, model,
+                                         worklist)});
     if (cand == max_pages) break;
   }
   if (cands.empty()) { *pages = 1; *splits = max_pages; return PA_OK; }
@@ -315,6 +331,27 @@ int check_rope(const pa_rope* rope, int64_t needed_positions) {
   if (!rope->cos || !rope->sin) return PA_ERR_NULL;
   if (!aligned(rope->cos, 4) || !aligned(rope->sin, 4)) return PA_ERR_ALIGN;
   if (rope->positions < 1 || rope->positions < needed_positions) return PA_ERR_VALUE;
+  return PA_OK;
+}
+
+int build_worklist(int batch, const int32_t* lens, int max_seq_len, int ps, int32_t* work,
+                   int capacity, int* count) {
+  struct Item { int pages, b, s; };
+  std::vector<Item> items;
+  for (int b = 0; b < batch; ++b) {
+    const int L = lens[b];
+    const int n = (L > 0 && L <= max_seq_len) ? ceil_div(L, pa::kPage) : 0;
+    const int nsb = n > 0 ? ceil_div(n, ps) : 1;
+    for (int k = 0; k < nsb; ++k) items.push_back({n > 0 ? std::min(ps, n - k * ps) : 0, b, k});
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return x.pages > y.pages; });
+  *count = (int)items.size();
+  if ((int)items.size() > capacity) return PA_ERR_VALUE;
+  for (size_t k = 0; k < items.size(); ++k) {
+    work[2 * k] = items[k].b;
+    work[2 * k + 1] = items[k].s;
+  }
   return PA_OK;
 }
 
@@ -424,7 +461,8 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
                 const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                 int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
                 int32_t pages_per_split, void* workspace, size_t workspace_bytes,
-                void* stream, void* event_before_main, void* event_after_main) {
+                void* stream, void* event_before_main, void* event_after_main,
+                const int32_t* work = nullptr, int32_t num_work = 0) {
   int rc = check_decode_sizes(shape, batch, max_seq_len);
   if (rc != PA_OK) return rc;
   if (out_dtype != PA_OUT_F32 && out_dtype != PA_OUT_BF16) return PA_ERR_VALUE;
@@ -443,6 +481,11 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
     if (rc != PA_OK) return rc;
   }
   if (shape->num_pages < 1 && max_seq_len > 0) return PA_ERR_VALUE;
+  if (work) {
+    // the list was built for one split size: it must be given, not planned
+    if (pages_per_split == 0 || num_work < 1) return PA_ERR_VALUE;
+    if (!aligned(work, 4)) return PA_ERR_ALIGN;
+  }
   int ps = 0, ns = 0;
   rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
   if (rc != PA_OK) return rc;
@@ -476,6 +519,9 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.max_seq_len = max_seq_len;
   a.pages_per_split = ps;
   a.num_splits = ns;
+  a.work = work;
+  a.num_work = num_work;
+  a.batch = batch;
   const hipError_t e = pa::launch_decode<false>(a, batch, out_dtype == PA_OUT_BF16, fused,
                                                 rope != nullptr, (hipStream_t)stream,
                                                 (hipEvent_t)event_before_main,
@@ -559,6 +605,45 @@ PA_API int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch, co
   return decode_impl(shape, batch, q, k_new, v_new, nullptr, k_pool, v_pool, block_tables,
                      seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
                      workspace_bytes, stream, event_before_main, event_after_main);
+}
+
+PA_API int pa_decode_worklist(const pa_shape* shape, int32_t batch, const int32_t* seq_lens_host,
+                              int32_t max_seq_len, int32_t pages_per_split, int32_t page_format,
+                              int32_t num_cus, int32_t* work, int32_t capacity, int32_t* count,
+                              int32_t* pages_out, int32_t* splits_out) {
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  if (!count || (batch > 0 && (!seq_lens_host || !work))) return PA_ERR_NULL;
+  if (capacity < 0 || num_cus < 0 || (page_format != 0 && page_format != 1)) return PA_ERR_VALUE;
+  int ps = pages_per_split, ns = 1;
+  if (batch > 0 && ps == 0) {
+    const PlanModel model = page_format == 1 ? plan_model_q8() : PlanModel();
+    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, model, &ps, &ns,
+                            true);
+    if (rc != PA_OK) return rc;
+  }
+  rc = plan_split(shape, batch, max_seq_len, ps == 0 ? 1 : ps, &ps, &ns);
+  if (rc != PA_OK) return rc;
+  *count = 0;
+  if (batch > 0) {
+    rc = build_worklist(batch, seq_lens_host, max_seq_len, ps, work, capacity, count);
+    if (rc != PA_OK) return rc;
+  }
+  if (pages_out) *pages_out = ps;
+  if (splits_out) *splits_out = ns;
+  return PA_OK;
+}
+
+PA_API int pa_append_decode_attention_worklist(
+    const pa_shape* shape, int32_t batch, const void* q, const void* k_new, const void* v_new,
+    void* k_pool, void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+    int32_t max_seq_len, float scale, void* out, int32_t out_dtype, int32_t pages_per_split,
+    const int32_t* work, int32_t num_work, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (batch > 0 && !work) return PA_ERR_NULL;
+  return decode_impl(shape, batch, q, k_new, v_new, nullptr, k_pool, v_pool, block_tables,
+                     seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
+                     workspace_bytes, stream, nullptr, nullptr, work, num_work);
 }
 
 PA_API int pa_validate_metadata(const pa_shape* shape, int32_t batch,

@@ -90,6 +90,11 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t pages_per_split;
   int32_t num_splits;
+  // optional work list: work item k (block k of a 1-D grid) is sequence
+  // work[2k], split work[2k+1]; NULL: block (x, y) is split x of sequence y
+  const int32_t* work;
+  int32_t num_work;
+  int32_t batch;
 };
 
 // Page-format constants of the LDS ring (per wavefront slot).
@@ -284,8 +289,13 @@ template <bool Q8, bool OUT_BF16, bool APPEND, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   using F = PageFormat<Q8>;
-  const int s = blockIdx.x;
-  const int b = blockIdx.y;
+  int s = blockIdx.x, b = blockIdx.y;
+  if (a.work) {
+    // entries outside the batch or the plan are skipped, never followed
+    b = a.work[2 * blockIdx.x];
+    s = a.work[2 * blockIdx.x + 1];
+    if ((unsigned)b >= (unsigned)a.batch || (unsigned)s >= (unsigned)a.num_splits) return;
+  }
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4;
@@ -581,7 +591,8 @@ template <bool Q8>
 inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
                                 bool rope, hipStream_t st, hipEvent_t event_before,
                                 hipEvent_t event_after) {
-  const dim3 grid(a.num_splits, batch), block(kThreads);
+  const dim3 grid = a.work ? dim3(a.num_work) : dim3(a.num_splits, batch);
+  const dim3 block(kThreads);
   hipError_t e = hipSuccess;
   if (event_before && (e = hipEventRecord(event_before, st)) != hipSuccess) return e;
   if (out_bf16) {

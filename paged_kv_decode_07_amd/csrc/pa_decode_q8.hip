@@ -108,14 +108,14 @@ __global__ __launch_bounds__(256) void fill_q8_kernel(const uint16_t* __restrict
 
 using namespace pa_host;
 
-namespace {
+namespace pa_host {
 
 // Planner cost model for INT8 pages: 17 KiB per page (8 KiB of K codes,
 // 8 KiB of V codes, 1 KiB of scales).  The per-page time of one CU alone, the
 // fixed cost per work-group and per empty grid slot were fitted to this
 // kernel's measured times on MI355X over batches of 8 to 512 sequences
 // (uniform and Zipf lengths) and split sizes 8 .. 128 pages.
-PlanModel q8_model() {
+PlanModel plan_model_q8() {
   PlanModel m;
   m.page_bytes = 2.0 * pa::kPageCodes + pa::kScalePageFloats * 4.0;
   m.page_us = 0.8;
@@ -123,6 +123,10 @@ PlanModel q8_model() {
   m.empty_us = 1.0;
   return m;
 }
+
+}  // namespace pa_host
+
+namespace {
 
 int check_pools_q8(const void* k_codes, const void* v_codes, const void* kv_scales) {
   if (!k_codes || !v_codes || !kv_scales) return PA_ERR_NULL;
@@ -172,7 +176,8 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
                    const void* v_codes, const void* kv_scales, const int32_t* block_tables,
                    const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out,
                    int32_t out_dtype, int32_t pages_per_split, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, void* stream, const int32_t* work = nullptr,
+                   int32_t num_work = 0) {
   int rc = check_decode_sizes(shape, batch, max_seq_len);
   if (rc != PA_OK) return rc;
   if (out_dtype != PA_OUT_F32 && out_dtype != PA_OUT_BF16) return PA_ERR_VALUE;
@@ -192,6 +197,11 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
     if (rc != PA_OK) return rc;
   }
   if (shape->num_pages < 1 && max_seq_len > 0) return PA_ERR_VALUE;
+  if (work) {
+    // the list was built for one split size: it must be given, not planned
+    if (pages_per_split == 0 || num_work < 1) return PA_ERR_VALUE;
+    if (!aligned(work, 4)) return PA_ERR_ALIGN;
+  }
   int ps = 0, ns = 0;
   rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
   if (rc != PA_OK) return rc;
@@ -227,6 +237,9 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
   a.max_seq_len = max_seq_len;
   a.pages_per_split = ps;
   a.num_splits = ns;
+  a.work = work;
+  a.num_work = num_work;
+  a.batch = batch;
   const hipError_t e = pa::launch_decode<true>(a, batch, out_dtype == PA_OUT_BF16, fused,
                                                rope != nullptr, (hipStream_t)stream, nullptr,
                                                nullptr);
@@ -312,6 +325,18 @@ PA_API int pa_append_decode_attention_rope_q8(const pa_shape* shape, int32_t bat
                         pages_per_split, workspace, workspace_bytes, stream);
 }
 
+PA_API int pa_append_decode_attention_worklist_q8(
+    const pa_shape* shape, int32_t batch, const void* q, const void* k_new, const void* v_new,
+    void* k_codes, void* v_codes, void* kv_scales, const int32_t* block_tables,
+    const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
+    int32_t pages_per_split, const int32_t* work, int32_t num_work, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (batch > 0 && !work) return PA_ERR_NULL;
+  return decode_q8_impl(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
+                        block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
+                        pages_per_split, workspace, workspace_bytes, stream, work, num_work);
+}
+
 PA_API int pa_decode_plan_lengths_q8(const pa_shape* shape, int32_t batch,
                                      const int32_t* seq_lens_host, int32_t max_seq_len,
                                      int32_t num_cus, int32_t* pages_out, int32_t* splits_out) {
@@ -321,7 +346,7 @@ PA_API int pa_decode_plan_lengths_q8(const pa_shape* shape, int32_t batch,
   if (num_cus < 0) return PA_ERR_VALUE;
   int ps = 1, ns = 1;
   if (batch > 0) {
-    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, q8_model(), &ps,
+    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, plan_model_q8(), &ps,
                             &ns);
     if (rc != PA_OK) return rc;
   }

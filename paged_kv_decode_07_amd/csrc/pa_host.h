@@ -33,11 +33,23 @@ struct PlanModel {
   double hbm_bytes_per_us = 6.1e6;
   double page_bytes = 2.0 * 16 * 8 * 64 * 2;   // one K page and one V page, BF16
 };
+// worklist: the work-groups run in pa_decode_worklist's order (largest
+// first, no empty slots) instead of the grid order.
 double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,
-                     const PlanModel& m);
+                     const PlanModel& m, bool worklist = false);
 int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int max_seq_len,
-                       int num_cus, const PlanModel& model, int* pages, int* splits);
+                       int num_cus, const PlanModel& model, int* pages, int* splits,
+                       bool worklist = false);
+// The cost model fitted to the INT8-page kernel (defined with the INT8 entry points).
+PlanModel plan_model_q8();
 // Bytes of split partials for `splits` splits per sequence (0 for one split).
 size_t workspace_for(int batch, int splits);
+
+// Work list for host lengths and a split size: one item (b, s) per split that
+// holds pages, plus split 0 of every sequence without pages (its output row
+// is still written), ordered by page count, largest first (ties: b, then s).
+// work: host int32 [2 * capacity]; *count receives the number of items.
+int build_worklist(int batch, const int32_t* lens, int max_seq_len, int ps, int32_t* work,
+                   int capacity, int* count);
 
 }  // namespace pa_host

@@ -241,3 +241,63 @@ def test_stream_read_argument_errors(lib):
     assert lib.pa_stream_read(F, 0, sink, 0, None) == -6
     assert lib.pa_stream_read(F, 1024, sink, -1, None) == -6
     assert lib.pa_stream_read(F, 1024, sink, 65537, None) == -6
+
+
+def test_worklist_covers_every_item_once_largest_first():
+    import numpy as np
+    lens = np.array([0, 1, 2048, 17, 300, 2049, 16, 33, 1000], np.int32)    # 2049: beyond the bound
+    for ps in (1, 3, 8, 128):
+        work, ps_out, ns = pa.decode_worklist(lens, 40000, max_seq_len=2048, pages_per_split=ps)
+        assert ps_out == ps and ns == -(-128 // ps)
+        pages = lambda b: -(-int(lens[b]) // 16) if 0 < lens[b] <= 2048 else 0
+        want = set()
+        for b in range(len(lens)):
+            n = pages(b)
+            want |= {(b, k) for k in range(max(1, -(-n // ps)))}
+        got = [tuple(x) for x in work.tolist()]
+        assert len(got) == len(set(got)) and set(got) == want
+        size = [min(ps, pages(b) - s * ps) if pages(b) else 0 for b, s in got]
+        assert size == sorted(size, reverse=True)
+        # ties keep the (sequence, split) order
+        for (b0, s0), (b1, s1), z0, z1 in zip(got, got[1:], size, size[1:]):
+            if z0 == z1:
+                assert (b0, s0) < (b1, s1)
+
+
+def test_worklist_capacity_and_arguments(lib):
+    import numpy as np
+    lens = (ctypes.c_int32 * 3)(100, 200, 300)
+    s = pa.make_shape(64, 128)
+    work = (ctypes.c_int32 * 4)()
+    count, ps, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    # 3 sequences x 19 pages at 1 page per split need more than 2 items
+    assert lib.pa_decode_worklist(ctypes.byref(s), 3, lens, 300, 1, 0, 0, work, 2,
+                                  ctypes.byref(count), ctypes.byref(ps), ctypes.byref(ns)) == -6
+    assert count.value == 7 + 13 + 19
+    assert lib.pa_decode_worklist(ctypes.byref(s), 3, lens, 300, 1, 2, 0, work, 2,
+                                  ctypes.byref(count), None, None) == -6         # bad format
+    assert lib.pa_decode_worklist(ctypes.byref(s), 3, None, 300, 1, 0, 0, work, 2,
+                                  ctypes.byref(count), None, None) == -1
+    F = FAKE
+    # a work list needs an explicit split size and at least one item
+    assert lib.pa_append_decode_attention_worklist(
+        ctypes.byref(s), 1, F, F, F, F, F, F, F, 37, 0.125, F, 0, 0, F, 4, F, 1 << 30, None) == -6
+    assert lib.pa_append_decode_attention_worklist(
+        ctypes.byref(s), 1, F, F, F, F, F, F, F, 37, 0.125, F, 0, 2, F, 0, F, 1 << 30, None) == -6
+    assert lib.pa_append_decode_attention_worklist(
+        ctypes.byref(s), 1, F, F, F, F, F, F, F, 37, 0.125, F, 0, 2, None, 4, F, 1 << 30, None) == -1
+    assert lib.pa_append_decode_attention_worklist_q8(
+        ctypes.byref(s), 1, F, F, F, F, F, F, F, F, 37, 0.125, F, 0, 0, F, 4, F, 1 << 30, None) == -6
+
+
+def test_worklist_planner_choices():
+    """Split sizes planned for work-list launches on a 256-CU part (measured fastest on MI355X
+    among 8..128 for workloads 2, 3 and 5, BF16 and INT8 pages alike: 8, 16, 32-64; the even
+    batch 4 keeps one 128-page split per sequence)."""
+    import workloads as W
+    expect = {2: 8, 3: 16, 4: 128, 5: 64}
+    for i, ps_best in expect.items():
+        lens = W.workload_seq_lens(i)
+        for int8 in (False, True):
+            work, ps, ns = pa.decode_worklist(lens, 40000, num_cus=256, int8=int8)
+            assert ps == ps_best, (i, int8, ps)
