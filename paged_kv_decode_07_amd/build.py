@@ -63,6 +63,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "decode_client.cpp")
+CLIENT = os.path.join(OUT_DIR, "decode_client")
+
+
+def build_client(verbose: bool = False) -> str:
+    """Build the C-ABI client used by the tests (a host program linked to the library)."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17",
+           "-I", os.path.join(ROOT, "include"), CLIENT_SRC, "-o", CLIENT + ".tmp",
+           "-L", OUT_DIR, "-lpa_decode", "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on the C client:\n" + res.stderr)
+    os.replace(CLIENT + ".tmp", CLIENT)
+    return CLIENT
+
+
 def undefined_kernel_stubs(lib_path: str) -> list:
     """Host launch stubs referenced by the library but not defined in it."""
     nm = next((c for c in ("/opt/rocm/llvm/bin/llvm-nm", shutil.which("nm")) if c and os.path.exists(c)),
@@ -75,3 +93,4 @@ def undefined_kernel_stubs(lib_path: str) -> list:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_client(verbose="-v" in sys.argv))

@@ -301,3 +301,13 @@ def test_worklist_planner_choices():
         for int8 in (False, True):
             work, ps, ns = pa.decode_worklist(lens, 40000, num_cus=256, int8=int8)
             assert ps == ps_best, (i, int8, ps)
+
+
+def test_c_client_is_built_and_rejects_bad_input(tmp_path):
+    """The C-ABI client links against the library; malformed input exits 2 before any HIP call."""
+    import subprocess
+    client = pb.CLIENT
+    if not os.path.exists(client):
+        pb.build_client()
+    assert subprocess.run([client], capture_output=True).returncode == 2
+    assert subprocess.run([client, str(tmp_path)], capture_output=True).returncode == 2
