@@ -427,7 +427,7 @@ def main() -> int:
         "allocator_us_per_decode_step": round(alloc_step_us, 1),
         "two_call_kv_gbps": round(kv / float(t_two.mean()) / 1e9, 2),
         "achievable_read": {
-            "kernel": "pa_stream_read over a 1 GiB buffer (median of the timed reads)",
+            "kernel": "pa_stream_read (non-temporal 16-byte loads) over a 1 GiB buffer (median of the timed reads)",
             "gbps": round(read_gbps, 1),
             "frac_of_peak": round(read_gbps / HBM_PEAK_GBPS, 4),
             "step_value_frac_of_achievable": round(value / read_gbps, 4),

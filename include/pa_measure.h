@@ -20,7 +20,8 @@ extern "C" {
 
 /*
  * Streaming read: every 16-byte word of buf[0 .. bytes) is read once (each
- * work-group takes 16 KiB chunks, 16 bytes per lane per load, and strides
+ * work-group takes 16 KiB chunks, 16 bytes per lane per load with the
+ * non-temporal cache policy, and strides
  * over the buffer) and folded into one 32-bit word per work-group, written
  * to sink[work-group] so the reads cannot be elided.  buf: device, 16-byte
  * aligned, bytes a positive multiple of 16.  sink: device, at least `groups`

@@ -12,20 +12,23 @@ namespace {
 
 // Each work-group reads 16 KiB chunks (256 lanes x 4 loads of 16 bytes, the
 // 4 loads of a lane 4 KiB apart, all issued before any use) and strides over
-// the chunks of the buffer; one folded word per work-group.
+// the chunks of the buffer; one folded word per work-group.  The loads carry
+// the non-temporal policy, the fastest plain streaming read measured on this
+// part (about 10% above the default policy).
 constexpr int kUnroll = 4;
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, size_t n,
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4v* __restrict__ buf, size_t n,
                                                           uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
   const size_t chunk = 256 * kUnroll;                       // words per chunk
   const size_t stride = (size_t)gridDim.x * chunk;
   for (size_t base = (size_t)blockIdx.x * chunk + threadIdx.x; base < n; base += stride) {
-    uint4 v[kUnroll];
+    u32x4v v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const size_t i = base + (size_t)u * 256;
-      v[u] = i < n ? buf[i] : make_uint4(0u, 0u, 0u, 0u);
+      v[u] = i < n ? __builtin_nontemporal_load(buf + i) : u32x4v{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -55,6 +58,6 @@ PA_API int pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t
     if (groups > 65536) groups = 65536;
   }
   hipLaunchKernelGGL(stream_read_kernel, dim3(groups), dim3(256), 0, (hipStream_t)stream,
-                     (const uint4*)buf, bytes / 16, sink);
+                     (const u32x4v*)buf, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
