@@ -15,9 +15,9 @@
 // slots, so explicit vmcnt waits are the only synchronisation.  The split's
 // block-table entries are preloaded into VGPRs and picked with v_readlane.
 // Every load instruction requests whole 128-byte lines (BF16: 8 token rows
-// of the head; INT8: the head's 1 KiB code block), and BF16 pages are read
-// with the non-temporal policy: on this part that pair streams about 12%
-// faster than half-line requests or the default policy.
+// of the head; INT8: the head's 1 KiB code block), with the non-temporal
+// policy: on this part that pair streams 10-12% faster than half-line
+// requests or the default policy.
 //
 // Arithmetic (the FP32 online softmax of the samir-vllm README's paged
 // decode attention, on the matrix cores):
@@ -251,19 +251,16 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
   }
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
   // A operand: rows 0..3 the BF16 weights, rows 4..7 their remainders
-  const uint32_t h01 = f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16);
-  const uint32_t h23 = f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16);
+  // (weight - its BF16 value is exact in FP32, then rounded again), rows
+  // 8..15 zero.  Every lane computes both and selects, so the wave does not
+  // diverge.
+  const uint32_t h01 = pack_bf16_rne(w[0], w[1]);
+  const uint32_t h23 = pack_bf16_rne(w[2], w[3]);
+  const uint32_t r01 = pack_bf16_rne(w[0] - bf16_lo(h01), w[1] - bf16_hi(h01));
+  const uint32_t r23 = pack_bf16_rne(w[2] - bf16_lo(h23), w[3] - bf16_hi(h23));
   u32x2 pa;
-  if (n < 4) {
-    pa = u32x2{h01, h23};
-  } else if (n < 8) {
-    const float r0 = w[0] - __uint_as_float(h01 << 16), r1 = w[1] - __uint_as_float(h01 & 0xffff0000u);
-    const float r2 = w[2] - __uint_as_float(h23 << 16), r3 = w[3] - __uint_as_float(h23 & 0xffff0000u);
-    pa = u32x2{f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16),
-               f32_to_bf16_rne(r2) | (f32_to_bf16_rne(r3) << 16)};
-  } else {
-    pa = u32x2{0u, 0u};
-  }
+  pa.x = n < 4 ? h01 : (n < 8 ? r01 : 0u);
+  pa.y = n < 4 ? h23 : (n < 8 ? r23 : 0u);
   const bf16x4_t A = __builtin_bit_cast(bf16x4_t, pa);
   if constexpr (Q8) {
 #pragma unroll
@@ -299,21 +296,17 @@ __device__ __forceinline__ int out_dim(int b, int n) {
   return 16 * b + n;
 }
 
-// Cache-policy bits of the page-stream loads (every page is read once):
-// BF16 pages stream non-temporally (whole lines per instruction), INT8 pages
-// with the default policy.
+// Cache-policy bits of the page-stream loads: every page is read once, so
+// both page formats stream with the non-temporal policy (nt = 2).
 #ifndef PA_STREAM_CPOL
 #define PA_STREAM_CPOL 2
 #endif
-#ifndef PA_STREAM_CPOL_Q8
-#define PA_STREAM_CPOL_Q8 0
-#endif
+constexpr int kStreamCpol = PA_STREAM_CPOL;
 
 template <bool Q8, bool OUT_BF16, bool APPEND, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   using F = PageFormat<Q8>;
-  constexpr int kStreamCpol = Q8 ? PA_STREAM_CPOL_Q8 : PA_STREAM_CPOL;
   int s = blockIdx.x, b = blockIdx.y;
   if (a.work) {
     // entries outside the batch or the plan are skipped, never followed

@@ -34,6 +34,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Two FP32 values -> a packed BF16 pair (a in the low half), rounded to
+// nearest even by gfx950's v_cvt_pk_bf16_f32: one instruction, no branch.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Round-to-nearest-even FP32 -> BF16 bits (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
