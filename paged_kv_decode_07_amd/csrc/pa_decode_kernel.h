@@ -319,6 +319,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const int G = lane >> 4;
   const int n = lane & 15;
 
+  // Everything that does not depend on the sequence's length is requested
+  // together with it: the query rows and the block-table entries of this
+  // split's window of the row.  The first pages can then be requested one
+  // memory round trip after the start instead of two.
+  const int p0 = s * a.pages_per_split;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  const int win = min(a.pages_per_split, a.max_blocks - p0);   // entries of the row in the window
+  int ent[kMaxSplitPages / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
+    const int j = c * 64 + lane;
+    ent[c] = (c * 64 < win && j < win) ? bt[p0 + j] : 0;
+  }
+  uint4 q_lo, q_hi;
+  {
+    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (n & 3)) * kD + 8 * G;
+    q_lo = *reinterpret_cast<const uint4*>(qr);
+    q_hi = *reinterpret_cast<const uint4*>(qr + 32);
+  }
   const int L = a.seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
   const bool bad_len = L < 0 || L > a.max_seq_len || n_pages > a.max_blocks ||
@@ -335,19 +354,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     return;
   }
 
-  const int p0 = s * a.pages_per_split;
   const int p1 = min(p0 + a.pages_per_split, n_pages);
   const int last = p1 - 1;
   const int tail_valid = L - last * kPage;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
 
   // B operand of the score product: column n = query head 4g + n%4, this
   // lane's 8 dims {8G..} (qlo) and {32+8G..} (qhi)
   bf16x8_t qlo, qhi;
   {
-    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (n & 3)) * kD + 8 * G;
-    uint4 lo = *reinterpret_cast<const uint4*>(qr);
-    uint4 hi = *reinterpret_cast<const uint4*>(qr + 32);
+    uint4 lo = q_lo, hi = q_hi;
     if (ROPE) {
       const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * G;
       rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
@@ -392,12 +407,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   st.m = -INFINITY;
   st.l = 0.f;
 
-  int ent[kMaxSplitPages / 64];
-#pragma unroll
-  for (int c = 0; c < kMaxSplitPages / 64; ++c) {
-    const int j = p0 + c * 64 + lane;
-    ent[c] = (c * 64 < p1 - p0 && j <= last) ? bt[j] : 0;
-  }
+  // ent[] (loaded above) holds the window's entries; only those up to
+  // `last` are ever picked
   bool bad_page = false;
   auto raw_page_id = [&](int i) -> int {
     const int j = i - p0;
