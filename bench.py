@@ -165,6 +165,92 @@ def cpu_baseline(gpu_out, seconds: float, pool=None, pool_workers: int = 0):
     return res
 
 
+def run_sweep(args) -> int:
+    """Every workload's fused append + attention step (one layer; workload 3 is its
+    first layer), cold caches, medians of ``--steps`` event-timed steps."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_decode_07_amd import accounting as A
+    from paged_kv_decode_07_amd import binding as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(2**28, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int32, device=dev)
+    workspace = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+
+    def up16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    def timed(fn, n):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(n):
+            if not args.no_flush:
+                torch.amax(flush_buf, dim=None, out=flush_out)
+            evs[i][0].record(stream)
+            fn()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+
+    for wi in (1, 2, 3, 4, 5):
+        t0 = time.perf_counter()
+        w = W.make_workload(wi, append=True)
+        log(f"workload {wi}: {w.batch} sequences, {w.num_pages} pages "
+            f"(generated in {time.perf_counter() - t0:.1f} s)")
+        q, kp, vp = up16(w.q), up16(w.k_pool), up16(w.v_pool)
+        kn, vn = up16(w.k_new), up16(w.v_new)
+        bt = torch.from_numpy(w.block_tables).to(dev)
+        lens = torch.from_numpy(w.seq_lens).to(dev)
+        out = torch.empty((w.batch, 32, 64), dtype=torch.float32, device=dev)
+        npg, msl = w.num_pages, w.max_seq_len
+        kc, vc, sc = pa.new_q8_pools(npg, device=dev)
+        pa.fill_kv_q8(kp.view(npg * 16, 8, 64), vp.view(npg * 16, 8, 64),
+                      torch.arange(npg, dtype=torch.int32, device=dev), 0, kc, vc, sc,
+                      stream=stream)
+        for q8 in (False, True):
+            acct = A.step_bytes_q8 if q8 else A.step_bytes
+            kv = acct(w.seq_lens, append=True)["kv"]
+            ps, ns = (pa.decode_plan_lengths_q8 if q8 else pa.decode_plan_lengths)(
+                w.seq_lens, npg, max_seq_len=msl)
+            cases = []
+            if q8:
+                cases.append(("grid (lengths plan)", ps, ns, lambda ps=ps: pa.append_decode_attention_q8(
+                    q, kn, vn, kc, vc, sc, bt, lens, msl, scale=w.scale, out=out,
+                    pages_per_split=ps, workspace=workspace, stream=stream)))
+            else:
+                cases.append(("grid (lengths plan)", ps, ns, lambda ps=ps: pa.append_decode_attention(
+                    q, kn, vn, kp, vp, bt, lens, msl, scale=w.scale, out=out,
+                    pages_per_split=ps, workspace=workspace, stream=stream)))
+            if w.batch > 1:
+                wl, wps, _ = pa.decode_worklist(w.seq_lens, npg, max_seq_len=msl, int8=q8)
+                wd = torch.from_numpy(wl).to(dev)
+                cases.append(("work list", wps, len(wl), lambda wd=wd, wps=wps:
+                              pa.append_decode_attention_worklist(
+                                  q, kn, vn, kc if q8 else kp, vc if q8 else vp, bt, lens, msl,
+                                  wd, wps, scale=w.scale, out=out, workspace=workspace,
+                                  stream=stream, kv_scales=sc if q8 else None)))
+            for launch, cps, units, fn in cases:
+                t = timed(fn, args.steps)
+                print(json.dumps({
+                    "workload": wi, "desc": W.WORKLOADS[wi], "pages": "int8" if q8 else "bf16",
+                    "launch": launch, "pages_per_split": int(cps),
+                    ("items" if launch == "work list" else "splits"): int(units),
+                    "step_us": round(t * 1e6, 2), "kv_bytes": int(kv),
+                    "kv_gbps": round(kv / t / 1e9, 1),
+                    "seq_per_s_per_layer": round(int(np.count_nonzero(w.seq_lens)) / t, 1)}),
+                    flush=True)
+        del q, kp, vp, kn, vn, bt, lens, out, kc, vc, sc
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +266,10 @@ def main() -> int:
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 256 MiB device copy per step (outside the timed events), "
                          "the known-size reference for hardware byte counters")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: time the fused step of every workload "
+                         "(1-5), BF16 and INT8 pages, grid launch with the library plan and "
+                         "work-list launch; one JSON line per case")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,6 +285,8 @@ def main() -> int:
     from paged_kv_decode_07_amd import accounting as A
     from paged_kv_decode_07_amd import binding as pa
 
+    if args.sweep:
+        return run_sweep(args)
 
     t0 = time.perf_counter()
     batch = W.make_workload(4, placement=args.placement, append=True)
