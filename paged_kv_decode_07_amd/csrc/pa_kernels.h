@@ -148,26 +148,60 @@ struct MergeArgs {
 
 // Log-sum-exp merge of the splits of each multi-split sequence, in split
 // order.  One work-group of 256 threads per sequence: thread = (head, 8 dims).
-// Splits are read 8 at a time with all loads issued before any use, so the
-// loop costs one memory latency per 8 splits rather than one per split.
+// Splits are read 8 at a time with all loads issued before any use.  The
+// first 8 splits' partials (rows that exist in the workspace whatever the
+// sequence's length) are requested together with the length, so a sequence
+// of up to 8 splits costs one memory latency.
 constexpr int kMergeBatch = 8;
+
+struct MergeBatch {
+  float m[kMergeBatch], l[kMergeBatch];
+  float4 x0[kMergeBatch], x1[kMergeBatch];
+};
+
+// Partials of splits s0 .. s0+7 (those below `avail`; the others read split 0).
+__device__ __forceinline__ void merge_load(MergeBatch& t, const MergeArgs& a, int64_t row0,
+                                           int d0, int s0, int avail) {
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const int64_t row = row0 + (int64_t)(s0 + k < avail ? s0 + k : 0) * kHq;
+    const float4* src = reinterpret_cast<const float4*>(a.part_acc + row * kD + d0);
+    t.m[k] = a.part_ml[row * 2];
+    t.l[k] = a.part_ml[row * 2 + 1];
+    t.x0[k] = src[0];
+    t.x1[k] = src[1];
+  }
+}
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int b = blockIdx.x;
+  const int h = threadIdx.x >> 3;
+  const int d0 = (threadIdx.x & 7) * 8;
+  const int64_t row0 = (int64_t)b * a.num_splits * kHq + h;   // split s at row0 + s*kHq
+  MergeBatch first;
+  merge_load(first, a, row0, d0, 0, a.num_splits);
   const int L = a.seq_lens[b];
+  // keep the partial loads ahead of the length test: without this the
+  // compiler moves them after the early exits, one memory latency later
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    asm volatile("" ::"v"(first.m[k]), "v"(first.l[k]),
+                 "v"(__builtin_bit_cast(f32x4_t, first.x0[k])),
+                 "v"(__builtin_bit_cast(f32x4_t, first.x1[k]))
+                 : "memory");
   const int n_pages = (L + kPage - 1) / kPage;
   if (L <= 0 || L > a.max_seq_len || n_pages > a.max_blocks ||
       n_pages > a.pages_per_split * a.num_splits)
     return;
   const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
   if (ns <= 1) return;
-  const int h = threadIdx.x >> 3;
-  const int d0 = (threadIdx.x & 7) * 8;
-  const int64_t row0 = (int64_t)b * a.num_splits * kHq + h;   // split s at row0 + s*kHq
   // pass 1: the largest running maximum over the splits
   float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    if (k < ns) M = fmaxf(M, first.m[k]);
+  for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
     float m[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k)
@@ -178,27 +212,21 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   // pass 2: weights 2^(m_s - M), sums in split order
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
-    float m[kMergeBatch], l[kMergeBatch];
-    float4 x0[kMergeBatch], x1[kMergeBatch];
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const bool in = s0 + k < ns;
-      const int64_t row = row0 + (int64_t)(in ? s0 + k : 0) * kHq;
-      const float4* src = reinterpret_cast<const float4*>(a.part_acc + row * kD + d0);
-      m[k] = in ? a.part_ml[row * 2] : -INFINITY;
-      l[k] = a.part_ml[row * 2 + 1];
-      x0[k] = src[0];
-      x1[k] = src[1];
-    }
+  auto accumulate = [&](const MergeBatch& t, int s0) {
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       if (s0 + k >= ns) break;
-      const float w = __builtin_amdgcn_exp2f(m[k] - M);
-      den += w * l[k];
-      num[0] += w * x0[k].x; num[1] += w * x0[k].y; num[2] += w * x0[k].z; num[3] += w * x0[k].w;
-      num[4] += w * x1[k].x; num[5] += w * x1[k].y; num[6] += w * x1[k].z; num[7] += w * x1[k].w;
+      const float w = __builtin_amdgcn_exp2f(t.m[k] - M);
+      den += w * t.l[k];
+      num[0] += w * t.x0[k].x; num[1] += w * t.x0[k].y; num[2] += w * t.x0[k].z; num[3] += w * t.x0[k].w;
+      num[4] += w * t.x1[k].x; num[5] += w * t.x1[k].y; num[6] += w * t.x1[k].z; num[7] += w * t.x1[k].w;
     }
+  };
+  accumulate(first, 0);
+  for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
+    MergeBatch t;
+    merge_load(t, a, row0, d0, s0, ns);
+    accumulate(t, s0);
   }
   const float inv = 1.f / den;
   const int64_t orow = (int64_t)b * kHq + h;
