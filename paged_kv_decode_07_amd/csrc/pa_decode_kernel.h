@@ -338,6 +338,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     q_lo = *reinterpret_cast<const uint4*>(qr);
     q_hi = *reinterpret_cast<const uint4*>(qr + 32);
   }
+  // fused append: lanes 0..3 hold the new K row of head g (lane c: dims
+  // {8c..} and {32+8c..}), lanes 4..7 the V row; every split loads them, the
+  // one holding the sequence's last page uses them
+  // (every lane loads, lane l the row part of lane l % 8: a load under a
+  // lane mask would make the compiler wait for it at the end of the mask)
+  uint4 new_lo{}, new_hi{};
+  if constexpr (APPEND) {
+    const uint16_t* src = ((lane & 7) < 4 ? a.k_new : a.v_new) + ((int64_t)b * kHkv + g) * kD +
+                          8 * (lane & 3);
+    new_lo = *reinterpret_cast<const uint4*>(src);
+    new_hi = *reinterpret_cast<const uint4*>(src + 32);
+  }
   const int L = a.seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
   const bool bad_len = L < 0 || L > a.max_seq_len || n_pages > a.max_blocks ||
@@ -358,48 +370,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const int last = p1 - 1;
   const int tail_valid = L - last * kPage;
 
-  // B operand of the score product: column n = query head 4g + n%4, this
-  // lane's 8 dims {8G..} (qlo) and {32+8G..} (qhi)
-  bf16x8_t qlo, qhi;
-  {
-    uint4 lo = q_lo, hi = q_hi;
-    if (ROPE) {
-      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * G;
-      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
-    }
-    qlo = __builtin_bit_cast(bf16x8_t, lo);
-    qhi = __builtin_bit_cast(bf16x8_t, hi);
-  }
 
-  // fused append: lanes 0..3 build the new K row of head g (lane c: dims
-  // {8c..} and {32+8c..}, rotated first with RoPE), lanes 4..7 the V row;
-  // BF16 pages park the rows, INT8 pages their codes and scales, in LDS
+  // B operand of the score product (set after the first page requests)
+  bf16x8_t qlo, qhi;
+
+  // fused append: the new rows (K rotated first with RoPE) are parked in LDS,
+  // as BF16 rows or as INT8 codes and scales, after the first page requests
   const bool app_here = APPEND && p1 == n_pages;
   const int app_slot = (L - 1) % kPage;
   __shared__ u32x4 new_rows[APPEND ? kWaves : 1][Q8 ? 8 : 16];   // 16-byte chunks
   __shared__ float new_scales[APPEND && Q8 ? kWaves : 1][2];
-  if (app_here && lane < 8) {
-    const int c = lane & 3;
-    const bool is_k = lane < 4;
-    const uint16_t* src = (is_k ? a.k_new : a.v_new) + ((int64_t)b * kHkv + g) * kD + 8 * c;
-    uint4 lo = *reinterpret_cast<const uint4*>(src);
-    uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
-    if (ROPE && is_k) {
-      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * c;
-      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
-    }
-    const int slot = APPEND ? g : 0;
-    if constexpr (Q8) {
-      u32x2 clo, chi;
-      const float sc = quantize_quad_row(lo, hi, clo, chi);
-      new_rows[slot][lane] = u32x4{clo.x, clo.y, chi.x, chi.y};
-      if (c == 0) new_scales[APPEND && Q8 ? g : 0][is_k ? 0 : 1] = sc;
-    } else {
-      // [K lo parts 0..3 | K hi parts | V lo | V hi] in 16 chunks: 2 per lane
-      reinterpret_cast<u32x4*>(&new_rows[slot][0])[(is_k ? 0 : 8) + c] = u32x4{lo.x, lo.y, lo.z, lo.w};
-      reinterpret_cast<u32x4*>(&new_rows[slot][0])[(is_k ? 0 : 8) + 4 + c] = u32x4{hi.x, hi.y, hi.z, hi.w};
-    }
-  }
 
   LaneState st;
 #pragma unroll
@@ -512,25 +492,65 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     constexpr bool MASK = decltype(masked)::value;
     const int slot = (i - p0) % F::kRingDepth;
     const uint32_t off = slot * kRingSlotBytes;
-    wait_vmem<F::kLoads * (F::kRingDepth - 1)>();          // page i has landed
+    wait_page<F::kLoads, F::kRingDepth>(min(last - i, F::kRingDepth - 1));   // page i landed
     if (MASK && app_here) park_new_row(slot0 + off);
     if constexpr (Q8) {
       PageQ8 cur;
       lds_page_issue(cur, ka + off, va + off, sa + off);
       lds_page_ready(cur);
-      fetch(min(i + F::kRingDepth, last), slot);
+      if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
       consume_page<true, MASK>(st, cur, qlo, qhi, a.xscale, lane, MASK ? tail_valid : kPage);
     } else {
       PageBF16 cur;
       lds_page_issue(cur, ad, off);
       lds_page_ready(cur);
-      fetch(min(i + F::kRingDepth, last), slot);
+      if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
       consume_page<false, MASK>(st, cur, qlo, qhi, a.xscale, lane, MASK ? tail_valid : kPage);
     }
   };
 
+  // The prologue's loads (block-table window, query rows, new rows) were
+  // requested together with the length and have arrived with it.  One
+  // explicit wait for all of them, visible to the compiler's wait tracking,
+  // keeps it from waiting on the page stream at their later uses.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-  for (int r = 0; r < F::kRingDepth; ++r) fetch(min(p0 + r, last), r);
+  for (int r = 0; r < F::kRingDepth; ++r)
+    if (p0 + r <= last) fetch(p0 + r, r);
+
+  // while the first pages are in flight: the query operand and the new rows
+  // B operand of the score product: column n = query head 4g + n%4, this
+  // lane's 8 dims {8G..} (qlo) and {32+8G..} (qhi)
+  {
+    uint4 lo = q_lo, hi = q_hi;
+    if (ROPE) {
+      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * G;
+      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+    }
+    qlo = __builtin_bit_cast(bf16x8_t, lo);
+    qhi = __builtin_bit_cast(bf16x8_t, hi);
+  }
+  if (app_here && lane < 8) {
+    const int c = lane & 3;
+    const bool is_k = lane < 4;
+    uint4 lo = new_lo, hi = new_hi;
+    if (ROPE && is_k) {
+      const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * c;
+      rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+    }
+    const int slot = APPEND ? g : 0;
+    const uint32_t rows = lds_address(&new_rows[slot][0]);
+    if constexpr (Q8) {
+      u32x2 clo, chi;
+      const float sc = quantize_quad_row(lo, hi, clo, chi);
+      lds_store16(rows + 16 * lane, u32x4{clo.x, clo.y, chi.x, chi.y});
+      if (c == 0) lds_store4(lds_address(&new_scales[APPEND && Q8 ? g : 0][is_k ? 0 : 1]), sc);
+    } else {
+      // [K lo parts 0..3 | K hi parts | V lo | V hi] in 16 chunks: 2 per lane
+      lds_store16(rows + 16 * ((is_k ? 0 : 8) + c), u32x4{lo.x, lo.y, lo.z, lo.w});
+      lds_store16(rows + 16 * ((is_k ? 0 : 8) + 4 + c), u32x4{hi.x, hi.y, hi.z, hi.w});
+    }
+  }
   for (int i = p0; i < last; ++i) step(i, std::false_type{});
   step(last, std::true_type{});
   wait_vmem<0>();

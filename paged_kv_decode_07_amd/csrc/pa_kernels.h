@@ -102,6 +102,35 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their
+// maxima), in the gfx9 encoding: vmcnt in bits 3:0 and 15:14.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Wait until the oldest page of a ring has landed while the `later` pages
+// requested after it (each LOADS instructions) may still be in flight;
+// `later` is wave-uniform and below DEPTH.
+template <int LOADS, int DEPTH>
+__device__ __forceinline__ void wait_page(int later) {
+  static_assert(DEPTH >= 2 && DEPTH <= 4, "ring depth");
+  if constexpr (DEPTH > 3) {
+    if (later >= 3) return wait_vmem<LOADS * 3>();
+  }
+  if constexpr (DEPTH > 2) {
+    if (later >= 2) return wait_vmem<LOADS * 2>();
+  }
+  if (later >= 1) return wait_vmem<LOADS>();
+  wait_vmem<0>();
+}
+
+// LDS stores the compiler does not see as LDS accesses: it would otherwise
+// wait for every outstanding direct-to-LDS load before them.
+__device__ __forceinline__ void lds_store16(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store4(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
