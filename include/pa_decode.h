@@ -167,7 +167,10 @@ int pa_decode_plan_lengths(const pa_shape* shape, int32_t batch,
  * Sequences longer than one split write FP32 partial results (running max,
  * sum, unnormalised output) to the workspace and a second kernel merges them
  * in split order; results are deterministic run to run and do not depend on
- * where pages sit in the pool.  `out` must not alias any input.
+ * where pages sit in the pool.  `out` must not alias any input.  One
+ * work-group runs per (sequence, split) of the plan, so batch x splits must
+ * not exceed 2^31 - 1 (PA_ERR_VALUE otherwise); there is no other limit on
+ * batch.
  */
 int pa_decode_attention(const pa_shape* shape, int32_t batch,
                         const void* q, const void* k_pool, const void* v_pool,

@@ -494,7 +494,7 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return PA_ERR_ALIGN;
   }
-  if ((int64_t)batch * ns > INT32_MAX || ns > 65535 || batch > 65535 * 64) return PA_ERR_VALUE;
+  if ((int64_t)batch * ns > INT32_MAX) return PA_ERR_VALUE;        // one block per (sequence, split)
 
   pa::DecodeArgs a = {};
   a.q = (const uint16_t*)q;

@@ -94,8 +94,9 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t pages_per_split;
   int32_t num_splits;
-  // optional work list: work item k (block k of a 1-D grid) is sequence
-  // work[2k], split work[2k+1]; NULL: block (x, y) is split x of sequence y
+  // optional work list: work item k (block k) is sequence work[2k], split
+  // work[2k+1]; NULL: block k is split k % num_splits of sequence
+  // k / num_splits
   const int32_t* work;
   int32_t num_work;
   int32_t batch;
@@ -307,7 +308,10 @@ template <bool Q8, bool OUT_BF16, bool APPEND, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   using F = PageFormat<Q8>;
-  int s = blockIdx.x, b = blockIdx.y;
+  // a one-dimensional grid: block k is split k % S of sequence k / S (the
+  // same dispatch order as a (S, B) grid, without its limit on B)
+  int b = (int)(blockIdx.x / (unsigned)a.num_splits);
+  int s = (int)blockIdx.x - b * a.num_splits;
   if (a.work) {
     // entries outside the batch or the plan are skipped, never followed
     b = a.work[2 * blockIdx.x];
@@ -649,7 +653,7 @@ template <bool Q8>
 inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
                                 bool rope, hipStream_t st, hipEvent_t event_before,
                                 hipEvent_t event_after) {
-  const dim3 grid = a.work ? dim3(a.num_work) : dim3(a.num_splits, batch);
+  const dim3 grid = a.work ? dim3(a.num_work) : dim3(a.num_splits * batch);
   const dim3 block(kThreads);
   hipError_t e = hipSuccess;
   if (event_before && (e = hipEventRecord(event_before, st)) != hipSuccess) return e;

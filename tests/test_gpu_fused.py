@@ -105,3 +105,29 @@ def test_fused_bad_last_page_writes_nothing_and_gives_nan():
     assert np.array_equal(host16(db.v_pool), v_ref)
     ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
     assert_close(got[[0, 2]], ref[[0, 2]], where="fused others")
+
+
+def test_fused_batch_of_70000_single_token_sequences():
+    """A batch larger than 65,535 (one block per sequence in a one-dimensional
+    grid): every sequence holds only its appended token, so each output row is
+    that token's V row exactly (softmax over one token)."""
+    from paged_kv_decode_07_amd import binding as pa
+    B = 70000
+    gen = torch.Generator(device="cuda").manual_seed(70000)
+    rows = lambda: torch.randn((B, 8, 64), generator=gen, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, 32, 64), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    kn, vn = rows(), rows()
+    k_pool = torch.zeros((B, 16, 8, 64), dtype=torch.int16, device="cuda")
+    v_pool = torch.zeros_like(k_pool)
+    bt = torch.full((B, W.MAX_BLOCKS), -1, dtype=torch.int32, device="cuda")
+    bt[:, 0] = torch.randperm(B, generator=gen, device="cuda").to(torch.int32)
+    lens = torch.ones(B, dtype=torch.int32, device="cuda")
+    print(f"fused batch {B}, seq_len 1", flush=True)
+    out = pa.append_decode_attention(q, kn.view(torch.int16), vn.view(torch.int16), k_pool, v_pool,
+                                     bt, lens, 1)
+    torch.cuda.synchronize()
+    want = vn.float().repeat_interleave(4, dim=1)                # head h reads KV head h // 4
+    assert torch.equal(out, want)
+    page = bt[:, 0].long()
+    assert torch.equal(v_pool[page, 0], vn.view(torch.int16))
+    assert torch.equal(k_pool[page, 0], kn.view(torch.int16))
