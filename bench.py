@@ -505,6 +505,7 @@ def main() -> int:
         "seq_per_s_per_layer": round(B / mean_step, 1),
         "kv_gbps_main_kernel": round(kv / float(t_main.mean()) / 1e9, 2),
         "algorithmic_bytes_per_step": by,
+        "all_bytes_gbps_step": round(by["total"] / mean_step / 1e9, 2),
         "times_us": {
             "step": round(mean_step * 1e6, 2),
             "step_min": round(float(t_step.min()) * 1e6, 2),
