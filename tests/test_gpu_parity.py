@@ -301,3 +301,32 @@ def test_plan_from_host_lengths_is_valid_and_correct():
     # uniform full-length batch covering the CUs: one split per sequence
     ps, ns = pa.decode_plan_lengths(np.full(256, 2048, np.int32), 32768)
     assert (ps, ns) == (128, 1)
+
+
+LONG_CONTEXT = [4096, 4000, 2600, 17, 0, 257]
+
+
+@pytest.mark.parametrize("pages_per_split", [0, 200, 256])
+def test_decode_4096_token_tables_and_256_page_splits(pages_per_split):
+    """Block tables of 256 entries (4,096-token sequences) and splits up to
+    256 pages, the most one work-group takes: every entry register of the
+    split's preloaded block-table window is used."""
+    w = W.make_batch(LONG_CONTEXT, sum(W.pages_for(L) for L in LONG_CONTEXT) + 7, seed=4096,
+                     max_blocks=256)
+    ref = oracle.decode_attention(w.q, w.k_pool, w.v_pool, w.block_tables, w.seq_lens, w.scale)
+    got = gpu_decode(DeviceBatch(w), pages_per_split=pages_per_split)
+    assert_close(got, ref, where=f"4096-token tables ps={pages_per_split}")
+
+
+def test_fused_4096_token_tables_one_split_each():
+    """The fused append on the 256th page of a 4,096-token sequence."""
+    from gpu_util import gpu_fused
+    w = W.make_batch(LONG_CONTEXT, sum(W.pages_for(L) for L in LONG_CONTEXT) + 7, seed=4097,
+                     max_blocks=256, append=True)
+    db = DeviceBatch(w)
+    got = gpu_fused(db, pages_per_split=256)
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    assert np.array_equal(host16(db.k_pool), k_ref) and np.array_equal(host16(db.v_pool), v_ref)
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got, ref, where="fused 4096-token tables")

@@ -293,3 +293,17 @@ def test_q8_full_batch256_len2048_bench_configuration():
             bound = kvquant.quantisation_error_bound(qf[b, h], Kb[:, g], K[:, g], Vb[:, g],
                                                      V[:, g], w.scale)
             assert np.all(np.abs(got[b, h] - ob) <= bound + 2e-3), (b, h)
+
+
+@pytest.mark.parametrize("pages_per_split", [0, 256])
+def test_q8_fused_4096_token_tables(pages_per_split):
+    """INT8 pages behind 256-entry block tables, splits up to 256 pages."""
+    lens = [4096, 3999, 33, 0, 1]
+    w = W.make_q8_batch(lens, sum(W.pages_for(L) for L in lens) + 5, 4098, append=True,
+                        max_blocks=256)
+    f = DevQ8(w)
+    fused = _fused(f, pages_per_split)
+    pools = kvquant.append_kv_q8(w.k_codes, w.v_codes, w.kv_scales, w.k_new, w.v_new,
+                                 w.block_tables, w.seq_lens)
+    _same_pools(f.pools(), pools)
+    assert_close(fused, _ref(w, pools=pools), where=f"q8 4096-token tables ps={pages_per_split}")

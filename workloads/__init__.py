@@ -84,7 +84,8 @@ def pages_for(seq_len: int) -> int:
 
 def make_batch(seq_lens, num_pages: int, seed, *, q_sigma: float = 1.0,
                append: bool = False, placement: str = "random",
-               name: str = "custom", recipe: Optional[dict] = None) -> DecodeBatch:
+               name: str = "custom", recipe: Optional[dict] = None,
+               max_blocks: int = MAX_BLOCKS) -> DecodeBatch:
     """Build a poisoned page pool holding random BF16 K/V for ``seq_lens``.
 
     ``placement`` is ``"random"`` (pages taken in the order of a seeded
@@ -93,13 +94,16 @@ def make_batch(seq_lens, num_pages: int, seed, *, q_sigma: float = 1.0,
     and the last token is returned separately in ``k_new``/``v_new``; its slot
     is poisoned until an append writes it.
 
+    ``max_blocks`` is the block-table row length (sequences up to
+    ``16 * max_blocks`` tokens; the model's context is 2,048, 128 blocks).
+
     Draw order (fixed, so a seed reproduces every byte): page permutation, q,
     then for each sequence in batch order its K block then its V block.
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = int(seq_lens.shape[0])
-    if np.any(seq_lens < 0) or np.any(seq_lens > MAX_CONTEXT):
-        raise ValueError("seq_lens must lie in [0, %d]" % MAX_CONTEXT)
+    if np.any(seq_lens < 0) or np.any(seq_lens > max_blocks * PAGE_SIZE):
+        raise ValueError("seq_lens must lie in [0, %d]" % (max_blocks * PAGE_SIZE))
     rng = np.random.default_rng(seed)
     n_pages = [pages_for(L) for L in seq_lens]
     need = sum(n_pages)
@@ -115,7 +119,7 @@ def make_batch(seq_lens, num_pages: int, seed, *, q_sigma: float = 1.0,
     else:
         raise ValueError(placement)
 
-    block_tables = np.full((B, MAX_BLOCKS), -1, dtype=np.int32)
+    block_tables = np.full((B, max_blocks), -1, dtype=np.int32)
     shape_pool = (num_pages, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
     k_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
     v_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
@@ -323,7 +327,8 @@ Q8_SCALE_RANGE = (0.018, 0.028)
 
 
 def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
-                  placement: str = "random", name: str = "q8") -> Q8Batch:
+                  placement: str = "random", name: str = "q8",
+                  max_blocks: int = MAX_BLOCKS) -> Q8Batch:
     """Random INT8 pages for ``seq_lens``, shaped like quantised N(0, 1) rows.
 
     Every stored (token, head) row gets codes round(N(0, 45)) clipped to
@@ -332,13 +337,15 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
     codes and a NaN scale (poison).  With ``append=True`` the slot of token
     L-1 stays poisoned and BF16 N(0, 1) rows for it come in ``k_new``/``v_new``.
 
+    ``max_blocks`` is the block-table row length, as in ``make_batch``.
+
     Draw order: page permutation, q, poison codes, then per sequence its K
     codes, V codes, K scales, V scales (and, appending, its new K and V rows).
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = int(seq_lens.shape[0])
-    if np.any(seq_lens < 0) or np.any(seq_lens > MAX_CONTEXT):
-        raise ValueError("seq_lens must lie in [0, %d]" % MAX_CONTEXT)
+    if np.any(seq_lens < 0) or np.any(seq_lens > max_blocks * PAGE_SIZE):
+        raise ValueError("seq_lens must lie in [0, %d]" % (max_blocks * PAGE_SIZE))
     rng = np.random.default_rng(seed)
     n_pages = [pages_for(L) for L in seq_lens]
     if sum(n_pages) > num_pages:
@@ -354,7 +361,7 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
     kv_scales = np.full((num_pages, NUM_KV_HEADS, 2, PAGE_SIZE), np.nan, dtype=np.float32)
     k_new = np.zeros((B, NUM_KV_HEADS, HEAD_DIM), np.uint16) if append else None
     v_new = np.zeros((B, NUM_KV_HEADS, HEAD_DIM), np.uint16) if append else None
-    block_tables = np.full((B, MAX_BLOCKS), -1, dtype=np.int32)
+    block_tables = np.full((B, max_blocks), -1, dtype=np.int32)
 
     def codes(T):
         c = np.clip(np.rint(rng.standard_normal((T, NUM_KV_HEADS, HEAD_DIM), dtype=np.float32)
