@@ -248,6 +248,59 @@ def run_sweep(args) -> int:
                     flush=True)
         del q, kp, vp, kn, vn, bt, lens, out, kc, vc, sc
         torch.cuda.empty_cache()
+
+    # workload 3 as a model step: the 16 layers' fused steps back to back (one
+    # pool region per layer), launched one by one and replayed as a HIP graph
+    layers = []
+    t0 = time.perf_counter()
+    for layer in range(16):
+        w = W.make_workload(3, layer=layer, append=True)
+        layers.append(dict(q=up16(w.q), kp=up16(w.k_pool), vp=up16(w.v_pool), kn=up16(w.k_new),
+                           vn=up16(w.v_new), bt=torch.from_numpy(w.block_tables).to(dev),
+                           lens=torch.from_numpy(w.seq_lens).to(dev),
+                           out=torch.empty((w.batch, 32, 64), dtype=torch.float32, device=dev)))
+    log(f"workload 3, 16 layers generated in {time.perf_counter() - t0:.1f} s")
+    w0 = W.make_workload(3, layer=0, append=True)
+    ps, ns = pa.decode_plan_lengths(w0.seq_lens, w0.num_pages, max_seq_len=w0.max_seq_len)
+    kv16 = 16 * A.step_bytes(w0.seq_lens, append=True)["kv"]
+
+    wl, wps, _ = pa.decode_worklist(w0.seq_lens, w0.num_pages, max_seq_len=w0.max_seq_len)
+    wd = torch.from_numpy(wl).to(dev)
+
+    def model_step(st, worklist):
+        for L in layers:
+            if worklist:
+                pa.append_decode_attention_worklist(
+                    L["q"], L["kn"], L["vn"], L["kp"], L["vp"], L["bt"], L["lens"],
+                    w0.max_seq_len, wd, wps, scale=w0.scale, out=L["out"], workspace=workspace,
+                    stream=st)
+            else:
+                pa.append_decode_attention(L["q"], L["kn"], L["vn"], L["kp"], L["vp"], L["bt"],
+                                           L["lens"], w0.max_seq_len, scale=w0.scale,
+                                           out=L["out"], pages_per_split=ps, workspace=workspace,
+                                           stream=st)
+
+    for worklist in (False, True):
+        t_eager = timed(lambda: model_step(stream, worklist), args.steps)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                model_step(side, worklist)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        t_graph = timed(graph.replay, args.steps)
+        base = "work list" if worklist else "grid (lengths plan)"
+        for launch, t in ((f"{base}, 16 calls", t_eager), (f"{base}, HIP graph of 16 calls", t_graph)):
+            print(json.dumps({
+                "workload": 3, "desc": W.WORKLOADS[3] + " (all 16 layers)", "pages": "bf16",
+                "launch": launch, "pages_per_split": int(wps if worklist else ps),
+                ("items" if worklist else "splits"): int(len(wl) if worklist else ns),
+                "step_us": round(t * 1e6, 2), "kv_bytes": int(kv16),
+                "kv_gbps": round(kv16 / t / 1e9, 1),
+                "seq_per_s": round(int(np.count_nonzero(w0.seq_lens)) / t, 1)}), flush=True)
+        del graph
     return 0
 
 
