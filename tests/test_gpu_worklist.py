@@ -26,9 +26,10 @@ def _zipf_lens(seed, B=96):
     return lens
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
 @pytest.mark.parametrize("q8", [False, True], ids=["bf16", "int8"])
 @pytest.mark.parametrize("fused", [False, True], ids=["decode", "fused"])
-def test_worklist_launch_matches_grid_launch(q8, fused):
+def test_worklist_launch_matches_grid_launch(q8, fused, out_dtype):
     from paged_kv_decode_07_amd import binding as pa
     lens = _zipf_lens(1500 + 2 * q8 + fused)
     pages = int(sum(W.pages_for(L) for L in lens)) + 8
@@ -46,29 +47,34 @@ def test_worklist_launch_matches_grid_launch(q8, fused):
             vn = dev16(w.v_new) if fused else None
             if use_list:
                 out = pa.append_decode_attention_worklist(dev16(w.q), kn, vn, kc, vc, dev32(w.block_tables),
-                                                          dev32(w.seq_lens), msl, work, ps, kv_scales=sc)
+                                                          dev32(w.seq_lens), msl, work, ps, kv_scales=sc,
+                                                          out_dtype=out_dtype)
             elif fused:
                 out = pa.append_decode_attention_q8(dev16(w.q), kn, vn, kc, vc, sc, dev32(w.block_tables),
-                                                    dev32(w.seq_lens), msl, pages_per_split=ps)
+                                                    dev32(w.seq_lens), msl, pages_per_split=ps,
+                                                    out_dtype=out_dtype)
             else:
                 out = pa.decode_attention_q8(dev16(w.q), kc, vc, sc, dev32(w.block_tables),
-                                             dev32(w.seq_lens), msl, pages_per_split=ps)
+                                             dev32(w.seq_lens), msl, pages_per_split=ps,
+                                             out_dtype=out_dtype)
             pools = (kc, vc, sc.view(torch.int32))
         else:
             w = W.make_batch(lens, pages, 1600, append=fused)
             d = DeviceBatch(w)
             if use_list:
                 out = pa.append_decode_attention_worklist(d.q, d.k_new, d.v_new, d.k_pool, d.v_pool, d.bt,
-                                                          d.lens, msl, work, ps)
+                                                          d.lens, msl, work, ps, out_dtype=out_dtype)
             elif fused:
                 out = pa.append_decode_attention(d.q, d.k_new, d.v_new, d.k_pool, d.v_pool, d.bt, d.lens,
-                                                 msl, pages_per_split=ps)
+                                                 msl, pages_per_split=ps, out_dtype=out_dtype)
             else:
-                out = pa.decode_attention(d.q, d.k_pool, d.v_pool, d.bt, d.lens, msl, pages_per_split=ps)
+                out = pa.decode_attention(d.q, d.k_pool, d.v_pool, d.bt, d.lens, msl, pages_per_split=ps,
+                                          out_dtype=out_dtype)
             pools = (d.k_pool, d.v_pool)
         torch.cuda.synchronize()
         outs.append((out.clone(), [p.clone() for p in pools]))
     (o0, p0), (o1, p1) = outs
+    assert o0.dtype == out_dtype
     assert torch.equal(o0, o1), "work-list launch differs from the grid launch"
     for a, b in zip(p0, p1):
         assert torch.equal(a, b), "pools differ"
