@@ -522,8 +522,11 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.work = work;
   a.num_work = num_work;
   a.batch = batch;
+  // a batch that fits the compute units merges with its partials requested up front
+  int cu = 0;
+  const bool merge_preload = current_cu_count(&cu) == PA_OK && batch <= cu;
   const hipError_t e = pa::launch_decode<false>(a, batch, out_dtype == PA_OUT_BF16, fused,
-                                                rope != nullptr, (hipStream_t)stream,
+                                                rope != nullptr, merge_preload, (hipStream_t)stream,
                                                 (hipEvent_t)event_before_main,
                                                 (hipEvent_t)event_after_main);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

@@ -651,8 +651,8 @@ namespace pa {
 // are recorded right around the decode kernel.  Returns a hipError_t.
 template <bool Q8>
 inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
-                                bool rope, hipStream_t st, hipEvent_t event_before,
-                                hipEvent_t event_after) {
+                                bool rope, bool merge_preload, hipStream_t st,
+                                hipEvent_t event_before, hipEvent_t event_after) {
   const dim3 grid = a.work ? dim3(a.num_work) : dim3(a.num_splits * batch);
   const dim3 block(kThreads);
   hipError_t e = hipSuccess;
@@ -678,6 +678,7 @@ inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, b
     m.max_seq_len = a.max_seq_len;
     m.pages_per_split = a.pages_per_split;
     m.num_splits = a.num_splits;
+    m.preload = merge_preload ? 1 : 0;
     if (out_bf16) hipLaunchKernelGGL(merge_kernel<true>, dim3(batch), dim3(256), 0, st, m);
     else hipLaunchKernelGGL(merge_kernel<false>, dim3(batch), dim3(256), 0, st, m);
     if ((e = hipGetLastError()) != hipSuccess) return e;

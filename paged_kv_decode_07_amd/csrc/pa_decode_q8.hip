@@ -240,9 +240,11 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
   a.work = work;
   a.num_work = num_work;
   a.batch = batch;
+  int cu = 0;
+  const bool merge_preload = pa_host::current_cu_count(&cu) == PA_OK && batch <= cu;
   const hipError_t e = pa::launch_decode<true>(a, batch, out_dtype == PA_OUT_BF16, fused,
-                                               rope != nullptr, (hipStream_t)stream, nullptr,
-                                               nullptr);
+                                               rope != nullptr, merge_preload, (hipStream_t)stream,
+                                               nullptr, nullptr);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -173,14 +173,19 @@ struct MergeArgs {
   int32_t max_seq_len;     // host-declared bound; longer sequences are flagged
   int32_t pages_per_split;
   int32_t num_splits;      // S: splits per sequence in the grid
+  int32_t preload;         // request partials before the length (small batches)
 };
 
 // Log-sum-exp merge of the splits of each multi-split sequence, in split
 // order.  One work-group of 256 threads per sequence: thread = (head, 8 dims).
-// Splits are read 8 at a time with all loads issued before any use.  The
-// first 8 splits' partials (rows that exist in the workspace whatever the
-// sequence's length) are requested together with the length, so a sequence
-// of up to 8 splits costs one memory latency.
+// Splits are read 8 at a time with all loads issued before any use, and each
+// batch is absorbed once: the running maximum rises with the batch maximum
+// (rescaling what was summed), then the batch's weights 2^(m_s - M) are
+// added in split order.  The first 16 splits' partials (rows that exist in
+// the workspace whatever the sequence's length) are requested together with
+// the length when the batch is small (`preload`), so a sequence of up to 16
+// splits costs one memory latency; a large batch, whose short sequences need
+// no merge, requests only the splits a sequence has, after its length.
 constexpr int kMergeBatch = 8;
 
 struct MergeBatch {
@@ -202,46 +207,59 @@ __device__ __forceinline__ void merge_load(MergeBatch& t, const MergeArgs& a, in
   }
 }
 
+// Keeps a batch's loads ahead of the code that follows: without this the
+// compiler moves them after the length test's early exits, one memory
+// latency later.
+__device__ __forceinline__ void merge_pin(const MergeBatch& t) {
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    asm volatile("" ::"v"(t.m[k]), "v"(t.l[k]), "v"(__builtin_bit_cast(f32x4_t, t.x0[k])),
+                 "v"(__builtin_bit_cast(f32x4_t, t.x1[k]))
+                 : "memory");
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int b = blockIdx.x;
   const int h = threadIdx.x >> 3;
   const int d0 = (threadIdx.x & 7) * 8;
   const int64_t row0 = (int64_t)b * a.num_splits * kHq + h;   // split s at row0 + s*kHq
-  MergeBatch first;
-  merge_load(first, a, row0, d0, 0, a.num_splits);
+  MergeBatch first, second;
+  const bool two = a.num_splits > kMergeBatch;   // uniform: a plan of more than 8 splits
+  if (a.preload) {
+    merge_load(first, a, row0, d0, 0, a.num_splits);
+    if (two) merge_load(second, a, row0, d0, kMergeBatch, a.num_splits);
+  }
   const int L = a.seq_lens[b];
-  // keep the partial loads ahead of the length test: without this the
-  // compiler moves them after the early exits, one memory latency later
-#pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k)
-    asm volatile("" ::"v"(first.m[k]), "v"(first.l[k]),
-                 "v"(__builtin_bit_cast(f32x4_t, first.x0[k])),
-                 "v"(__builtin_bit_cast(f32x4_t, first.x1[k]))
-                 : "memory");
+  if (a.preload) {
+    merge_pin(first);
+    if (two) merge_pin(second);
+  }
   const int n_pages = (L + kPage - 1) / kPage;
   if (L <= 0 || L > a.max_seq_len || n_pages > a.max_blocks ||
       n_pages > a.pages_per_split * a.num_splits)
     return;
   const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
   if (ns <= 1) return;
-  // pass 1: the largest running maximum over the splits
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k)
-    if (k < ns) M = fmaxf(M, first.m[k]);
-  for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
-    float m[kMergeBatch];
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k)
-      m[k] = (s0 + k < ns) ? a.part_ml[(row0 + (int64_t)(s0 + k) * kHq) * 2] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, m[k]);
+  if (!a.preload) {
+    merge_load(first, a, row0, d0, 0, ns);
+    if (ns > kMergeBatch) merge_load(second, a, row0, d0, kMergeBatch, ns);
   }
-  // pass 2: weights 2^(m_s - M), sums in split order
+  float M = -INFINITY;                           // running maximum (log2 units)
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  auto accumulate = [&](const MergeBatch& t, int s0) {
+  auto absorb = [&](const MergeBatch& t, int s0) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (s0 + k < ns) bm = fmaxf(bm, t.m[k]);
+    if (bm > M) {                                // 2^(-inf) = 0 clears the empty start
+      const float r = __builtin_amdgcn_exp2f(M - bm);
+      den *= r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] *= r;
+      M = bm;
+    }
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       if (s0 + k >= ns) break;
@@ -251,11 +269,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       num[4] += w * t.x1[k].x; num[5] += w * t.x1[k].y; num[6] += w * t.x1[k].z; num[7] += w * t.x1[k].w;
     }
   };
-  accumulate(first, 0);
-  for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
+  absorb(first, 0);
+  if (ns > kMergeBatch) absorb(second, kMergeBatch);    // ns > 8 implies `two`
+  for (int s0 = 2 * kMergeBatch; s0 < ns; s0 += kMergeBatch) {
     MergeBatch t;
     merge_load(t, a, row0, d0, s0, ns);
-    accumulate(t, s0);
+    absorb(t, s0);
   }
   const float inv = 1.f / den;
   const int64_t orow = (int64_t)b * kHq + h;
