@@ -118,9 +118,9 @@ namespace pa_host {
 PlanModel plan_model_q8() {
   PlanModel m;
   m.page_bytes = 2.0 * pa::kPageCodes + pa::kScalePageFloats * 4.0;
-  m.page_us = 0.8;
-  m.group_us = 2.0;
-  m.empty_us = 1.0;
+  m.page_us = 0.5;
+  m.group_us = 3.0;
+  m.empty_us = 0.5;
   return m;
 }
 

@@ -29,8 +29,8 @@ int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pa
 // The defaults were fitted to the BF16 kernel on MI355X over batch 8 .. 512
 // and split sizes 8 .. 128.
 struct PlanModel {
-  double page_us = 0.85, group_us = 6.0, empty_us = 0.5, merge_us = 8.0;
-  double hbm_bytes_per_us = 6.1e6;
+  double page_us = 0.6, group_us = 3.0, empty_us = 0.5, merge_us = 8.0;
+  double hbm_bytes_per_us = 6.6e6;
   double page_bytes = 2.0 * 16 * 8 * 64 * 2;   // one K page and one V page, BF16
 };
 // worklist: the work-groups run in pa_decode_worklist's order (largest
