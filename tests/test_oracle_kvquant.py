@@ -18,19 +18,19 @@ def test_kvquant_pin(pin):
 
 
 MUTANTS = {
-    "divide_by_128": ("scale = (amax / np.float32(QMAX))", "scale = (amax / np.float32(128))"),
+    "divide_by_qmax_plus_one": ("scale = (amax / np.float32(qmax))", "scale = (amax / np.float32(qmax + 1))"),
     "one_scale_per_tensor": ("amax = np.max(np.abs(x), axis=-1)",
                              "amax = np.max(np.abs(x), axis=-1) * 0 + np.max(np.abs(x))"),
-    "truncating_round": ("codes = np.clip(np.rint(ratio), QMIN, QMAX)",
-                         "codes = np.clip(np.trunc(ratio), QMIN, QMAX)"),
-    "ties_up": ("codes = np.clip(np.rint(ratio), QMIN, QMAX)",
-                "codes = np.clip(np.floor(ratio + np.float32(0.5)), QMIN, QMAX)"),
+    "truncating_round": ("codes = np.clip(np.rint(ratio), qmin, qmax)",
+                         "codes = np.clip(np.trunc(ratio), qmin, qmax)"),
+    "ties_up": ("codes = np.clip(np.rint(ratio), qmin, qmax)",
+                "codes = np.clip(np.floor(ratio + np.float32(0.5)), qmin, qmax)"),
     "multiply_by_scale": ("ratio = (x / safe[..., None])", "ratio = (x * safe[..., None])"),
     "v_scale_into_k_slot": ("scales[physical, :, 1, slot] = vs", "scales[physical, :, 0, slot] = vs"),
     "scale_slot_wrong": ("scales[physical, :, 0, slot] = ks", "scales[physical, :, 0, 0] = ks"),
     "k_codes_not_written": ("    k_codes[physical, :, slot] = kc\n", "    pass\n"),
-    "gather_k_scale_for_v": ("dequantize(codes[physical, :, slot], scales[physical, :, which, slot])",
-                             "dequantize(codes[physical, :, slot], scales[physical, :, 0, slot])"),
+    "gather_k_scale_for_v": ("rows.append(dequantize(c, scales[physical, :, which, slot]))",
+                             "rows.append(dequantize(c, scales[physical, :, 0, slot]))"),
     "dequantize_without_scale": ("return np.asarray(codes, np.float64) * np.asarray(scale, np.float64)[..., None]",
                                  "return np.asarray(codes, np.float64)"),
     "append_slot_off_by_one": ("_write_token(kc, vc, sc, physical, pos % page_size,",

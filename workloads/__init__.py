@@ -308,6 +308,7 @@ class Q8Batch:
     k_new: Optional[np.ndarray] = None   # uint16 [B][8][64] BF16 rows when the step appends
     v_new: Optional[np.ndarray] = None
     recipe: dict = field(default_factory=dict)
+    nbits: int = 8              # 4: codes are uint8 [num_pages][8][16][32], two per byte
 
     @property
     def batch(self) -> int:
@@ -324,11 +325,13 @@ class Q8Batch:
 
 Q8_CODE_SIGMA = 45.0            # codes of N(0, 1) rows of 64 values: amax ~ 2.8 -> 127
 Q8_SCALE_RANGE = (0.018, 0.028)
+Q4_CODE_SIGMA = 2.5             # the same rows at 4 bits: amax ~ 2.8 -> 7
+Q4_SCALE_RANGE = (0.32, 0.5)
 
 
 def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
                   placement: str = "random", name: str = "q8",
-                  max_blocks: int = MAX_BLOCKS) -> Q8Batch:
+                  max_blocks: int = MAX_BLOCKS, nbits: int = 8) -> Q8Batch:
     """Random INT8 pages for ``seq_lens``, shaped like quantised N(0, 1) rows.
 
     Every stored (token, head) row gets codes round(N(0, 45)) clipped to
@@ -338,6 +341,11 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
     L-1 stays poisoned and BF16 N(0, 1) rows for it come in ``k_new``/``v_new``.
 
     ``max_blocks`` is the block-table row length, as in ``make_batch``.
+
+    ``nbits=4`` draws INT4 pages instead: codes ``round(N(0, 2.5))`` clipped to
+    [-7, 7] with one +-7 per row, scales uniform in [0.32, 0.5], stored two
+    per byte as code + 8 (dim 2j in the low nibble of byte j); unused slots
+    hold random bytes and NaN scales.
 
     Draw order: page permutation, q, poison codes, then per sequence its K
     codes, V codes, K scales, V scales (and, appending, its new K and V rows).
@@ -354,10 +362,19 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
     order = perm if placement == "random" else np.arange(num_pages, dtype=np.int32)
     if placement not in ("random", "identity"):
         raise ValueError(placement)
+    if nbits not in (8, 4):
+        raise ValueError("nbits must be 8 or 4")
     q = f32_to_bf16_bits(rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM), dtype=np.float32))
-    shape = (num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM)
-    k_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
-    v_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
+    if nbits == 8:
+        shape = (num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM)
+        k_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
+        v_codes = rng.integers(-128, 128, size=shape, dtype=np.int8)
+        sigma, qmax, scale_range = Q8_CODE_SIGMA, 127, Q8_SCALE_RANGE
+    else:
+        shape = (num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM // 2)
+        k_codes = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        v_codes = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        sigma, qmax, scale_range = Q4_CODE_SIGMA, 7, Q4_SCALE_RANGE
     kv_scales = np.full((num_pages, NUM_KV_HEADS, 2, PAGE_SIZE), np.nan, dtype=np.float32)
     k_new = np.zeros((B, NUM_KV_HEADS, HEAD_DIM), np.uint16) if append else None
     v_new = np.zeros((B, NUM_KV_HEADS, HEAD_DIM), np.uint16) if append else None
@@ -365,10 +382,13 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
 
     def codes(T):
         c = np.clip(np.rint(rng.standard_normal((T, NUM_KV_HEADS, HEAD_DIM), dtype=np.float32)
-                            * np.float32(Q8_CODE_SIGMA)), -127, 127).astype(np.int8)
+                            * np.float32(sigma)), -qmax, qmax).astype(np.int8)
         pick = rng.integers(0, HEAD_DIM, size=(T, NUM_KV_HEADS))
-        sign = rng.choice(np.array([-127, 127], np.int8), size=(T, NUM_KV_HEADS))
+        sign = rng.choice(np.array([-qmax, qmax], np.int8), size=(T, NUM_KV_HEADS))
         np.put_along_axis(c, pick[..., None], sign[..., None], axis=-1)
+        if nbits == 4:                 # two per byte, offset by 8
+            u = (c.astype(np.int16) + 8).astype(np.uint8)
+            c = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
         return c
 
     cursor = 0
@@ -380,8 +400,8 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
         if L == 0:
             continue
         kc, vc = codes(L), codes(L)
-        ks = rng.uniform(*Q8_SCALE_RANGE, size=(L, NUM_KV_HEADS)).astype(np.float32)
-        vs = rng.uniform(*Q8_SCALE_RANGE, size=(L, NUM_KV_HEADS)).astype(np.float32)
+        ks = rng.uniform(*scale_range, size=(L, NUM_KV_HEADS)).astype(np.float32)
+        vs = rng.uniform(*scale_range, size=(L, NUM_KV_HEADS)).astype(np.float32)
         stored = L - 1 if append else L
         for t in range(stored):
             page, slot = pages[t // PAGE_SIZE], t % PAGE_SIZE
@@ -393,10 +413,10 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
             k_new[b] = f32_to_bf16_bits(rng.standard_normal((NUM_KV_HEADS, HEAD_DIM), dtype=np.float32))
             v_new[b] = f32_to_bf16_bits(rng.standard_normal((NUM_KV_HEADS, HEAD_DIM), dtype=np.float32))
     recipe = dict(num_pages=num_pages, placement=placement, append=append, seed=_seed_repr(seed),
-                  code_sigma=Q8_CODE_SIGMA, scale_range=Q8_SCALE_RANGE)
+                  code_sigma=sigma, scale_range=scale_range, nbits=nbits)
     return Q8Batch(name=name, q=q, k_codes=k_codes, v_codes=v_codes, kv_scales=kv_scales,
                    block_tables=block_tables, seq_lens=seq_lens, k_new=k_new, v_new=v_new,
-                   recipe=recipe)
+                   recipe=recipe, nbits=nbits)
 
 
 def poison_summary(batch: DecodeBatch) -> dict:
