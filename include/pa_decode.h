@@ -276,8 +276,10 @@ int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
  * out, except split 0 of a sequence without pages (its output row is still
  * written: zeros, or NaN for a length beyond max_seq_len).
  *   pages_per_split: the split size, or 0 to plan it from the lengths (the
- *     cost model of pa_decode_plan_lengths, or of pa_decode_plan_lengths_q8
- *     when page_format is 1 (INT8 pages); 0 = BF16 pages);
+ *     cost model of pa_decode_plan_lengths for page_format 0 (BF16 pages),
+ *     of pa_decode_plan_lengths_q8 for 1 (INT8 pages), of
+ *     pa_decode_plan_lengths_q4 for 2 (INT4 pages); other values are
+ *     PA_ERR_VALUE);
  *   num_cus: compute units assumed by the planner (0 = current device);
  *   work: host int32 [2 * capacity]; item k is sequence work[2k], split
  *     work[2k+1]; *count receives the number of items (PA_ERR_VALUE when it

@@ -23,7 +23,8 @@ _lib = None
 PA_OUT_F32, PA_OUT_BF16 = 0, 1
 HQ, HKV, D, PAGE = 32, 8, 64, 16
 
-# names declared in include/pa_decode.h, include/pa_decode_q8.h and include/pa_kvpool.h
+# names declared in include/pa_decode.h, include/pa_decode_q8.h, include/pa_decode_q4.h,
+# include/pa_measure.h and include/pa_kvpool.h
 EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_decode_plan_lengths",
            "pa_decode_attention", "pa_append_decode_attention", "pa_decode_attention_profiled",
            "pa_append_kv_rope", "pa_append_decode_attention_rope", "pa_fill_kv",
@@ -33,6 +34,10 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_append_kv_q8", "pa_append_kv_rope_q8", "pa_fill_kv_q8", "pa_decode_attention_q8",
            "pa_append_decode_attention_q8", "pa_append_decode_attention_rope_q8",
            "pa_decode_plan_lengths_q8", "pa_append_decode_attention_worklist_q8",
+           # include/pa_decode_q4.h
+           "pa_append_kv_q4", "pa_append_kv_rope_q4", "pa_fill_kv_q4", "pa_decode_attention_q4",
+           "pa_append_decode_attention_q4", "pa_append_decode_attention_rope_q4",
+           "pa_decode_plan_lengths_q4", "pa_append_decode_attention_worklist_q4",
            # include/pa_measure.h
            "pa_stream_read",
            # include/pa_kvpool.h
@@ -91,18 +96,22 @@ def load_library(path: str | None = None):
         lib.pa_append_decode_attention_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, I32,
                                                         ctypes.c_float, P, I32, I32, P, SZ, P]
         lib.pa_fill_kv.argtypes = [SP, P, P, I32, I32, P, P, P, P]
-        lib.pa_append_kv_q8.argtypes = [SP, I32, P, P, P, P, P, P, P, P]
-        lib.pa_append_kv_rope_q8.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P, P, P]
-        lib.pa_fill_kv_q8.argtypes = [SP, P, P, I32, I32, P, P, P, P, P]
-        lib.pa_decode_attention_q8.argtypes = [SP, I32, P, P, P, P, P, P, I32, ctypes.c_float,
-                                               P, I32, I32, P, SZ, P]
-        lib.pa_append_decode_attention_q8.argtypes = [SP, I32, P, P, P, P, P, P, P, P, I32,
-                                                      ctypes.c_float, P, I32, I32, P, SZ, P]
-        lib.pa_append_decode_attention_rope_q8.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P,
-                                                           I32, ctypes.c_float, P, I32, I32, P,
-                                                           SZ, P]
-        lib.pa_decode_plan_lengths_q8.argtypes = [SP, I32, P, I32, I32, ctypes.POINTER(I32),
-                                                  ctypes.POINTER(I32)]
+        for sfx in ("_q8", "_q4"):
+            getattr(lib, "pa_append_kv" + sfx).argtypes = [SP, I32, P, P, P, P, P, P, P, P]
+            getattr(lib, "pa_append_kv_rope" + sfx).argtypes = [SP, I32, P, P, P, RP, P, P, P, P,
+                                                                P, P, P]
+            getattr(lib, "pa_fill_kv" + sfx).argtypes = [SP, P, P, I32, I32, P, P, P, P, P]
+            getattr(lib, "pa_decode_attention" + sfx).argtypes = [
+                SP, I32, P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I32, P, SZ, P]
+            getattr(lib, "pa_append_decode_attention" + sfx).argtypes = [
+                SP, I32, P, P, P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I32, P, SZ, P]
+            getattr(lib, "pa_append_decode_attention_rope" + sfx).argtypes = [
+                SP, I32, P, P, P, RP, P, P, P, P, P, I32, ctypes.c_float, P, I32, I32, P, SZ, P]
+            getattr(lib, "pa_decode_plan_lengths" + sfx).argtypes = [
+                SP, I32, P, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+            getattr(lib, "pa_append_decode_attention_worklist" + sfx).argtypes = [
+                SP, I32, P, P, P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I32, P, I32, P, SZ,
+                P]
         lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
         lib.pa_decode_worklist.argtypes = [SP, I32, P, I32, I32, I32, I32, P, I32,
                                            ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -110,9 +119,6 @@ def load_library(path: str | None = None):
         lib.pa_append_decode_attention_worklist.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
                                                             ctypes.c_float, P, I32, I32, P, I32,
                                                             P, SZ, P]
-        lib.pa_append_decode_attention_worklist_q8.argtypes = [SP, I32, P, P, P, P, P, P, P, P,
-                                                               I32, ctypes.c_float, P, I32, I32,
-                                                               P, I32, P, SZ, P]
         I64 = ctypes.c_int64
         PP = ctypes.POINTER(ctypes.c_void_p)
         lib.pa_kvpool_create.argtypes = [I32, I32, I32, I32, I32, PP]
@@ -132,22 +138,9 @@ def load_library(path: str | None = None):
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_abi_version.argtypes = []
-        for name in ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan",
-                     "pa_decode_plan_lengths",
-                     "pa_decode_attention", "pa_decode_attention_profiled",
-                     "pa_append_decode_attention", "pa_append_kv_rope",
-                     "pa_append_decode_attention_rope", "pa_validate_metadata",
-                     "pa_abi_version", "pa_fill_kv", "pa_kvpool_create", "pa_kvpool_destroy",
-                     "pa_kvpool_credit", "pa_kvpool_submit", "pa_kvpool_admit",
-                     "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
-                     "pa_kvpool_block_table", "pa_kvpool_request_info",
-                     "pa_kvpool_get_stats", "pa_append_kv_q8", "pa_append_kv_rope_q8",
-                     "pa_fill_kv_q8", "pa_decode_attention_q8", "pa_append_decode_attention_q8",
-                     "pa_append_decode_attention_rope_q8", "pa_decode_plan_lengths_q8",
-                     "pa_stream_read", "pa_decode_worklist",
-                     "pa_append_decode_attention_worklist",
-                     "pa_append_decode_attention_worklist_q8"):
-            getattr(lib, name).restype = ctypes.c_int
+        for name in EXPORTS:
+            if name != "pa_status_string":
+                getattr(lib, name).restype = ctypes.c_int
         if path == _build.LIB:
             _lib = lib
         return lib
@@ -430,8 +423,12 @@ def fill_kv(k_rows, v_rows, block_table_row, start: int, k_pool, v_pool, stream=
 
 
 # ---------------------------------------------------------------------------
-# INT8 K/V pages (include/pa_decode_q8.h)
+# INT8 and INT4 K/V pages (include/pa_decode_q8.h, include/pa_decode_q4.h).
+# The INT4 functions take the same arguments as their INT8 namesakes.
 # ---------------------------------------------------------------------------
+_SUFFIX = {8: "_q8", 4: "_q4"}
+
+
 def new_q8_pools(num_pages: int, device="cuda"):
     """Zeroed INT8 pools: K codes, V codes (int8 ``[pages][8][16][64]``, head-major
     within a page) and scales (float32 ``[pages][8][2][16]``)."""
@@ -441,11 +438,22 @@ def new_q8_pools(num_pages: int, device="cuda"):
             torch.zeros((num_pages, HKV, 2, PAGE), dtype=torch.float32, device=device))
 
 
-def _q8_pools(k_codes, v_codes, kv_scales) -> int:
+def new_q4_pools(num_pages: int, device="cuda"):
+    """Zeroed INT4 pools: K codes, V codes (uint8 ``[pages][8][16][32]``, two codes
+    per byte) and scales (float32 ``[pages][8][2][16]``)."""
+    codes = (num_pages, HKV, PAGE, D // 2)
+    return (torch.zeros(codes, dtype=torch.uint8, device=device),
+            torch.zeros(codes, dtype=torch.uint8, device=device),
+            torch.zeros((num_pages, HKV, 2, PAGE), dtype=torch.float32, device=device))
+
+
+def _q8_pools(k_codes, v_codes, kv_scales, nbits: int = 8) -> int:
+    dtype, width = (torch.int8, D) if nbits == 8 else (torch.uint8, D // 2)
     for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
-        if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() or \
-                tuple(t.shape[1:]) != (HKV, PAGE, D):
-            raise ValueError(f"{name}: must be a contiguous int8 [pages][8][16][64] device tensor")
+        if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or \
+                tuple(t.shape[1:]) != (HKV, PAGE, width):
+            raise ValueError(f"{name}: must be a contiguous {str(dtype)[6:]} "
+                             f"[pages][8][16][{width}] device tensor")
     if k_codes.shape != v_codes.shape:
         raise ValueError("k_codes and v_codes differ in shape")
     n = int(k_codes.shape[0])
@@ -456,22 +464,23 @@ def _q8_pools(k_codes, v_codes, kv_scales) -> int:
 
 
 def append_kv_q8(k_new, v_new, k_codes, v_codes, kv_scales, block_tables, seq_lens,
-                 stream=None) -> None:
+                 stream=None, nbits: int = 8) -> None:
     """Quantise each sequence's new K/V row (``[B][8][64]`` BF16) into its page slot."""
     B = int(seq_lens.shape[0])
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
     if k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("batch dimension mismatch")
-    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales), int(block_tables.shape[1]))
-    rc = load_library().pa_append_kv_q8(
+    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales, nbits), int(block_tables.shape[1]))
+    fn = "pa_append_kv" + _SUFFIX[nbits]
+    rc = getattr(load_library(), fn)(
         ctypes.byref(shape), B, _ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(v_codes),
         _ptr(kv_scales), _ptr(block_tables), _ptr(seq_lens), _stream_ptr(stream))
-    _check(rc, "pa_append_kv_q8")
+    _check(rc, fn)
 
 
 def append_kv_rope_q8(q, k_new, v_new, rope_cos, rope_sin, k_codes, v_codes, kv_scales,
-                      block_tables, seq_lens, q_out=None, stream=None):
+                      block_tables, seq_lens, q_out=None, stream=None, nbits: int = 8):
     """Rotate the new q/k at position L-1, quantise K/V into the slot; returns ``q_out``."""
     B = int(seq_lens.shape[0])
     _bits16(q, "q", (HQ, D))
@@ -483,32 +492,35 @@ def append_kv_rope_q8(q, k_new, v_new, rope_cos, rope_sin, k_codes, v_codes, kv_
         q_out = torch.empty_like(q)
     _bits16(q_out, "q_out", (HQ, D))
     rope = _rope(rope_cos, rope_sin)
-    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales), int(block_tables.shape[1]))
-    rc = load_library().pa_append_kv_rope_q8(
+    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales, nbits), int(block_tables.shape[1]))
+    fn = "pa_append_kv_rope" + _SUFFIX[nbits]
+    rc = getattr(load_library(), fn)(
         ctypes.byref(shape), B, _ptr(q), _ptr(k_new), _ptr(v_new), ctypes.byref(rope),
         _ptr(q_out), _ptr(k_codes), _ptr(v_codes), _ptr(kv_scales), _ptr(block_tables),
         _ptr(seq_lens), _stream_ptr(stream))
-    _check(rc, "pa_append_kv_rope_q8")
+    _check(rc, fn)
     return q_out
 
 
 def fill_kv_q8(k_rows, v_rows, block_table_row, start: int, k_codes, v_codes, kv_scales,
-               stream=None) -> None:
+               stream=None, nbits: int = 8) -> None:
     """Quantised prefill fill: tokens ``start .. start+T-1`` of one sequence."""
     _bits16(k_rows, "k_rows", (HKV, D)); _bits16(v_rows, "v_rows", (HKV, D))
     _i32(block_table_row, "block_table_row")
     if k_rows.shape != v_rows.shape:
         raise ValueError("k_rows and v_rows differ in shape")
-    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales), int(block_table_row.shape[-1]))
-    rc = load_library().pa_fill_kv_q8(ctypes.byref(shape), _ptr(k_rows), _ptr(v_rows),
-                                      int(k_rows.shape[0]), int(start), _ptr(block_table_row),
-                                      _ptr(k_codes), _ptr(v_codes), _ptr(kv_scales),
-                                      _stream_ptr(stream))
-    _check(rc, "pa_fill_kv_q8")
+    shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales, nbits),
+                       int(block_table_row.shape[-1]))
+    fn = "pa_fill_kv" + _SUFFIX[nbits]
+    rc = getattr(load_library(), fn)(ctypes.byref(shape), _ptr(k_rows), _ptr(v_rows),
+                                     int(k_rows.shape[0]), int(start), _ptr(block_table_row),
+                                     _ptr(k_codes), _ptr(v_codes), _ptr(kv_scales),
+                                     _stream_ptr(stream))
+    _check(rc, fn)
 
 
 def decode_plan_lengths_q8(seq_lens_host, num_pages: int, max_blocks: int = 128,
-                           max_seq_len: int | None = None, num_cus: int = 0):
+                           max_seq_len: int | None = None, num_cus: int = 0, nbits: int = 8):
     """(pages_per_split, splits) for INT8 pages from host sequence lengths."""
     import numpy as np
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
@@ -516,15 +528,17 @@ def decode_plan_lengths_q8(seq_lens_host, num_pages: int, max_blocks: int = 128,
         max_seq_len = int(lens.max()) if lens.size else 0
     shape = make_shape(num_pages, max_blocks)
     ps, ns = ctypes.c_int32(), ctypes.c_int32()
-    rc = load_library().pa_decode_plan_lengths_q8(
+    fn = "pa_decode_plan_lengths" + _SUFFIX[nbits]
+    rc = getattr(load_library(), fn)(
         ctypes.byref(shape), int(lens.size), lens.ctypes.data_as(ctypes.c_void_p),
         int(max_seq_len), int(num_cus), ctypes.byref(ps), ctypes.byref(ns))
-    _check(rc, "pa_decode_plan_lengths_q8")
+    _check(rc, fn)
     return ps.value, ns.value
 
 
 def _decode_q8(fn, q, k_new, v_new, rope, k_codes, v_codes, kv_scales, block_tables, seq_lens,
-               max_seq_len, scale, out, out_dtype, pages_per_split, workspace, stream):
+               max_seq_len, scale, out, out_dtype, pages_per_split, workspace, stream, nbits=8):
+    fn += _SUFFIX[nbits]
     B = int(seq_lens.shape[0])
     _bits16(q, "q", (HQ, D))
     if k_new is not None:
@@ -534,7 +548,7 @@ def _decode_q8(fn, q, k_new, v_new, rope, k_codes, v_codes, kv_scales, block_tab
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
     if q.shape[0] != B or block_tables.shape[0] != B:
         raise ValueError("batch dimension mismatch")
-    num_pages = _q8_pools(k_codes, v_codes, kv_scales)
+    num_pages = _q8_pools(k_codes, v_codes, kv_scales, nbits)
     code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
     if code is None:
         raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
@@ -561,34 +575,68 @@ def _decode_q8(fn, q, k_new, v_new, rope, k_codes, v_codes, kv_scales, block_tab
 
 def decode_attention_q8(q, k_codes, v_codes, kv_scales, block_tables, seq_lens, max_seq_len: int,
                         scale: float = 0.125, out=None, out_dtype=torch.float32,
-                        pages_per_split: int = 0, workspace=None, stream=None):
-    """Decode attention over INT8 pages; returns ``out`` ``[B][32][64]``."""
-    return _decode_q8("pa_decode_attention_q8", q, None, None, None, k_codes, v_codes, kv_scales,
+                        pages_per_split: int = 0, workspace=None, stream=None, nbits: int = 8):
+    """Decode attention over INT8 (or ``nbits=4``: INT4) pages; returns ``out`` ``[B][32][64]``."""
+    return _decode_q8("pa_decode_attention", q, None, None, None, k_codes, v_codes, kv_scales,
                       block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
-                      pages_per_split, workspace, stream)
+                      pages_per_split, workspace, stream, nbits)
 
 
 def append_decode_attention_q8(q, k_new, v_new, k_codes, v_codes, kv_scales, block_tables,
                                seq_lens, max_seq_len: int, scale: float = 0.125, out=None,
                                out_dtype=torch.float32, pages_per_split: int = 0,
-                               workspace=None, stream=None, rope_cos=None, rope_sin=None):
+                               workspace=None, stream=None, rope_cos=None, rope_sin=None,
+                               nbits: int = 8):
     """Fused quantised decode step (optionally with RoPE of the new q/k); returns ``out``."""
     if (rope_cos is None) != (rope_sin is None):
         raise ValueError("give both rope_cos and rope_sin, or neither")
     if rope_cos is None:
-        return _decode_q8("pa_append_decode_attention_q8", q, k_new, v_new, None, k_codes,
+        return _decode_q8("pa_append_decode_attention", q, k_new, v_new, None, k_codes,
                           v_codes, kv_scales, block_tables, seq_lens, max_seq_len, scale, out,
-                          out_dtype, pages_per_split, workspace, stream)
-    return _decode_q8("pa_append_decode_attention_rope_q8", q, k_new, v_new,
+                          out_dtype, pages_per_split, workspace, stream, nbits)
+    return _decode_q8("pa_append_decode_attention_rope", q, k_new, v_new,
                       _rope(rope_cos, rope_sin), k_codes, v_codes, kv_scales, block_tables,
                       seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, workspace,
-                      stream)
+                      stream, nbits)
+
+
+def append_kv_q4(*args, **kw) -> None:
+    """INT4 pages: ``append_kv_q8`` with ``[pages][8][16][32]`` uint8 code pools."""
+    return append_kv_q8(*args, nbits=4, **kw)
+
+
+def append_kv_rope_q4(*args, **kw):
+    """INT4 pages: ``append_kv_rope_q8`` with INT4 code pools."""
+    return append_kv_rope_q8(*args, nbits=4, **kw)
+
+
+def fill_kv_q4(*args, **kw) -> None:
+    """INT4 pages: ``fill_kv_q8`` with INT4 code pools."""
+    return fill_kv_q8(*args, nbits=4, **kw)
+
+
+def decode_plan_lengths_q4(*args, **kw):
+    """INT4 pages: ``decode_plan_lengths_q8`` with the INT4 cost model."""
+    return decode_plan_lengths_q8(*args, nbits=4, **kw)
+
+
+def decode_attention_q4(*args, **kw):
+    """INT4 pages: ``decode_attention_q8`` with INT4 code pools."""
+    return decode_attention_q8(*args, nbits=4, **kw)
+
+
+def append_decode_attention_q4(*args, **kw):
+    """INT4 pages: ``append_decode_attention_q8`` with INT4 code pools."""
+    return append_decode_attention_q8(*args, nbits=4, **kw)
 
 
 def decode_worklist(seq_lens_host, num_pages: int, max_blocks: int = 128,
                     max_seq_len: int | None = None, pages_per_split: int = 0,
-                    int8: bool = False, num_cus: int = 0):
-    """Longest-first work list for host lengths: (work int32 [n][2], pages_per_split, splits)."""
+                    int8: bool = False, num_cus: int = 0, int4: bool = False):
+    """Longest-first work list for host lengths: (work int32 [n][2], pages_per_split, splits).
+    ``int8`` / ``int4`` pick the planner's cost model for those page formats."""
+    if int8 and int4:
+        raise ValueError("int8 and int4 are exclusive")
     import numpy as np
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     if max_seq_len is None:
@@ -599,7 +647,7 @@ def decode_worklist(seq_lens_host, num_pages: int, max_blocks: int = 128,
     count, ps, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     rc = load_library().pa_decode_worklist(
         ctypes.byref(shape), int(lens.size), lens.ctypes.data_as(ctypes.c_void_p),
-        int(max_seq_len), int(pages_per_split), 1 if int8 else 0, int(num_cus),
+        int(max_seq_len), int(pages_per_split), 2 if int4 else (1 if int8 else 0), int(num_cus),
         work.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(count), ctypes.byref(ps),
         ctypes.byref(ns))
     _check(rc, "pa_decode_worklist")
@@ -611,7 +659,7 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
                                      scale: float = 0.125, out=None, out_dtype=torch.float32,
                                      workspace=None, stream=None, kv_scales=None):
     """Decode step over a device work list (``decode_worklist``); k_new/v_new may be None
-    (decode only).  With ``kv_scales`` the pools are INT8 code pools."""
+    (decode only).  With ``kv_scales`` the pools are INT8 (int8) or INT4 (uint8) code pools."""
     B = int(seq_lens.shape[0])
     _bits16(q, "q", (HQ, D))
     if (k_new is None) != (v_new is None):
@@ -623,7 +671,8 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
     if work.dim() != 2 or work.shape[1] != 2 or work.shape[0] < 1:
         raise ValueError("work: int32 [n][2] device tensor with n >= 1")
     q8 = kv_scales is not None
-    num_pages = _q8_pools(k_pool, v_pool, kv_scales) if q8 else int(k_pool.shape[0])
+    nbits = 4 if q8 and k_pool.dtype == torch.uint8 else 8
+    num_pages = _q8_pools(k_pool, v_pool, kv_scales, nbits) if q8 else int(k_pool.shape[0])
     if not q8:
         _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
     code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
@@ -639,7 +688,7 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
     nk = _ptr(k_new) if k_new is not None else None
     nv = _ptr(v_new) if v_new is not None else None
     pools = [_ptr(k_pool), _ptr(v_pool)] + ([_ptr(kv_scales)] if q8 else [])
-    fn = "pa_append_decode_attention_worklist_q8" if q8 else "pa_append_decode_attention_worklist"
+    fn = "pa_append_decode_attention_worklist" + (_SUFFIX[nbits] if q8 else "")
     rc = getattr(load_library(), fn)(
         ctypes.byref(shape), B, _ptr(q), nk, nv, *pools, _ptr(block_tables), _ptr(seq_lens),
         int(max_seq_len), float(scale), _ptr(out), code, int(pages_per_split), _ptr(work),

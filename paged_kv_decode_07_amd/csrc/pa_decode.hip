@@ -525,7 +525,7 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   // a batch that fits the compute units merges with its partials requested up front
   int cu = 0;
   const bool merge_preload = current_cu_count(&cu) == PA_OK && batch <= cu;
-  const hipError_t e = pa::launch_decode<false>(a, batch, out_dtype == PA_OUT_BF16, fused,
+  const hipError_t e = pa::launch_decode<pa::kFmtBF16>(a, batch, out_dtype == PA_OUT_BF16, fused,
                                                 rope != nullptr, merge_preload, (hipStream_t)stream,
                                                 (hipEvent_t)event_before_main,
                                                 (hipEvent_t)event_after_main);
@@ -617,10 +617,12 @@ PA_API int pa_decode_worklist(const pa_shape* shape, int32_t batch, const int32_
   int rc = check_decode_sizes(shape, batch, max_seq_len);
   if (rc != PA_OK) return rc;
   if (!count || (batch > 0 && (!seq_lens_host || !work))) return PA_ERR_NULL;
-  if (capacity < 0 || num_cus < 0 || (page_format != 0 && page_format != 1)) return PA_ERR_VALUE;
+  if (capacity < 0 || num_cus < 0 || page_format < 0 || page_format > 2) return PA_ERR_VALUE;
   int ps = pages_per_split, ns = 1;
   if (batch > 0 && ps == 0) {
-    const PlanModel model = page_format == 1 ? plan_model_q8() : PlanModel();
+    const PlanModel model = page_format == 1   ? plan_model_q8()
+                            : page_format == 2 ? plan_model_q4()
+                                               : PlanModel();
     rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, model, &ps, &ns,
                             true);
     if (rc != PA_OK) return rc;

@@ -1,5 +1,5 @@
 // Decode kernel of the paged GQA decode library for gfx950 (CDNA4, wave64),
-// for BF16 pages and INT8 pages.
+// for BF16, INT8 and INT4 pages.
 //
 // Work decomposition: one work-group per (sequence b, split s); a split is a
 // run of at most `pages_per_split` consecutive logical pages of sequence b.
@@ -15,7 +15,8 @@
 // slots, so explicit vmcnt waits are the only synchronisation.  The split's
 // block-table entries are preloaded into VGPRs and picked with v_readlane.
 // Every load instruction requests whole 128-byte lines (BF16: 8 token rows
-// of the head; INT8: the head's 1 KiB code block), with the non-temporal
+// of the head; INT8: the head's 1 KiB code block; INT4: the head's K and V
+// blocks of 512 bytes, one per half-wave), with the non-temporal
 // policy: on this part that pair streams 10-12% faster than half-line
 // requests or the default policy.
 //
@@ -57,6 +58,16 @@
 // to BF16 exactly and the V scale joins the weight (w * v_scale), while the
 // normaliser sums w alone.
 //
+// INT4 pages: a nibble u = code + 8 becomes the BF16 value 16 + u = code + 24
+// with two bit operations per pair (no conversion instruction); the bias is
+// removed after each product.  Scores: 24 x (the sum of the query row) is
+// subtracted before the K scale.  Values: each lane also sums its weights
+// (w * v_scale), rescaled with the accumulators, and 24 x that sum is
+// subtracted from the output.  The packed K word gives its dims in the order
+// 0 4 1 5 2 6 3 7, and the query operand is permuted to match.  One
+// transposed read gives a lane 4 tokens x 4 dims (the 16-bit unit is 4
+// codes), so tile e of the value product is dims 4n + e.
+//
 // Masking: slots past the sequence in its last page may hold any bits.  Their
 // scores are selected to -inf, their weights to 0, and for BF16 pages their V
 // values are replaced by zeros before the product (0 * NaN would be NaN).
@@ -73,9 +84,9 @@ typedef short bf16x4_t __attribute__((ext_vector_type(4)));
 // Arguments of the decode kernel (either page format).
 struct DecodeArgs {
   const uint16_t* q;
-  const void* k_pool;          // BF16 [pages][16][8][64] or int8 codes [pages][8][16][64]
-  const void* v_pool;
-  const float* kv_scales;      // INT8 only: [pages][8][2][16]
+  const void* k_pool;          // BF16 [pages][16][8][64], int8 codes [pages][8][16][64]
+  const void* v_pool;          // or INT4 code bytes [pages][8][16][32]
+  const float* kv_scales;      // INT8 and INT4: [pages][8][2][16]
   const uint16_t* k_new;       // fused append: [B][8][64] BF16 rows
   const uint16_t* v_new;
   void* k_pool_w;              // fused append: the same pools, written at slot L-1
@@ -103,10 +114,10 @@ struct DecodeArgs {
 };
 
 // Page-format constants of the LDS ring (per wavefront slot).
-template <bool Q8>
+template <int FMT>
 struct PageFormat;
 template <>
-struct PageFormat<false> {
+struct PageFormat<kFmtBF16> {
   static constexpr int kRingDepth = kRing;      // 2 slots of 4 KiB
   static constexpr int kSlot = 4096;            // [K | V] x 16 token rows x 128 B (swizzled pieces)
   static constexpr int kLoads = 4;              // direct-to-LDS loads per page
@@ -123,10 +134,16 @@ __device__ __forceinline__ constexpr uint32_t bf16_slot_offset(int t, int p) {
   return (uint32_t)(16 * (8 * t + (p ^ (t >> 1))));
 }
 template <>
-struct PageFormat<true> {
+struct PageFormat<kFmtINT8> {
   static constexpr int kRingDepth = kRingQ8;    // slots of 2304 B
   static constexpr int kSlot = kSlotQ8;         // [K codes 16 x 64 B | V codes 16 x 64 B | scales]
   static constexpr int kLoads = 3;
+};
+template <>
+struct PageFormat<kFmtINT4> {
+  static constexpr int kRingDepth = kRingQ4;    // slots of 1280 B
+  static constexpr int kSlot = kSlotQ4;         // [K codes 16 x 32 B | V codes 16 x 32 B | scales]
+  static constexpr int kLoads = 2;              // K and V codes in one load, the scales
 };
 
 // Registers of one page for one lane.
@@ -141,6 +158,11 @@ struct SlotAddrBF16 {
 struct PageQ8 {
   u32x2 k0, k1;       // K codes, 8 dims each
   u32x2 v[2];         // V codes: 4 tokens x (even, odd) dim pairs, dims 0..31 and 32..63
+  u32x4 ks, vs;       // K and V scales of tokens 4G .. 4G+3
+};
+struct PageQ4 {
+  uint32_t k0, k1;    // K codes of token n, dims 8G .. 8G+7 and 32+8G .. 32+8G+7
+  u32x2 v;            // V codes: 4 tokens x dims 4n .. 4n+3 (transposed read)
   u32x4 ks, vs;       // K and V scales of tokens 4G .. 4G+3
 };
 
@@ -182,6 +204,24 @@ __device__ __forceinline__ void lds_page_ready(PageQ8& r) {
                : "+v"(r.k0), "+v"(r.k1), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ks), "+v"(r.vs)::"memory");
 }
 
+// kaddr: K codes of (token n, dims 8G..); vaddr: V chunk of this lane; saddr: scales + 16 G.
+__device__ __forceinline__ void lds_page_issue(PageQ4& r, uint32_t kaddr, uint32_t vaddr,
+                                         uint32_t saddr) {
+  asm volatile(
+      "ds_read_b32 %0, %5\n\t"
+      "ds_read_b32 %1, %5 offset:16\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "ds_read_b128 %4, %7 offset:64"
+      : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v), "=&v"(r.ks), "=&v"(r.vs)
+      : "v"(kaddr), "v"(vaddr), "v"(saddr)
+      : "memory");
+}
+__device__ __forceinline__ void lds_page_ready(PageQ4& r) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r.k0), "+v"(r.k1), "+v"(r.v), "+v"(r.ks), "+v"(r.vs)::"memory");
+}
+
 // 4 INT8 codes (bytes b0..b3 of w) -> BF16 pairs (b0, b2) and (b1, b3): the
 // even-dim and odd-dim values of two tokens when w holds (t, even), (t, odd),
 // (t+1, even), (t+1, odd).
@@ -192,17 +232,22 @@ __device__ __forceinline__ void codes_even_odd(uint32_t w, uint32_t& even, uint3
 
 // Running state of one lane: the accumulators of the P V products (4 tiles
 // of 16 x 16, this lane's rows 4G .. 4G+3 of column n), the head's running
-// maximum m (log2 units, same in all lanes of the head) and this lane's
-// partial normaliser l.
+// maximum m (log2 units, same in all lanes of the head), this lane's
+// partial normaliser l and, for INT4 pages, its partial sum of weights wsum.
 struct LaneState {
   f32x4_t acc[4];
   float m;
   float l;
+  float wsum;
 };
 
-template <bool Q8, bool MASK, typename Page>
+// qbias (INT4 pages): 24 x the sum of this lane's query row
+template <int FMT, bool MASK, typename Page>
 __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t qlo, bf16x8_t qhi,
-                                           float xscale, int lane, int valid) {
+                                           float xscale, float qbias, int lane, int valid) {
+  constexpr bool Q8 = FMT == kFmtINT8;
+  constexpr bool Q4 = FMT == kFmtINT4;
+  constexpr bool QUANT = Q8 || Q4;
   const int G = lane >> 4;            // token group: tokens 4G .. 4G+3
   const int n = lane & 15;            // head slot (query head 4g + n%4); P row
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -210,6 +255,9 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
   if constexpr (Q8) {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k0), qlo, zero, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k1), qhi, s, 0, 0, 0);
+  } else if constexpr (Q4) {
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nibbles_to_bf16x8(r.k0), qlo, zero, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nibbles_to_bf16x8(r.k1), qhi, s, 0, 0, 0);
   } else {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k0), qlo, zero, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k1), qhi, s, 0, 0, 0);
@@ -218,8 +266,8 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     float xs = xscale;
-    if constexpr (Q8) xs = xscale * __uint_as_float(r.ks[c]);
-    x[c] = s[c] * xs;
+    if constexpr (QUANT) xs = xscale * __uint_as_float(r.ks[c]);
+    x[c] = (Q4 ? s[c] - qbias : s[c]) * xs;
     if (MASK) x[c] = (4 * G + c < valid) ? x[c] : -INFINITY;
   }
   const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -232,6 +280,7 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
     const float a = __builtin_amdgcn_exp2f(st.m - mn);    // m = -inf -> 0
     st.m = mn;
     st.l *= a;
+    if constexpr (Q4) st.wsum *= a;
     // rows 4G + r of this lane's tiles belong to head r (rows 0..7)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -245,12 +294,13 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
   for (int c = 0; c < 4; ++c) {
     p[c] = __builtin_amdgcn_exp2f(x[c] - st.m);           // masked: exp2(-inf) = 0
     w[c] = p[c];
-    if constexpr (Q8) {
+    if constexpr (QUANT) {
       w[c] = p[c] * __uint_as_float(r.vs[c]);
       if (MASK) w[c] = (4 * G + c < valid) ? w[c] : 0.f;  // scale bits of a dead slot
     }
   }
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (Q4) st.wsum += (w[0] + w[1]) + (w[2] + w[3]);
   // A operand: rows 0..3 the BF16 weights, rows 4..7 their remainders
   // (weight - its BF16 value is exact in FP32, then rounded again), rows
   // 8..15 zero.  Every lane computes both and selects, so the wave does not
@@ -263,7 +313,22 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
   pa.x = n < 4 ? h01 : (n < 8 ? r01 : 0u);
   pa.y = n < 4 ? h23 : (n < 8 ? r23 : 0u);
   const bf16x4_t A = __builtin_bit_cast(bf16x4_t, pa);
-  if constexpr (Q8) {
+  if constexpr (Q4) {
+    // tile e: dim 4n + e of tokens 4G .. 4G+3 (nibble e of each 16-bit unit);
+    // dead slots hold finite values code + 24 and weight 0
+    st.acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<0>(r.v.x), nibble_pair_bf16<0>(r.v.y)}),
+        st.acc[0], 0, 0, 0);
+    st.acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<1>(r.v.x), nibble_pair_bf16<1>(r.v.y)}),
+        st.acc[1], 0, 0, 0);
+    st.acc[2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<2>(r.v.x), nibble_pair_bf16<2>(r.v.y)}),
+        st.acc[2], 0, 0, 0);
+    st.acc[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<3>(r.v.x), nibble_pair_bf16<3>(r.v.y)}),
+        st.acc[3], 0, 0, 0);
+  } else if constexpr (Q8) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t e0, o0, e1, o1;
@@ -290,10 +355,12 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
 }
 
 // Output dim of column n of tile b: BF16 pages, tile b = dims 16b .. 16b+15;
-// INT8 pages, tile 2h + e = dims 32h + 8(n/4) + 2(n%4) + e.
-template <bool Q8>
+// INT8 pages, tile 2h + e = dims 32h + 8(n/4) + 2(n%4) + e; INT4 pages, tile
+// e = dims 4n + e.
+template <int FMT>
 __device__ __forceinline__ int out_dim(int b, int n) {
-  if constexpr (Q8) return 32 * (b >> 1) + 8 * (n >> 2) + 2 * (n & 3) + (b & 1);
+  if constexpr (FMT == kFmtINT8) return 32 * (b >> 1) + 8 * (n >> 2) + 2 * (n & 3) + (b & 1);
+  if constexpr (FMT == kFmtINT4) return 4 * n + b;
   return 16 * b + n;
 }
 
@@ -304,10 +371,13 @@ __device__ __forceinline__ int out_dim(int b, int n) {
 #endif
 constexpr int kStreamCpol = PA_STREAM_CPOL;
 
-template <bool Q8, bool OUT_BF16, bool APPEND, bool ROPE = false>
+template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
-  using F = PageFormat<Q8>;
+  constexpr bool Q8 = FMT == kFmtINT8;
+  constexpr bool Q4 = FMT == kFmtINT4;
+  constexpr bool QUANT = Q8 || Q4;
+  using F = PageFormat<FMT>;
   // a one-dimensional grid: block k is split k % S of sequence k / S (the
   // same dispatch order as a (S, B) grid, without its limit on B)
   int b = (int)(blockIdx.x / (unsigned)a.num_splits);
@@ -378,18 +448,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   // B operand of the score product (set after the first page requests)
   bf16x8_t qlo, qhi;
 
+  float qbias = 0.f;             // INT4 pages: 24 x the sum of the query row
+
   // fused append: the new rows (K rotated first with RoPE) are parked in LDS,
-  // as BF16 rows or as INT8 codes and scales, after the first page requests
+  // as BF16 rows or as codes and scales, after the first page requests
   const bool app_here = APPEND && p1 == n_pages;
   const int app_slot = (L - 1) % kPage;
-  __shared__ u32x4 new_rows[APPEND ? kWaves : 1][Q8 ? 8 : 16];   // 16-byte chunks
-  __shared__ float new_scales[APPEND && Q8 ? kWaves : 1][2];
+  __shared__ u32x4 new_rows[APPEND ? kWaves : 1][QUANT ? 8 : 16];   // 16-byte chunks
+  __shared__ float new_scales[APPEND && QUANT ? kWaves : 1][2];
 
   LaneState st;
 #pragma unroll
   for (int t = 0; t < 4; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
+  st.wsum = 0.f;
 
   // ent[] (loaded above) holds the window's entries; only those up to
   // `last` are ever picked
@@ -415,12 +488,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const char* s_base = reinterpret_cast<const char*>(a.kv_scales);
   // DMA lane offsets (bytes within a page): INT8 lane l takes bytes 16 l of
   // the head's code block (token l/4, dims 16 (l%4) ..) and float l%32 of its
-  // scale line; BF16 load j (tokens 8j .. 8j+7) has lane l take token
+  // scale line; INT4 lane l takes bytes 16 (l%32) of the head's K (l < 32) or
+  // V block, and the same scale float; BF16 load j (tokens 8j .. 8j+7) has lane l take token
   // t = 8j + l/8 and the piece whose swizzled position is l%8, so that lane l
   // lands at byte bf16_slot_offset(t, that piece) - 1024 j of its destination
   uint32_t dma_k, dma_k1 = 0, dma_s = 0;
+  const char* kv_base = k_base;
   if constexpr (Q8) {
     dma_k = (uint32_t)(g * kHeadCodes + 16 * lane);                 // the head's 1 KiB block
+    dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
+  } else if constexpr (Q4) {
+    kv_base = lane < 32 ? k_base : v_base;
+    dma_k = (uint32_t)(g * kHeadCodes4 + 16 * (lane & 31));         // 512 B of K, 512 B of V
     dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
   } else {
     const int t0 = lane >> 3, t1 = 8 + (lane >> 3);
@@ -436,6 +515,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 1024, 16, 0, kStreamCpol);
       __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + dma_s,
                                        dst + 2048, 4, 0, kStreamCpol);
+    } else if constexpr (Q4) {
+      __builtin_amdgcn_global_load_lds(kv_base + id * (int64_t)kPageCodes4 + dma_k, dst, 16, 0,
+                                       kStreamCpol);
+      __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + dma_s,
+                                       dst + 1024, 4, 0, kStreamCpol);
     } else {
       const int64_t off = id * (int64_t)(kPageElems * 2);
       __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
@@ -454,6 +538,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     ka = slot0 + 64 * n + 8 * G;
     va = slot0 + 1024 + 64 * (4 * G + jq) + 8 * jr;
     sa = slot0 + 2048 + 16 * G;
+  } else if constexpr (Q4) {
+    // K: token n, bytes 4G (dims 8G ..) and 16 + 4G; V: dims 16 jr .. 16 jr + 15
+    // of token 4G + jq, so that lane n receives dims 4n .. 4n+3 of 4 tokens
+    ka = slot0 + 32 * n + 4 * G;
+    va = slot0 + 512 + 32 * (4 * G + jq) + 8 * jr;
+    sa = slot0 + 1024 + 16 * G;
   } else {
     // K: token n, pieces G and G + 4; V block b (dims 16b .. 16b+15): dims
     // 4 jr .. 4 jr + 3 of token 4G + jq are bytes 8 (jr % 2) of piece 2b + jr/2
@@ -467,17 +557,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   auto park_new_row = [&](uint32_t slot_base) {
     // overwrite the appended token's slot in the ring with the new row
     const int sl = APPEND ? g : 0;
-    if constexpr (Q8) {
+    if constexpr (QUANT) {
+      using QL = QuantLayout<Q8 ? kFmtINT8 : kFmtINT4>;
       if (lane < 8) {
         const u32x4 w = new_rows[sl][lane];
-        const int c = lane & 3;
-        char* base = &ring[0][g][0] + (slot_base - slot0) + (lane < 4 ? 0 : 1024) + 64 * app_slot + 8 * c;
-        *reinterpret_cast<u32x2*>(base) = u32x2{w.x, w.y};
-        *reinterpret_cast<u32x2*>(base + 32) = u32x2{w.z, w.w};
+        uint8_t* row = reinterpret_cast<uint8_t*>(&ring[0][g][0]) + (slot_base - slot0) +
+                       (lane < 4 ? 0 : QL::kHead) + QL::kRow * app_slot;
+        store_quad_codes<FMT>(row, lane & 3, u32x2{w.x, w.y}, u32x2{w.z, w.w});
       }
       if (lane < 2) {
-        float* sp = reinterpret_cast<float*>(&ring[0][g][0] + (slot_base - slot0) + 2048);
-        sp[lane * 16 + app_slot] = new_scales[APPEND && Q8 ? g : 0][lane];
+        float* sp = reinterpret_cast<float*>(&ring[0][g][0] + (slot_base - slot0) + 2 * QL::kHead);
+        sp[lane * 16 + app_slot] = new_scales[APPEND && QUANT ? g : 0][lane];
       }
     } else {
       if (lane < 16) {
@@ -503,13 +593,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       lds_page_issue(cur, ka + off, va + off, sa + off);
       lds_page_ready(cur);
       if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
-      consume_page<true, MASK>(st, cur, qlo, qhi, a.xscale, lane, MASK ? tail_valid : kPage);
+      consume_page<FMT, MASK>(st, cur, qlo, qhi, a.xscale, qbias, lane, MASK ? tail_valid : kPage);
+    } else if constexpr (Q4) {
+      PageQ4 cur;
+      lds_page_issue(cur, ka + off, va + off, sa + off);
+      lds_page_ready(cur);
+      if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
+      consume_page<FMT, MASK>(st, cur, qlo, qhi, a.xscale, qbias, lane, MASK ? tail_valid : kPage);
     } else {
       PageBF16 cur;
       lds_page_issue(cur, ad, off);
       lds_page_ready(cur);
       if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
-      consume_page<false, MASK>(st, cur, qlo, qhi, a.xscale, lane, MASK ? tail_valid : kPage);
+      consume_page<FMT, MASK>(st, cur, qlo, qhi, a.xscale, qbias, lane, MASK ? tail_valid : kPage);
     }
   };
 
@@ -531,6 +627,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       const int64_t row = (int64_t)(L - 1) * (kD / 2) + 8 * G;
       rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
     }
+    if constexpr (Q4) {
+      // the row's sum (all 64 dims: this lane's 16, then the 4 token groups)
+      float sum = 0.f;
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum += bf16_lo(w[k]) + bf16_hi(w[k]);
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      qbias = kNibbleBias4 * sum;
+      lo = interleave_halves8(lo);
+      hi = interleave_halves8(hi);
+    }
     qlo = __builtin_bit_cast(bf16x8_t, lo);
     qhi = __builtin_bit_cast(bf16x8_t, hi);
   }
@@ -544,11 +652,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     }
     const int slot = APPEND ? g : 0;
     const uint32_t rows = lds_address(&new_rows[slot][0]);
-    if constexpr (Q8) {
+    if constexpr (QUANT) {
       u32x2 clo, chi;
-      const float sc = quantize_quad_row(lo, hi, clo, chi);
+      const float sc = quantize_quad_row<FMT>(lo, hi, clo, chi);
       lds_store16(rows + 16 * lane, u32x4{clo.x, clo.y, chi.x, chi.y});
-      if (c == 0) lds_store4(lds_address(&new_scales[APPEND && Q8 ? g : 0][is_k ? 0 : 1]), sc);
+      if (c == 0) lds_store4(lds_address(&new_scales[APPEND && QUANT ? g : 0][is_k ? 0 : 1]), sc);
     } else {
       // [K lo parts 0..3 | K hi parts | V lo | V hi] in 16 chunks: 2 per lane
       lds_store16(rows + 16 * ((is_k ? 0 : 8) + c), u32x4{lo.x, lo.y, lo.z, lo.w});
@@ -559,21 +667,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   step(last, std::true_type{});
   wait_vmem<0>();
 
-  if (app_here && lane < (Q8 ? 8 : 16)) {
+  if (app_here && lane < (QUANT ? 8 : 16)) {
     const int id = raw_page_id(last);
     if ((unsigned)id < (unsigned)a.num_pages) {
       const int sl = APPEND ? g : 0;
-      if constexpr (Q8) {
+      if constexpr (QUANT) {
+        using QL = QuantLayout<Q8 ? kFmtINT8 : kFmtINT4>;
         const int c = lane & 3;
         const bool is_k = lane < 4;
         const u32x4 w = new_rows[sl][lane];
-        int8_t* dst = reinterpret_cast<int8_t*>(is_k ? a.k_pool_w : a.v_pool_w) +
-                      (int64_t)id * kPageCodes + g * kHeadCodes + app_slot * kD + 8 * c;
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w.x, w.y};
-        *reinterpret_cast<u32x2*>(dst + 32) = u32x2{w.z, w.w};
+        uint8_t* row = reinterpret_cast<uint8_t*>(is_k ? a.k_pool_w : a.v_pool_w) +
+                       (int64_t)id * QL::kPageBytes + g * QL::kHead + app_slot * QL::kRow;
+        store_quad_codes<FMT>(row, c, u32x2{w.x, w.y}, u32x2{w.z, w.w});
         if (c == 0)
           a.kv_scales_w[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + app_slot] =
-              new_scales[APPEND && Q8 ? g : 0][is_k ? 0 : 1];
+              new_scales[APPEND && QUANT ? g : 0][is_k ? 0 : 1];
       } else {
         // chunk lane: K (lanes 0..7) or V (8..15); dims 8 (lane%4) (+32 for the hi parts)
         const u32x4 w = reinterpret_cast<const u32x4*>(&new_rows[sl][0])[lane];
@@ -595,6 +703,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) o[t][rr] = st.acc[t][rr] + __shfl_down(st.acc[t][rr], 16);
+  if constexpr (Q4) {
+    // the values were code + 24: take 24 x the head's weight sum back out
+    st.wsum += __shfl_xor(st.wsum, 16);
+    st.wsum += __shfl_xor(st.wsum, 32);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float bias = kNibbleBias4 * __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.wsum), rr));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t][rr] -= bias;
+    }
+  }
 
   float m_out = st.m, l_out = st.l;
   if (bad_page) {
@@ -620,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         const int64_t orow = ((int64_t)b * kHq + kGroup * g + rr) * kD;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int d = out_dim<Q8>(t, n);
+          const int d = out_dim<FMT>(t, n);
           if (OUT_BF16)
             reinterpret_cast<uint16_t*>(a.out)[orow + d] = (uint16_t)f32_to_bf16_rne(o[t][rr] * inv);
           else
@@ -632,7 +752,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) a.part_acc[(prow + rr) * kD + out_dim<Q8>(t, n)] = o[t][rr];
+        for (int t = 0; t < 4; ++t) a.part_acc[(prow + rr) * kD + out_dim<FMT>(t, n)] = o[t][rr];
         if (n == 0) {
           a.part_ml[(prow + rr) * 2 + 0] = mh[rr];
           a.part_ml[(prow + rr) * 2 + 1] = lh[rr];
@@ -646,10 +766,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 
 namespace pa {
 
-// Host: enqueue the decode kernel for page format Q8 (plus the split merge
+// Host: enqueue the decode kernel for page format FMT (plus the split merge
 // when the plan has more than one split).  event_before/after (may be NULL)
 // are recorded right around the decode kernel.  Returns a hipError_t.
-template <bool Q8>
+template <int FMT>
 inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
                                 bool rope, bool merge_preload, hipStream_t st,
                                 hipEvent_t event_before, hipEvent_t event_after) {
@@ -658,13 +778,13 @@ inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, b
   hipError_t e = hipSuccess;
   if (event_before && (e = hipEventRecord(event_before, st)) != hipSuccess) return e;
   if (out_bf16) {
-    if (rope) hipLaunchKernelGGL((decode_kernel<Q8, true, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_kernel<Q8, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<Q8, true, false>), grid, block, 0, st, a);
+    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, true, true, true>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<FMT, true, false>), grid, block, 0, st, a);
   } else {
-    if (rope) hipLaunchKernelGGL((decode_kernel<Q8, false, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_kernel<Q8, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<Q8, false, false>), grid, block, 0, st, a);
+    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, false, true, true>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<FMT, false, false>), grid, block, 0, st, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (event_after && (e = hipEventRecord(event_after, st)) != hipSuccess) return e;

@@ -1,10 +1,12 @@
-// Host side of the INT8 K/V page entry points (C ABI in include/pa_decode.h):
-// argument checks and launches of the kernels in pa_kernels_q8.h.
+// Host side of the INT8 and INT4 K/V page entry points (C ABI in
+// include/pa_decode_q8.h and include/pa_decode_q4.h): argument checks, the
+// quantised append and fill kernels, and launches of the decode kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 
 #include "pa_decode.h"
+#include "pa_decode_q4.h"
 #include "pa_decode_q8.h"
 #include "pa_host.h"
 #include "pa_decode_kernel.h"
@@ -13,18 +15,19 @@
 
 namespace pa {
 
-// Quantised one-token append: one wavefront per sequence; lane = 4 * row + c
+// Quantised one-token append (FMT: INT8 or INT4 codes): one wavefront per
+// sequence; lane = 4 * row + c
 // with row = 2 * head + (0: K, 1: V) and c the lane's dims {8c..} and
 // {32+8c..} of that row.  With ROPE (256 threads) the new query is rotated
 // into q_out by all four wavefronts as in append_rope_kernel, and the new key
 // is rotated before it is quantised.  Idle slots and out-of-range metadata
 // write no pool bytes (q_out still gets q, rotated or copied).
-template <bool ROPE>
-__global__ __launch_bounds__(ROPE ? 256 : 64) void append_q8_kernel(
+template <int FMT, bool ROPE>
+__global__ __launch_bounds__(ROPE ? 256 : 64) void append_quant_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, uint16_t* __restrict__ q_out,
-    int8_t* __restrict__ k_codes, int8_t* __restrict__ v_codes, float* __restrict__ kv_scales,
+    uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, float* __restrict__ kv_scales,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     int32_t max_blocks, int32_t num_pages) {
   const int b = blockIdx.x;
@@ -64,25 +67,27 @@ __global__ __launch_bounds__(ROPE ? 256 : 64) void append_q8_kernel(
     const int64_t cs = (int64_t)pos * (kD / 2) + 8 * c;
     rope_pairs8(lo, hi, rope_cos + cs, rope_sin + cs);
   }
+  using QL = QuantLayout<FMT>;
   u32x2 clo, chi;
-  const float sc = quantize_quad_row(lo, hi, clo, chi);
+  const float sc = quantize_quad_row<FMT>(lo, hi, clo, chi);
   const int slot = pos % kPage;
-  int8_t* dst = (is_k ? k_codes : v_codes) + (int64_t)id * kPageCodes + g * kHeadCodes + slot * kD + 8 * c;
-  *reinterpret_cast<u32x2*>(dst) = clo;
-  *reinterpret_cast<u32x2*>(dst + 32) = chi;
+  store_quad_codes<FMT>((is_k ? k_codes : v_codes) + (int64_t)id * QL::kPageBytes + g * QL::kHead +
+                            slot * QL::kRow,
+                        c, clo, chi);
   if (c == 0) kv_scales[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + slot] = sc;
 }
 
 // Quantised prefill fill: tokens start .. start+T-1 of one sequence, one
-// wavefront per token (lane mapping of append_q8_kernel), 4 per work-group.
-__global__ __launch_bounds__(256) void fill_q8_kernel(const uint16_t* __restrict__ k_rows,
-                                                      const uint16_t* __restrict__ v_rows,
-                                                      int32_t num_tokens, int32_t start,
-                                                      const int32_t* __restrict__ bt_row,
-                                                      int8_t* __restrict__ k_codes,
-                                                      int8_t* __restrict__ v_codes,
-                                                      float* __restrict__ kv_scales,
-                                                      int32_t num_pages) {
+// wavefront per token (lane mapping of append_quant_kernel), 4 per work-group.
+template <int FMT>
+__global__ __launch_bounds__(256) void fill_quant_kernel(const uint16_t* __restrict__ k_rows,
+                                                         const uint16_t* __restrict__ v_rows,
+                                                         int32_t num_tokens, int32_t start,
+                                                         const int32_t* __restrict__ bt_row,
+                                                         uint8_t* __restrict__ k_codes,
+                                                         uint8_t* __restrict__ v_codes,
+                                                         float* __restrict__ kv_scales,
+                                                         int32_t num_pages) {
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (tok >= num_tokens) return;                    // whole wavefront: quads stay complete
@@ -95,12 +100,13 @@ __global__ __launch_bounds__(256) void fill_q8_kernel(const uint16_t* __restrict
   const uint16_t* src = (is_k ? k_rows : v_rows) + ((int64_t)tok * kHkv + g) * kD + 8 * c;
   const uint4 lo = *reinterpret_cast<const uint4*>(src);
   const uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
+  using QL = QuantLayout<FMT>;
   u32x2 clo, chi;
-  const float sc = quantize_quad_row(lo, hi, clo, chi);
+  const float sc = quantize_quad_row<FMT>(lo, hi, clo, chi);
   const int slot = t % kPage;
-  int8_t* dst = (is_k ? k_codes : v_codes) + (int64_t)id * kPageCodes + g * kHeadCodes + slot * kD + 8 * c;
-  *reinterpret_cast<u32x2*>(dst) = clo;
-  *reinterpret_cast<u32x2*>(dst + 32) = chi;
+  store_quad_codes<FMT>((is_k ? k_codes : v_codes) + (int64_t)id * QL::kPageBytes + g * QL::kHead +
+                            slot * QL::kRow,
+                        c, clo, chi);
   if (c == 0) kv_scales[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + slot] = sc;
 }
 
@@ -124,6 +130,19 @@ PlanModel plan_model_q8() {
   return m;
 }
 
+// Planner cost model for INT4 pages: 9 KiB per page (4 KiB of K codes, 4 KiB
+// of V codes, 1 KiB of scales); the per-page time of one CU alone and the
+// fixed costs as measured for the INT8 kernel, whose per-page work is the
+// same apart from the widening of the codes.
+PlanModel plan_model_q4() {
+  PlanModel m;
+  m.page_bytes = 2.0 * pa::kPageCodes4 + pa::kScalePageFloats * 4.0;
+  m.page_us = 0.5;
+  m.group_us = 3.0;
+  m.empty_us = 0.5;
+  return m;
+}
+
 }  // namespace pa_host
 
 namespace {
@@ -134,7 +153,8 @@ int check_pools_q8(const void* k_codes, const void* v_codes, const void* kv_scal
   return PA_OK;
 }
 
-int append_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_new,
+template <int FMT>
+int append_quant_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_new,
                    const void* v_new, const pa_rope* rope, void* q_out, void* k_codes,
                    void* v_codes, void* kv_scales, const int32_t* block_tables,
                    const int32_t* seq_lens, void* stream) {
@@ -157,21 +177,22 @@ int append_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
   if (shape->num_pages < 1) return PA_ERR_VALUE;
   hipStream_t st = (hipStream_t)stream;
   if (rope)
-    hipLaunchKernelGGL(pa::append_q8_kernel<true>, dim3(batch), dim3(256), 0, st,
+    hipLaunchKernelGGL((pa::append_quant_kernel<FMT, true>), dim3(batch), dim3(256), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new,
-                       rope->cos, rope->sin, (uint16_t*)q_out, (int8_t*)k_codes, (int8_t*)v_codes,
-                       (float*)kv_scales, block_tables, seq_lens, shape->max_blocks_per_seq,
-                       shape->num_pages);
+                       rope->cos, rope->sin, (uint16_t*)q_out, (uint8_t*)k_codes,
+                       (uint8_t*)v_codes, (float*)kv_scales, block_tables, seq_lens,
+                       shape->max_blocks_per_seq, shape->num_pages);
   else
-    hipLaunchKernelGGL(pa::append_q8_kernel<false>, dim3(batch), dim3(64), 0, st, nullptr,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, nullptr, nullptr, nullptr,
-                       (int8_t*)k_codes, (int8_t*)v_codes, (float*)kv_scales, block_tables,
-                       seq_lens, shape->max_blocks_per_seq, shape->num_pages);
+    hipLaunchKernelGGL((pa::append_quant_kernel<FMT, false>), dim3(batch), dim3(64), 0, st,
+                       nullptr, (const uint16_t*)k_new, (const uint16_t*)v_new, nullptr, nullptr,
+                       nullptr, (uint8_t*)k_codes, (uint8_t*)v_codes, (float*)kv_scales,
+                       block_tables, seq_lens, shape->max_blocks_per_seq, shape->num_pages);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 // k_new/v_new non-NULL: the quantised append is fused into the main kernel
-int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_new,
+template <int FMT>
+int decode_quant_impl(const pa_shape* shape, int32_t batch, const void* q, const void* k_new,
                    const void* v_new, const pa_rope* rope, const void* k_codes,
                    const void* v_codes, const void* kv_scales, const int32_t* block_tables,
                    const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out,
@@ -242,7 +263,7 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
   a.batch = batch;
   int cu = 0;
   const bool merge_preload = pa_host::current_cu_count(&cu) == PA_OK && batch <= cu;
-  const hipError_t e = pa::launch_decode<true>(a, batch, out_dtype == PA_OUT_BF16, fused,
+  const hipError_t e = pa::launch_decode<FMT>(a, batch, out_dtype == PA_OUT_BF16, fused,
                                                rope != nullptr, merge_preload, (hipStream_t)stream,
                                                nullptr, nullptr);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -253,8 +274,8 @@ int decode_q8_impl(const pa_shape* shape, int32_t batch, const void* q, const vo
 PA_API int pa_append_kv_q8(const pa_shape* shape, int32_t batch, const void* k_new,
                            const void* v_new, void* k_codes, void* v_codes, void* kv_scales,
                            const int32_t* block_tables, const int32_t* seq_lens, void* stream) {
-  return append_q8_impl(shape, batch, nullptr, k_new, v_new, nullptr, nullptr, k_codes, v_codes,
-                        kv_scales, block_tables, seq_lens, stream);
+  return append_quant_impl<pa::kFmtINT8>(shape, batch, nullptr, k_new, v_new, nullptr, nullptr, k_codes,
+                                                v_codes, kv_scales, block_tables, seq_lens, stream);
 }
 
 PA_API int pa_append_kv_rope_q8(const pa_shape* shape, int32_t batch, const void* q,
@@ -263,13 +284,16 @@ PA_API int pa_append_kv_rope_q8(const pa_shape* shape, int32_t batch, const void
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 void* stream) {
   if (batch > 0 && !rope) return PA_ERR_NULL;
-  return append_q8_impl(shape, batch, q, k_new, v_new, rope, q_out, k_codes, v_codes, kv_scales,
+  return append_quant_impl<pa::kFmtINT8>(shape, batch, q, k_new, v_new, rope, q_out, k_codes, v_codes, kv_scales,
                         block_tables, seq_lens, stream);
 }
 
-PA_API int pa_fill_kv_q8(const pa_shape* shape, const void* k_rows, const void* v_rows,
-                         int32_t num_tokens, int32_t start, const int32_t* block_table_row,
-                         void* k_codes, void* v_codes, void* kv_scales, void* stream) {
+namespace {
+
+template <int FMT>
+int fill_quant_impl(const pa_shape* shape, const void* k_rows, const void* v_rows,
+                    int32_t num_tokens, int32_t start, const int32_t* block_table_row,
+                    void* k_codes, void* v_codes, void* kv_scales, void* stream) {
   int rc = check_shape(shape);
   if (rc != PA_OK) return rc;
   if (num_tokens < 0 || start < 0 ||
@@ -282,11 +306,41 @@ PA_API int pa_fill_kv_q8(const pa_shape* shape, const void* k_rows, const void* 
   if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(block_table_row, 4))
     return PA_ERR_ALIGN;
   if (shape->num_pages < 1) return PA_ERR_VALUE;
-  hipLaunchKernelGGL(pa::fill_q8_kernel, dim3(ceil_div(num_tokens, 4)), dim3(256), 0,
+  hipLaunchKernelGGL(pa::fill_quant_kernel<FMT>, dim3(ceil_div(num_tokens, 4)), dim3(256), 0,
                      (hipStream_t)stream, (const uint16_t*)k_rows, (const uint16_t*)v_rows,
-                     num_tokens, start, block_table_row, (int8_t*)k_codes, (int8_t*)v_codes,
+                     num_tokens, start, block_table_row, (uint8_t*)k_codes, (uint8_t*)v_codes,
                      (float*)kv_scales, shape->num_pages);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <int FMT>
+int plan_lengths_quant(const pa_shape* shape, int32_t batch, const int32_t* seq_lens_host,
+                       int32_t max_seq_len, int32_t num_cus, int32_t* pages_out,
+                       int32_t* splits_out) {
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  if (batch > 0 && !seq_lens_host) return PA_ERR_NULL;
+  if (num_cus < 0) return PA_ERR_VALUE;
+  int ps = 1, ns = 1;
+  if (batch > 0) {
+    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus,
+                            FMT == pa::kFmtINT8 ? plan_model_q8() : plan_model_q4(), &ps, &ns);
+    if (rc != PA_OK) return rc;
+  }
+  if (pages_out) *pages_out = ps;
+  if (splits_out) *splits_out = ns;
+  return PA_OK;
+}
+
+}  // namespace
+
+// INT8 pages (include/pa_decode_q8.h)
+
+PA_API int pa_fill_kv_q8(const pa_shape* shape, const void* k_rows, const void* v_rows,
+                         int32_t num_tokens, int32_t start, const int32_t* block_table_row,
+                         void* k_codes, void* v_codes, void* kv_scales, void* stream) {
+  return fill_quant_impl<pa::kFmtINT8>(shape, k_rows, v_rows, num_tokens, start, block_table_row,
+                                       k_codes, v_codes, kv_scales, stream);
 }
 
 PA_API int pa_decode_attention_q8(const pa_shape* shape, int32_t batch, const void* q,
@@ -295,7 +349,7 @@ PA_API int pa_decode_attention_q8(const pa_shape* shape, int32_t batch, const vo
                                   const int32_t* seq_lens, int32_t max_seq_len, float scale,
                                   void* out, int32_t out_dtype, int32_t pages_per_split,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_q8_impl(shape, batch, q, nullptr, nullptr, nullptr, k_codes, v_codes, kv_scales,
+  return decode_quant_impl<pa::kFmtINT8>(shape, batch, q, nullptr, nullptr, nullptr, k_codes, v_codes, kv_scales,
                         block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
                         pages_per_split, workspace, workspace_bytes, stream);
 }
@@ -308,7 +362,7 @@ PA_API int pa_append_decode_attention_q8(const pa_shape* shape, int32_t batch, c
                                          int32_t out_dtype, int32_t pages_per_split,
                                          void* workspace, size_t workspace_bytes, void* stream) {
   if (batch > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
-  return decode_q8_impl(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
+  return decode_quant_impl<pa::kFmtINT8>(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
                         block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
                         pages_per_split, workspace, workspace_bytes, stream);
 }
@@ -322,7 +376,7 @@ PA_API int pa_append_decode_attention_rope_q8(const pa_shape* shape, int32_t bat
                                               int32_t pages_per_split, void* workspace,
                                               size_t workspace_bytes, void* stream) {
   if (batch > 0 && (!k_new || !v_new || !rope)) return PA_ERR_NULL;
-  return decode_q8_impl(shape, batch, q, k_new, v_new, rope, k_codes, v_codes, kv_scales,
+  return decode_quant_impl<pa::kFmtINT8>(shape, batch, q, k_new, v_new, rope, k_codes, v_codes, kv_scales,
                         block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
                         pages_per_split, workspace, workspace_bytes, stream);
 }
@@ -334,7 +388,7 @@ PA_API int pa_append_decode_attention_worklist_q8(
     int32_t pages_per_split, const int32_t* work, int32_t num_work, void* workspace,
     size_t workspace_bytes, void* stream) {
   if (batch > 0 && !work) return PA_ERR_NULL;
-  return decode_q8_impl(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
+  return decode_quant_impl<pa::kFmtINT8>(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
                         block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
                         pages_per_split, workspace, workspace_bytes, stream, work, num_work);
 }
@@ -342,17 +396,89 @@ PA_API int pa_append_decode_attention_worklist_q8(
 PA_API int pa_decode_plan_lengths_q8(const pa_shape* shape, int32_t batch,
                                      const int32_t* seq_lens_host, int32_t max_seq_len,
                                      int32_t num_cus, int32_t* pages_out, int32_t* splits_out) {
-  int rc = check_decode_sizes(shape, batch, max_seq_len);
-  if (rc != PA_OK) return rc;
-  if (batch > 0 && !seq_lens_host) return PA_ERR_NULL;
-  if (num_cus < 0) return PA_ERR_VALUE;
-  int ps = 1, ns = 1;
-  if (batch > 0) {
-    rc = plan_split_lengths(shape, batch, seq_lens_host, max_seq_len, num_cus, plan_model_q8(), &ps,
-                            &ns);
-    if (rc != PA_OK) return rc;
-  }
-  if (pages_out) *pages_out = ps;
-  if (splits_out) *splits_out = ns;
-  return PA_OK;
+  return plan_lengths_quant<pa::kFmtINT8>(shape, batch, seq_lens_host, max_seq_len, num_cus,
+                                          pages_out, splits_out);
+}
+
+// INT4 pages (include/pa_decode_q4.h)
+
+PA_API int pa_append_kv_q4(const pa_shape* shape, int32_t batch, const void* k_new,
+                           const void* v_new, void* k_codes, void* v_codes, void* kv_scales,
+                           const int32_t* block_tables, const int32_t* seq_lens, void* stream) {
+  return append_quant_impl<pa::kFmtINT4>(shape, batch, nullptr, k_new, v_new, nullptr, nullptr, k_codes,
+                                                v_codes, kv_scales, block_tables, seq_lens, stream);
+}
+
+PA_API int pa_append_kv_rope_q4(const pa_shape* shape, int32_t batch, const void* q,
+                                const void* k_new, const void* v_new, const pa_rope* rope,
+                                void* q_out, void* k_codes, void* v_codes, void* kv_scales,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                void* stream) {
+  if (batch > 0 && !rope) return PA_ERR_NULL;
+  return append_quant_impl<pa::kFmtINT4>(shape, batch, q, k_new, v_new, rope, q_out, k_codes, v_codes, kv_scales,
+                        block_tables, seq_lens, stream);
+}
+
+PA_API int pa_fill_kv_q4(const pa_shape* shape, const void* k_rows, const void* v_rows,
+                         int32_t num_tokens, int32_t start, const int32_t* block_table_row,
+                         void* k_codes, void* v_codes, void* kv_scales, void* stream) {
+  return fill_quant_impl<pa::kFmtINT4>(shape, k_rows, v_rows, num_tokens, start, block_table_row,
+                                       k_codes, v_codes, kv_scales, stream);
+}
+
+PA_API int pa_decode_attention_q4(const pa_shape* shape, int32_t batch, const void* q,
+                                  const void* k_codes, const void* v_codes,
+                                  const void* kv_scales, const int32_t* block_tables,
+                                  const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                  void* out, int32_t out_dtype, int32_t pages_per_split,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_quant_impl<pa::kFmtINT4>(shape, batch, q, nullptr, nullptr, nullptr, k_codes, v_codes, kv_scales,
+                        block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
+                        pages_per_split, workspace, workspace_bytes, stream);
+}
+
+PA_API int pa_append_decode_attention_q4(const pa_shape* shape, int32_t batch, const void* q,
+                                         const void* k_new, const void* v_new, void* k_codes,
+                                         void* v_codes, void* kv_scales,
+                                         const int32_t* block_tables, const int32_t* seq_lens,
+                                         int32_t max_seq_len, float scale, void* out,
+                                         int32_t out_dtype, int32_t pages_per_split,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
+  return decode_quant_impl<pa::kFmtINT4>(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
+                        block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
+                        pages_per_split, workspace, workspace_bytes, stream);
+}
+
+PA_API int pa_append_decode_attention_rope_q4(const pa_shape* shape, int32_t batch, const void* q,
+                                              const void* k_new, const void* v_new,
+                                              const pa_rope* rope, void* k_codes, void* v_codes,
+                                              void* kv_scales, const int32_t* block_tables,
+                                              const int32_t* seq_lens, int32_t max_seq_len,
+                                              float scale, void* out, int32_t out_dtype,
+                                              int32_t pages_per_split, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  if (batch > 0 && (!k_new || !v_new || !rope)) return PA_ERR_NULL;
+  return decode_quant_impl<pa::kFmtINT4>(shape, batch, q, k_new, v_new, rope, k_codes, v_codes, kv_scales,
+                        block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
+                        pages_per_split, workspace, workspace_bytes, stream);
+}
+
+PA_API int pa_append_decode_attention_worklist_q4(
+    const pa_shape* shape, int32_t batch, const void* q, const void* k_new, const void* v_new,
+    void* k_codes, void* v_codes, void* kv_scales, const int32_t* block_tables,
+    const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
+    int32_t pages_per_split, const int32_t* work, int32_t num_work, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (batch > 0 && !work) return PA_ERR_NULL;
+  return decode_quant_impl<pa::kFmtINT4>(shape, batch, q, k_new, v_new, nullptr, k_codes, v_codes, kv_scales,
+                        block_tables, seq_lens, max_seq_len, scale, out, out_dtype,
+                        pages_per_split, workspace, workspace_bytes, stream, work, num_work);
+}
+
+PA_API int pa_decode_plan_lengths_q4(const pa_shape* shape, int32_t batch,
+                                     const int32_t* seq_lens_host, int32_t max_seq_len,
+                                     int32_t num_cus, int32_t* pages_out, int32_t* splits_out) {
+  return plan_lengths_quant<pa::kFmtINT4>(shape, batch, seq_lens_host, max_seq_len, num_cus,
+                                          pages_out, splits_out);
 }

@@ -42,6 +42,8 @@ int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int ma
                        bool worklist = false);
 // The cost model fitted to the INT8-page kernel (defined with the INT8 entry points).
 PlanModel plan_model_q8();
+// The cost model for INT4 pages (defined with the quantised entry points).
+PlanModel plan_model_q4();
 // Bytes of split partials for `splits` splits per sequence (0 for one split).
 size_t workspace_for(int batch, int splits);
 

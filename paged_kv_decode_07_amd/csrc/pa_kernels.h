@@ -1,7 +1,7 @@
 // Shared device code of the paged GQA decode library for gfx950 (CDNA4,
 // wave64): geometry constants, BF16 and RoPE helpers, LDS and wait helpers,
 // the output-row store and the split merge kernel.  The decode kernel is in
-// pa_decode_kernel.h, the INT8 page format in pa_kernels_q8.h.
+// pa_decode_kernel.h, the INT8 and INT4 page formats in pa_kernels_q8.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -109,17 +109,15 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // Wait until the oldest page of a ring has landed while the `later` pages
 // requested after it (each LOADS instructions) may still be in flight;
 // `later` is wave-uniform and below DEPTH.
-template <int LOADS, int DEPTH>
+template <int LOADS, int DEPTH, int K = DEPTH - 1>
 __device__ __forceinline__ void wait_page(int later) {
-  static_assert(DEPTH >= 2 && DEPTH <= 4, "ring depth");
-  if constexpr (DEPTH > 3) {
-    if (later >= 3) return wait_vmem<LOADS * 3>();
+  static_assert(DEPTH >= 2 && LOADS * (DEPTH - 1) <= 63, "ring depth beyond the vmcnt range");
+  if constexpr (K == 0) {
+    wait_vmem<0>();
+  } else {
+    if (later >= K) return wait_vmem<LOADS * K>();
+    wait_page<LOADS, DEPTH, K - 1>(later);
   }
-  if constexpr (DEPTH > 2) {
-    if (later >= 2) return wait_vmem<LOADS * 2>();
-  }
-  if (later >= 1) return wait_vmem<LOADS>();
-  wait_vmem<0>();
 }
 
 // LDS stores the compiler does not see as LDS accesses: it would otherwise

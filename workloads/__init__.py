@@ -290,11 +290,13 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
 
 @dataclass
 class Q8Batch:
-    """One layer's decode-step inputs over INT8 pages.
+    """One layer's decode-step inputs over INT8 (or INT4) pages.
 
     Codes are int8 ``[num_pages][8][16][64]`` (per page, each KV head's 16
-    token rows contiguous), scales float32 ``[num_pages][8][2][16]`` (per page
-    and KV head: 16 K scales, 16 V scales).
+    token rows contiguous), or for ``nbits == 4`` uint8 ``[num_pages][8][16][32]``
+    (two codes per byte, each stored as code + 8, dim 2j in the low nibble);
+    scales float32 ``[num_pages][8][2][16]`` (per page and KV head: 16 K
+    scales, 16 V scales).
     """
 
     name: str
