@@ -71,3 +71,23 @@ def step_bytes_q8(seq_lens, out_bytes: int = 4, append: bool = False) -> dict:
     out = dict(base, kv=kv, app=app)
     out["total"] = kv + base["q"] + base["out"] + base["meta"] + app
     return out
+
+
+# INT4 pages: two codes per byte plus the same per-row FP32 scales (section
+# 5.1's lower-precision cache at 4 bits)
+Q4_TOKEN_BYTES = 2 * KV_HEADS * (HEAD_DIM // 2 + 4)                  # 576 per layer
+Q4_PAGE_BYTES = PAGE * Q4_TOKEN_BYTES                                # 9 KiB (K+V+scales)
+
+
+def step_bytes_q4(seq_lens, out_bytes: int = 4, append: bool = False) -> dict:
+    """As ``step_bytes`` for INT4 pages: ``kv`` counts 576 bytes per valid token;
+    the append reads a BF16 row pair and writes its codes and scales."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    base = step_bytes(lens, out_bytes=out_bytes, append=False)
+    active = int(np.count_nonzero(lens))
+    kv = int(lens.sum()) * Q4_TOKEN_BYTES
+    app = active * (KV_TOKEN_BYTES + Q4_TOKEN_BYTES + 8) if append else 0
+    out = dict(base, kv=kv, app=app)
+    out["total"] = kv + base["q"] + base["out"] + base["meta"] + app
+    return out
+

@@ -116,11 +116,16 @@ struct DecodeArgs {
 // Page-format constants of the LDS ring (per wavefront slot).
 template <int FMT>
 struct PageFormat;
+// kPairs: full pages are consumed two at a time (needs a ring of 3 or more).
+#ifndef PA_PAIR_STEPS
+#define PA_PAIR_STEPS 1
+#endif
 template <>
 struct PageFormat<kFmtBF16> {
   static constexpr int kRingDepth = kRing;      // 2 slots of 4 KiB
   static constexpr int kSlot = 4096;            // [K | V] x 16 token rows x 128 B (swizzled pieces)
   static constexpr int kLoads = 4;              // direct-to-LDS loads per page
+  static constexpr bool kPairs = PA_PAIR_STEPS && kRingDepth >= 3;
 };
 
 // BF16 slot layout: the head's K rows (2 KiB) then its V rows.  Each
@@ -138,12 +143,14 @@ struct PageFormat<kFmtINT8> {
   static constexpr int kRingDepth = kRingQ8;    // slots of 2304 B
   static constexpr int kSlot = kSlotQ8;         // [K codes 16 x 64 B | V codes 16 x 64 B | scales]
   static constexpr int kLoads = 3;
+  static constexpr bool kPairs = PA_PAIR_STEPS && kRingDepth >= 3;
 };
 template <>
 struct PageFormat<kFmtINT4> {
   static constexpr int kRingDepth = kRingQ4;    // slots of 1280 B
   static constexpr int kSlot = kSlotQ4;         // [K codes 16 x 32 B | V codes 16 x 32 B | scales]
   static constexpr int kLoads = 2;              // K and V codes in one load, the scales
+  static constexpr bool kPairs = PA_PAIR_STEPS && kRingDepth >= 3;
 };
 
 // Registers of one page for one lane.
@@ -241,38 +248,53 @@ struct LaneState {
   float wsum;
 };
 
-// qbias (INT4 pages): 24 x the sum of this lane's query row
-template <int FMT, bool MASK, typename Page>
-__device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t qlo, bf16x8_t qhi,
-                                           float xscale, float qbias, int lane, int valid) {
-  constexpr bool Q8 = FMT == kFmtINT8;
-  constexpr bool Q4 = FMT == kFmtINT4;
-  constexpr bool QUANT = Q8 || Q4;
-  const int G = lane >> 4;            // token group: tokens 4G .. 4G+3
-  const int n = lane & 15;            // head slot (query head 4g + n%4); P row
+// Per-lane constants of the page arithmetic.  qbias (INT4 pages): 24 x the
+// sum of this lane's query row; nib: the widening constants.
+struct PageConsts {
+  float xscale;
+  float qbias;
+  NibbleConsts nib;
+};
+
+// Raw scores of one page for this lane: tokens 4G .. 4G+3, column n (INT4:
+// the code bias already removed, through the product's accumulator input).
+template <int FMT, typename Page>
+__device__ __forceinline__ f32x4_t page_scores(const Page& r, bf16x8_t qlo, bf16x8_t qhi,
+                                               const PageConsts& pc) {
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
   f32x4_t s;
-  if constexpr (Q8) {
+  if constexpr (FMT == kFmtINT8) {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k0), qlo, zero, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k1), qhi, s, 0, 0, 0);
-  } else if constexpr (Q4) {
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nibbles_to_bf16x8(r.k0), qlo, zero, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nibbles_to_bf16x8(r.k1), qhi, s, 0, 0, 0);
+  } else if constexpr (FMT == kFmtINT4) {
+    bf16x8_t k0, k1;
+    nibbles_to_bf16x8x2(r.k0, r.k1, pc.nib, k0, k1);
+    const f32x4_t nb = {-pc.qbias, -pc.qbias, -pc.qbias, -pc.qbias};
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qlo, nb, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qhi, s, 0, 0, 0);
   } else {
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k0), qlo, zero, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k1), qhi, s, 0, 0, 0);
   }
-  float x[4];
+  return s;
+}
+
+// Scores in log2 units (scale, log2(e) and the K scale applied).
+template <int FMT, typename Page>
+__device__ __forceinline__ void page_logits(const Page& r, f32x4_t s, float xscale, float* x) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     float xs = xscale;
-    if constexpr (QUANT) xs = xscale * __uint_as_float(r.ks[c]);
-    x[c] = (Q4 ? s[c] - qbias : s[c]) * xs;
-    if (MASK) x[c] = (4 * G + c < valid) ? x[c] : -INFINITY;
+    if constexpr (FMT != kFmtBF16) xs = xscale * __uint_as_float(r.ks[c]);
+    x[c] = s[c] * xs;
   }
-  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+}
+
+// Raise the running maximum when a score passed it by more than kTau (the
+// page maximum mx is this lane's; the new maximum is reduced over the four
+// token groups) and rescale the accumulators.
+__device__ __forceinline__ void raise_max(LaneState& st, float mx) {
   if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau)) {
-    // rare: raise the maximum of every head whose page maximum passed it
     float pm = mx;
     pm = fmaxf(pm, __shfl_xor(pm, 16));
     pm = fmaxf(pm, __shfl_xor(pm, 32));
@@ -280,7 +302,7 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
     const float a = __builtin_amdgcn_exp2f(st.m - mn);    // m = -inf -> 0
     st.m = mn;
     st.l *= a;
-    if constexpr (Q4) st.wsum *= a;
+    st.wsum *= a;
     // rows 4G + r of this lane's tiles belong to head r (rows 0..7)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -289,22 +311,13 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
       for (int b = 0; b < 4; ++b) st.acc[b][rr] *= ar;
     }
   }
-  float p[4], w[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    p[c] = __builtin_amdgcn_exp2f(x[c] - st.m);           // masked: exp2(-inf) = 0
-    w[c] = p[c];
-    if constexpr (QUANT) {
-      w[c] = p[c] * __uint_as_float(r.vs[c]);
-      if (MASK) w[c] = (4 * G + c < valid) ? w[c] : 0.f;  // scale bits of a dead slot
-    }
-  }
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  if constexpr (Q4) st.wsum += (w[0] + w[1]) + (w[2] + w[3]);
-  // A operand: rows 0..3 the BF16 weights, rows 4..7 their remainders
-  // (weight - its BF16 value is exact in FP32, then rounded again), rows
-  // 8..15 zero.  Every lane computes both and selects, so the wave does not
-  // diverge.
+}
+
+// A operand of the P V product: rows 0..3 the BF16 weights, rows 4..7 their
+// remainders (weight - its BF16 value is exact in FP32, then rounded again),
+// rows 8..15 zero.  Every lane computes both and selects, so the wave does
+// not diverge.
+__device__ __forceinline__ bf16x4_t weight_operand(const float* w, int n) {
   const uint32_t h01 = pack_bf16_rne(w[0], w[1]);
   const uint32_t h23 = pack_bf16_rne(w[2], w[3]);
   const uint32_t r01 = pack_bf16_rne(w[0] - bf16_lo(h01), w[1] - bf16_hi(h01));
@@ -312,34 +325,88 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
   u32x2 pa;
   pa.x = n < 4 ? h01 : (n < 8 ? r01 : 0u);
   pa.y = n < 4 ? h23 : (n < 8 ? r23 : 0u);
-  const bf16x4_t A = __builtin_bit_cast(bf16x4_t, pa);
-  if constexpr (Q4) {
+  return __builtin_bit_cast(bf16x4_t, pa);
+}
+
+// acc += A V for one page (BF16 pages: V of dead slots already zeroed).
+// B operands of the P V product for one page: tile t (16 output dims) as 4
+// BF16 values, tokens 4G .. 4G+3 of this lane's column (BF16 pages: V of
+// dead slots already zeroed; INT4: code + 24).
+template <int FMT, typename Page>
+__device__ __forceinline__ void page_v_operands(const Page& r, const PageConsts& pc, u32x2* bv) {
+  if constexpr (FMT == kFmtINT4) {
     // tile e: dim 4n + e of tokens 4G .. 4G+3 (nibble e of each 16-bit unit);
     // dead slots hold finite values code + 24 and weight 0
-    st.acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<0>(r.v.x), nibble_pair_bf16<0>(r.v.y)}),
-        st.acc[0], 0, 0, 0);
-    st.acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<1>(r.v.x), nibble_pair_bf16<1>(r.v.y)}),
-        st.acc[1], 0, 0, 0);
-    st.acc[2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<2>(r.v.x), nibble_pair_bf16<2>(r.v.y)}),
-        st.acc[2], 0, 0, 0);
-    st.acc[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-        A, __builtin_bit_cast(bf16x4_t, u32x2{nibble_pair_bf16<3>(r.v.x), nibble_pair_bf16<3>(r.v.y)}),
-        st.acc[3], 0, 0, 0);
-  } else if constexpr (Q8) {
+    uint32_t x[4], y[4];
+    nibble_pairs2<0>(r.v.x, r.v.y, pc.nib, x[0], y[0]);
+    nibble_pairs2<1>(r.v.x, r.v.y, pc.nib, x[1], y[1]);
+    nibble_pairs2<2>(r.v.x, r.v.y, pc.nib, x[2], y[2]);
+    nibble_pairs2<3>(r.v.x, r.v.y, pc.nib, x[3], y[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = u32x2{x[e], y[e]};
+  } else if constexpr (FMT == kFmtINT8) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t e0, o0, e1, o1;
       codes_even_odd(r.v[h].x, e0, o0);                    // tokens 4G, 4G+1
       codes_even_odd(r.v[h].y, e1, o1);                    // tokens 4G+2, 4G+3
-      st.acc[2 * h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          A, __builtin_bit_cast(bf16x4_t, u32x2{e0, e1}), st.acc[2 * h], 0, 0, 0);
-      st.acc[2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          A, __builtin_bit_cast(bf16x4_t, u32x2{o0, o1}), st.acc[2 * h + 1], 0, 0, 0);
+      bv[2 * h] = u32x2{e0, e1};
+      bv[2 * h + 1] = u32x2{o0, o1};
     }
   } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bv[b] = r.v[b];
+  }
+}
+
+// acc += A V for one page.
+template <int FMT, typename Page>
+__device__ __forceinline__ void page_pv(LaneState& st, const Page& r, bf16x4_t A,
+                                        const PageConsts& pc) {
+  u32x2 bv[4];
+  page_v_operands<FMT>(r, pc, bv);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, bv[b]),
+                                                          st.acc[b], 0, 0, 0);
+}
+
+// Weights of 4 tokens (p: softmax numerators; w: the P V operand, p times
+// the V scale for quantised pages), dead slots (MASK) at 0.
+template <int FMT, bool MASK, typename Page>
+__device__ __forceinline__ void page_weights(LaneState& st, const Page& r, const float* x, int G,
+                                             int valid, float* w) {
+  float p[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    p[c] = __builtin_amdgcn_exp2f(x[c] - st.m);           // masked: exp2(-inf) = 0
+    w[c] = p[c];
+    if constexpr (FMT != kFmtBF16) {
+      w[c] = p[c] * __uint_as_float(r.vs[c]);
+      if (MASK) w[c] = (4 * G + c < valid) ? w[c] : 0.f;  // scale bits of a dead slot
+    }
+  }
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (FMT == kFmtINT4) st.wsum += (w[0] + w[1]) + (w[2] + w[3]);
+}
+
+// One page into the running state; MASK: only the first `valid` tokens exist.
+template <int FMT, bool MASK, typename Page>
+__device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t qlo, bf16x8_t qhi,
+                                           const PageConsts& pc, int lane, int valid) {
+  const int G = lane >> 4;            // token group: tokens 4G .. 4G+3
+  const int n = lane & 15;            // head slot (query head 4g + n%4); P row
+  float x[4];
+  page_logits<FMT>(r, page_scores<FMT>(r, qlo, qhi, pc), pc.xscale, x);
+  if (MASK) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = (4 * G + c < valid) ? x[c] : -INFINITY;
+  }
+  raise_max(st, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  float w[4];
+  page_weights<FMT, MASK>(st, r, x, G, valid, w);
+  const bf16x4_t A = weight_operand(w, n);
+  if constexpr (FMT == kFmtBF16) {
     if (MASK) {
       // tokens 4G .. 4G+3 sit in (lo, hi) halves of the two words
       const uint32_t m0 = (4 * G < valid ? 0x0000ffffu : 0u) | (4 * G + 1 < valid ? 0xffff0000u : 0u);
@@ -347,11 +414,44 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
 #pragma unroll
       for (int b = 0; b < 4; ++b) r.v[b] = u32x2{r.v[b].x & m0, r.v[b].y & m1};
     }
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4_t, r.v[b]),
-                                                            st.acc[b], 0, 0, 0);
   }
+  page_pv<FMT>(st, r, A, pc);
+}
+
+// Two full pages at once: their score products are independent, one vote and
+// at most one rescale covers both, and their P V products follow each other;
+// the two dependency chains overlap instead of running one after the other.
+template <int FMT, typename Page>
+__device__ __forceinline__ void consume_pages2(LaneState& st, const Page& ra, const Page& rb,
+                                               bf16x8_t qlo, bf16x8_t qhi, const PageConsts& pc,
+                                               int lane) {
+  const int G = lane >> 4;
+  const int n = lane & 15;
+  const f32x4_t sa = page_scores<FMT>(ra, qlo, qhi, pc);
+  const f32x4_t sb = page_scores<FMT>(rb, qlo, qhi, pc);
+  float xa[4], xb[4];
+  page_logits<FMT>(ra, sa, pc.xscale, xa);
+  page_logits<FMT>(rb, sb, pc.xscale, xb);
+  const float mx = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
+                         fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])));
+  raise_max(st, mx);
+  float wa[4], wb[4];
+  page_weights<FMT, false>(st, ra, xa, G, kPage, wa);
+  page_weights<FMT, false>(st, rb, xb, G, kPage, wb);
+  // one product over 32 tokens per tile: k = 8G .. 8G+7 of this lane are
+  // tokens 4G .. 4G+3 of page a, then of page b, in both operands
+  const bf16x4_t Aa = weight_operand(wa, n);
+  const bf16x4_t Ab = weight_operand(wb, n);
+  const u32x4 A8 = {__builtin_bit_cast(u32x2, Aa).x, __builtin_bit_cast(u32x2, Aa).y,
+                    __builtin_bit_cast(u32x2, Ab).x, __builtin_bit_cast(u32x2, Ab).y};
+  u32x2 va[4], vb[4];
+  page_v_operands<FMT>(ra, pc, va);
+  page_v_operands<FMT>(rb, pc, vb);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8_t, A8), __builtin_bit_cast(bf16x8_t, u32x4{va[b].x, va[b].y, vb[b].x, vb[b].y}),
+        st.acc[b], 0, 0, 0);
 }
 
 // Output dim of column n of tile b: BF16 pages, tile b = dims 16b .. 16b+15;
@@ -448,7 +548,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   // B operand of the score product (set after the first page requests)
   bf16x8_t qlo, qhi;
 
-  float qbias = 0.f;             // INT4 pages: 24 x the sum of the query row
+  PageConsts pc;                 // xscale; INT4: the query bias and the widening constants
+  pc.xscale = a.xscale;
+  pc.qbias = 0.f;
+  if constexpr (Q4) pc.nib = nibble_consts();
 
   // fused append: the new rows (K rotated first with RoPE) are parked in LDS,
   // as BF16 rows or as codes and scales, after the first page requests
@@ -582,31 +685,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     }
   };
 
+  using PageT = std::conditional_t<Q8, PageQ8, std::conditional_t<Q4, PageQ4, PageBF16>>;
+  auto lds_read = [&](PageT& pg, uint32_t off) {
+    if constexpr (QUANT) lds_page_issue(pg, ka + off, va + off, sa + off);
+    else lds_page_issue(pg, ad, off);
+  };
   auto step = [&](int i, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     const int slot = (i - p0) % F::kRingDepth;
     const uint32_t off = slot * kRingSlotBytes;
     wait_page<F::kLoads, F::kRingDepth>(min(last - i, F::kRingDepth - 1));   // page i landed
     if (MASK && app_here) park_new_row(slot0 + off);
-    if constexpr (Q8) {
-      PageQ8 cur;
-      lds_page_issue(cur, ka + off, va + off, sa + off);
-      lds_page_ready(cur);
-      if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
-      consume_page<FMT, MASK>(st, cur, qlo, qhi, a.xscale, qbias, lane, MASK ? tail_valid : kPage);
-    } else if constexpr (Q4) {
-      PageQ4 cur;
-      lds_page_issue(cur, ka + off, va + off, sa + off);
-      lds_page_ready(cur);
-      if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
-      consume_page<FMT, MASK>(st, cur, qlo, qhi, a.xscale, qbias, lane, MASK ? tail_valid : kPage);
-    } else {
-      PageBF16 cur;
-      lds_page_issue(cur, ad, off);
-      lds_page_ready(cur);
-      if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
-      consume_page<FMT, MASK>(st, cur, qlo, qhi, a.xscale, qbias, lane, MASK ? tail_valid : kPage);
-    }
+    PageT cur;
+    lds_read(cur, off);
+    lds_page_ready(cur);
+    if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
+    consume_page<FMT, MASK>(st, cur, qlo, qhi, pc, lane, MASK ? tail_valid : kPage);
+  };
+  // pages i and i+1, both before the last page, in one pass; the ring keeps
+  // depth - 2 pages in flight while they are used
+  auto step2 = [&](int i) {
+    const int slot_a = (i - p0) % F::kRingDepth;
+    const int slot_b = (i + 1 - p0) % F::kRingDepth;
+    wait_page<F::kLoads, F::kRingDepth>(min(last - i - 1, F::kRingDepth - 2));   // page i+1 landed
+    PageT pa_, pb_;
+    lds_read(pa_, slot_a * kRingSlotBytes);
+    lds_read(pb_, slot_b * kRingSlotBytes);
+    lds_page_ready(pa_);
+    lds_page_ready(pb_);
+    if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot_a);
+    if (i + 1 + F::kRingDepth <= last) fetch(i + 1 + F::kRingDepth, slot_b);
+    consume_pages2<FMT>(st, pa_, pb_, qlo, qhi, pc, lane);
   };
 
   // The prologue's loads (block-table window, query rows, new rows) were
@@ -635,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       for (int k = 0; k < 8; ++k) sum += bf16_lo(w[k]) + bf16_hi(w[k]);
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
-      qbias = kNibbleBias4 * sum;
+      pc.qbias = kNibbleBias4 * sum;
       lo = interleave_halves8(lo);
       hi = interleave_halves8(hi);
     }
@@ -663,7 +772,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       lds_store16(rows + 16 * ((is_k ? 0 : 8) + 4 + c), u32x4{hi.x, hi.y, hi.z, hi.w});
     }
   }
-  for (int i = p0; i < last; ++i) step(i, std::false_type{});
+  int i = p0;
+  if constexpr (F::kPairs)
+    for (; i + 1 < last; i += 2) step2(i);
+  for (; i < last; ++i) step(i, std::false_type{});
   step(last, std::true_type{});
   wait_vmem<0>();
 

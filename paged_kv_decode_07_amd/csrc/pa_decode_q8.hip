@@ -131,14 +131,16 @@ PlanModel plan_model_q8() {
 }
 
 // Planner cost model for INT4 pages: 9 KiB per page (4 KiB of K codes, 4 KiB
-// of V codes, 1 KiB of scales); the per-page time of one CU alone and the
-// fixed costs as measured for the INT8 kernel, whose per-page work is the
-// same apart from the widening of the codes.
+// of V codes, 1 KiB of scales).  The per-page time of one CU alone and the
+// fixed costs were fitted to this kernel's measured times on MI355X over
+// batches of 8 to 512 sequences (uniform and Zipf lengths) and split sizes
+// 8 .. 128 pages; at this page size the per-page arithmetic, not HBM, sets
+// the rate.
 PlanModel plan_model_q4() {
   PlanModel m;
   m.page_bytes = 2.0 * pa::kPageCodes4 + pa::kScalePageFloats * 4.0;
   m.page_us = 0.5;
-  m.group_us = 3.0;
+  m.group_us = 2.0;
   m.empty_us = 0.5;
   return m;
 }

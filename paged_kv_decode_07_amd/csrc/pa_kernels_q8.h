@@ -44,7 +44,7 @@ constexpr int kRowBytes4 = kD / 2;               // 32 bytes: one row of INT4 co
 constexpr int kHeadCodes4 = kPage * kRowBytes4;  // 512 bytes: one head's 16 rows in a page
 constexpr int kPageCodes4 = kHkv * kHeadCodes4;  // 4 KiB per page (K or V)
 #ifndef PA_Q4_RING_DEPTH
-#define PA_Q4_RING_DEPTH 4
+#define PA_Q4_RING_DEPTH 3
 #endif
 constexpr int kRingQ4 = PA_Q4_RING_DEPTH;
 constexpr int kSlotQ4 = 512 + 512 + 256;         // K codes, V codes, scales (2 x 128 B used)
@@ -87,24 +87,44 @@ __device__ __forceinline__ bf16x8_t codes_to_bf16x8(u32x2 c) {
 // with BF16 operands are exact, and the bias is taken out afterwards (24 x
 // the sum of the other operand).  kNibbleBias4 is that offset.
 constexpr float kNibbleBias4 = 24.f;
-// Nibble pair at bits 4E .. 4E+3 and 16+4E .. 16+4E+3 of w -> a BF16 pair
-// (code + 24 each; the first in the low half).
+// The two constants of the widening, held in registers the compiler cannot
+// see through, so that mask-and-bias is one v_and_or_b32 (a VALU instruction
+// here takes one scalar operand and no literal besides it).
+struct NibbleConsts {
+  uint32_t mask;   // 0x00780078: bits 3..6 of each half
+  uint32_t bias;   // 0x41804180: BF16 16.0 in each half
+};
+__device__ __forceinline__ NibbleConsts nibble_consts() {
+  NibbleConsts c;
+  asm volatile("s_mov_b32 %0, 0x00780078" : "=s"(c.mask));
+  asm volatile("v_mov_b32 %0, 0x41804180" : "=v"(c.bias));
+  return c;
+}
+// Nibble pair at bits 4E .. 4E+3 and 16+4E .. 16+4E+3 of w0 and of w1 -> a
+// BF16 pair for each (code + 24 each; the first in the low half).  One 64-bit
+// shift serves both words: the bits it carries across them fall outside the
+// mask.
 template <int E>
-__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w) {
-  uint32_t f;
+__device__ __forceinline__ void nibble_pairs2(uint32_t w0, uint32_t w1, const NibbleConsts& k,
+                                              uint32_t& o0, uint32_t& o1) {
+  const uint64_t w = ((uint64_t)w1 << 32) | w0;
+  uint64_t f;
   if constexpr (E == 0) f = w << 3;
   else f = w >> (4 * E - 3);
-  return (f & 0x00780078u) | 0x41804180u;
+  o0 = ((uint32_t)f & k.mask) | k.bias;
+  o1 = ((uint32_t)(f >> 32) & k.mask) | k.bias;
 }
-// One word of 8 INT4 codes (dims 0..7 of a row piece) -> 8 BF16 values
-// code + 24, in the dim order 0 4 1 5 2 6 3 7.
-__device__ __forceinline__ bf16x8_t nibbles_to_bf16x8(uint32_t w) {
-  u32x4 o;
-  o.x = nibble_pair_bf16<0>(w);
-  o.y = nibble_pair_bf16<1>(w);
-  o.z = nibble_pair_bf16<2>(w);
-  o.w = nibble_pair_bf16<3>(w);
-  return __builtin_bit_cast(bf16x8_t, o);
+// Two words of 8 INT4 codes each (dims 0..7 of a row piece) -> 8 BF16 values
+// code + 24 per word, in the dim order 0 4 1 5 2 6 3 7.
+__device__ __forceinline__ void nibbles_to_bf16x8x2(uint32_t w0, uint32_t w1, const NibbleConsts& k,
+                                                    bf16x8_t& b0, bf16x8_t& b1) {
+  uint32_t a[4], b[4];
+  nibble_pairs2<0>(w0, w1, k, a[0], b[0]);
+  nibble_pairs2<1>(w0, w1, k, a[1], b[1]);
+  nibble_pairs2<2>(w0, w1, k, a[2], b[2]);
+  nibble_pairs2<3>(w0, w1, k, a[3], b[3]);
+  b0 = __builtin_bit_cast(bf16x8_t, u32x4{a[0], a[1], a[2], a[3]});
+  b1 = __builtin_bit_cast(bf16x8_t, u32x4{b[0], b[1], b[2], b[3]});
 }
 // The matching reorder of 8 BF16 values (dims 0..7 -> 0 4 1 5 2 6 3 7), for
 // the operand the INT4 codes are multiplied with.

@@ -157,24 +157,26 @@ def test_host_length_planner_choices():
 
 
 def decode_q8(lib, s, batch=1, max_seq_len=37, ptrs=None, scale=0.125, out_dtype=0, ps=1,
-              ws=FAKE, ws_bytes=1 << 30, align_off=0, fused=False):
-    # as decode(): every case must be rejected before a launch (fake pointers)
+              ws=FAKE, ws_bytes=1 << 30, align_off=0, fused=False, sfx="_q8"):
+    # as decode(): every case must be rejected before a launch (fake pointers);
+    # sfx "_q8" or "_q4" picks the INT8 or the INT4 entry points
     n = 9 if fused else 7
     p = ptrs or [ctypes.c_void_p(0x10000 + align_off)] * n
     sp = ctypes.byref(s) if s is not None else None
     if fused:
-        rc = lib.pa_append_decode_attention_q8(sp, batch, *p[:8], max_seq_len, scale, p[8],
-                                               out_dtype, ps, ws, ws_bytes, None)
+        rc = getattr(lib, "pa_append_decode_attention" + sfx)(
+            sp, batch, *p[:8], max_seq_len, scale, p[8], out_dtype, ps, ws, ws_bytes, None)
     else:
-        rc = lib.pa_decode_attention_q8(sp, batch, *p[:6], max_seq_len, scale, p[6], out_dtype,
-                                        ps, ws, ws_bytes, None)
+        rc = getattr(lib, "pa_decode_attention" + sfx)(
+            sp, batch, *p[:6], max_seq_len, scale, p[6], out_dtype, ps, ws, ws_bytes, None)
     assert rc < 0 or batch == 0, "a fake-pointer call was not rejected on the host"
     return rc
 
 
+@pytest.mark.parametrize("sfx", ["_q8", "_q4"])
 @pytest.mark.parametrize("fused", [False, True])
-def test_q8_decode_argument_errors(lib, fused):
-    d = lambda *a, **k: decode_q8(lib, *a, fused=fused, **k)
+def test_quant_decode_argument_errors(lib, fused, sfx):
+    d = lambda *a, **k: decode_q8(lib, *a, fused=fused, sfx=sfx, **k)
     n = 9 if fused else 7
     assert d(None) == -1
     assert d(shape(num_kv_heads=4)) == -2
@@ -194,27 +196,29 @@ def test_q8_decode_argument_errors(lib, fused):
     assert d(shape(), ptrs=p) == -3
 
 
-def test_q8_append_and_fill_argument_errors(lib):
+@pytest.mark.parametrize("sfx", ["_q8", "_q4"])
+def test_quant_append_and_fill_argument_errors(lib, sfx):
+    fn = lambda name: getattr(lib, name + sfx)
     s, F = shape(), FAKE
     bad = ctypes.c_void_p(0x10008)
-    assert lib.pa_append_kv_q8(None, 1, F, F, F, F, F, F, F, None) == -1
-    assert lib.pa_append_kv_q8(ctypes.byref(shape(head_dim=32)), 1, F, F, F, F, F, F, F, None) == -2
-    assert lib.pa_append_kv_q8(ctypes.byref(s), -1, F, F, F, F, F, F, F, None) == -6
-    assert lib.pa_append_kv_q8(ctypes.byref(s), 0, None, None, None, None, None, None, None,
+    assert fn("pa_append_kv")(None, 1, F, F, F, F, F, F, F, None) == -1
+    assert fn("pa_append_kv")(ctypes.byref(shape(head_dim=32)), 1, F, F, F, F, F, F, F, None) == -2
+    assert fn("pa_append_kv")(ctypes.byref(s), -1, F, F, F, F, F, F, F, None) == -6
+    assert fn("pa_append_kv")(ctypes.byref(s), 0, None, None, None, None, None, None, None,
                                None) == 0
-    assert lib.pa_append_kv_q8(ctypes.byref(s), 1, F, F, F, F, None, F, F, None) == -1
-    assert lib.pa_append_kv_q8(ctypes.byref(s), 1, F, F, bad, F, F, F, F, None) == -3
-    assert lib.pa_append_kv_q8(ctypes.byref(shape(num_pages=0)), 1, F, F, F, F, F, F, F,
+    assert fn("pa_append_kv")(ctypes.byref(s), 1, F, F, F, F, None, F, F, None) == -1
+    assert fn("pa_append_kv")(ctypes.byref(s), 1, F, F, bad, F, F, F, F, None) == -3
+    assert fn("pa_append_kv")(ctypes.byref(shape(num_pages=0)), 1, F, F, F, F, F, F, F,
                                None) == -6
     # RoPE variant: the tables are required
-    assert lib.pa_append_kv_rope_q8(ctypes.byref(s), 1, F, F, F, None, F, F, F, F, F, F,
+    assert fn("pa_append_kv_rope")(ctypes.byref(s), 1, F, F, F, None, F, F, F, F, F, F,
                                     None) == -1
     # fill
-    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, -1, 0, F, F, F, F, None) == -6
-    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 10, 2040, F, F, F, F, None) == -6
-    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 0, 0, None, None, None, None, None) == 0
-    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 4, 0, F, F, F, None, None) == -1
-    assert lib.pa_fill_kv_q8(ctypes.byref(s), F, F, 4, 0, F, F, bad, F, None) == -3
+    assert fn("pa_fill_kv")(ctypes.byref(s), F, F, -1, 0, F, F, F, F, None) == -6
+    assert fn("pa_fill_kv")(ctypes.byref(s), F, F, 10, 2040, F, F, F, F, None) == -6
+    assert fn("pa_fill_kv")(ctypes.byref(s), F, F, 0, 0, None, None, None, None, None) == 0
+    assert fn("pa_fill_kv")(ctypes.byref(s), F, F, 4, 0, F, F, F, None, None) == -1
+    assert fn("pa_fill_kv")(ctypes.byref(s), F, F, 4, 0, F, F, bad, F, None) == -3
 
 
 def test_q8_planner_choices():
@@ -229,6 +233,23 @@ def test_q8_planner_choices():
     for i, ps_best in expect.items():
         lens = W.workload_seq_lens(i)
         ps, ns = pa.decode_plan_lengths_q8(lens, 40000, num_cus=256)
+        assert ps == ps_best, (i, ps)
+        assert ns == -(-W.pages_for(int(lens.max())) // ps)
+
+
+def test_q4_planner_choices():
+    """The INT4 plan for known lengths on a 256-CU part, on workloads 2..5.
+
+    Measured fastest split sizes for INT4 pages on MI355X: 8, 16, 64, 32
+    pages; the fitted model picks 32 for workload 3 (27.1 against 25.9 us)
+    and 128 for workload 4 (71.3 against 68.0 us), where the arithmetic of
+    two work-groups sharing a CU, which the model does not describe, decides.
+    """
+    import workloads as W
+    expect = {2: 8, 3: 32, 4: 128, 5: 32}
+    for i, ps_best in expect.items():
+        lens = W.workload_seq_lens(i)
+        ps, ns = pa.decode_plan_lengths_q4(lens, 40000, num_cus=256)
         assert ps == ps_best, (i, ps)
         assert ns == -(-W.pages_for(int(lens.max())) // ps)
 
@@ -275,8 +296,13 @@ def test_worklist_capacity_and_arguments(lib):
     assert lib.pa_decode_worklist(ctypes.byref(s), 3, lens, 300, 1, 0, 0, work, 2,
                                   ctypes.byref(count), ctypes.byref(ps), ctypes.byref(ns)) == -6
     assert count.value == 7 + 13 + 19
-    assert lib.pa_decode_worklist(ctypes.byref(s), 3, lens, 300, 1, 2, 0, work, 2,
-                                  ctypes.byref(count), None, None) == -6         # bad format
+    big = (ctypes.c_int32 * 80)()
+    for fmt in (0, 1, 2):
+        assert lib.pa_decode_worklist(ctypes.byref(s), 3, lens, 300, 1, fmt, 0, big, 40,
+                                      ctypes.byref(count), None, None) == 0
+    for fmt in (-1, 3):
+        assert lib.pa_decode_worklist(ctypes.byref(s), 3, lens, 300, 1, fmt, 0, big, 40,
+                                      ctypes.byref(count), None, None) == -6     # bad format
     assert lib.pa_decode_worklist(ctypes.byref(s), 3, None, 300, 1, 0, 0, work, 2,
                                   ctypes.byref(count), None, None) == -1
     F = FAKE
@@ -287,8 +313,10 @@ def test_worklist_capacity_and_arguments(lib):
         ctypes.byref(s), 1, F, F, F, F, F, F, F, 37, 0.125, F, 0, 2, F, 0, F, 1 << 30, None) == -6
     assert lib.pa_append_decode_attention_worklist(
         ctypes.byref(s), 1, F, F, F, F, F, F, F, 37, 0.125, F, 0, 2, None, 4, F, 1 << 30, None) == -1
-    assert lib.pa_append_decode_attention_worklist_q8(
-        ctypes.byref(s), 1, F, F, F, F, F, F, F, F, 37, 0.125, F, 0, 0, F, 4, F, 1 << 30, None) == -6
+    for sfx in ("_q8", "_q4"):
+        assert getattr(lib, "pa_append_decode_attention_worklist" + sfx)(
+            ctypes.byref(s), 1, F, F, F, F, F, F, F, F, 37, 0.125, F, 0, 0, F, 4, F, 1 << 30,
+            None) == -6
 
 
 def test_worklist_planner_choices():
