@@ -18,8 +18,8 @@ leaves no dirty lines whose write-back would land inside the next step.
 Pass A times the K steps with one event pair around each step; pass B
 repeats them with the library recording events right around its main
 kernel (the roofline figure); pass C times the two-call form; pass D the
-fused step with RoPE; pass E the fused step over INT8 pages (the BF16 cache
-quantised on the GPU first).  Two diagnostics follow: the same step with the
+fused step with RoPE; pass E the fused step over INT8 pages and pass F over
+INT4 pages (the BF16 cache quantised on the GPU first).  Two diagnostics follow: the same step with the
 pages in identity order, and a plain streaming read of 1 GiB (the achievable
 read bandwidth, beside the published peak).  The flush is outside every event
 pair.  The oracle baseline runs on one core and on a pool of worker processes
@@ -43,6 +43,7 @@ METRIC = "decode-attention KV-read GB/s (% of MI355X HBM peak) + sequences/s per
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic_b256_l2048.json")
 TRAFFIC_FILE_Q8 = os.path.join(ROOT, "profiles", "decode_q8_kernel_traffic_b256_l2048.json")
+TRAFFIC_FILE_Q4 = os.path.join(ROOT, "profiles", "decode_q4_kernel_traffic_b256_l2048.json")
 _CSRC = os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc")
 _DEVICE = ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_kernel.h", "pa_host.h")
 KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode.hip",)]
@@ -210,43 +211,51 @@ def run_sweep(args) -> int:
         lens = torch.from_numpy(w.seq_lens).to(dev)
         out = torch.empty((w.batch, 32, 64), dtype=torch.float32, device=dev)
         npg, msl = w.num_pages, w.max_seq_len
+        ident = torch.arange(npg, dtype=torch.int32, device=dev)
         kc, vc, sc = pa.new_q8_pools(npg, device=dev)
-        pa.fill_kv_q8(kp.view(npg * 16, 8, 64), vp.view(npg * 16, 8, 64),
-                      torch.arange(npg, dtype=torch.int32, device=dev), 0, kc, vc, sc,
+        pa.fill_kv_q8(kp.view(npg * 16, 8, 64), vp.view(npg * 16, 8, 64), ident, 0, kc, vc, sc,
                       stream=stream)
-        for q8 in (False, True):
-            acct = A.step_bytes_q8 if q8 else A.step_bytes
+        kc4, vc4, sc4 = pa.new_q4_pools(npg, device=dev)
+        pa.fill_kv_q4(kp.view(npg * 16, 8, 64), vp.view(npg * 16, 8, 64), ident, 0, kc4, vc4,
+                      sc4, stream=stream)
+        formats = {"bf16": (A.step_bytes, pa.decode_plan_lengths, (kp, vp), None),
+                   "int8": (A.step_bytes_q8, pa.decode_plan_lengths_q8, (kc, vc), sc),
+                   "int4": (A.step_bytes_q4, pa.decode_plan_lengths_q4, (kc4, vc4), sc4)}
+        for fmt, (acct, plan, (kpool, vpool), scales) in formats.items():
             kv = acct(w.seq_lens, append=True)["kv"]
-            ps, ns = (pa.decode_plan_lengths_q8 if q8 else pa.decode_plan_lengths)(
-                w.seq_lens, npg, max_seq_len=msl)
+            ps, ns = plan(w.seq_lens, npg, max_seq_len=msl)
             cases = []
-            if q8:
-                cases.append(("grid (lengths plan)", ps, ns, lambda ps=ps: pa.append_decode_attention_q8(
-                    q, kn, vn, kc, vc, sc, bt, lens, msl, scale=w.scale, out=out,
-                    pages_per_split=ps, workspace=workspace, stream=stream)))
-            else:
+            if fmt == "bf16":
                 cases.append(("grid (lengths plan)", ps, ns, lambda ps=ps: pa.append_decode_attention(
                     q, kn, vn, kp, vp, bt, lens, msl, scale=w.scale, out=out,
                     pages_per_split=ps, workspace=workspace, stream=stream)))
+            else:
+                fused = pa.append_decode_attention_q8 if fmt == "int8" else pa.append_decode_attention_q4
+                cases.append(("grid (lengths plan)", ps, ns,
+                              lambda ps=ps, fused=fused, kpool=kpool, vpool=vpool, scales=scales:
+                              fused(q, kn, vn, kpool, vpool, scales, bt, lens, msl, scale=w.scale,
+                                    out=out, pages_per_split=ps, workspace=workspace,
+                                    stream=stream)))
             if w.batch > 1:
-                wl, wps, _ = pa.decode_worklist(w.seq_lens, npg, max_seq_len=msl, int8=q8)
+                wl, wps, _ = pa.decode_worklist(w.seq_lens, npg, max_seq_len=msl,
+                                                int8=fmt == "int8", int4=fmt == "int4")
                 wd = torch.from_numpy(wl).to(dev)
-                cases.append(("work list", wps, len(wl), lambda wd=wd, wps=wps:
+                cases.append(("work list", wps, len(wl),
+                              lambda wd=wd, wps=wps, kpool=kpool, vpool=vpool, scales=scales:
                               pa.append_decode_attention_worklist(
-                                  q, kn, vn, kc if q8 else kp, vc if q8 else vp, bt, lens, msl,
-                                  wd, wps, scale=w.scale, out=out, workspace=workspace,
-                                  stream=stream, kv_scales=sc if q8 else None)))
+                                  q, kn, vn, kpool, vpool, bt, lens, msl, wd, wps, scale=w.scale,
+                                  out=out, workspace=workspace, stream=stream, kv_scales=scales)))
             for launch, cps, units, fn in cases:
                 t = timed(fn, args.steps)
                 print(json.dumps({
-                    "workload": wi, "desc": W.WORKLOADS[wi], "pages": "int8" if q8 else "bf16",
+                    "workload": wi, "desc": W.WORKLOADS[wi], "pages": fmt,
                     "launch": launch, "pages_per_split": int(cps),
                     ("items" if launch == "work list" else "splits"): int(units),
                     "step_us": round(t * 1e6, 2), "kv_bytes": int(kv),
                     "kv_gbps": round(kv / t / 1e9, 1),
                     "seq_per_s_per_layer": round(int(np.count_nonzero(w.seq_lens)) / t, 1)}),
                     flush=True)
-        del q, kp, vp, kn, vn, bt, lens, out, kc, vc, sc
+        del q, kp, vp, kn, vn, bt, lens, out, kc, vc, sc, kc4, vc4, sc4, formats, cases
         torch.cuda.empty_cache()
 
     # workload 3 as a model step: the 16 layers' fused steps back to back (one
@@ -505,6 +514,24 @@ def main() -> int:
     log(f"{K} INT8-page steps done")
     del q8_k, q8_v, q8_s
 
+    # pass F: the same over INT4 pages (quantised on the GPU as for pass E)
+    q4_k, q4_v, q4_s = pa.new_q4_pools(npg, device=dev)
+    pa.fill_kv_q4(k_pool.view(npg * 16, 8, 64), v_pool.view(npg * 16, 8, 64), ident, 0,
+                  q4_k, q4_v, q4_s, stream=stream)
+    ps4, ns4 = pa.decode_plan_lengths_q4(batch.seq_lens, npg, max_seq_len=msl)
+    out_q4 = torch.empty_like(out)
+
+    def q4_step():
+        pa.append_decode_attention_q4(q, k_new, v_new, q4_k, q4_v, q4_s, bt, lens, msl,
+                                      scale=batch.scale, out=out_q4, pages_per_split=ps4,
+                                      workspace=workspace, stream=stream)
+    for _ in range(Wm):
+        pre_step()
+        q4_step()
+    t_q4 = timed(q4_step, K)
+    log(f"{K} INT4-page steps done")
+    del q4_k, q4_v, q4_s
+
     # diagnostic: the same step with the pages in identity order (each
     # sequence's pages consecutive in the pool)
     order = bt.reshape(-1).long()
@@ -529,6 +556,7 @@ def main() -> int:
     by = A.step_bytes(batch.seq_lens, out_bytes=4, append=True)
     kv = by["kv"]
     by_q8 = A.step_bytes_q8(batch.seq_lens)["kv"]
+    by_q4 = A.step_bytes_q4(batch.seq_lens)["kv"]
     mean_step = float(t_step.mean())
     value = kv / mean_step / 1e9
     achieved = kv / float(t_main.mean()) / 1e9
@@ -589,6 +617,19 @@ def main() -> int:
             "seq_per_s_per_layer": round(B / float(t_q8.mean()), 1),
             "format": "int8 codes + one FP32 scale per (token, KV head) row, K and V",
             "traffic": measured_traffic(TRAFFIC_FILE_Q8, KERNEL_SOURCES_Q8),
+            "kernel_source_sha": kernel_source_hash(KERNEL_SOURCES_Q8),
+        },
+        "int4_pages": {
+            "step_us": round(float(t_q4.mean()) * 1e6, 2),
+            "step_min_us": round(float(t_q4.min()) * 1e6, 2),
+            "pages_per_split": ps4, "splits": ns4,
+            "kv_bytes": by_q4,
+            "kv_gbps": round(by_q4 / float(t_q4.mean()) / 1e9, 2),
+            "hbm_peak_frac": round(by_q4 / float(t_q4.mean()) / 1e9 / HBM_PEAK_GBPS, 4),
+            "speedup_vs_bf16_step": round(mean_step / float(t_q4.mean()), 3),
+            "seq_per_s_per_layer": round(B / float(t_q4.mean()), 1),
+            "format": "int4 codes, two per byte, + one FP32 scale per (token, KV head) row, K and V",
+            "traffic": measured_traffic(TRAFFIC_FILE_Q4, KERNEL_SOURCES_Q8),
             "kernel_source_sha": kernel_source_hash(KERNEL_SOURCES_Q8),
         },
         "roofline": {

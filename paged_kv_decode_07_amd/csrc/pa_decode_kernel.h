@@ -59,14 +59,18 @@
 // normaliser sums w alone.
 //
 // INT4 pages: a nibble u = code + 8 becomes the BF16 value 16 + u = code + 24
-// with two bit operations per pair (no conversion instruction); the bias is
-// removed after each product.  Scores: 24 x (the sum of the query row) is
-// subtracted before the K scale.  Values: each lane also sums its weights
-// (w * v_scale), rescaled with the accumulators, and 24 x that sum is
-// subtracted from the output.  The packed K word gives its dims in the order
-// 0 4 1 5 2 6 3 7, and the query operand is permuted to match.  One
-// transposed read gives a lane 4 tokens x 4 dims (the 16-bit unit is 4
-// codes), so tile e of the value product is dims 4n + e.
+// with a shift and one mask-and-or per pair (no conversion instruction); the
+// bias is removed around each product.  Scores: -24 x (the sum of the query
+// row) is the accumulator input of the score product.  Values: each lane also
+// sums its weights (w * v_scale), rescaled with the accumulators, and 24 x
+// that sum is subtracted from the output.  The packed K word gives its dims
+// in the order 0 4 1 5 2 6 3 7, and the query operand is permuted to match.
+// One transposed read gives a lane 4 tokens x 4 dims (the 16-bit unit is 4
+// codes), so tile e of the value product is dims 4n + e.  With its smaller
+// pages this format is bound by the arithmetic per page rather than by HBM:
+// its 3-deep ring lets full pages be consumed two at a time (one vote and
+// rescale for both, one 16x16x32 value product per tile over their 32
+// tokens).
 //
 // Masking: slots past the sequence in its last page may hold any bits.  Their
 // scores are selected to -inf, their weights to 0, and for BF16 pages their V
