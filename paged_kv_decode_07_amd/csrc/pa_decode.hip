@@ -200,7 +200,7 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
   const int S = ceil_div(max_pages, ps);
   const double chip_rate = m.hbm_bytes_per_us / m.page_bytes;    // pages/us, whole chip
   const double cu_rate = 1.0 / m.page_us;                        // pages/us, one CU alone
-  const int per_xcd = cu / xcds > 0 ? cu / xcds : 1;
+  const int per_xcd = (cu / xcds > 0 ? cu / xcds : 1) * (m.resident > 1 ? m.resident : 1);
   struct Item { double fixed, pages; };
   std::vector<Item> items;
   items.reserve((size_t)batch * S);
@@ -241,7 +241,11 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
   for (int x = 0; x < xcds; ++x) fill(x);
   while (!fixed_end.empty() || !stream_end.empty()) {
     const int ns = (int)stream_end.size();
-    const double r = ns > 0 ? std::min(cu_rate, chip_rate / ns) : cu_rate;
+    // beyond one streaming work-group per CU, each extra one adds
+    // (shared_gain - 1) of a CU's rate (work-groups spread evenly over CUs)
+    const double cap = ns <= cu ? cu_rate
+                                : cu_rate * (cu + (ns - cu) * (m.shared_gain - 1.0)) / ns;
+    const double r = ns > 0 ? std::min(cap, chip_rate / ns) : cu_rate;
     const double dt_fixed = fixed_end.empty() ? 1e300 : fixed_end.top().first - t;
     const double dt_stream = stream_end.empty() ? 1e300 : (stream_end.top().first - V) / r;
     if (dt_fixed <= dt_stream) {
@@ -290,12 +294,20 @@ int plan_split_lengths(const pa_shape* s, int batch, const int32_t* lens, int ma
     const int L = lens[b] < 0 ? 0 : (lens[b] > max_seq_len ? max_seq_len : lens[b]);
     min_pages = std::min(min_pages, ceil_div(L, pa::kPage));
   }
-  const bool long_splits = !worklist || (batch >= cu && 2 * min_pages >= max_pages);
+  const bool even = 2 * min_pages >= max_pages;
+  const bool long_splits = !worklist || (batch >= cu && even);
+  // The model spreads work-groups that share a CU evenly over the CUs, which
+  // holds when they all stream about as long.  In a skewed batch two long
+  // work-groups can stay paired on one CU to the end (INT4 pages, 512-sequence
+  // Zipf batch, 128-page grid: modelled 68 us, measured 111 us), so such a
+  // batch is planned with one work-group per CU.
+  PlanModel mm = model;
+  if (!even) mm.resident = 1;
   for (int ps : {8, 16, 32, 64, 128, 256}) {
     if (!long_splits && ps > 64) break;
     const int cand = ps < max_pages ? ps : max_pages;
     if (cand > s->max_blocks_per_seq || cand > pa::kMaxSplitPages) break;
-    cands.push_back({cand, simulate_plan(lens, batch, max_seq_len, cand, cu, xcds, model,
+    cands.push_back({cand, simulate_plan(lens, batch, max_seq_len, cand, cu, xcds, mm,
                                          worklist)});
     if (cand == max_pages) break;
   }

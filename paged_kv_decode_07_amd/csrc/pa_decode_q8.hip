@@ -135,13 +135,18 @@ PlanModel plan_model_q8() {
 // fixed costs were fitted to this kernel's measured times on MI355X over
 // batches of 8 to 512 sequences (uniform and Zipf lengths) and split sizes
 // 8 .. 128 pages; at this page size the per-page arithmetic, not HBM, sets
-// the rate.
+// the rate.  Two work-groups fit on a CU (92 VGPRs, 30 KiB of LDS each), and
+// two sharing a CU stream 1.3x the pages of one alone: at 256 sequences of
+// 2,048 tokens, 64-page splits (two per CU) measured 69.2 us against 74.8 us
+// for one 128-page split per CU.
 PlanModel plan_model_q4() {
   PlanModel m;
   m.page_bytes = 2.0 * pa::kPageCodes4 + pa::kScalePageFloats * 4.0;
   m.page_us = 0.5;
   m.group_us = 2.0;
   m.empty_us = 0.5;
+  m.resident = 2;
+  m.shared_gain = 1.3;
   return m;
 }
 
