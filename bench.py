@@ -520,17 +520,20 @@ def main() -> int:
                   q4_k, q4_v, q4_s, stream=stream)
     ps4, ns4 = pa.decode_plan_lengths_q4(batch.seq_lens, npg, max_seq_len=msl)
     out_q4 = torch.empty_like(out)
+    # the INT4 plan may split where the BF16 one does not: a workspace of its own
+    ws4 = torch.empty(max(pa.decode_workspace_bytes(B, msl, npg, 128, ps4), 256),
+                      dtype=torch.uint8, device=dev)
 
     def q4_step():
         pa.append_decode_attention_q4(q, k_new, v_new, q4_k, q4_v, q4_s, bt, lens, msl,
                                       scale=batch.scale, out=out_q4, pages_per_split=ps4,
-                                      workspace=workspace, stream=stream)
+                                      workspace=ws4, stream=stream)
     for _ in range(Wm):
         pre_step()
         q4_step()
     t_q4 = timed(q4_step, K)
     log(f"{K} INT4-page steps done")
-    del q4_k, q4_v, q4_s
+    del q4_k, q4_v, q4_s, ws4
 
     # diagnostic: the same step with the pages in identity order (each
     # sequence's pages consecutive in the pool)
