@@ -25,17 +25,24 @@
 //
 //   * scores are computed transposed, S^T = K Q^T, with one
 //     v_mfma_f32_16x16x32_bf16 per 32 dims: the A operand is the page's K
-//     (row = token, 8 dims per lane), the B operand is Q^T with the 4 query
-//     heads repeated over the 16 columns.  Lane l = 16 G + n receives the
-//     scores of tokens 4G .. 4G+3 for head slot n (query head 4g + n % 4),
-//     scaled by scale * log2(e) so that exp2 is the hardware v_exp_f32;
-//   * that is exactly the A-operand layout of v_mfma_f32_16x16x16_bf16 with
-//     k = tokens: row n, tokens 4G .. 4G+3.  So P V runs on the matrix cores
-//     with no data movement between the two products: rows 0..3 carry the
-//     weights of heads 0..3 rounded to BF16, rows 4..7 the remainders
-//     (weight - its BF16 value, rounded again), rows 8..15 zero; one
-//     product per 16 output dims accumulates both parts, summed at the end
-//     (each weight is carried to about 2^-16 relative);
+//     (row = token, 8 dims per lane), the B operand is Q^T with column n
+//     holding query head 4g + n / 4, so each head fills the 4 columns of one
+//     quad of lanes.  Lane l = 16 G + n receives the scores of tokens
+//     4G .. 4G+3 for column n; of these it keeps one, token 4G + n % 4, so
+//     the 16 lanes of a head's quads in the four token groups hold its 16
+//     scores once each.  The softmax then costs one exp2 per lane and page
+//     (scores scaled by scale * log2(e) so that exp2 is the hardware
+//     v_exp_f32);
+//   * the P V product is v_mfma_f32_16x16x16_bf16 with k = tokens, whose A
+//     operand lane 16 G + n supplies row n, tokens 4G .. 4G+3.  Each lane
+//     packs its weight rounded to BF16 and the remainder (weight - its BF16
+//     value, rounded again) into one word; a quad broadcast (DPP quad_perm)
+//     gives every lane of the quad the words of its head's four tokens, and
+//     v_perm keeps the BF16 halves for rows 4h, 4h+2 and the remainders for
+//     rows 4h+1, 4h+3 (h = n / 4).  Each weight is carried to about 2^-16
+//     relative.  Output rows 4G and 4G+1 of lane 16 G + n add up to head G's
+//     unnormalised output in column n; rows 4G+2, 4G+3 repeat them and are
+//     never read;
 //   * V reaches the B operand (column = dim, k = 4 tokens per lane) through
 //     gfx950's transposing LDS read ds_read_b64_tr_b16: within each group of
 //     16 lanes, output lane i takes element i % 4 of the 4-element chunks
@@ -46,17 +53,18 @@
 //   * the online softmax keeps one running maximum per head, equal in every
 //     lane of that head (the product sums over tokens, so a page's weights
 //     share it); it is raised only when a score exceeds it by more than
-//     kTau (a wave-wide vote; the page maximum is then reduced across the
-//     four token groups).  Weights are then at most 2^kTau and the rescale
+//     kTau (a wave-wide vote; the page maximum is then reduced over the
+//     head's 16 lanes).  Weights are then at most 2^kTau and the rescale
 //     of the accumulators is almost never executed after the first page.  The
-//     normaliser is a per-lane partial sum, reduced at the end;
+//     normaliser is a per-lane partial sum, reduced over the head's lanes at
+//     the end;
 //   * the accumulator is 4 products x 4 floats per lane (16 VGPRs), and the
 //     VALU carries no multiply-add of P V.
 //
 // INT8 pages: K codes are widened to BF16 exactly for the score product and
 // the K scale of each token joins the score multiplier; V codes are widened
-// to BF16 exactly and the V scale joins the weight (w * v_scale), while the
-// normaliser sums w alone.
+// to BF16 exactly and the V scale joins the weight (p * v_scale), while the
+// normaliser sums p alone.
 //
 // INT4 pages: a nibble u = code + 8 becomes the BF16 value 16 + u = code + 24
 // with a shift and one mask-and-or per pair (no conversion instruction); the
@@ -169,12 +177,12 @@ struct SlotAddrBF16 {
 struct PageQ8 {
   u32x2 k0, k1;       // K codes, 8 dims each
   u32x2 v[2];         // V codes: 4 tokens x (even, odd) dim pairs, dims 0..31 and 32..63
-  u32x4 ks, vs;       // K and V scales of tokens 4G .. 4G+3
+  uint32_t ks, vs;    // K and V scales of this lane's token 4G + n % 4
 };
 struct PageQ4 {
   uint32_t k0, k1;    // K codes of token n, dims 8G .. 8G+7 and 32+8G .. 32+8G+7
   u32x2 v;            // V codes: 4 tokens x dims 4n .. 4n+3 (transposed read)
-  u32x4 ks, vs;       // K and V scales of tokens 4G .. 4G+3
+  uint32_t ks, vs;    // K and V scales of this lane's token 4G + n % 4
 };
 
 // The slot's reads for one lane: its two K pieces and its transposed-read
@@ -196,7 +204,8 @@ __device__ __forceinline__ void lds_page_ready(PageBF16& r) {
   asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(r.k0), "+v"(r.k1), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.v[2]), "+v"(r.v[3])::"memory");
 }
-// kaddr: K codes of (token, 8G); vaddr: V chunk of this lane; saddr: scales + 16 G.
+// kaddr: K codes of (token, 8G); vaddr: V chunk of this lane; saddr: the K
+// scale of token 4G + n % 4 (its V scale 64 bytes on).
 __device__ __forceinline__ void lds_page_issue(PageQ8& r, uint32_t kaddr, uint32_t vaddr,
                                          uint32_t saddr) {
   asm volatile(
@@ -204,8 +213,8 @@ __device__ __forceinline__ void lds_page_issue(PageQ8& r, uint32_t kaddr, uint32
       "ds_read_b64 %1, %6 offset:32\n\t"
       "ds_read_b64_tr_b16 %2, %7\n\t"
       "ds_read_b64_tr_b16 %3, %7 offset:32\n\t"
-      "ds_read_b128 %4, %8\n\t"
-      "ds_read_b128 %5, %8 offset:64"
+      "ds_read_b32 %4, %8\n\t"
+      "ds_read_b32 %5, %8 offset:64"
       : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.ks), "=&v"(r.vs)
       : "v"(kaddr), "v"(vaddr), "v"(saddr)
       : "memory");
@@ -215,15 +224,16 @@ __device__ __forceinline__ void lds_page_ready(PageQ8& r) {
                : "+v"(r.k0), "+v"(r.k1), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ks), "+v"(r.vs)::"memory");
 }
 
-// kaddr: K codes of (token n, dims 8G..); vaddr: V chunk of this lane; saddr: scales + 16 G.
+// kaddr: K codes of (token n, dims 8G..); vaddr: V chunk of this lane; saddr:
+// the K scale of token 4G + n % 4 (its V scale 64 bytes on).
 __device__ __forceinline__ void lds_page_issue(PageQ4& r, uint32_t kaddr, uint32_t vaddr,
                                          uint32_t saddr) {
   asm volatile(
       "ds_read_b32 %0, %5\n\t"
       "ds_read_b32 %1, %5 offset:16\n\t"
       "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "ds_read_b128 %4, %7 offset:64"
+      "ds_read_b32 %3, %7\n\t"
+      "ds_read_b32 %4, %7 offset:64"
       : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v), "=&v"(r.ks), "=&v"(r.vs)
       : "v"(kaddr), "v"(vaddr), "v"(saddr)
       : "memory");
@@ -257,6 +267,7 @@ struct LaneState {
 struct PageConsts {
   float xscale;
   float qbias;
+  uint32_t sel;        // v_perm selector of the weight operand (row parity)
   NibbleConsts nib;
 };
 
@@ -283,23 +294,34 @@ __device__ __forceinline__ f32x4_t page_scores(const Page& r, bf16x8_t qlo, bf16
   return s;
 }
 
-// Scores in log2 units (scale, log2(e) and the K scale applied).
-template <int FMT, typename Page>
-__device__ __forceinline__ void page_logits(const Page& r, f32x4_t s, float xscale, float* x) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float xs = xscale;
-    if constexpr (FMT != kFmtBF16) xs = xscale * __uint_as_float(r.ks[c]);
-    x[c] = s[c] * xs;
-  }
+// This lane's own score: element q = n % 4 of its 4 (tokens 4G .. 4G+3 of
+// column n), i.e. token 4G + q of query head n / 4.
+__device__ __forceinline__ float own_score(f32x4_t s, int q) {
+  float v = s[0];
+  v = q == 1 ? s[1] : v;
+  v = q == 2 ? s[2] : v;
+  v = q == 3 ? s[3] : v;
+  return v;
 }
 
-// Raise the running maximum when a score passed it by more than kTau (the
-// page maximum mx is this lane's; the new maximum is reduced over the four
-// token groups) and rescale the accumulators.
-__device__ __forceinline__ void raise_max(LaneState& st, float mx) {
+// The lane's score in log2 units (scale, log2(e) and the K scale applied).
+template <int FMT, typename Page>
+__device__ __forceinline__ float page_logit(const Page& r, f32x4_t s, float xscale, int q) {
+  float xs = xscale;
+  if constexpr (FMT != kFmtBF16) xs = xscale * __uint_as_float(r.ks);
+  return own_score(s, q) * xs;
+}
+
+// Raise the running maximum when a score passed it by more than kTau (mx is
+// this lane's score; the new maximum is reduced over the 16 lanes of the
+// head: its quad and the four token groups) and rescale.  The normaliser and
+// weight sum belong to the lane's head n / 4; the accumulator rows of lane
+// 16 G + n belong to head G, whose factor is taken from lane 4G.
+__device__ __forceinline__ void raise_max(LaneState& st, float mx, int G) {
   if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau)) {
     float pm = mx;
+    pm = fmaxf(pm, dpp_mov<0xB1>(pm));          // quad_perm [1,0,3,2]
+    pm = fmaxf(pm, dpp_mov<0x4E>(pm));          // quad_perm [2,3,0,1]
     pm = fmaxf(pm, __shfl_xor(pm, 16));
     pm = fmaxf(pm, __shfl_xor(pm, 32));
     const float mn = (pm > st.m + kTau) ? pm : st.m;
@@ -307,32 +329,40 @@ __device__ __forceinline__ void raise_max(LaneState& st, float mx) {
     st.m = mn;
     st.l *= a;
     st.wsum *= a;
-    // rows 4G + r of this lane's tiles belong to head r (rows 0..7)
+    const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), 0));
+    const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), 4));
+    const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), 8));
+    const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), 12));
+    const float ag = G == 0 ? a0 : (G == 1 ? a1 : (G == 2 ? a2 : a3));
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float ar = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), rr));
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) st.acc[b][rr] *= ar;
-    }
+      for (int rr = 0; rr < 4; ++rr) st.acc[b][rr] *= ag;
   }
 }
 
-// A operand of the P V product: rows 0..3 the BF16 weights, rows 4..7 their
-// remainders (weight - its BF16 value is exact in FP32, then rounded again),
-// rows 8..15 zero.  Every lane computes both and selects, so the wave does
-// not diverge.
-__device__ __forceinline__ bf16x4_t weight_operand(const float* w, int n) {
-  const uint32_t h01 = pack_bf16_rne(w[0], w[1]);
-  const uint32_t h23 = pack_bf16_rne(w[2], w[3]);
-  const uint32_t r01 = pack_bf16_rne(w[0] - bf16_lo(h01), w[1] - bf16_hi(h01));
-  const uint32_t r23 = pack_bf16_rne(w[2] - bf16_lo(h23), w[3] - bf16_hi(h23));
-  u32x2 pa;
-  pa.x = n < 4 ? h01 : (n < 8 ? r01 : 0u);
-  pa.y = n < 4 ? h23 : (n < 8 ? r23 : 0u);
-  return __builtin_bit_cast(bf16x4_t, pa);
+// A operand of the P V product, built from each lane's own weight w (token
+// 4G + q of head h = n / 4, q = n % 4).  Row n = 4h + q carries, for tokens
+// 4G .. 4G+3 of head h, the BF16 weights (q even) or their remainders (q
+// odd: weight - its BF16 value, rounded again); rows 4h+2 and 4h+3 repeat
+// rows 4h and 4h+1 and their products are never read.  Each lane packs its
+// weight and remainder into one word; a quad broadcast gives every lane of
+// the quad the four tokens' words, and v_perm keeps the halves of its row.
+// sel: 0x05040100 (q even, low halves) or 0x07060302 (q odd, high halves).
+__device__ __forceinline__ bf16x4_t weight_operand(float w, uint32_t sel) {
+  const uint32_t h = pack_bf16_rne(w, 0.f);
+  const uint32_t hr = pack_bf16_rne(w, w - bf16_lo(h));     // [BF16(w) | BF16(remainder)]
+  // quad_perm [c,c,c,c] (control 0x55 c): every lane of the quad gets lane c's word
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hr, 0x00, 0xF, 0xF, false);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hr, 0x55, 0xF, 0xF, false);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hr, 0xAA, 0xF, 0xF, false);
+  const uint32_t t3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hr, 0xFF, 0xF, 0xF, false);
+  u32x2 a;
+  a.x = __builtin_amdgcn_perm(t1, t0, sel);                  // tokens 4G, 4G+1
+  a.y = __builtin_amdgcn_perm(t3, t2, sel);                  // tokens 4G+2, 4G+3
+  return __builtin_bit_cast(bf16x4_t, a);
 }
 
-// acc += A V for one page (BF16 pages: V of dead slots already zeroed).
 // B operands of the P V product for one page: tile t (16 output dims) as 4
 // BF16 values, tokens 4G .. 4G+3 of this lane's column (BF16 pages: V of
 // dead slots already zeroed; INT4: code + 24).
@@ -375,23 +405,20 @@ __device__ __forceinline__ void page_pv(LaneState& st, const Page& r, bf16x4_t A
                                                           st.acc[b], 0, 0, 0);
 }
 
-// Weights of 4 tokens (p: softmax numerators; w: the P V operand, p times
-// the V scale for quantised pages), dead slots (MASK) at 0.
+// The lane's weight (p: softmax numerator; w: the P V weight, p times the V
+// scale for quantised pages), a dead slot (MASK, own token at or past
+// `valid`) at 0.
 template <int FMT, bool MASK, typename Page>
-__device__ __forceinline__ void page_weights(LaneState& st, const Page& r, const float* x, int G,
-                                             int valid, float* w) {
-  float p[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    p[c] = __builtin_amdgcn_exp2f(x[c] - st.m);           // masked: exp2(-inf) = 0
-    w[c] = p[c];
-    if constexpr (FMT != kFmtBF16) {
-      w[c] = p[c] * __uint_as_float(r.vs[c]);
-      if (MASK) w[c] = (4 * G + c < valid) ? w[c] : 0.f;  // scale bits of a dead slot
-    }
+__device__ __forceinline__ float page_weight(LaneState& st, const Page& r, float x, bool dead) {
+  const float p = __builtin_amdgcn_exp2f(x - st.m);         // masked: exp2(-inf) = 0
+  float w = p;
+  if constexpr (FMT != kFmtBF16) {
+    w = p * __uint_as_float(r.vs);
+    if (MASK) w = dead ? 0.f : w;                            // scale bits of a dead slot
   }
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  if constexpr (FMT == kFmtINT4) st.wsum += (w[0] + w[1]) + (w[2] + w[3]);
+  st.l += p;
+  if constexpr (FMT == kFmtINT4) st.wsum += w;
+  return w;
 }
 
 // One page into the running state; MASK: only the first `valid` tokens exist.
@@ -399,17 +426,13 @@ template <int FMT, bool MASK, typename Page>
 __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t qlo, bf16x8_t qhi,
                                            const PageConsts& pc, int lane, int valid) {
   const int G = lane >> 4;            // token group: tokens 4G .. 4G+3
-  const int n = lane & 15;            // head slot (query head 4g + n%4); P row
-  float x[4];
-  page_logits<FMT>(r, page_scores<FMT>(r, qlo, qhi, pc), pc.xscale, x);
-  if (MASK) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = (4 * G + c < valid) ? x[c] : -INFINITY;
-  }
-  raise_max(st, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-  float w[4];
-  page_weights<FMT, MASK>(st, r, x, G, valid, w);
-  const bf16x4_t A = weight_operand(w, n);
+  const int q = lane & 3;             // own token 4G + q (head n / 4)
+  float x = page_logit<FMT>(r, page_scores<FMT>(r, qlo, qhi, pc), pc.xscale, q);
+  const bool dead = MASK && 4 * G + q >= valid;
+  if (MASK) x = dead ? -INFINITY : x;
+  raise_max(st, x, G);
+  const float w = page_weight<FMT, MASK>(st, r, x, dead);
+  const bf16x4_t A = weight_operand(w, pc.sel);
   if constexpr (FMT == kFmtBF16) {
     if (MASK) {
       // tokens 4G .. 4G+3 sit in (lo, hi) halves of the two words
@@ -430,22 +453,18 @@ __device__ __forceinline__ void consume_pages2(LaneState& st, const Page& ra, co
                                                bf16x8_t qlo, bf16x8_t qhi, const PageConsts& pc,
                                                int lane) {
   const int G = lane >> 4;
-  const int n = lane & 15;
+  const int q = lane & 3;
   const f32x4_t sa = page_scores<FMT>(ra, qlo, qhi, pc);
   const f32x4_t sb = page_scores<FMT>(rb, qlo, qhi, pc);
-  float xa[4], xb[4];
-  page_logits<FMT>(ra, sa, pc.xscale, xa);
-  page_logits<FMT>(rb, sb, pc.xscale, xb);
-  const float mx = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
-                         fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])));
-  raise_max(st, mx);
-  float wa[4], wb[4];
-  page_weights<FMT, false>(st, ra, xa, G, kPage, wa);
-  page_weights<FMT, false>(st, rb, xb, G, kPage, wb);
+  const float xa = page_logit<FMT>(ra, sa, pc.xscale, q);
+  const float xb = page_logit<FMT>(rb, sb, pc.xscale, q);
+  raise_max(st, fmaxf(xa, xb), G);
+  const float wa = page_weight<FMT, false>(st, ra, xa, false);
+  const float wb = page_weight<FMT, false>(st, rb, xb, false);
   // one product over 32 tokens per tile: k = 8G .. 8G+7 of this lane are
   // tokens 4G .. 4G+3 of page a, then of page b, in both operands
-  const bf16x4_t Aa = weight_operand(wa, n);
-  const bf16x4_t Ab = weight_operand(wb, n);
+  const bf16x4_t Aa = weight_operand(wa, pc.sel);
+  const bf16x4_t Ab = weight_operand(wb, pc.sel);
   const u32x4 A8 = {__builtin_bit_cast(u32x2, Aa).x, __builtin_bit_cast(u32x2, Aa).y,
                     __builtin_bit_cast(u32x2, Ab).x, __builtin_bit_cast(u32x2, Ab).y};
   u32x2 va[4], vb[4];
@@ -512,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   }
   uint4 q_lo, q_hi;
   {
-    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (n & 3)) * kD + 8 * G;
+    const uint16_t* qr = a.q + ((int64_t)b * kHq + kGroup * g + (n >> 2)) * kD + 8 * G;
     q_lo = *reinterpret_cast<const uint4*>(qr);
     q_hi = *reinterpret_cast<const uint4*>(qr + 32);
   }
@@ -555,6 +574,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   PageConsts pc;                 // xscale; INT4: the query bias and the widening constants
   pc.xscale = a.xscale;
   pc.qbias = 0.f;
+  pc.sel = (n & 1) ? 0x07060302u : 0x05040100u;
   if constexpr (Q4) pc.nib = nibble_consts();
 
   // fused append: the new rows (K rotated first with RoPE) are parked in LDS,
@@ -644,13 +664,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   if constexpr (Q8) {
     ka = slot0 + 64 * n + 8 * G;
     va = slot0 + 1024 + 64 * (4 * G + jq) + 8 * jr;
-    sa = slot0 + 2048 + 16 * G;
+    sa = slot0 + 2048 + 4 * (4 * G + (n & 3));
   } else if constexpr (Q4) {
     // K: token n, bytes 4G (dims 8G ..) and 16 + 4G; V: dims 16 jr .. 16 jr + 15
     // of token 4G + jq, so that lane n receives dims 4n .. 4n+3 of 4 tokens
     ka = slot0 + 32 * n + 4 * G;
     va = slot0 + 512 + 32 * (4 * G + jq) + 8 * jr;
-    sa = slot0 + 1024 + 16 * G;
+    sa = slot0 + 1024 + 4 * (4 * G + (n & 3));
   } else {
     // K: token n, pieces G and G + 4; V block b (dims 16b .. 16b+15): dims
     // 4 jr .. 4 jr + 3 of token 4G + jq are bytes 8 (jr % 2) of piece 2b + jr/2
@@ -810,70 +830,59 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // finish: the normaliser over the 4 token groups; the BF16 and remainder
-  // rows of each head added (lane n of group 0 gets lane n of group 1)
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
-  float o[4][4];                                 // [tile][row = head]
+  // finish: the normaliser and weight sum of head n / 4 over its 16 lanes
+  // (the quad and the four token groups); lane 16 G + n then takes head G's
+  // values from lane 4G, and its tiles' rows 4G (BF16 weights) and 4G + 1
+  // (remainders) add up to head G's unnormalised output at column n
+  auto head_sum = [](float v) {
+    v += dpp_mov<0xB1>(v);                       // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);                       // quad_perm [2,3,0,1]
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+  };
+  auto of_head = [G](float v) {                  // v of head G (from lane 4G)
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 4));
+    const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 8));
+    const float v3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 12));
+    return G == 0 ? v0 : (G == 1 ? v1 : (G == 2 ? v2 : v3));
+  };
+  st.l = head_sum(st.l);
+  float o[4];                                    // [tile]: head G, column n
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) o[t][rr] = st.acc[t][rr] + __shfl_down(st.acc[t][rr], 16);
+  for (int t = 0; t < 4; ++t) o[t] = st.acc[t][0] + st.acc[t][1];
   if constexpr (Q4) {
     // the values were code + 24: take 24 x the head's weight sum back out
-    st.wsum += __shfl_xor(st.wsum, 16);
-    st.wsum += __shfl_xor(st.wsum, 32);
+    const float bias = kNibbleBias4 * of_head(head_sum(st.wsum));
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float bias = kNibbleBias4 * __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.wsum), rr));
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[t][rr] -= bias;
-    }
+    for (int t = 0; t < 4; ++t) o[t] -= bias;
   }
-
-  float m_out = st.m, l_out = st.l;
+  float m_out = of_head(st.m), l_out = of_head(st.l);
   if (bad_page) {
     m_out = __builtin_nanf("");
     l_out = __builtin_nanf("");
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) o[t][rr] = __builtin_nanf("");
+    for (int t = 0; t < 4; ++t) o[t] = __builtin_nanf("");
   }
-  // head r's m and l live in lanes with n % 4 == r; lane n (group 0) needs all 4
-  float mh[4], lh[4];
+  if (n_splits_b == 1) {
+    const float inv = 1.f / l_out;
+    const int64_t orow = ((int64_t)b * kHq + kGroup * g + G) * kD;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    mh[rr] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_out), rr));
-    lh[rr] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_out), rr));
-  }
-  if (G == 0) {
-    if (n_splits_b == 1) {
+    for (int t = 0; t < 4; ++t) {
+      const int d = out_dim<FMT>(t, n);
+      if (OUT_BF16)
+        reinterpret_cast<uint16_t*>(a.out)[orow + d] = (uint16_t)f32_to_bf16_rne(o[t] * inv);
+      else
+        reinterpret_cast<float*>(a.out)[orow + d] = o[t] * inv;
+    }
+  } else {
+    const int64_t prow = ((int64_t)b * a.num_splits + s) * kHq + kGroup * g + G;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float inv = 1.f / lh[rr];
-        const int64_t orow = ((int64_t)b * kHq + kGroup * g + rr) * kD;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int d = out_dim<FMT>(t, n);
-          if (OUT_BF16)
-            reinterpret_cast<uint16_t*>(a.out)[orow + d] = (uint16_t)f32_to_bf16_rne(o[t][rr] * inv);
-          else
-            reinterpret_cast<float*>(a.out)[orow + d] = o[t][rr] * inv;
-        }
-      }
-    } else {
-      const int64_t prow = ((int64_t)b * a.num_splits + s) * kHq + kGroup * g;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a.part_acc[(prow + rr) * kD + out_dim<FMT>(t, n)] = o[t][rr];
-        if (n == 0) {
-          a.part_ml[(prow + rr) * 2 + 0] = mh[rr];
-          a.part_ml[(prow + rr) * 2 + 1] = lh[rr];
-        }
-      }
+    for (int t = 0; t < 4; ++t) a.part_acc[prow * kD + out_dim<FMT>(t, n)] = o[t];
+    if (n == 0) {
+      a.part_ml[prow * 2 + 0] = m_out;
+      a.part_ml[prow * 2 + 1] = l_out;
     }
   }
 }
