@@ -70,7 +70,7 @@
 // with a shift and one mask-and-or per pair (no conversion instruction); the
 // bias is removed around each product.  Scores: -24 x (the sum of the query
 // row) is the accumulator input of the score product.  Values: each lane also
-// sums its weights (w * v_scale), rescaled with the accumulators, and 24 x
+// sums its weights (p * v_scale), rescaled with the accumulators, and 24 x
 // that sum is subtracted from the output.  The packed K word gives its dims
 // in the order 0 4 1 5 2 6 3 7, and the query operand is permuted to match.
 // One transposed read gives a lane 4 tokens x 4 dims (the 16-bit unit is 4
