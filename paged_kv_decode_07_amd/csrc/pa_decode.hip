@@ -218,6 +218,10 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
   if (worklist)
     std::stable_sort(items.begin(), items.end(),
                      [](const Item& x, const Item& y) { return x.pages > y.pages; });
+  // two wavefronts per KV head when the plan's grid (batch x splits) fits the
+  // CUs and the splits are long enough
+  const bool two_waves = (int64_t)batch * S <= cu && ps >= kTwoWaveMinPages;
+  const double cu_rate1 = two_waves ? cu_rate * m.two_wave_gain : cu_rate;
   // Streaming progress is tracked in virtual pages V (every streaming
   // work-group advances by the same rate), so a work-group that starts
   // streaming r pages at V0 ends when V reaches V0 + r.
@@ -243,9 +247,9 @@ double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, in
     const int ns = (int)stream_end.size();
     // beyond one streaming work-group per CU, each extra one adds
     // (shared_gain - 1) of a CU's rate (work-groups spread evenly over CUs)
-    const double cap = ns <= cu ? cu_rate
+    const double cap = ns <= cu ? cu_rate1
                                 : cu_rate * (cu + (ns - cu) * (m.shared_gain - 1.0)) / ns;
-    const double r = ns > 0 ? std::min(cap, chip_rate / ns) : cu_rate;
+    const double r = ns > 0 ? std::min(cap, chip_rate / ns) : cu_rate1;
     const double dt_fixed = fixed_end.empty() ? 1e300 : fixed_end.top().first - t;
     const double dt_stream = stream_end.empty() ? 1e300 : (stream_end.top().first - V) / r;
     if (dt_fixed <= dt_stream) {
@@ -538,7 +542,8 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   int cu = 0;
   const bool merge_preload = current_cu_count(&cu) == PA_OK && batch <= cu;
   const hipError_t e = pa::launch_decode<pa::kFmtBF16>(a, batch, out_dtype == PA_OUT_BF16, fused,
-                                                rope != nullptr, merge_preload, (hipStream_t)stream,
+                                                rope != nullptr, merge_preload, false,
+                                                (hipStream_t)stream,
                                                 (hipEvent_t)event_before_main,
                                                 (hipEvent_t)event_after_main);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

@@ -494,8 +494,14 @@ __device__ __forceinline__ int out_dim(int b, int n) {
 #endif
 constexpr int kStreamCpol = PA_STREAM_CPOL;
 
-template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE = false>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+// WPH: wavefronts per KV head (1 or 2).  With 2, the two wavefronts of a head
+// stream the first and second half of the split's pages, each with its own
+// ring, and merge their running states through LDS at the end: the
+// occupancy of two work-groups per CU without split partials or a merge
+// launch.
+template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE = false, int WPH = 1>
+__global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeArgs a) {
+  static_assert(WPH == 1 || WPH == 2, "one or two wavefronts per KV head");
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   constexpr bool Q8 = FMT == kFmtINT8;
   constexpr bool Q4 = FMT == kFmtINT4;
@@ -511,7 +517,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     s = a.work[2 * blockIdx.x + 1];
     if ((unsigned)b >= (unsigned)a.batch || (unsigned)s >= (unsigned)a.num_splits) return;
   }
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = wave % kWaves;                  // KV head
+  const int wh = wave / kWaves;                 // which half of the split's pages (WPH = 2)
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4;
   const int n = lane & 15;
@@ -564,7 +572,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   }
 
   const int p1 = min(p0 + a.pages_per_split, n_pages);
-  const int last = p1 - 1;
+  // this wavefront streams pages q0 .. last of the split (all of them for
+  // WPH = 1; with WPH = 2 the second half may be empty)
+  const int per = (p1 - p0 + WPH - 1) / WPH;
+  const int q0 = p0 + wh * per;
+  const int last = min(q0 + per, p1) - 1;
+  const bool has_pages = q0 <= last;
   const int tail_valid = L - last * kPage;
 
 
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 
   // fused append: the new rows (K rotated first with RoPE) are parked in LDS,
   // as BF16 rows or as codes and scales, after the first page requests
-  const bool app_here = APPEND && p1 == n_pages;
+  const bool app_here = APPEND && has_pages && last == n_pages - 1;
   const int app_slot = (L - 1) % kPage;
   __shared__ u32x4 new_rows[APPEND ? kWaves : 1][QUANT ? 8 : 16];   // 16-byte chunks
   __shared__ float new_scales[APPEND && QUANT ? kWaves : 1][2];
@@ -609,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     return ok ? id : 0;
   };
 
-  __shared__ __attribute__((aligned(16))) char ring[F::kRingDepth][kWaves][F::kSlot];
+  __shared__ __attribute__((aligned(16))) char ring[F::kRingDepth][kWaves * WPH][F::kSlot];
   const char* k_base = reinterpret_cast<const char*>(a.k_pool);
   const char* v_base = reinterpret_cast<const char*>(a.v_pool);
   const char* s_base = reinterpret_cast<const char*>(a.kv_scales);
@@ -635,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   }
   auto fetch = [&](int page, int slot) {
     const int64_t id = page_id(page);
-    char* dst = &ring[slot][g][0];
+    char* dst = &ring[slot][wave][0];
     if constexpr (Q8) {
       const int64_t off = id * (int64_t)kPageCodes;
       __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
@@ -656,8 +669,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     }
   };
   // LDS read addresses of this lane in slot 0 of its wavefront
-  const uint32_t slot0 = lds_address(&ring[0][g][0]);
-  constexpr uint32_t kRingSlotBytes = kWaves * F::kSlot;
+  const uint32_t slot0 = lds_address(&ring[0][wave][0]);
+  constexpr uint32_t kRingSlotBytes = kWaves * WPH * F::kSlot;
   const int jq = n >> 2, jr = n & 3;              // transposed-read chunk: token 4G + jq
   uint32_t ka = 0, va = 0, sa = 0;
   SlotAddrBF16 ad{};
@@ -688,12 +701,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       using QL = QuantLayout<Q8 ? kFmtINT8 : kFmtINT4>;
       if (lane < 8) {
         const u32x4 w = new_rows[sl][lane];
-        uint8_t* row = reinterpret_cast<uint8_t*>(&ring[0][g][0]) + (slot_base - slot0) +
+        uint8_t* row = reinterpret_cast<uint8_t*>(&ring[0][wave][0]) + (slot_base - slot0) +
                        (lane < 4 ? 0 : QL::kHead) + QL::kRow * app_slot;
         store_quad_codes<FMT>(row, lane & 3, u32x2{w.x, w.y}, u32x2{w.z, w.w});
       }
       if (lane < 2) {
-        float* sp = reinterpret_cast<float*>(&ring[0][g][0] + (slot_base - slot0) + 2 * QL::kHead);
+        float* sp = reinterpret_cast<float*>(&ring[0][wave][0] + (slot_base - slot0) + 2 * QL::kHead);
         sp[lane * 16 + app_slot] = new_scales[APPEND && QUANT ? g : 0][lane];
       }
     } else {
@@ -702,7 +715,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         // piece 4 (row % 2) + part of K (rows 0, 1) or V (rows 2, 3)
         const u32x4 w = reinterpret_cast<const u32x4*>(&new_rows[sl][0])[lane];
         const int row = lane >> 2;
-        char* base = &ring[0][g][0] + (slot_base - slot0) + 2048 * (row >> 1) +
+        char* base = &ring[0][wave][0] + (slot_base - slot0) + 2048 * (row >> 1) +
                      bf16_slot_offset(app_slot, 4 * (row & 1) + (lane & 3));
         *reinterpret_cast<u32x4*>(base) = w;
       }
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   };
   auto step = [&](int i, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    const int slot = (i - p0) % F::kRingDepth;
+    const int slot = (i - q0) % F::kRingDepth;
     const uint32_t off = slot * kRingSlotBytes;
     wait_page<F::kLoads, F::kRingDepth>(min(last - i, F::kRingDepth - 1));   // page i landed
     if (MASK && app_here) park_new_row(slot0 + off);
@@ -729,8 +742,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   // pages i and i+1, both before the last page, in one pass; the ring keeps
   // depth - 2 pages in flight while they are used
   auto step2 = [&](int i) {
-    const int slot_a = (i - p0) % F::kRingDepth;
-    const int slot_b = (i + 1 - p0) % F::kRingDepth;
+    const int slot_a = (i - q0) % F::kRingDepth;
+    const int slot_b = (i + 1 - q0) % F::kRingDepth;
     wait_page<F::kLoads, F::kRingDepth>(min(last - i - 1, F::kRingDepth - 2));   // page i+1 landed
     PageT pa_, pb_;
     lds_read(pa_, slot_a * kRingSlotBytes);
@@ -749,7 +762,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
   for (int r = 0; r < F::kRingDepth; ++r)
-    if (p0 + r <= last) fetch(p0 + r, r);
+    if (q0 + r <= last) fetch(q0 + r, r);
 
   // while the first pages are in flight: the query operand and the new rows
   // B operand of the score product: column n = query head 4g + n%4, this
@@ -796,11 +809,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       lds_store16(rows + 16 * ((is_k ? 0 : 8) + 4 + c), u32x4{hi.x, hi.y, hi.z, hi.w});
     }
   }
-  int i = p0;
-  if constexpr (F::kPairs)
-    for (; i + 1 < last; i += 2) step2(i);
-  for (; i < last; ++i) step(i, std::false_type{});
-  step(last, std::true_type{});
+  if (has_pages) {
+    int i = q0;
+    if constexpr (F::kPairs)
+      for (; i + 1 < last; i += 2) step2(i);
+    for (; i < last; ++i) step(i, std::false_type{});
+    step(last, std::true_type{});
+  }
   wait_vmem<0>();
 
   if (app_here && lane < (QUANT ? 8 : 16)) {
@@ -830,6 +845,50 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  auto of_head = [G](float v) {                  // v of head G (from lane 4G)
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 4));
+    const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 8));
+    const float v3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 12));
+    return G == 0 ? v0 : (G == 1 ? v1 : (G == 2 ? v2 : v3));
+  };
+
+  if constexpr (WPH == 2) {
+    // the second half's state joins the first through LDS, lane by lane (the
+    // two wavefronts of a head have the same lane layout): the larger running
+    // maximum is kept and each side is scaled by 2^(its maximum - the kept
+    // one); the normaliser and weight sum belong to head n / 4, the
+    // accumulator rows to head G, whose factors come from lane 4G
+    constexpr int kXfer = 20;                    // 16 accumulators, m, l, wsum, bad-page flag
+    __shared__ float xfer[kWaves][kXfer][64];
+    if (wh == 1) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) xfer[g][4 * t + rr][lane] = st.acc[t][rr];
+      xfer[g][16][lane] = st.m;
+      xfer[g][17][lane] = st.l;
+      xfer[g][18][lane] = st.wsum;
+      xfer[g][19][lane] = bad_page ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (wh == 1) return;
+    const float m1 = xfer[g][16][lane];
+    const float mx = fmaxf(st.m, m1);            // the first half always holds a page
+    const float a0 = __builtin_amdgcn_exp2f(st.m - mx);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - mx);   // an empty second half: m1 = -inf -> 0
+    const float a0g = of_head(a0), a1g = of_head(a1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        st.acc[t][rr] = st.acc[t][rr] * a0g + xfer[g][4 * t + rr][lane] * a1g;
+    st.m = mx;
+    st.l = st.l * a0 + xfer[g][17][lane] * a1;
+    st.wsum = st.wsum * a0 + xfer[g][18][lane] * a1;
+    bad_page |= xfer[g][19][lane] != 0.f;
+  }
+
   // finish: the normaliser and weight sum of head n / 4 over its 16 lanes
   // (the quad and the four token groups); lane 16 G + n then takes head G's
   // values from lane 4G, and its tiles' rows 4G (BF16 weights) and 4G + 1
@@ -840,13 +899,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     return v;
-  };
-  auto of_head = [G](float v) {                  // v of head G (from lane 4G)
-    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 4));
-    const float v2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 8));
-    const float v3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 12));
-    return G == 0 ? v0 : (G == 1 ? v1 : (G == 2 ? v2 : v3));
   };
   st.l = head_sum(st.l);
   float o[4];                                    // [tile]: head G, column n
@@ -891,25 +943,38 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 
 namespace pa {
 
+template <int FMT, int WPH>
+inline void launch_decode_kernel(const DecodeArgs& a, dim3 grid, bool out_bf16, bool fused,
+                                 bool rope, hipStream_t st) {
+  const dim3 block(kThreads * WPH);
+  if (out_bf16) {
+    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, true, true, true, WPH>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, true, true, false, WPH>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<FMT, true, false, false, WPH>), grid, block, 0, st, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, false, true, true, WPH>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, false, true, false, WPH>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<FMT, false, false, false, WPH>), grid, block, 0, st, a);
+  }
+}
+
 // Host: enqueue the decode kernel for page format FMT (plus the split merge
-// when the plan has more than one split).  event_before/after (may be NULL)
-// are recorded right around the decode kernel.  Returns a hipError_t.
+// when the plan has more than one split).  two_waves (INT4 pages only): two
+// wavefronts per KV head, for plans whose grid fits the CUs at once (and
+// whose splits are long; the caller decides).  event_before/after (may be NULL) are recorded right around the
+// decode kernel.  Returns a hipError_t.
 template <int FMT>
 inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
-                                bool rope, bool merge_preload, hipStream_t st,
+                                bool rope, bool merge_preload, bool two_waves, hipStream_t st,
                                 hipEvent_t event_before, hipEvent_t event_after) {
   const dim3 grid = a.work ? dim3(a.num_work) : dim3(a.num_splits * batch);
-  const dim3 block(kThreads);
   hipError_t e = hipSuccess;
   if (event_before && (e = hipEventRecord(event_before, st)) != hipSuccess) return e;
-  if (out_bf16) {
-    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, true, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<FMT, true, false>), grid, block, 0, st, a);
+  if constexpr (FMT == kFmtINT4) {
+    if (two_waves) launch_decode_kernel<FMT, 2>(a, grid, out_bf16, fused, rope, st);
+    else launch_decode_kernel<FMT, 1>(a, grid, out_bf16, fused, rope, st);
   } else {
-    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, false, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<FMT, false, false>), grid, block, 0, st, a);
+    launch_decode_kernel<FMT, 1>(a, grid, out_bf16, fused, rope, st);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (event_after && (e = hipEventRecord(event_after, st)) != hipSuccess) return e;

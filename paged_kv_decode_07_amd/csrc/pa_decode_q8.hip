@@ -147,6 +147,7 @@ PlanModel plan_model_q4() {
   m.empty_us = 0.5;
   m.resident = 2;
   m.shared_gain = 1.3;
+  m.two_wave_gain = 1.3;
   return m;
 }
 
@@ -269,10 +270,19 @@ int decode_quant_impl(const pa_shape* shape, int32_t batch, const void* q, const
   a.num_work = num_work;
   a.batch = batch;
   int cu = 0;
-  const bool merge_preload = pa_host::current_cu_count(&cu) == PA_OK && batch <= cu;
+  const bool have_cu = pa_host::current_cu_count(&cu) == PA_OK;
+  const bool merge_preload = have_cu && batch <= cu;
+  // INT4 pages are bound by their arithmetic: when every work-group of the
+  // plan fits the CUs at once and its splits are long, two wavefronts per KV
+  // head give each CU the waves of two work-groups without split partials.
+  // The choice depends on the plan (batch x splits, split size) alone, so a
+  // work-list launch of the same plan sums in the same order as the grid
+  // launch and matches it bit for bit.
+  const bool two_waves = FMT == pa::kFmtINT4 && have_cu && (int64_t)batch * ns <= cu &&
+                         ps >= pa_host::kTwoWaveMinPages;
   const hipError_t e = pa::launch_decode<FMT>(a, batch, out_dtype == PA_OUT_BF16, fused,
-                                               rope != nullptr, merge_preload, (hipStream_t)stream,
-                                               nullptr, nullptr);
+                                               rope != nullptr, merge_preload, two_waves,
+                                               (hipStream_t)stream, nullptr, nullptr);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

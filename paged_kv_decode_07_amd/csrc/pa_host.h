@@ -37,7 +37,16 @@ struct PlanModel {
   double page_bytes = 2.0 * 16 * 8 * 64 * 2;   // one K page and one V page, BF16
   int resident = 1;
   double shared_gain = 1.0;
+  // a plan whose grid (batch x splits) fits the CUs at once, with splits of
+  // at least kTwoWaveMinPages pages, streams two_wave_gain times faster per
+  // work-group (INT4 pages: two wavefronts per KV head, for the grid and the
+  // work-list launch alike)
+  double two_wave_gain = 1.0;
 };
+// Shorter splits run one wavefront per KV head: their halves are too short to
+// pay for the larger work-group and the merge of the two states (3- and
+// 8-page splits measured 9% and 4% slower with two).
+constexpr int kTwoWaveMinPages = 32;
 // worklist: the work-groups run in pa_decode_worklist's order (largest
 // first, no empty slots) instead of the grid order.
 double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,

@@ -238,16 +238,14 @@ def test_q8_planner_choices():
 
 
 def test_q4_planner_choices():
-    """The INT4 cost model (two work-groups per CU for even batches) picks 8, 32, 64, 32
-    pages for workloads 2-5.
+    """The INT4 cost model picks 8, 32, 128, 32 pages for workloads 2-5.
 
-    Measured fastest split sizes for INT4 pages on MI355X (grid launch): 8, 16, 64, 32/64
-    pages; at workload 3 the model's 32 measured 27.6 us against 25.6 us at 16.  At
-    workload 4, 64-page splits (two work-groups per CU) measured 69.2 us against 74.8 us
-    for the 128-page split that a one-per-CU model picks.
+    It allows two work-groups per CU for even batches, and a launch whose work-groups all
+    fit the CUs runs two wavefronts per KV head.  At workload 4, one 128-page split per
+    sequence then streams with two wavefronts per head and no split merge.
     """
     import workloads as W
-    expect = {2: 8, 3: 32, 4: 64, 5: 32}
+    expect = {2: 8, 3: 32, 4: 128, 5: 32}
     for i, ps_best in expect.items():
         lens = W.workload_seq_lens(i)
         ps, ns = pa.decode_plan_lengths_q4(lens, 40000, num_cus=256)

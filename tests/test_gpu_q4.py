@@ -5,7 +5,9 @@
 * decode over INT4 pages (random packed codes and scales from the seeded
   generator, random bytes and NaN scales in every unused slot): within the
   attention tolerance of the float64 oracle over the dequantised cache, over
-  split sizes, output types, edge lengths and bad metadata;
+  split sizes, output types, edge lengths and bad metadata, with one and with
+  two wavefronts per KV head (plans whose grid fits the CUs with splits of 32
+  pages or more), including empty and uneven second halves;
 * the fused quantise-append + decode: pools bit-identical to the two-call
   form, outputs identical to it and within tolerance of the oracle; with
   RoPE; behind 256-entry block tables; launched from a work list;
@@ -169,6 +171,28 @@ def test_q4_decode_edge_lengths(pages_per_split):
     got = _decode(DevQ4(w), pages_per_split)
     assert_close(got, _ref(w), where=f"q4 edge ps={pages_per_split}")
     assert np.all(got[-1] == 0.0)
+
+
+def test_q4_two_waves_per_head_uneven_halves():
+    """Plans whose grid (batch x splits) fits the CUs and whose splits hold 32 pages or more run
+    two wavefronts per KV head: each streams half of its split's pages and the two states merge
+    through LDS.  Sequences of 1, 2, 17, 33 and 63 pages under 32- and 33-page splits give
+    empty, single-page, even and uneven second halves.  A block-table entry outside the pool
+    that only the second wavefront reads must still turn that sequence's outputs into NaN."""
+    lens = [1, 16, 17 * 16, 33 * 16 - 5, 63 * 16, 2048, 0]
+    w = W.make_q8_batch(lens, sum(W.pages_for(L) for L in lens) + 5, 1931, nbits=NB)
+    d = DevQ4(w)
+    ref = _ref(w)
+    for ps in (32, 33, 128):
+        assert_close(_decode(d, ps), ref, where=f"q4 two waves ps={ps}")
+    # sequence 4 (63 pages in one 128-page split): halves 0..31 and 32..62
+    bt = w.block_tables.copy()
+    bt[4, 40] = w.k_codes.shape[0] + 3
+    d.bt = dev32(bt)
+    got = _decode(d, 128)
+    assert np.all(np.isnan(got[4]))
+    others = [0, 1, 2, 3, 5, 6]
+    assert_close(got[others], ref[others], where="q4 two waves, other sequences")
 
 
 def test_q4_decode_bf16_out():
