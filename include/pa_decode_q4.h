@@ -82,7 +82,13 @@ int pa_fill_kv_q4(const pa_shape* shape, const void* k_rows, const void* v_rows,
  * Decode attention over INT4 pages: pa_decode_attention's result on the
  * dequantised cache (code * scale), with its arguments, planning and
  * workspace; accuracy against float64 attention over the dequantised cache
- * as for BF16 pages.
+ * as for BF16 pages.  A plan whose grid (batch x splits) fits the device's
+ * compute units at once, with splits of 32 pages or more, runs two
+ * wavefronts per KV head (each takes half of a split's pages; their states
+ * are merged in the work-group): the summation order, and so the last bits
+ * of the result, depend on the plan and the device's compute-unit count.
+ * Results are deterministic run to run on one device, and the grid and
+ * work-list launches of one plan agree bit for bit.
  */
 int pa_decode_attention_q4(const pa_shape* shape, int32_t batch, const void* q,
                            const void* k_codes, const void* v_codes, const void* kv_scales,
