@@ -271,21 +271,26 @@ def test_q4_fused_matches_two_call_and_oracle(pages_per_split):
     assert_close(fused, _ref(w, pools=pools), where=f"q4 fused ps={pages_per_split}")
 
 
-def test_q4_fused_bf16_out():
+@pytest.mark.parametrize("pages_per_split", [2, 128])
+def test_q4_fused_bf16_out(pages_per_split):
+    # 2-page splits: one wavefront per KV head; 128-page splits: two
     w = W.make_q8_batch(EDGE, sum(W.pages_for(L) for L in EDGE) + 9, 1933, append=True, nbits=NB)
-    got = _fused(DevQ4(w), 2, out_dtype=torch.bfloat16)
-    assert_close(got, _ref(w, pools=_appended_pools(w)), bf16_out=True, where="q4 fused bf16 out")
+    got = _fused(DevQ4(w), pages_per_split, out_dtype=torch.bfloat16)
+    assert_close(got, _ref(w, pools=_appended_pools(w)), bf16_out=True,
+                 where=f"q4 fused bf16 out ps={pages_per_split}")
 
 
-def test_q4_fused_rope_matches_oracle():
+@pytest.mark.parametrize("pages_per_split", [3, 64])
+def test_q4_fused_rope_matches_oracle(pages_per_split):
+    # 3-page splits: one wavefront per KV head; 64-page splits (22 work-groups): two
     w = W.make_q8_batch(EDGE, sum(W.pages_for(L) for L in EDGE) + 9, 1932, append=True, nbits=NB)
     cos, sin = W.rope_table()
     f = DevQ4(w)
-    got = _fused(f, 3, rope=(cos, sin))
+    got = _fused(f, pages_per_split, rope=(cos, sin))
     q_rot, k_rot = oracle.rope.rope_new_token(w.q, w.k_new, w.seq_lens, cos, sin)
     pools = _appended_pools(w, k_rows=k_rot)
     _same_pools(f.pools(), pools)
-    assert_close(got, _ref(w, pools=pools, q=q_rot), where="q4 fused rope")
+    assert_close(got, _ref(w, pools=pools, q=q_rot), where=f"q4 fused rope ps={pages_per_split}")
 
 
 @pytest.mark.parametrize("pages_per_split", [0, 256])
