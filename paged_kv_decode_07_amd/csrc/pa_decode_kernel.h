@@ -5,7 +5,9 @@
 // run of at most `pages_per_split` consecutive logical pages of sequence b.
 // The 8 wavefronts of a work-group serve the 8 KV heads: wavefront g streams
 // its head's slice of every page of the split (grouped-query attention: 32
-// query heads share 8 KV heads; query heads 4g .. 4g+3 read KV head g).
+// query heads share 8 KV heads; query heads 4g .. 4g+3 read KV head g).  With
+// WPH = 2 (INT4 plans whose grid fits the CUs) a work-group has 16
+// wavefronts, two per KV head, each streaming half of the split's pages.
 //
 // Page stream: each wavefront keeps a ring of page slots in LDS, filled with
 // gfx950's direct-to-LDS loads (every lane's 4 or 16 bytes land at lane*size
@@ -765,7 +767,7 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
     if (q0 + r <= last) fetch(q0 + r, r);
 
   // while the first pages are in flight: the query operand and the new rows
-  // B operand of the score product: column n = query head 4g + n%4, this
+  // B operand of the score product: column n = query head 4g + n/4, this
   // lane's 8 dims {8G..} (qlo) and {32+8G..} (qhi)
   {
     uint4 lo = q_lo, hi = q_hi;
