@@ -5,7 +5,8 @@ the step can be captured once (launch shape fixed by the declared capacity)
 and replayed with new inputs written into the same buffers.  Every replay is
 checked bit for bit against the same step run eagerly on a twin set of
 buffers, with eager work and synchronisations between the replays; the last
-step is also checked against the oracle.
+step is also checked against the oracle.  BF16, INT8 and INT4 pages; the INT4
+step runs 32-page splits, the launch with two wavefronts per KV head.
 """
 
 from __future__ import annotations
@@ -34,11 +35,16 @@ def _device():
     torch.cuda.synchronize()
 
 
-def _state(q8: bool, seed: int):
+# split size per page format: INT4 pages at 32-page splits take the launch with
+# two wavefronts per KV head (the plan's grid fits the CUs)
+SPLIT = {"bf16": 8, "int8": 8, "int4": 32}
+
+
+def _state(fmt: str, seed: int):
     lens0 = np.array([5, 100, 250, 31, 0, 390 - STEPS], np.int32)
     pages = len(lens0) * W.pages_for(CAP) + 4
-    if q8:
-        w = W.make_q8_batch(lens0, pages, seed)
+    if fmt != "bf16":
+        w = W.make_q8_batch(lens0, pages, seed, nbits=4 if fmt == "int4" else 8)
         pools = [torch.from_numpy(a.copy()).cuda() for a in (w.k_codes, w.v_codes, w.kv_scales)]
     else:
         w = W.make_batch(lens0, pages, seed)
@@ -56,31 +62,29 @@ def _state(q8: bool, seed: int):
     return w, pools, bt, lens0
 
 
-def _run(q8, pools, q, kn, vn, bt, lens, out, ws):
+def _run(fmt, pools, q, kn, vn, bt, lens, out, ws):
     from paged_kv_decode_07_amd import binding as pa
-    if q8:
-        pa.append_decode_attention_q8(q, kn, vn, *pools, bt, lens, CAP, out=out,
-                                      pages_per_split=8, workspace=ws)
-    else:
-        pa.append_decode_attention(q, kn, vn, *pools, bt, lens, CAP, out=out,
-                                   pages_per_split=8, workspace=ws)
+    fn = {"bf16": pa.append_decode_attention, "int8": pa.append_decode_attention_q8,
+          "int4": pa.append_decode_attention_q4}[fmt]
+    fn(q, kn, vn, *pools, bt, lens, CAP, out=out, pages_per_split=SPLIT[fmt], workspace=ws)
 
 
-@pytest.mark.parametrize("q8", [False, True], ids=["bf16", "int8"])
-def test_graph_replays_match_eager_steps(q8):
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+def test_graph_replays_match_eager_steps(fmt):
     from paged_kv_decode_07_amd import binding as pa
-    w, pools_g, bt_h, lens0 = _state(q8, 1300 + q8)
+    seed = {"bf16": 0, "int8": 1, "int4": 2}[fmt]
+    w, pools_g, bt_h, lens0 = _state(fmt, 1300 + seed)
     pools_e = [p.clone() for p in pools_g]
     B = len(lens0)
     bt = dev32(bt_h)
-    rng = np.random.default_rng(1400 + q8)
+    rng = np.random.default_rng(1400 + seed)
     q_s = torch.zeros((B, 32, 64), dtype=torch.int16, device="cuda")
     kn_s = torch.zeros((B, 8, 64), dtype=torch.int16, device="cuda")
     vn_s = torch.zeros_like(kn_s)
     lens_s = torch.zeros(B, dtype=torch.int32, device="cuda")
     out_g = torch.empty((B, 32, 64), dtype=torch.float32, device="cuda")
     out_e = torch.empty_like(out_g)
-    need = pa.decode_workspace_bytes(B, CAP, pools_g[0].shape[0], W.MAX_BLOCKS, 8)
+    need = pa.decode_workspace_bytes(B, CAP, pools_g[0].shape[0], W.MAX_BLOCKS, SPLIT[fmt])
     ws_g = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     ws_e = torch.empty_like(ws_g)
 
@@ -90,7 +94,7 @@ def test_graph_replays_match_eager_steps(q8):
 
     # warm-up outside the capture (device queries, first launches), on throw-away copies
     scratch = [p.clone() for p in pools_g]
-    _run(q8, scratch, q_s, kn_s, vn_s, bt, lens_s, out_g, ws_g)
+    _run(fmt, scratch, q_s, kn_s, vn_s, bt, lens_s, out_g, ws_g)
     torch.cuda.synchronize()
     del scratch
 
@@ -99,7 +103,7 @@ def test_graph_replays_match_eager_steps(q8):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            _run(q8, pools_g, q_s, kn_s, vn_s, bt, lens_s, out_g, ws_g)
+            _run(fmt, pools_g, q_s, kn_s, vn_s, bt, lens_s, out_g, ws_g)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
@@ -111,21 +115,22 @@ def test_graph_replays_match_eager_steps(q8):
         graph.replay()
         torch.cuda.synchronize()
         # the same step, eagerly, on the twin buffers
-        _run(q8, pools_e, dev16(qh), dev16(knh), dev16(vnh), bt, dev32(lens), out_e, ws_e)
+        _run(fmt, pools_e, dev16(qh), dev16(knh), dev16(vnh), bt, dev32(lens), out_e, ws_e)
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), f"replay {step}: output differs from the eager step"
         for pg, pe in zip(pools_g, pools_e):
-            # bit patterns: the INT8 scale pool keeps NaN poison in its unused slots
+            # bit patterns: the scale pool keeps NaN poison in its unused slots
             bits = (lambda t: t.view(torch.int32)) if pg.dtype == torch.float32 else (lambda t: t)
             assert torch.equal(bits(pg), bits(pe)), f"replay {step}: pools differ from the eager step"
         last = (qh, lens)
 
     # the final state against the oracle (the cache holds every appended token)
     qh, lens = last
-    if q8:
+    if fmt != "bf16":
         kc, vc, sc = (p.cpu().numpy() for p in pools_g)
-        ref = kvquant.decode_attention_q8(qh, kc, vc, sc, bt_h, lens, W.SCALE)
+        ref = kvquant.decode_attention_q8(qh, kc, vc, sc, bt_h, lens, W.SCALE,
+                                          nbits=4 if fmt == "int4" else 8)
     else:
         kp, vp = (p.cpu().numpy().view(np.uint16) for p in pools_g)
         ref = oracle.decode_attention(qh, kp, vp, bt_h, lens, W.SCALE)
-    assert_close(out_g.cpu().numpy().astype(np.float64), ref, where=f"graph final ({'int8' if q8 else 'bf16'})")
+    assert_close(out_g.cpu().numpy().astype(np.float64), ref, where=f"graph final ({fmt})")
