@@ -1,9 +1,9 @@
 """The library driven from C++ alone: a host program (tests/c_client) that
-allocates with hipMalloc, calls the header's pa_append_decode_attention on the
-default stream and writes the results back to files.  No Python binding or
-torch tensor takes part in the step; the outputs are checked against the
-oracle as in the binding's parity tests (pools bit-exact, attention within
-the FP32 bound)."""
+allocates with hipMalloc, calls the header's pa_append_decode_attention (or
+its INT8 and INT4 forms) on the default stream and writes the results back to
+files.  No Python binding or torch tensor takes part in the step; the outputs
+are checked against the oracle as in the binding's parity tests (pools
+bit-exact, attention within the FP32 bound)."""
 
 from __future__ import annotations
 
@@ -16,6 +16,7 @@ import pytest
 import oracle
 import workloads as W
 from gpu_util import ATOL_F32
+from oracle import kvquant
 
 pytestmark = pytest.mark.gpu
 
@@ -51,3 +52,37 @@ def test_c_client_step_matches_oracle(tmp_path, lens, pps):
     err = float(np.max(np.abs(out - ref)))
     assert err <= ATOL_F32, err
     assert np.all(out[w.seq_lens == 0] == 0)          # an idle slot's rows are zero
+
+
+@pytest.mark.parametrize("bits,lens,pps", [(8, [37, 1, 200, 16, 0, 513], 0),
+                                           (4, [37, 1, 200, 16, 0, 513], 0),
+                                           (4, [2048] * 3, 64)],
+                         ids=["int8-ragged-auto", "int4-ragged-auto", "int4-long-split64"])
+def test_c_client_quantised_step_matches_oracle(tmp_path, bits, lens, pps):
+    if not os.path.exists(CLIENT):
+        pytest.fail("decode_client is not built (build the library and the client first)")
+    pages = sum(W.pages_for(L) for L in lens) + 5
+    w = W.make_q8_batch(lens, pages, 2300 + bits + len(lens), append=True, nbits=bits)
+    B = len(lens)
+    for name, arr in (("q", w.q), ("k_new", w.k_new), ("v_new", w.v_new), ("k_pool", w.k_codes),
+                      ("v_pool", w.v_codes), ("scales", w.kv_scales), ("bt", w.block_tables),
+                      ("lens", w.seq_lens)):
+        np.ascontiguousarray(arr).tofile(tmp_path / f"{name}.bin")
+    (tmp_path / "meta.txt").write_text(f"{B} {pages} {W.MAX_BLOCKS} {max(lens)} {pps} {bits}\n")
+    print(f"c_client: {bits}-bit pages, lens {lens} pps {pps}", flush=True)
+    res = subprocess.run([CLIENT, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, f"client exit {res.returncode}: {res.stdout}{res.stderr}"
+
+    kc, vc, sc = kvquant.append_kv_q8(w.k_codes, w.v_codes, w.kv_scales, w.k_new, w.v_new,
+                                      w.block_tables, w.seq_lens, nbits=bits)
+    k_out = np.fromfile(tmp_path / "k_pool_out.bin", kc.dtype).reshape(kc.shape)
+    v_out = np.fromfile(tmp_path / "v_pool_out.bin", vc.dtype).reshape(vc.shape)
+    s_out = np.fromfile(tmp_path / "scales_out.bin", np.uint32).reshape(sc.shape)
+    assert np.array_equal(k_out, kc) and np.array_equal(v_out, vc)
+    assert np.array_equal(s_out, sc.view(np.uint32))             # NaN poison kept bit for bit
+    ref = kvquant.decode_attention_q8(w.q, kc, vc, sc, w.block_tables, w.seq_lens, w.scale,
+                                      nbits=bits)
+    out = np.fromfile(tmp_path / "out.bin", np.float32).reshape(ref.shape).astype(np.float64)
+    err = float(np.max(np.abs(out - ref)))
+    assert err <= ATOL_F32, err
+    assert np.all(out[w.seq_lens == 0] == 0)
