@@ -15,15 +15,22 @@ Timing: the inputs are resident in HBM before the timed region.  Before each
 step a separate 1 GiB buffer is read (a reduction), so the step starts with
 L2 and Infinity Cache holding none of its inputs; the flush only reads, so it
 leaves no dirty lines whose write-back would land inside the next step.
-Pass A times the K steps with one event pair around each step; pass B
-repeats them with the library recording events right around its main
-kernel (the roofline figure); pass C times the two-call form; pass D the
+Pass A times the K steps with one event pair around each step, and the
+library records a second pair right around its main kernel inside the same
+steps (the roofline figure); pass C times the two-call form; pass D the
 fused step with RoPE; pass E the fused step over INT8 pages and pass F over
-INT4 pages (the BF16 cache quantised on the GPU first).  Two diagnostics follow: the same step with the
-pages in identity order, and a plain streaming read of 1 GiB (the achievable
-read bandwidth, beside the published peak).  The flush is outside every event
-pair.  The oracle baseline runs on one core and on a pool of worker processes
-forked before the GPU is initialised.  Prints one JSON line.
+INT4 pages (the BF16 cache quantised on the GPU first).  Two diagnostics
+follow: the same step with the pages in identity order, and a plain
+streaming read of 1 GiB (the achievable read bandwidth, beside the published
+peak).  The flush is outside every event pair.
+
+Then every other configuration (1: one 37-token sequence; 2: batch 8 of
+uniform lengths; 3: the 16-layer step of batch 64; 5: batch 512 of clipped
+Zipf lengths) is measured the same way, its fused step under each candidate
+launch (the default plan, the host-lengths plan, the work list), the fastest
+reported, with every output compared against the oracle.  The oracle runs on
+one core and on a pool of worker processes forked before the GPU is
+initialised, on every configuration.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -78,7 +85,30 @@ def measured_traffic(path: str = TRAFFIC_FILE, sources=None):
     return int(round(t["hbm_bytes_per_launch"]))
 
 
-_CPU_STATE = None          # (batch, k_ref, v_ref): set before the pool forks
+TRACE_FILE = os.path.join(ROOT, "profiles", "decode_kernel_trace_b256_l2048.json")
+
+
+def rocprof_kernel_time(path: str = TRACE_FILE):
+    """The main kernel's average duration from the committed rocprofv3 kernel
+    trace of this workload, and the roofline fraction it gives; None when
+    absent or when the kernel has changed since."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    us = float(t["avg_us"])
+    gbps = t["algorithmic_kv_bytes"] / us / 1e3
+    return {"avg_us": us, "achieved": round(gbps, 2), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "calls": t.get("calls"), "source": os.path.relpath(path, ROOT)}
+
+
+# host inputs of every measured configuration, set before the pool forks:
+# {config: [(batch, k_ref, v_ref) per layer]}, k_ref/v_ref the oracle's pools
+# after the append (the workers inherit them and never touch the GPU)
+_STATES = {}
+CONFIGS = (1, 2, 3, 4, 5)
 
 
 def _blas_one_thread():
@@ -89,74 +119,103 @@ def _blas_one_thread():
         pass
 
 
-def _oracle_decodes(first: int, stride: int, seconds: float, gpu_out=None):
-    """Decode sequences first, first+stride, ... (cycling) with the oracle for ``seconds``."""
+def config_layers(ci: int, placement: str = "random"):
+    """Host inputs of configuration ``ci`` with the append: one batch per layer
+    (16 for configuration 3, one pool region each)."""
+    import workloads as W
+    if ci == 3:
+        return [W.make_workload(3, layer=layer, placement=placement, append=True)
+                for layer in range(W.NUM_LAYERS_W3)]
+    return [W.make_workload(ci, placement=placement, append=True)]
+
+
+def prepare_states(configs, placement: str, headline=None):
+    """Inputs and the oracle's appended pools of each configuration (host only)."""
+    import oracle
+    for ci in configs:
+        t0 = time.perf_counter()
+        layers = [headline] if (ci == 4 and headline is not None) else config_layers(ci, placement)
+        st = []
+        for w in layers:
+            k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new,
+                                            w.block_tables, w.seq_lens)
+            st.append((w, k_ref, v_ref))
+        _STATES[ci] = st
+        log(f"config {ci}: {len(st)} layer(s) x {st[0][0].batch} sequences generated in "
+            f"{time.perf_counter() - t0:.1f} s")
+
+
+def _items(ci):
+    """(layer, sequence) pairs of configuration ``ci``, layer by layer."""
+    return [(li, b) for li, (w, _, _) in enumerate(_STATES[ci]) for b in range(w.batch)]
+
+
+def _oracle_decodes(ci: int, first: int, stride: int, seconds: float, gpu_outs=None):
+    """Decode items first, first+stride, ... (cycling) with the oracle for ``seconds``.
+
+    Returns (items done, seconds, tokens, max-abs against ``gpu_outs`` [layer][B][32][64]).
+    """
     import numpy as np
     import oracle
-    batch, k_ref, v_ref = _CPU_STATE
-    done, worst, t0 = [], 0.0, time.perf_counter()
+    items = _items(ci)
+    done, tokens, worst, t0 = 0, 0, 0.0, time.perf_counter()
     while True:
-        b = (first + stride * len(done)) % batch.batch
-        ref = oracle.decode_attention(batch.q, k_ref, v_ref, batch.block_tables,
-                                      batch.seq_lens, batch.scale, sequences=[b])
-        if gpu_out is not None:
-            worst = max(worst, float(np.max(np.abs(ref[b] - gpu_out[b]))))
-        done.append(b)
-        if time.perf_counter() - t0 >= seconds and len(done) >= 2:
+        li, b = items[(first + stride * done) % len(items)]
+        w, k_ref, v_ref = _STATES[ci][li]
+        ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale,
+                                      sequences=[b])
+        if gpu_outs is not None:
+            worst = max(worst, float(np.max(np.abs(ref[b] - gpu_outs[li][b]))))
+        done += 1
+        tokens += int(w.seq_lens[b])
+        if time.perf_counter() - t0 >= seconds and done >= 2:
             break
-    return done, time.perf_counter() - t0, worst
+    return done, time.perf_counter() - t0, tokens, worst
 
 
 def _pool_leg(args):
-    first, stride, seconds = args
-    done, dt, _ = _oracle_decodes(first, stride, seconds)
-    return done, dt
+    ci, first, stride, seconds = args
+    done, dt, tokens, _ = _oracle_decodes(ci, first, stride, seconds)
+    return done, dt, tokens
 
 
-def prepare_cpu_baseline(batch, pool_workers: int):
-    """Append on the host and fork the worker pool, before the GPU is initialised
-    (the workers inherit the inputs and never touch the GPU)."""
-    global _CPU_STATE
+def fork_pool(pool_workers: int):
+    """The oracle's worker processes, forked before the GPU is first touched."""
     import multiprocessing as mp
-    import oracle
-    k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new,
-                                    batch.block_tables, batch.seq_lens)
-    _CPU_STATE = (batch, k_ref, v_ref)
     if pool_workers <= 1:
         return None
     return mp.get_context("fork").Pool(pool_workers, initializer=_blas_one_thread)
 
 
-def cpu_baseline(gpu_out, seconds: float, pool=None, pool_workers: int = 0):
-    """The oracle, as it stands, over the same workload: one core, then a process pool."""
+def oracle_rates(ci: int, seconds: float, pool=None, pool_workers: int = 0, gpu_outs=None):
+    """The oracle, as it stands, on configuration ``ci``: one core, then the process pool."""
     import contextlib
-    batch = _CPU_STATE[0]
     try:
         from threadpoolctl import threadpool_limits
         limit = threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
         limit = contextlib.nullcontext()
     with limit:
-        done, dt, worst = _oracle_decodes(0, 1, seconds, gpu_out)
-    tokens = int(sum(int(batch.seq_lens[b]) for b in done))
+        done, dt, tokens, worst = _oracle_decodes(ci, 0, 1, seconds, gpu_outs)
     kv = tokens * 2048
     res = {
         "value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{len(done)} sequence decodes cycling over the {batch.batch} sequences "
-                   f"({tokens} tokens, {kv / 2**20:.0f} MiB of K/V), float64 NumPy, "
+        "sample": (f"{done} sequence decodes cycling over the {len(_items(ci))} (layer, sequence) "
+                   f"pairs ({tokens} tokens, {kv / 2**20:.0f} MiB of K/V), float64 NumPy, "
                    f"1 BLAS thread, {dt:.1f} s"),
-        "seq_per_s": round(len(done) / dt, 3),
+        "seq_per_s": round(done / dt, 3),
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "blas_threads": 1,
-        "max_abs_vs_gpu_on_sample": worst,
     }
+    if gpu_outs is not None:
+        res["max_abs_vs_gpu_on_sample"] = worst
     if pool is not None:
         t0 = time.perf_counter()
-        legs = pool.map(_pool_leg, [(w, pool_workers, seconds) for w in range(pool_workers)])
+        legs = pool.map(_pool_leg, [(ci, w, pool_workers, seconds) for w in range(pool_workers)])
         wall = time.perf_counter() - t0
-        n = sum(len(d) for d, _ in legs)
-        ptok = sum(int(batch.seq_lens[b]) for d, _ in legs for b in d)
+        n = sum(d for d, _, _ in legs)
+        ptok = sum(t for _, _, t in legs)
         res["pool"] = {
             "value": round(ptok * 2048 / wall / 1e9, 4), "unit": "GB/s", "cores": pool_workers,
             "sample": (f"{n} sequence decodes over {pool_workers} worker processes "
@@ -164,6 +223,102 @@ def cpu_baseline(gpu_out, seconds: float, pool=None, pool_workers: int = 0):
             "seq_per_s": round(n / wall, 3),
         }
     return res
+
+
+def oracle_refs(ci: int):
+    """The oracle's output of every sequence of every layer of configuration ``ci``."""
+    import oracle
+    return [oracle.decode_attention(w.q, k, v, w.block_tables, w.seq_lens, w.scale)
+            for w, k, v in _STATES[ci]]
+
+
+def parity(gpu_outs, refs):
+    """(max-abs, max-rel with denominator max(|ref|, 1e-2)) over every element."""
+    import numpy as np
+    err = max(float(np.max(np.abs(g - r))) for g, r in zip(gpu_outs, refs))
+    rel = max(float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-2)))
+              for g, r in zip(gpu_outs, refs))
+    return err, rel
+
+
+def measure_config(ci: int, args, stream, dev, flush, refs):
+    """Every candidate launch of configuration ``ci``'s fused step (all its
+    layers back to back), cold caches; the fastest is the configuration's figure."""
+    import numpy as np
+    import torch
+
+    from paged_kv_decode_07_amd import accounting as A
+    from paged_kv_decode_07_amd import binding as pa
+
+    def up16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    states = _STATES[ci]
+    w0 = states[0][0]
+    B, npg, msl = w0.batch, w0.num_pages, w0.max_seq_len
+    layers = [dict(q=up16(w.q), kp=up16(w.k_pool), vp=up16(w.v_pool), kn=up16(w.k_new),
+                   vn=up16(w.v_new), bt=torch.from_numpy(w.block_tables).to(dev),
+                   lens=torch.from_numpy(w.seq_lens).to(dev),
+                   out=torch.empty((B, 32, 64), dtype=torch.float32, device=dev))
+              for w, _, _ in states]
+    kv = sum(A.step_bytes(w.seq_lens, append=True)["kv"] for w, _, _ in states)
+    cands = [("grid, default plan (pages_per_split=0)", 0, None)]
+    ps_l, _ = pa.decode_plan_lengths(w0.seq_lens, npg, max_seq_len=msl)
+    cands.append(("grid, host-lengths plan", ps_l, None))
+    if B > 1:
+        wl, wps, _ = pa.decode_worklist(w0.seq_lens, npg, max_seq_len=msl)
+        cands.append(("work list", wps, torch.from_numpy(wl).to(dev)))
+    need = max(pa.decode_workspace_bytes(B, msl, npg, 128, ps) for _, ps, _ in cands)
+    workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def run(ps, work):
+        for L in layers:
+            if work is None:
+                pa.append_decode_attention(L["q"], L["kn"], L["vn"], L["kp"], L["vp"], L["bt"],
+                                           L["lens"], msl, scale=w0.scale, out=L["out"],
+                                           pages_per_split=ps, workspace=workspace, stream=stream)
+            else:
+                pa.append_decode_attention_worklist(
+                    L["q"], L["kn"], L["vn"], L["kp"], L["vp"], L["bt"], L["lens"], msl, work,
+                    ps, scale=w0.scale, out=L["out"], workspace=workspace, stream=stream)
+
+    res, best = {}, None
+    for name, ps, work in cands:
+        for _ in range(max(args.warmup, 1)):
+            flush()
+            run(ps, work)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in evs:
+            flush()
+            e[0].record(stream)
+            run(ps, work)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+        outs = [L["out"].cpu().numpy().astype(np.float64) for L in layers]
+        err, rel = parity(outs, refs) if refs is not None else (None, None)
+        res[name] = {"pages_per_split": int(ps), "step_us": round(float(t.mean()) * 1e6, 2),
+                     "step_min_us": round(float(t.min()) * 1e6, 2),
+                     "kv_gbps": round(kv / float(t.mean()) / 1e9, 1),
+                     "max_abs_vs_oracle": err, "max_rel_vs_oracle": rel}
+        if best is None or t.mean() < best[1]:
+            best = (name, float(t.mean()), outs)
+    name, t_best, outs = best
+    nl = len(layers)
+    line = {
+        "workload": states[0][0].recipe.get("workload", ""), "layers": nl, "batch": B,
+        "launch": name, "pages_per_split": res[name]["pages_per_split"],
+        "step_us": round(t_best * 1e6, 2), "per_layer_us": round(t_best / nl * 1e6, 2),
+        "kv_bytes": int(kv), "kv_gbps": round(kv / t_best / 1e9, 1),
+        "hbm_peak_frac": round(kv / t_best / 1e9 / HBM_PEAK_GBPS, 4),
+        "seq_per_s_per_layer": round(int(np.count_nonzero(w0.seq_lens)) * nl / t_best, 1),
+        "max_abs_vs_oracle": res[name]["max_abs_vs_oracle"],
+        "max_rel_vs_oracle": res[name]["max_rel_vs_oracle"],
+        "launches": res,
+    }
+    del layers, workspace
+    torch.cuda.empty_cache()
+    return line, outs
 
 
 def run_sweep(args) -> int:
@@ -313,6 +468,15 @@ def run_sweep(args) -> int:
     return 0
 
 
+def parse_configs(text: str):
+    """Configurations of ``--configs`` (sorted, unique), or None if one is not 1, 2, 3 or 5."""
+    try:
+        cs = sorted(set(int(c) for c in text.split(",") if c.strip()))
+    except ValueError:
+        return None
+    return None if any(c not in CONFIGS or c == 4 for c in cs) else cs
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +492,15 @@ def main() -> int:
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 256 MiB device copy per step (outside the timed events), "
                          "the known-size reference for hardware byte counters")
+    ap.add_argument("--configs", default="1,2,3,5",
+                    help="configurations measured beside the headline (comma list of 1-5; "
+                         "'' for none): each one's fused step, its oracle rates and its "
+                         "max-abs over every output")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="oracle time per configuration, one core and then the pool")
+    ap.add_argument("--only-config", type=int, default=0,
+                    help="measure this one configuration's candidate launches only (no "
+                         "headline passes, no oracle): for profiling runs")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused step of every workload "
                          "(1-5), BF16 and INT8 pages, grid launch with the library plan and "
@@ -349,15 +522,25 @@ def main() -> int:
 
     if args.sweep:
         return run_sweep(args)
+    if args.only_config:
+        if args.only_config not in CONFIGS:
+            print("--only-config takes 1..5", file=sys.stderr)
+            return 2
+        return run_one_config(args)
 
+    others = parse_configs(args.configs)
+    if others is None:
+        print("--configs takes configurations 1, 2, 3 and 5 (4 is the headline)", file=sys.stderr)
+        return 2
     t0 = time.perf_counter()
     batch = W.make_workload(4, placement=args.placement, append=True)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s "
         f"({batch.batch} sequences, {batch.num_pages} pages)")
+    prepare_states([4] + others, args.placement, headline=batch)
     pool, pool_workers = None, 0
     if not args.no_cpu_baseline:
         pool_workers = args.cpu_workers or min(len(os.sched_getaffinity(0)), 16)
-        pool = prepare_cpu_baseline(batch, pool_workers)
+        pool = fork_pool(pool_workers)
 
     # the GPU is first touched here, after the oracle's worker processes were forked
     dev = torch.device("cuda:0")
@@ -425,23 +608,25 @@ def main() -> int:
         torch.cuda.synchronize()
         return np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
 
-    # pass A (the timed K steps)
+    # pass A: the timed K steps, each bracketed by an event pair, with the
+    # library recording a second pair right around its main kernel inside the
+    # same step (so the kernel's time is part of the step it belongs to)
+    evA = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for row in evA:                     # create the HIP events before use
+        for e in row:
+            e.record(stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_step = timed(step, K)
-    wall = time.perf_counter() - wall0
-    log(f"{K} timed steps done in {wall:.3f} s wall (cache flushes included)")
-
-    # pass B: events recorded by the library right before / after its main kernel
-    evB = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    for row in evB:                     # create the HIP events before use
-        row[0].record(stream)
-        row[1].record(stream)
     for i in range(K):
         pre_step()
-        step(marks=evB[i])
+        evA[i][0].record(stream)
+        step(marks=(evA[i][1], evA[i][2]))
+        evA[i][3].record(stream)
     torch.cuda.synchronize()
-    t_main = np.array([e[0].elapsed_time(e[1]) for e in evB]) * 1e-3
+    wall = time.perf_counter() - wall0
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in evA]) * 1e-3
+    t_main = np.array([e[1].elapsed_time(e[2]) for e in evA]) * 1e-3
+    log(f"{K} timed steps done in {wall:.3f} s wall (cache flushes included)")
     # pass C: the same step as two calls
     t_two = timed(two_call_step, K)
     # pass D: the fused step with the rotary embedding of the new q/k fused in
@@ -645,20 +830,77 @@ def main() -> int:
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": kv,
             "avg_launch_us": round(float(t_main.mean()) * 1e6, 2),
+            "timing": "events recorded by the library around the main kernel, inside the "
+                      "same timed steps as ms_per_step (they include the launch's dispatch)",
+            "rocprof": rocprof_kernel_time(),
         },
         "kernel_source_sha": kernel_source_hash(),
     }
+    out_host = out.cpu().numpy().astype(np.float64)
+    del out_id, q, k_pool, v_pool, k_new, v_new, workspace
+    torch.cuda.empty_cache()
+
+    # every configuration: the fastest candidate launch of its fused step, its
+    # parity over every output, the oracle beside it
+    configs = {}
+    refs4 = oracle_refs(4)
+    err4, rel4 = parity([out_host], refs4)
+    configs["4"] = {
+        "workload": W.WORKLOADS[4], "layers": 1, "batch": B, "launch": "grid, default plan "
+        "(pages_per_split=0)", "pages_per_split": ps, "step_us": round(mean_step * 1e6, 2),
+        "per_layer_us": round(mean_step * 1e6, 2), "kv_bytes": int(kv),
+        "kv_gbps": round(value, 1), "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "seq_per_s_per_layer": round(B / mean_step, 1), "max_abs_vs_oracle": err4,
+        "max_rel_vs_oracle": rel4, "note": "the headline line's own figures"}
+    for ci in others:
+        t0 = time.perf_counter()
+        refs = oracle_refs(ci)
+        configs[str(ci)], _ = measure_config(ci, args, stream, dev, flush, refs)
+        c = configs[str(ci)]
+        log(f"config {ci}: {c['launch']}, {c['per_layer_us']} us per layer, {c['kv_gbps']} GB/s, "
+            f"max-abs {c['max_abs_vs_oracle']:.2e} ({time.perf_counter() - t0:.1f} s)")
+    line["configs"] = configs
+
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s on one core, then "
             f"{args.cpu_seconds:.0f} s on {pool_workers} processes")
-        line["cpu_baseline"] = cpu_baseline(out.cpu().numpy().astype(np.float64),
-                                            args.cpu_seconds, pool, pool_workers)
+        line["cpu_baseline"] = oracle_rates(4, args.cpu_seconds, pool, pool_workers,
+                                            gpu_outs=[out_host])
+        for ci in others:
+            configs[str(ci)]["oracle"] = oracle_rates(ci, args.config_cpu_seconds, pool,
+                                                      pool_workers)
+        configs["4"]["oracle"] = {k: line["cpu_baseline"][k] for k in
+                                  ("value", "unit", "cores", "seq_per_s", "pool")
+                                  if k in line["cpu_baseline"]}
+        log(f"oracle rates of configurations {others} done")
         if pool is not None:
             pool.close()
             pool.join()
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_one_config(args) -> int:
+    """Only configuration ``--only-config``'s candidate launches (no oracle, no
+    headline passes): one JSON line; for profiling runs."""
+    import torch
+    from paged_kv_decode_07_amd import binding as pa
+    ci = args.only_config
+    prepare_states([ci], args.placement)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(2**28, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int32, device=dev)
+
+    def flush():
+        if not args.no_flush:
+            torch.amax(flush_buf, dim=None, out=flush_out)
+    line, _ = measure_config(ci, args, stream, dev, flush, None)
+    print(json.dumps({"config": ci, **line}), flush=True)
     return 0
 
 

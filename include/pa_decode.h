@@ -189,7 +189,11 @@ int pa_decode_attention(const pa_shape* shape, int32_t batch,
  * (L-1)%16 of page block_tables[b][(L-1)/16] and takes that token's K/V from
  * registers.  Pools end bit-identical to the two-call sequence and outputs
  * are identical too.  Same layouts, alignment and error rules as the two
- * calls; k_new and v_new are required when batch > 0.
+ * calls; k_new and v_new are required when batch > 0.  The append follows
+ * pa_append_kv's rule for every sequence: the row is written whenever
+ * 1 <= L <= 16 * max_blocks_per_seq and the target page id lies in
+ * [0, num_pages), also when L exceeds max_seq_len (whose output row is NaN,
+ * as in pa_decode_attention).
  */
 int pa_append_decode_attention(const pa_shape* shape, int32_t batch,
                                const void* q, const void* k_new, const void* v_new,
@@ -235,7 +239,11 @@ int pa_append_kv_rope(const pa_shape* shape, int32_t batch,
  * pa_decode_attention on its q_out, in one launch (plus the split merge).
  * Every work-group rotates its own query rows; the one holding the last
  * page rotates and writes the new key.  Outputs and pools are identical to
- * the two-call form.  The tables must cover max_seq_len positions.
+ * the two-call form.  The tables must cover max_seq_len positions.  A
+ * sequence longer than max_seq_len (NaN output row) still has its rotated
+ * row written, as pa_append_decode_attention does, when the tables hold
+ * position L-1; pa_append_kv_rope refuses tables shorter than the block
+ * table's capacity, so with such tables both forms write it.
  */
 int pa_append_decode_attention_rope(const pa_shape* shape, int32_t batch,
                                     const void* q, const void* k_new, const void* v_new,

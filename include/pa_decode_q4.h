@@ -100,7 +100,8 @@ int pa_decode_attention_q4(const pa_shape* shape, int32_t batch, const void* q,
 /*
  * Fused decode step over INT4 pages: pa_append_kv_q4 followed by
  * pa_decode_attention_q4 in one launch (plus the split merge); pools and
- * outputs identical to the two-call form.
+ * outputs identical to the two-call form, with the same append rule for a
+ * sequence longer than max_seq_len as pa_append_decode_attention_q8.
  */
 int pa_append_decode_attention_q4(const pa_shape* shape, int32_t batch, const void* q,
                                   const void* k_new, const void* v_new,

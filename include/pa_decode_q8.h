@@ -96,7 +96,10 @@ int pa_decode_attention_q8(const pa_shape* shape, int32_t batch, const void* q,
  * pa_decode_attention_q8, in one launch (plus the split merge).  The
  * work-group holding a sequence's last page quantises the new rows, writes
  * their codes and scales, and uses the codes in place of what it read for
- * that slot; pools and outputs are identical to the two-call form.
+ * that slot; pools and outputs are identical to the two-call form,
+ * including for a sequence longer than max_seq_len (NaN output row; its new
+ * row is still quantised and written when 1 <= L <= 16 * max_blocks_per_seq
+ * and the page id is valid, as pa_append_kv_q8 does).
  */
 int pa_append_decode_attention_q8(const pa_shape* shape, int32_t batch, const void* q,
                                   const void* k_new, const void* v_new,

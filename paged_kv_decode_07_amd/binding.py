@@ -179,10 +179,15 @@ def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _is_device(t: torch.Tensor) -> bool:
+    """Whether ``t`` lives in device memory (the library takes device pointers only)."""
+    return t.is_cuda
+
+
 def _bits16(t: torch.Tensor, name: str, shape_tail) -> torch.Tensor:
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{name}: expected bfloat16 (or its 16-bit patterns), got {t.dtype}")
-    if not t.is_cuda:
+    if not _is_device(t):
         raise ValueError(f"{name}: must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
@@ -192,9 +197,38 @@ def _bits16(t: torch.Tensor, name: str, shape_tail) -> torch.Tensor:
 
 
 def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+    if t.dtype != torch.int32 or not _is_device(t) or not t.is_contiguous():
         raise ValueError(f"{name}: must be a contiguous int32 device tensor")
     return t
+
+
+def _same_batch(B: int, **tensors) -> None:
+    """Every given tensor's first dimension is the batch."""
+    for name, t in tensors.items():
+        if t is not None and (t.dim() < 1 or int(t.shape[0]) != B):
+            raise ValueError(f"batch dimension mismatch: {name} has {tuple(t.shape)}, batch {B}")
+
+
+def _out_code(out_dtype) -> int:
+    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    return code
+
+
+def _out(out, B: int, out_dtype, device) -> torch.Tensor:
+    """The caller's output tensor, checked, or a new one: contiguous [B][32][64] of out_dtype."""
+    if out is None:
+        return torch.empty((B, HQ, D), dtype=out_dtype, device=device)
+    if out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous() \
+            or not _is_device(out):
+        raise ValueError("out must be a contiguous [B][32][64] device tensor of out_dtype")
+    return out
+
+
+def _same_pools(k_pool, v_pool) -> None:
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
 
 
 def append_kv(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, stream=None) -> None:
@@ -203,10 +237,8 @@ def append_kv(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, stream=None)
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
-    if k_pool.shape != v_pool.shape:
-        raise ValueError("k_pool and v_pool differ in shape")
+    _same_batch(B, k_new=k_new, v_new=v_new, block_tables=block_tables)
+    _same_pools(k_pool, v_pool)
     shape = make_shape(int(k_pool.shape[0]), int(block_tables.shape[1]))
     rc = load_library().pa_append_kv(ctypes.byref(shape), B, _ptr(k_new), _ptr(v_new),
                                      _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
@@ -268,18 +300,11 @@ def decode_attention(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int
     _bits16(q, "q", (HQ, D))
     _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if q.shape[0] != B or block_tables.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
-    if k_pool.shape != v_pool.shape:
-        raise ValueError("k_pool and v_pool differ in shape")
-    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
-    if code is None:
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    _same_batch(B, q=q, block_tables=block_tables)
+    _same_pools(k_pool, v_pool)
+    code = _out_code(out_dtype)
     num_pages, max_blocks = int(k_pool.shape[0]), int(block_tables.shape[1])
-    if out is None:
-        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
-    elif out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][32][64] tensor of out_dtype")
+    out = _out(out, B, out_dtype, q.device)
     need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -312,18 +337,11 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, seq_l
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if q.shape[0] != B or block_tables.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
-    if k_pool.shape != v_pool.shape:
-        raise ValueError("k_pool and v_pool differ in shape")
-    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
-    if code is None:
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
+    _same_pools(k_pool, v_pool)
+    code = _out_code(out_dtype)
     num_pages, max_blocks = int(k_pool.shape[0]), int(block_tables.shape[1])
-    if out is None:
-        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
-    elif out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][32][64] tensor of out_dtype")
+    out = _out(out, B, out_dtype, q.device)
     need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -345,7 +363,7 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, seq_l
 
 def _rope(cos, sin) -> PaRope:
     for name, t in (("rope_cos", cos), ("rope_sin", sin)):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2 \
+        if t.dtype != torch.float32 or not _is_device(t) or not t.is_contiguous() or t.dim() != 2 \
                 or t.shape[1] != D // 2:
             raise ValueError(f"{name}: must be a contiguous float32 [positions][32] device tensor")
     if cos.shape != sin.shape:
@@ -361,11 +379,12 @@ def append_kv_rope(q, k_new, v_new, rope_cos, rope_sin, k_pool, v_pool, block_ta
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if q.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
+    _same_pools(k_pool, v_pool)
     if q_out is None:
         q_out = torch.empty_like(q)
     _bits16(q_out, "q_out", (HQ, D))
+    _same_batch(B, q_out=q_out)
     rope = _rope(rope_cos, rope_sin)
     shape = make_shape(int(k_pool.shape[0]), int(block_tables.shape[1]))
     rc = load_library().pa_append_kv_rope(
@@ -386,14 +405,11 @@ def append_decode_attention_rope(q, k_new, v_new, rope_cos, rope_sin, k_pool, v_
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if q.shape[0] != B or block_tables.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
-    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
-    if code is None:
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
+    _same_pools(k_pool, v_pool)
+    code = _out_code(out_dtype)
     num_pages, max_blocks = int(k_pool.shape[0]), int(block_tables.shape[1])
-    if out is None:
-        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    out = _out(out, B, out_dtype, q.device)
     need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -415,6 +431,7 @@ def fill_kv(k_rows, v_rows, block_table_row, start: int, k_pool, v_pool, stream=
     _i32(block_table_row, "block_table_row")
     if k_rows.shape != v_rows.shape:
         raise ValueError("k_rows and v_rows differ in shape")
+    _same_pools(k_pool, v_pool)
     shape = make_shape(int(k_pool.shape[0]), int(block_table_row.shape[-1]))
     rc = load_library().pa_fill_kv(ctypes.byref(shape), _ptr(k_rows), _ptr(v_rows),
                                    int(k_rows.shape[0]), int(start), _ptr(block_table_row),
@@ -450,14 +467,14 @@ def new_q4_pools(num_pages: int, device="cuda"):
 def _q8_pools(k_codes, v_codes, kv_scales, nbits: int = 8) -> int:
     dtype, width = (torch.int8, D) if nbits == 8 else (torch.uint8, D // 2)
     for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
-        if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or \
+        if t.dtype != dtype or not _is_device(t) or not t.is_contiguous() or \
                 tuple(t.shape[1:]) != (HKV, PAGE, width):
             raise ValueError(f"{name}: must be a contiguous {str(dtype)[6:]} "
                              f"[pages][8][16][{width}] device tensor")
     if k_codes.shape != v_codes.shape:
         raise ValueError("k_codes and v_codes differ in shape")
     n = int(k_codes.shape[0])
-    if kv_scales.dtype != torch.float32 or not kv_scales.is_cuda or \
+    if kv_scales.dtype != torch.float32 or not _is_device(kv_scales) or \
             not kv_scales.is_contiguous() or tuple(kv_scales.shape) != (n, HKV, 2, PAGE):
         raise ValueError("kv_scales: must be a contiguous float32 [pages][8][2][16] device tensor")
     return n
@@ -469,8 +486,7 @@ def append_kv_q8(k_new, v_new, k_codes, v_codes, kv_scales, block_tables, seq_le
     B = int(seq_lens.shape[0])
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
+    _same_batch(B, k_new=k_new, v_new=v_new, block_tables=block_tables)
     shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales, nbits), int(block_tables.shape[1]))
     fn = "pa_append_kv" + _SUFFIX[nbits]
     rc = getattr(load_library(), fn)(
@@ -486,11 +502,11 @@ def append_kv_rope_q8(q, k_new, v_new, rope_cos, rope_sin, k_codes, v_codes, kv_
     _bits16(q, "q", (HQ, D))
     _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if q.shape[0] != B or k_new.shape[0] != B or v_new.shape[0] != B or block_tables.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
     if q_out is None:
         q_out = torch.empty_like(q)
     _bits16(q_out, "q_out", (HQ, D))
+    _same_batch(B, q_out=q_out)
     rope = _rope(rope_cos, rope_sin)
     shape = make_shape(_q8_pools(k_codes, v_codes, kv_scales, nbits), int(block_tables.shape[1]))
     fn = "pa_append_kv_rope" + _SUFFIX[nbits]
@@ -543,20 +559,12 @@ def _decode_q8(fn, q, k_new, v_new, rope, k_codes, v_codes, kv_scales, block_tab
     _bits16(q, "q", (HQ, D))
     if k_new is not None:
         _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
-        if k_new.shape[0] != B or v_new.shape[0] != B:
-            raise ValueError("batch dimension mismatch")
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
-    if q.shape[0] != B or block_tables.shape[0] != B:
-        raise ValueError("batch dimension mismatch")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
     num_pages = _q8_pools(k_codes, v_codes, kv_scales, nbits)
-    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
-    if code is None:
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    code = _out_code(out_dtype)
     max_blocks = int(block_tables.shape[1])
-    if out is None:
-        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
-    elif out.dtype != out_dtype or tuple(out.shape) != (B, HQ, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][32][64] tensor of out_dtype")
+    out = _out(out, B, out_dtype, q.device)
     need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -667,6 +675,7 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
     if k_new is not None:
         _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
     _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
     _i32(work, "work")
     if work.dim() != 2 or work.shape[1] != 2 or work.shape[0] < 1:
         raise ValueError("work: int32 [n][2] device tensor with n >= 1")
@@ -675,12 +684,10 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
     num_pages = _q8_pools(k_pool, v_pool, kv_scales, nbits) if q8 else int(k_pool.shape[0])
     if not q8:
         _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
-    code = {torch.float32: PA_OUT_F32, torch.bfloat16: PA_OUT_BF16}.get(out_dtype)
-    if code is None:
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+        _same_pools(k_pool, v_pool)
+    code = _out_code(out_dtype)
     max_blocks = int(block_tables.shape[1])
-    if out is None:
-        out = torch.empty((B, HQ, D), dtype=out_dtype, device=q.device)
+    out = _out(out, B, out_dtype, q.device)
     need = decode_workspace_bytes(B, max_seq_len, num_pages, max_blocks, pages_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -522,6 +522,7 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.v_pool_w = const_cast<void*>(v_pool);
   a.rope_cos = rope ? rope->cos : nullptr;
   a.rope_sin = rope ? rope->sin : nullptr;
+  a.rope_positions = rope ? rope->positions : 0;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = out;

@@ -108,6 +108,7 @@ struct DecodeArgs {
   float* kv_scales_w;
   const float* rope_cos;
   const float* rope_sin;
+  int32_t rope_positions;      // rows of rope_cos / rope_sin
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
@@ -496,6 +497,36 @@ __device__ __forceinline__ int out_dim(int b, int n) {
 #endif
 constexpr int kStreamCpol = PA_STREAM_CPOL;
 
+// The new K/V row of KV head g straight into the pool (no LDS parking): lane
+// c (K) and 4 + c (V), c = 0..3, hold the row parts {8c..8c+7} (lo) and
+// {32+8c..} (hi); K is rotated first with RoPE at position `pos`, quantised
+// pages quantise each row over its quad of lanes.  Lanes 0..7 call it
+// together (the quantiser's quad reductions need all four lanes of a row).
+template <int FMT, bool ROPE>
+__device__ __forceinline__ void append_row_direct(const DecodeArgs& a, uint4 lo, uint4 hi, int id,
+                                                  int slot, int pos, int g, int lane) {
+  const int c = lane & 3;
+  const bool is_k = lane < 4;
+  if (ROPE && is_k) {
+    const int64_t row = (int64_t)pos * (kD / 2) + 8 * c;
+    rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
+  }
+  if constexpr (FMT == kFmtBF16) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(is_k ? a.k_pool_w : a.v_pool_w) +
+                    (int64_t)id * kPageElems + slot * kRowElems + g * kD + 8 * c;
+    *reinterpret_cast<uint4*>(dst) = lo;
+    *reinterpret_cast<uint4*>(dst + 32) = hi;
+  } else {
+    using QL = QuantLayout<FMT>;
+    u32x2 clo, chi;
+    const float sc = quantize_quad_row<FMT>(lo, hi, clo, chi);
+    uint8_t* row = reinterpret_cast<uint8_t*>(is_k ? a.k_pool_w : a.v_pool_w) +
+                   (int64_t)id * QL::kPageBytes + g * QL::kHead + slot * QL::kRow;
+    store_quad_codes<FMT>(row, c, clo, chi);
+    if (c == 0) a.kv_scales_w[(int64_t)id * kScalePageFloats + (g * 2 + (is_k ? 0 : 1)) * kPage + slot] = sc;
+  }
+}
+
 // WPH: wavefronts per KV head (1 or 2).  With 2, the two wavefronts of a head
 // stream the first and second half of the split's pages, each with its own
 // ring, and merge their running states through LDS at the end: the
@@ -570,6 +601,17 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
 #pragma unroll
     for (int e = 0; e < 16; ++e) res[e] = fill;
     if (n < kGroup) store_row16<OUT_BF16>(a.out, (int64_t)b * kHq + kGroup * g + n, G, res);
+    // A length the call cannot attend (above max_seq_len, or beyond what the
+    // plan's splits cover) still gets its new row, under the rule of the
+    // separate append: 1 <= L <= 16 max_blocks and a valid page id (and, with
+    // RoPE, a table row for position L-1).  Split 0's first wavefront of each
+    // head writes it straight to the pool.
+    if (APPEND && bad_len && wh == 0 && L >= 1 && n_pages <= a.max_blocks &&
+        (!ROPE || L <= a.rope_positions)) {
+      const int id = bt[n_pages - 1];
+      if ((unsigned)id < (unsigned)a.num_pages && lane < 8)
+        append_row_direct<FMT, ROPE>(a, new_lo, new_hi, id, (L - 1) % kPage, L - 1, g, lane);
+    }
     return;
   }
 

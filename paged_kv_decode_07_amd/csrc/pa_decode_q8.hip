@@ -253,6 +253,7 @@ int decode_quant_impl(const pa_shape* shape, int32_t batch, const void* q, const
   a.kv_scales_w = (float*)const_cast<void*>(kv_scales);
   a.rope_cos = rope ? rope->cos : nullptr;
   a.rope_sin = rope ? rope->sin : nullptr;
+  a.rope_positions = rope ? rope->positions : 0;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = out;

@@ -30,3 +30,41 @@ def test_traffic_is_dropped_when_the_kernel_changed(tmp_path, monkeypatch):
                              "hbm_bytes_per_launch": 7.0}))
     assert bench.measured_traffic(str(f), bench.KERNEL_SOURCES_Q8) == 7
 
+
+def test_config_lists_are_checked_before_any_work():
+    for bad in (["--configs", "4"], ["--configs", "1,7"], ["--configs", "x"],
+                ["--only-config", "6"]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *bad],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2, (bad, r.stderr)
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.parse_configs("5,1,3,3") == [1, 3, 5]
+    assert bench.parse_configs("") == []
+
+
+def test_rocprof_time_is_dropped_when_the_kernel_changed(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    f = tmp_path / "t.json"
+    f.write_text(json.dumps({"kernel_source_sha": "0" * 16, "avg_us": 160.0,
+                             "algorithmic_kv_bytes": 1 << 30}))
+    assert bench.rocprof_kernel_time(str(f)) is None
+    f.write_text(json.dumps({"kernel_source_sha": bench.kernel_source_hash(), "avg_us": 160.0,
+                             "algorithmic_kv_bytes": 1 << 30, "calls": 20}))
+    r = bench.rocprof_kernel_time(str(f))
+    assert r["avg_us"] == 160.0 and abs(r["achieved"] - (1 << 30) / 160e3) < 0.01
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+
+
+def test_oracle_rates_and_parity_on_the_host():
+    sys.path.insert(0, ROOT)
+    import bench
+    bench.prepare_states([1], "random")
+    r = bench.oracle_rates(1, 0.2)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["seq_per_s"] > 0
+    refs = bench.oracle_refs(1)
+    bumped = [x.copy() for x in refs]
+    bumped[0][0, 3, 5] += 1e-3
+    err, rel = bench.parity(bumped, refs)
+    assert abs(err - 1e-3) < 1e-12 and rel > 0

@@ -64,30 +64,30 @@ def test_fused_seq_len_one_returns_the_new_v_row():
 def test_fused_full_batch512_zipf():
     w = W.make_workload(5)
     got = _two_call_vs_fused(w, 0)
-    seqs = sorted(set([int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 3, 100, 511]))
     k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
                                     w.seq_lens)
-    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale,
-                                  sequences=seqs)
-    assert_close(got[seqs], ref[seqs], where="fused batch512 sampled")
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got, ref, where="fused batch512 every sequence")
 
 
 def test_fused_full_batch256_len2048_bench_configuration():
     w = W.make_workload(4, append=True)
     got = _two_call_vs_fused(w, 0)
-    seqs = [0, 77, 255]
     k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
                                     w.seq_lens)
-    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale,
-                                  sequences=seqs)
-    assert_close(got[seqs], ref[seqs], where="fused batch256 sampled")
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got, ref, where="fused batch256 every sequence")
 
 
-def test_fused_16_layer_workload_first_and_last_layer():
-    for layer in (0, W.NUM_LAYERS_W3 - 1):
+def test_fused_16_layer_workload_every_layer():
+    for layer in range(W.NUM_LAYERS_W3):
+        print(f"fused: 16-layer workload, layer {layer}", flush=True)
         w = W.make_workload(3, layer=layer)
         got = _two_call_vs_fused(w, 0)
-        assert np.all(np.isfinite(got))
+        k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                        w.seq_lens)
+        ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+        assert_close(got, ref, where=f"fused 16-layer layer {layer}")
 
 
 def test_fused_bad_last_page_writes_nothing_and_gives_nan():
@@ -131,3 +131,80 @@ def test_fused_batch_of_70000_single_token_sequences():
     page = bt[:, 0].long()
     assert torch.equal(v_pool[page, 0], vn.view(torch.int16))
     assert torch.equal(k_pool[page, 0], kn.view(torch.int16))
+
+
+OVER = [40, 300, 17, 129]          # with max_seq_len 100, sequences 1 and 3 are over it
+
+
+@pytest.mark.parametrize("pages_per_split", [0, 3])
+def test_fused_over_length_appends_like_the_two_call_form(pages_per_split):
+    """A length above max_seq_len (but within the block table) gets a NaN
+    output row from both forms, and its new row is written by both, as the
+    separate append writes every row within the table's capacity."""
+    from gpu_util import dev16
+    from paged_kv_decode_07_amd import binding as pa
+    w = W.make_batch(OVER, sum(W.pages_for(L) for L in OVER) + 5, seed=74, append=True)
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    a = DeviceBatch(w)
+    gpu_append(a)
+    two = pa.decode_attention(a.q, a.k_pool, a.v_pool, a.bt, a.lens, 100,
+                              pages_per_split=pages_per_split)
+    f = DeviceBatch(w)
+    fused = pa.append_decode_attention(f.q, f.k_new, f.v_new, f.k_pool, f.v_pool, f.bt, f.lens,
+                                       100, pages_per_split=pages_per_split)
+    torch.cuda.synchronize()
+    for d in (a, f):
+        assert np.array_equal(host16(d.k_pool), k_ref) and np.array_equal(host16(d.v_pool), v_ref)
+    two, fused = two.cpu().numpy(), fused.cpu().numpy()
+    for b in (1, 3):
+        assert np.all(np.isnan(two[b])) and np.all(np.isnan(fused[b]))
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(fused[[0, 2]].astype(np.float64), ref[[0, 2]], where="over-length others")
+    assert np.array_equal(fused[[0, 2]], two[[0, 2]])
+    # with RoPE: tables covering the capacity, both forms rotate and write every row
+    cos, sin = W.rope_table()
+    rc, rs = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    a = DeviceBatch(w)
+    pa.append_kv_rope(a.q, a.k_new, a.v_new, rc, rs, a.k_pool, a.v_pool, a.bt, a.lens)
+    f = DeviceBatch(w)
+    pa.append_decode_attention_rope(f.q, f.k_new, f.v_new, rc, rs, f.k_pool, f.v_pool, f.bt,
+                                    f.lens, 100, pages_per_split=pages_per_split)
+    torch.cuda.synchronize()
+    _, k_rot = oracle.rope.rope_new_token(w.q, w.k_new, w.seq_lens, cos, sin)
+    k_rref, v_rref = oracle.append_kv(w.k_pool, w.v_pool, k_rot, w.v_new, w.block_tables,
+                                      w.seq_lens)
+    for d in (a, f):
+        assert np.array_equal(host16(d.k_pool), k_rref)
+        assert np.array_equal(host16(d.v_pool), v_rref)
+
+
+@pytest.mark.parametrize("nbits", [8, 4])
+def test_fused_quantised_over_length_appends_like_the_two_call_form(nbits):
+    from gpu_util import dev16, dev32
+    from oracle import kvquant
+    from paged_kv_decode_07_amd import binding as pa
+    w = W.make_q8_batch(OVER, sum(W.pages_for(L) for L in OVER) + 5, 75, append=True,
+                        nbits=nbits)
+    want = kvquant.append_kv_q8(w.k_codes, w.v_codes, w.kv_scales, w.k_new, w.v_new,
+                                w.block_tables, w.seq_lens, nbits=nbits)
+    q, kn, vn = dev16(w.q), dev16(w.k_new), dev16(w.v_new)
+    bt, lens = dev32(w.block_tables), dev32(w.seq_lens)
+
+    def pools():
+        return tuple(torch.from_numpy(np.ascontiguousarray(x)).cuda()
+                     for x in (w.k_codes, w.v_codes, w.kv_scales))
+    a = pools()
+    pa.append_kv_q8(kn, vn, *a, bt, lens, nbits=nbits)
+    two = pa.decode_attention_q8(q, *a, bt, lens, 100, nbits=nbits)
+    f = pools()
+    fused = pa.append_decode_attention_q8(q, kn, vn, *f, bt, lens, 100, nbits=nbits)
+    torch.cuda.synchronize()
+    for d in (a, f):
+        got = [t.cpu().numpy() for t in d]
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+        assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+    two, fused = two.cpu().numpy(), fused.cpu().numpy()
+    for b in (1, 3):
+        assert np.all(np.isnan(two[b])) and np.all(np.isnan(fused[b]))
+    assert np.array_equal(fused[[0, 2]], two[[0, 2]])

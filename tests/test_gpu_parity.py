@@ -2,9 +2,10 @@
 
 Append: bit-exact, whole pool compared.  Attention: max-abs 2e-3 and
 relative 1e-2 (denominator max(|ref|, 1e-2)) with FP32 output; every output
-element at the small sizes, sampled sequences (all heads) at the full sizes,
-plus properties that hold at any size (finite, deterministic run to run,
-bitwise independent of where pages sit in the pool).
+element, at the small sizes and at the full ones (every sequence of the
+256 x 2048 batch, the 512-sequence Zipf batch and all 16 layers of the
+64-sequence workload), plus properties that hold at any size (deterministic
+run to run, bitwise independent of where pages sit in the pool).
 """
 
 from __future__ import annotations
@@ -226,14 +227,6 @@ def test_decode_rejects_small_workspace():
 # --------------------------------------------------------------------------
 # full sizes, launch configuration of the benchmark (library-planned splits)
 # --------------------------------------------------------------------------
-def _sample(lens, k, seed):
-    order = np.argsort(lens, kind="stable")
-    rng = np.random.default_rng(seed)
-    pick = set([int(order[0]), int(order[-1]), int(order[len(order) // 2])])
-    pick |= set(int(i) for i in rng.choice(len(lens), size=k, replace=False))
-    return sorted(pick)
-
-
 def test_full_batch256_len2048():
     _say("full: batch 256 x 2048, random placement")
     w = W.make_workload(4)
@@ -241,10 +234,7 @@ def test_full_batch256_len2048():
     got = gpu_decode(db)
     again = gpu_decode(db)
     assert np.array_equal(got, again), "not deterministic"
-    assert np.all(np.isfinite(got))
-    seqs = _sample(w.seq_lens, 6, 51)
-    ref = oracle_decode(w, sequences=seqs)
-    assert_close(got[seqs], ref[seqs], where="batch256 sampled")
+    assert_close(got, oracle_decode(w), where="batch256 every sequence")
     del db
     _say("full: batch 256 x 2048, identity placement")
     wi = W.make_workload(4, placement="identity")
@@ -262,11 +252,8 @@ def test_full_batch512_zipf_append_then_decode():
     assert np.array_equal(host16(db.k_pool), k_ref)
     assert np.array_equal(host16(db.v_pool), v_ref)
     got = gpu_decode(db)
-    assert np.all(np.isfinite(got))
-    seqs = _sample(w.seq_lens, 10, 52)
-    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale,
-                                  sequences=seqs)
-    assert_close(got[seqs], ref[seqs], where="batch512 sampled")
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got, ref, where="batch512 every sequence")
 
 
 def test_full_16_layers_append_then_decode():
@@ -280,10 +267,8 @@ def test_full_16_layers_append_then_decode():
                                         w.block_tables, w.seq_lens)
         assert np.array_equal(k_dev, k_ref) and np.array_equal(v_dev, v_ref), layer
         got = gpu_decode(db)
-        seqs = _sample(w.seq_lens, 3, 60 + layer)
-        ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens,
-                                      w.scale, sequences=seqs)
-        assert_close(got[seqs], ref[seqs], where=f"16-layer layer {layer}")
+        ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+        assert_close(got, ref, where=f"16-layer layer {layer}")
         del db
         torch.cuda.empty_cache()
 
@@ -295,9 +280,7 @@ def test_plan_from_host_lengths_is_valid_and_correct():
         ps, ns = pa.decode_plan_lengths(w.seq_lens, w.num_pages)
         assert 1 <= ps <= 256 and ns == -(-W.pages_for(w.max_seq_len) // ps)
         got = gpu_decode(DeviceBatch(w), pages_per_split=ps)
-        seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 0]
-        ref = oracle_decode(w, sequences=seqs)
-        assert_close(got[seqs], ref[seqs], where=f"host-length plan w{wi} ps={ps}")
+        assert_close(got, oracle_decode(w), where=f"host-length plan w{wi} ps={ps}")
     # uniform full-length batch covering the CUs: one split per sequence
     ps, ns = pa.decode_plan_lengths(np.full(256, 2048, np.int32), 32768)
     assert (ps, ns) == (128, 1)

@@ -12,7 +12,7 @@
   form, outputs identical to it and within tolerance of the oracle; with
   RoPE; behind 256-entry block tables; launched from a work list;
 * at the full 256 x 2048 size with the planner's split size: the BF16 cache
-  quantised on the GPU, sampled pages and outputs against the oracle, and
+  quantised on the GPU, every page and output against the oracle, and
   the quantisation error against BF16 attention within the oracle's
   analytic bound.
 """
@@ -205,9 +205,7 @@ def test_q4_decode_random_lengths_identity_placement():
     lens = W.workload_seq_lens(3)
     w = W.make_q8_batch(lens, 8192, 1923, placement="identity", nbits=NB)
     got = _decode(DevQ4(w))
-    seqs = list(range(0, len(lens), 7))
-    ref = _ref(w, sequences=seqs)
-    assert_close(got[seqs], ref[seqs], where="q4 batch 64 identity")
+    assert_close(got, _ref(w), where="q4 batch 64 identity")
 
 
 def test_q4_decode_sharp_scores():
@@ -322,9 +320,7 @@ def test_q4_worklist_matches_grid():
     got = out.cpu().numpy().astype(np.float64)
     _same_pools(f.pools(), g.pools())
     assert np.array_equal(got, grid)
-    seqs = list(range(0, len(lens), 5))
-    assert_close(got[seqs], _ref(w, sequences=seqs, pools=_appended_pools(w))[seqs],
-                 where="q4 work list")
+    assert_close(got, _ref(w, pools=_appended_pools(w)), where="q4 work list")
 
 
 # ---------------------------------------------------------------------------
@@ -347,7 +343,7 @@ def test_q4_full_batch256_len2048_bench_configuration():
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     qf = oracle.bf16_bits_to_f64(w.q)
-    for b in (0, 77, 255):
+    for b in range(w.batch):
         L = int(w.seq_lens[b])
         pages = w.block_tables[b, :W.pages_for(L)]
         kr = w.k_pool[pages].reshape(-1, HKV, D)[:L].copy()

@@ -9,7 +9,7 @@
 * the fused quantise-append + decode: pools bit-identical to the two-call
   form, outputs identical to it and within tolerance of the oracle;
 * at the full 256 x 2048 size, in the launch configuration the benchmark
-  times: the BF16 cache quantised on the GPU, sampled pages and outputs
+  times: the BF16 cache quantised on the GPU, every page and output
   against the oracle, and the quantisation error against BF16 attention
   within the oracle's analytic bound.
 """
@@ -179,9 +179,7 @@ def test_q8_decode_random_lengths_identity_placement():
     w = W.make_q8_batch(lens, 8192, 923, placement="identity")
     d = DevQ8(w)
     got = _decode(d)
-    seqs = list(range(0, len(lens), 7))
-    ref = _ref(w, sequences=seqs)
-    assert_close(got[seqs], ref[seqs], where="q8 batch 64 identity")
+    assert_close(got, _ref(w), where="q8 batch 64 identity")
 
 
 def test_q8_decode_bad_metadata():
@@ -267,7 +265,7 @@ def test_q8_full_batch256_len2048_bench_configuration():
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     qf = oracle.bf16_bits_to_f64(w.q)
-    for b in (0, 77, 255):
+    for b in range(w.batch):
         L = int(w.seq_lens[b])
         pages = w.block_tables[b, :W.pages_for(L)]
         # logical rows of the sequence (the held-back token appended)

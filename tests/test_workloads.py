@@ -67,3 +67,84 @@ def test_placement_does_not_change_the_logical_cache():
         L = int(a.seq_lens[i])
         assert np.array_equal(oracle.gather_sequence(a.k_pool, a.block_tables[i], L),
                               oracle.gather_sequence(b.k_pool, b.block_tables[i], L))
+
+
+# ---------------------------------------------------------------------------
+# Sharp-score inputs: they must really raise a page-wise running maximum far
+# past its first value, or the GPU tests built on them prove nothing about the
+# rescale of the online softmax.
+# ---------------------------------------------------------------------------
+SHARP_LENS = [37, 100, 255, 256, 1000, 2047, 2048, 17, 1, 0]
+RAISE_LOG2 = 8.0          # the decode kernel's lazy-rescale threshold, in log2 units
+
+
+def _page_maxima_log2(w, b, h, k_pool, v_pool):
+    """Per-page maxima of head h's scores of sequence b, in log2 units (float64)."""
+    import oracle
+    L = int(w.seq_lens[b])
+    K = oracle.gather_sequence(k_pool, w.block_tables[b], L)[:, h // 4, :]
+    q = oracle.bf16_bits_to_f64(w.q[b, h])
+    s = w.scale * (K @ q) / np.log(2.0)
+    return np.array([s[i:i + 16].max() for i in range(0, L, 16)])
+
+
+def _rises(w, k_pool, v_pool):
+    """(number of (sequence, head) whose running maximum rises by more than the
+    threshold after the first page, spread of their page maxima)."""
+    rises, spread = 0, 0.0
+    for b in range(w.batch):
+        if w.seq_lens[b] <= 16:
+            continue
+        for h in range(0, 32, 5):
+            pm = _page_maxima_log2(w, b, h, k_pool, v_pool)
+            if np.max(pm[1:]) > pm[0] + RAISE_LOG2:
+                rises += 1
+            spread = max(spread, float(pm.max() - pm.min()))
+    return rises, spread
+
+
+def test_sharp_inputs_raise_the_running_maximum_after_the_first_page():
+    import oracle
+    for mode in W.SHARP_MODES:
+        w = W.make_sharp_batch(SHARP_LENS, 1200, 7, mode, append=True)
+        k, v = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                w.seq_lens)
+        rises, spread = _rises(w, k, v)
+        if mode == "ramp_down":
+            assert spread > RAISE_LOG2, mode        # split maxima far apart, largest first
+        else:
+            assert rises >= 5, (mode, rises)
+            assert spread > 2 * RAISE_LOG2, (mode, spread)
+    # the N(0, 1) workloads at scale 1/8 essentially never do (why these inputs exist)
+    w = W.make_batch(SHARP_LENS, 1200, 7)
+    assert _rises(w, w.k_pool, w.v_pool)[0] == 0
+
+
+def test_sharp_tail_max_sits_on_the_appended_token_in_a_part_filled_page():
+    import oracle
+    w = W.make_sharp_batch(SHARP_LENS, 1200, 8, "tail_max", append=True)
+    k, v = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables, w.seq_lens)
+    for b, L in enumerate(w.seq_lens):
+        if L < 2:
+            continue
+        K = oracle.gather_sequence(k, w.block_tables[b], int(L))
+        for h in range(32):
+            s = K[:, h // 4, :] @ oracle.bf16_bits_to_f64(w.q[b, h])
+            assert int(np.argmax(s)) == L - 1, (b, h)
+    assert any(L % 16 for L in SHARP_LENS if L)
+
+
+def test_sharp_batch_layout_matches_make_batch_conventions():
+    w = W.make_sharp_batch(SHARP_LENS, 1200, 9, "ramp_up", append=True)
+    used = []
+    for b, L in enumerate(w.seq_lens):
+        n = W.pages_for(L)
+        assert np.all(w.block_tables[b, n:] == -1)
+        used.extend(w.block_tables[b, :n].tolist())
+        if L:
+            page = w.block_tables[b, (L - 1) // 16]
+            assert np.all(w.k_pool[page, (L - 1) % 16] == W.BF16_NAN)
+    assert len(used) == len(set(used))
+    assert W.make_sharp_batch(SHARP_LENS, 1200, 9, "scale2").scale == W.SHARP_SCALE2
+    rows = W.logical_rows(w.k_pool, w.block_tables[2], 254)
+    assert rows.shape == (254, 8, 64) and not np.any(rows == W.BF16_NAN)

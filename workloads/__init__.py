@@ -421,6 +421,108 @@ def make_q8_batch(seq_lens, num_pages: int, seed, *, append: bool = False,
                    recipe=recipe, nbits=nbits)
 
 
+# ---------------------------------------------------------------------------
+# Sharp-score inputs: later keys score far above earlier ones, so a running
+# maximum taken page by page must be raised (and what was summed under the old
+# one rescaled) long after the first page, and split maxima lie far apart.
+# Each mode only shapes the key rows (or the scale); the values stay N(0, 1).
+# ---------------------------------------------------------------------------
+SHARP_MODES = ("ramp_up", "ramp_down", "tail_max", "mid_max", "scale2")
+SHARP_SCALE2 = 2.0              # the scale of mode "scale2" (scores of sigma 16)
+SPIKE_GAIN = 1.5                # a spike key is 1.5 x the sum of its group's query rows
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """BF16 bit patterns -> float32 values (the upper half of a binary32 word)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_sharp_batch(seq_lens, num_pages: int, seed, mode: str, *, append: bool = False,
+                     placement: str = "random", max_blocks: int = MAX_BLOCKS) -> DecodeBatch:
+    """Inputs whose scores rise far past the running maximum after the first page.
+
+    Modes (K of token ``t`` of a sequence of length ``L``; q, V and the other
+    keys N(0, 1); scale 1/8 unless stated):
+
+    * ``ramp_up``: ``K[t]`` scaled by ``0.25 + 5.75 t / (L - 1)``: every later
+      page's scores spread wider than the earlier ones' (standard deviation
+      0.25 on the first page, 6 at the end);
+    * ``ramp_down``: the reverse ramp (the largest scores on the first pages);
+    * ``tail_max``: the last token's key of each KV head ``g`` is 1.5 x the sum
+      of the query rows of heads ``4g .. 4g+3``, its score about 12 above the
+      others.  It sits in the last page, which ends mid-page for most
+      lengths; with ``append=True`` it is the appended token;
+    * ``mid_max``: the same spike on token ``L // 2``;
+    * ``scale2``: no shaping; the batch's scale is 2.0 (score sigma 16).
+
+    Draw order: as ``make_batch`` (page permutation, q, then per sequence its
+    K block then its V block).
+    """
+    if mode not in SHARP_MODES:
+        raise ValueError(mode)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = int(seq_lens.shape[0])
+    if np.any(seq_lens < 0) or np.any(seq_lens > max_blocks * PAGE_SIZE):
+        raise ValueError("seq_lens must lie in [0, %d]" % (max_blocks * PAGE_SIZE))
+    rng = np.random.default_rng(seed)
+    n_pages = [pages_for(L) for L in seq_lens]
+    if sum(n_pages) > num_pages:
+        raise ValueError(f"pool of {num_pages} pages cannot hold {sum(n_pages)} pages")
+    perm = rng.permutation(num_pages).astype(np.int32)
+    if placement not in ("random", "identity"):
+        raise ValueError(placement)
+    order = perm if placement == "random" else np.arange(num_pages, dtype=np.int32)
+    q = f32_to_bf16_bits(rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM), dtype=np.float32))
+    qf = bf16_bits_to_f32(q)
+    group = NUM_Q_HEADS // NUM_KV_HEADS
+    shape_pool = (num_pages, PAGE_SIZE, NUM_KV_HEADS, HEAD_DIM)
+    k_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
+    v_pool = np.full(shape_pool, BF16_NAN, dtype=np.uint16)
+    block_tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    k_new = np.full((B, NUM_KV_HEADS, HEAD_DIM), BF16_NAN, dtype=np.uint16) if append else None
+    v_new = np.full((B, NUM_KV_HEADS, HEAD_DIM), BF16_NAN, dtype=np.uint16) if append else None
+    cursor = 0
+    for b in range(B):
+        L, n = int(seq_lens[b]), n_pages[b]
+        pages = order[cursor:cursor + n]
+        cursor += n
+        block_tables[b, :n] = pages
+        if L == 0:
+            continue
+        K = rng.standard_normal((L, NUM_KV_HEADS, HEAD_DIM), dtype=np.float32)
+        V = f32_to_bf16_bits(rng.standard_normal((L, NUM_KV_HEADS, HEAD_DIM), dtype=np.float32))
+        pos = np.arange(L, dtype=np.float32) / np.float32(max(L - 1, 1))
+        if mode == "ramp_up":
+            K *= (np.float32(0.25) + np.float32(5.75) * pos)[:, None, None]
+        elif mode == "ramp_down":
+            K *= (np.float32(6.0) - np.float32(5.75) * pos)[:, None, None]
+        elif mode in ("tail_max", "mid_max"):
+            t = L - 1 if mode == "tail_max" else L // 2
+            spike = qf[b].reshape(NUM_KV_HEADS, group, HEAD_DIM).sum(axis=1)
+            K[t] = np.float32(SPIKE_GAIN) * spike
+        K = f32_to_bf16_bits(K)
+        stored = L
+        if append:
+            k_new[b], v_new[b] = K[L - 1], V[L - 1]
+            stored = L - 1
+        _place(k_pool, pages, K[:stored])
+        _place(v_pool, pages, V[:stored])
+    recipe = dict(num_pages=num_pages, placement=placement, append=append,
+                  seed=_seed_repr(seed), sharp_mode=mode)
+    return DecodeBatch(name=f"sharp_{mode}", q=q, k_pool=k_pool, v_pool=v_pool,
+                       block_tables=block_tables, seq_lens=seq_lens,
+                       scale=SHARP_SCALE2 if mode == "scale2" else SCALE,
+                       k_new=k_new, v_new=v_new, recipe=recipe)
+
+
+def logical_rows(pool: np.ndarray, block_table_row, count: int) -> np.ndarray:
+    """Tokens ``0 .. count-1`` of one sequence as ``[count][8][64]`` BF16 bits
+    (the page pool read back through the block table; layout only)."""
+    n = pages_for(count)
+    return np.ascontiguousarray(pool[np.asarray(block_table_row[:n])]
+                                .reshape(-1, NUM_KV_HEADS, HEAD_DIM)[:count])
+
+
 def poison_summary(batch: DecodeBatch) -> dict:
     """Counts of poisoned pool rows and block-table entries (for reports)."""
     nan_rows = int(np.count_nonzero(batch.k_pool[..., 0, 0] == BF16_NAN))
