@@ -337,6 +337,31 @@ const char* pa_status_string(int status);
 /* ABI version of this header (bumped on incompatible changes). */
 int pa_abi_version(void);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fused
+ * step of pa_append_decode_attention, same arguments minus the workspace,
+ * same results bit for bit.  The split partials go to a scratch array that
+ * the library holds in device memory for the life of the process (one per
+ * GPU it runs on, PA_NOALLOC_SCRATCH_BYTES bytes); nothing is allocated by
+ * the call.  A plan whose partials need more than that (batch x splits x
+ * 32 heads x 66 floats, rounded up to 256 bytes, plus 2 floats per row:
+ * pa_decode_workspace_bytes) returns PA_ERR_WORKSPACE before any launch.
+ * The partials need no clearing: every row read is written first in the same
+ * call.  Calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (on different streams, or from several host threads) race and must be
+ * serialised by the caller.  The first call on a device looks the scratch up
+ * (hipGetSymbolAddress); a failure there returns PA_ERR_DEVICE.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_append_decode_attention_noalloc(const pa_shape* shape, int32_t batch,
+                                       const void* q, const void* k_new, const void* v_new,
+                                       void* k_pool, void* v_pool,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       int32_t max_seq_len, float scale,
+                                       void* out, int32_t out_dtype,
+                                       int32_t pages_per_split, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,7 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_append_kv_rope", "pa_append_decode_attention_rope", "pa_fill_kv",
            "pa_validate_metadata", "pa_status_string", "pa_abi_version",
            "pa_decode_worklist", "pa_append_decode_attention_worklist",
+           "pa_append_decode_attention_noalloc",
            # include/pa_decode_q8.h
            "pa_append_kv_q8", "pa_append_kv_rope_q8", "pa_fill_kv_q8", "pa_decode_attention_q8",
            "pa_append_decode_attention_q8", "pa_append_decode_attention_rope_q8",
@@ -91,6 +92,8 @@ def load_library(path: str | None = None):
                                                      ctypes.c_float, P, I32, I32, P, SZ, P, P, P]
         lib.pa_append_decode_attention.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
                                                    ctypes.c_float, P, I32, I32, P, SZ, P]
+        lib.pa_append_decode_attention_noalloc.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
+                                                           ctypes.c_float, P, I32, I32, P]
         RP = ctypes.POINTER(PaRope)
         lib.pa_append_kv_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, P, P]
         lib.pa_append_decode_attention_rope.argtypes = [SP, I32, P, P, P, RP, P, P, P, P, I32,
@@ -358,6 +361,36 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, seq_l
         rc = lib.pa_decode_attention_profiled(*args, *_event_handles(event_before_main,
                                                                       event_after_main))
     _check(rc, "pa_append_decode_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # PA_NOALLOC_SCRATCH_BYTES of include/pa_decode.h
+
+
+def append_decode_attention_noalloc(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                                    max_seq_len: int, out, scale: float = 0.125,
+                                    out_dtype=torch.float32, pages_per_split: int = 0,
+                                    stream=None):
+    """The fused step of ``append_decode_attention`` with the split partials in the
+    library's own device scratch: the call allocates nothing, so ``out`` must be
+    given.  Calls that overlap in time on one GPU share that scratch and race."""
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
+    _same_pools(k_pool, v_pool)
+    code = _out_code(out_dtype)
+    if out is None:
+        raise ValueError("out is required: this call allocates nothing")
+    out = _out(out, B, out_dtype, q.device)
+    shape = make_shape(int(k_pool.shape[0]), int(block_tables.shape[1]))
+    rc = load_library().pa_append_decode_attention_noalloc(
+        ctypes.byref(shape), B, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), _ptr(seq_lens), int(max_seq_len), float(scale), _ptr(out), code,
+        int(pages_per_split), _stream_ptr(stream))
+    _check(rc, "pa_append_decode_attention_noalloc")
     return out
 
 

@@ -669,6 +669,53 @@ PA_API int pa_append_decode_attention_worklist(
                      workspace_bytes, stream, nullptr, nullptr, work, num_work);
 }
 
+// Split partials of pa_append_decode_attention_noalloc: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): each device's address is looked up once, with that device
+// current, and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace pa_host {
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's scratch array, or NULL.
+void* current_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_rc[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_rc[dev] == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+}  // namespace pa_host
+
+PA_API int pa_append_decode_attention_noalloc(const pa_shape* shape, int32_t batch,
+                                              const void* q, const void* k_new,
+                                              const void* v_new, void* k_pool, void* v_pool,
+                                              const int32_t* block_tables,
+                                              const int32_t* seq_lens, int32_t max_seq_len,
+                                              float scale, void* out, int32_t out_dtype,
+                                              int32_t pages_per_split, void* stream) {
+  if (batch > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
+  int rc = check_decode_sizes(shape, batch, max_seq_len);
+  if (rc != PA_OK) return rc;
+  if (batch == 0) return PA_OK;
+  int ps = 0, ns = 0;
+  rc = plan_split(shape, batch, max_seq_len, pages_per_split, &ps, &ns);
+  if (rc != PA_OK) return rc;
+  if (workspace_for(batch, ns) > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = current_scratch();
+  if (!ws) return PA_ERR_DEVICE;
+  return decode_impl(shape, batch, q, k_new, v_new, nullptr, k_pool, v_pool, block_tables,
+                     seq_lens, max_seq_len, scale, out, out_dtype, pages_per_split, ws,
+                     PA_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
+}
+
 PA_API int pa_validate_metadata(const pa_shape* shape, int32_t batch,
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 int32_t max_seq_len, void* stream, int64_t* bad_index) {

@@ -339,3 +339,29 @@ def test_c_client_is_built_and_rejects_bad_input(tmp_path):
         pb.build_client()
     assert subprocess.run([client], capture_output=True).returncode == 2
     assert subprocess.run([client, str(tmp_path)], capture_output=True).returncode == 2
+
+
+def test_noalloc_entry_point_refuses_on_the_host(lib):
+    """The allocation-free fused step checks its arguments and the size of the
+    plan's partials against its fixed scratch before touching any device."""
+    f = lib.pa_append_decode_attention_noalloc
+    P = FAKE
+
+    def call(s, batch, max_seq_len, ps, k_new=P, out_dtype=0, scale=0.125):
+        return f(ctypes.byref(s) if s is not None else None, batch, P, k_new, P, P, P, P, P,
+                 max_seq_len, scale, P, out_dtype, ps, None)
+    assert call(shape(), 0, 37, 1) == 0                            # batch 0: nothing to do
+    assert call(None, 1, 37, 1) == -1                              # PA_ERR_NULL
+    assert call(shape(), 1, 37, 1, k_new=None) == -1
+    assert call(shape(num_q_heads=16), 1, 37, 1) == -2             # PA_ERR_SHAPE
+    assert call(shape(), 1, 5000, 1) == -6                         # PA_ERR_VALUE: beyond the table
+    assert call(shape(), 1, 37, 300) == -6                         # split larger than 256 pages
+    # partials larger than the scratch: 8192 sequences x 16 splits of 8 pages
+    need = ctypes.c_size_t()
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(shape()), 8192, 2048, 8,
+                                         ctypes.byref(need)) == 0
+    assert need.value > pa.NOALLOC_SCRATCH_BYTES
+    assert call(shape(), 8192, 2048, 8) == -4                      # PA_ERR_WORKSPACE
+    assert pa.NOALLOC_SCRATCH_BYTES == 32 << 20
+    text = open(os.path.join(pb.ROOT, "include", "pa_decode.h")).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
