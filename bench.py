@@ -27,7 +27,8 @@ peak).  The flush is outside every event pair.
 Then every other configuration (1: one 37-token sequence; 2: batch 8 of
 uniform lengths; 3: the 16-layer step of batch 64; 5: batch 512 of clipped
 Zipf lengths) is measured the same way, its fused step under each candidate
-launch (the default plan, the host-lengths plan, the work list), the fastest
+launch (the default plan, the host-lengths plan, the work list, the balanced
+launch over a host plan), the fastest
 reported, with every output compared against the oracle.  The oracle runs on
 one core and on a pool of worker processes forked before the GPU is
 initialised, on every configuration.  Prints one JSON line.
@@ -268,12 +269,23 @@ def measure_config(ci: int, args, stream, dev, flush, refs):
     if B > 1:
         wl, wps, _ = pa.decode_worklist(w0.seq_lens, npg, max_seq_len=msl)
         cands.append(("work list", wps, torch.from_numpy(wl).to(dev)))
+    for h in (8, 2, 1):
+        try:
+            plan = pa.balance_plan(w0.seq_lens, npg, max_seq_len=msl, heads_together=h,
+                                   device=dev)
+        except RuntimeError:
+            continue                       # this batch cannot be planned with such lanes
+        cands.append((f"balanced, {h} KV head{'s' if h > 1 else ''} per lane", 0, plan))
     need = max(pa.decode_workspace_bytes(B, msl, npg, 128, ps) for _, ps, _ in cands)
     workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def run(ps, work):
         for L in layers:
-            if work is None:
+            if isinstance(work, pa.BalancedPlan):
+                pa.decode_balanced(L["q"], L["kp"], L["vp"], L["bt"], L["lens"], msl, work,
+                                   k_new=L["kn"], v_new=L["vn"], scale=w0.scale, out=L["out"],
+                                   stream=stream)
+            elif work is None:
                 pa.append_decode_attention(L["q"], L["kn"], L["vn"], L["kp"], L["vp"], L["bt"],
                                            L["lens"], msl, scale=w0.scale, out=L["out"],
                                            pages_per_split=ps, workspace=workspace, stream=stream)

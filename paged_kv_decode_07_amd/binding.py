@@ -31,6 +31,8 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_validate_metadata", "pa_status_string", "pa_abi_version",
            "pa_decode_worklist", "pa_append_decode_attention_worklist",
            "pa_append_decode_attention_noalloc",
+           # include/pa_decode_balanced.h
+           "pa_balance_plan", "pa_decode_balanced",
            # include/pa_decode_q8.h
            "pa_append_kv_q8", "pa_append_kv_rope_q8", "pa_fill_kv_q8", "pa_decode_attention_q8",
            "pa_append_decode_attention_q8", "pa_append_decode_attention_rope_q8",
@@ -115,6 +117,11 @@ def load_library(path: str | None = None):
             getattr(lib, "pa_append_decode_attention_worklist" + sfx).argtypes = [
                 SP, I32, P, P, P, P, P, P, P, P, I32, ctypes.c_float, P, I32, I32, P, I32, P, SZ,
                 P]
+        I64_ = ctypes.c_int64
+        lib.pa_balance_plan.argtypes = [SP, I32, P, I32, I32, I32, P, I64_,
+                                        ctypes.POINTER(I64_), ctypes.POINTER(I32)]
+        lib.pa_decode_balanced.argtypes = [SP, I32, P, P, P, RP, P, P, P, I32, P, P, I32,
+                                           ctypes.c_float, P, I32, P, I64_, I32, P]
         lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
         lib.pa_decode_worklist.argtypes = [SP, I32, P, I32, I32, I32, I32, P, I32,
                                            ctypes.POINTER(I32), ctypes.POINTER(I32),
@@ -735,6 +742,89 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
         int(work.shape[0]), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_ptr(stream))
     _check(rc, fn)
+    return out
+
+
+class BalancedPlan:
+    """A plan of ``pa_balance_plan`` on the device: ``plan`` (int32 device tensor),
+    ``groups`` (work-groups to launch) and the host lengths it was built for."""
+
+    def __init__(self, plan, groups: int, seq_lens_host):
+        self.plan, self.groups, self.seq_lens_host = plan, int(groups), seq_lens_host
+
+    @property
+    def words(self) -> int:
+        return int(self.plan.numel())
+
+
+def balance_plan(seq_lens_host, num_pages: int, max_blocks: int = 128,
+                 max_seq_len: int | None = None, num_cus: int = 0, heads_together: int = 8,
+                 device="cuda", host_only: bool = False):
+    """Plan of the balanced launch for host lengths (``include/pa_decode_balanced.h``).
+
+    Returns a ``BalancedPlan`` with the plan copied to ``device`` (or, with
+    ``host_only``, the host int32 array and the work-group count)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    if max_seq_len is None:
+        max_seq_len = int(lens.max()) if lens.size else 0
+    shape = make_shape(num_pages, max_blocks)
+    lib = load_library()
+    words, groups = ctypes.c_int64(), ctypes.c_int32()
+    args = (ctypes.byref(shape), int(lens.size), lens.ctypes.data_as(ctypes.c_void_p),
+            int(max_seq_len), int(num_cus), int(heads_together))
+    _check(lib.pa_balance_plan(*args, None, 0, ctypes.byref(words), ctypes.byref(groups)),
+           "pa_balance_plan")
+    host = np.zeros(words.value, dtype=np.int32)
+    _check(lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
+                               ctypes.byref(words), ctypes.byref(groups)), "pa_balance_plan")
+    if host_only:
+        return host, groups.value
+    return BalancedPlan(torch.from_numpy(host).to(device), groups.value, lens)
+
+
+def decode_balanced(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int, plan,
+                    k_new=None, v_new=None, kv_scales=None, scale: float = 0.125, out=None,
+                    out_dtype=torch.float32, rope_cos=None, rope_sin=None, stream=None):
+    """Decode step over a ``BalancedPlan`` (optionally with the fused append and RoPE).
+
+    BF16 pools as ``decode_attention``; with ``kv_scales`` the pools are INT8
+    (int8) or INT4 (uint8) code pools.  Returns ``out``; no workspace."""
+    B = int(seq_lens.shape[0])
+    _bits16(q, "q", (HQ, D))
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _bits16(k_new, "k_new", (HKV, D)); _bits16(v_new, "v_new", (HKV, D))
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    _same_batch(B, q=q, k_new=k_new, v_new=v_new, block_tables=block_tables)
+    if not isinstance(plan, BalancedPlan):
+        raise TypeError("plan must come from balance_plan")
+    _i32(plan.plan, "plan")
+    if plan.seq_lens_host is not None and len(plan.seq_lens_host) != B:
+        raise ValueError("the plan was built for another batch")
+    fmt = 0
+    if kv_scales is not None:
+        fmt = 2 if k_pool.dtype == torch.uint8 else 1
+        num_pages = _q8_pools(k_pool, v_pool, kv_scales, 4 if fmt == 2 else 8)
+    else:
+        _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+        _same_pools(k_pool, v_pool)
+        num_pages = int(k_pool.shape[0])
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("give both rope_cos and rope_sin, or neither")
+    rope = _rope(rope_cos, rope_sin) if rope_cos is not None else None
+    code = _out_code(out_dtype)
+    out = _out(out, B, out_dtype, q.device)
+    shape = make_shape(num_pages, int(block_tables.shape[1]))
+    rc = load_library().pa_decode_balanced(
+        ctypes.byref(shape), B, _ptr(q), _ptr(k_new) if k_new is not None else None,
+        _ptr(v_new) if v_new is not None else None,
+        ctypes.byref(rope) if rope is not None else None, _ptr(k_pool), _ptr(v_pool),
+        _ptr(kv_scales) if kv_scales is not None else None, fmt, _ptr(block_tables),
+        _ptr(seq_lens), int(max_seq_len), float(scale), _ptr(out), code, _ptr(plan.plan),
+        plan.words, plan.groups, _stream_ptr(stream))
+    _check(rc, "pa_decode_balanced")
     return out
 
 

@@ -1,0 +1,263 @@
+"""The balanced launch (pa_decode_balanced over a pa_balance_plan) against the oracle.
+
+One wavefront per (sequence, KV head) stream, streams packed into
+work-groups on the host, pieces of a stream merged in LDS.  Every output
+element is compared with the float64 oracle (max-abs 2e-3, relative 1e-2),
+pools bit-exact; BF16, INT8 and INT4 pages; attention only and with the fused
+append (and RoPE); sharp scores; the full-size workloads; plans for fewer
+compute units (several rounds of work-groups); and the failure rules: a
+device length other than the plan's, or a page id outside the pool, gives that
+sequence NaN rows (the first also no append), and nothing else changes.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import DeviceBatch, assert_close, dev16, dev32, gpu_append, host16
+from oracle import kvquant
+
+pytestmark = pytest.mark.gpu
+
+EDGE = [1, 2, 15, 16, 17, 32, 33, 100, 255, 256, 257, 1000, 2047, 2048, 0, 37]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from paged_kv_decode_07_amd import binding
+    binding.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _pa():
+    from paged_kv_decode_07_amd import binding as pa
+    return pa
+
+
+def _run(db, plan, append=True, out_dtype=torch.float32, rope=None, max_seq_len=None):
+    pa = _pa()
+    kw = {}
+    if rope is not None:
+        kw = dict(rope_cos=torch.from_numpy(rope[0]).cuda(), rope_sin=torch.from_numpy(rope[1]).cuda())
+    out = pa.decode_balanced(db.q, db.k_pool, db.v_pool, db.bt, db.lens,
+                             db.h.max_seq_len if max_seq_len is None else max_seq_len, plan,
+                             k_new=db.k_new if append else None, v_new=db.v_new if append else None,
+                             scale=db.h.scale, out_dtype=out_dtype, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def _bf16_case(w, num_cus=0, out_dtype=torch.float32, h=8):
+    pa = _pa()
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    plan = pa.balance_plan(w.seq_lens, w.num_pages, max_seq_len=w.max_seq_len, num_cus=num_cus,
+                           heads_together=h)
+    # fused append + attention
+    f = DeviceBatch(w)
+    got = _run(f, plan, out_dtype=out_dtype)
+    assert np.array_equal(host16(f.k_pool), k_ref) and np.array_equal(host16(f.v_pool), v_ref)
+    assert_close(got, ref, bf16_out=out_dtype == torch.bfloat16, where=f"balanced {w.name}")
+    # attention only, after the separate append: the same bits
+    a = DeviceBatch(w)
+    gpu_append(a)
+    only = _run(a, plan, append=False, out_dtype=out_dtype)
+    assert np.array_equal(only, got), "attention-only differs from the fused step"
+    return got, ref
+
+
+@pytest.mark.parametrize("h", [1, 2, 8])
+@pytest.mark.parametrize("num_cus", [0, 80, 7])
+def test_balanced_bf16_edge_lengths(num_cus, h):
+    w = W.make_batch(EDGE, sum(W.pages_for(L) for L in EDGE) + 9, seed=8101, append=True)
+    got, _ = _bf16_case(w, num_cus, h=h)
+    assert np.all(got[EDGE.index(0)] == 0.0)
+
+
+def test_balanced_bf16_output_and_repeatable():
+    w = W.make_batch(EDGE, sum(W.pages_for(L) for L in EDGE) + 9, seed=8102, append=True)
+    got, _ = _bf16_case(w, out_dtype=torch.bfloat16)
+    again, _ = _bf16_case(w, out_dtype=torch.bfloat16)
+    assert np.array_equal(got, again)
+
+
+@pytest.mark.parametrize("h", [1, 8])
+@pytest.mark.parametrize("mode", W.SHARP_MODES)
+def test_balanced_bf16_sharp_scores(mode, h):
+    lens = [37, 100, 255, 256, 1000, 2047, 2048, 17, 1, 0]
+    w = W.make_sharp_batch(lens, sum(W.pages_for(L) for L in lens) + 11, 8200, mode, append=True)
+    for cus in (0, 7):
+        _bf16_case(w, cus, h=h)
+
+
+def test_balanced_many_single_token_sequences():
+    """4,000 one-token sequences: the planner needs many work-groups."""
+    lens = [1] * 4000
+    w = W.make_batch(lens, 4100, seed=8103, append=True)
+    got, _ = _bf16_case(w)
+    for b in range(0, 4000, 397):
+        vnew = oracle.bf16_bits_to_f64(w.v_new[b])
+        for h in range(0, 32, 7):
+            assert np.array_equal(got[b, h], vnew[h // 4])
+
+
+@pytest.mark.parametrize("h", [1, 8])
+@pytest.mark.parametrize("wi", [1, 2, 4, 5])
+def test_balanced_full_workloads(wi, h):
+    print(f"balanced: workload {wi}, heads together {h}", flush=True)
+    w = W.make_workload(wi, append=True)
+    _bf16_case(w, h=h)
+
+
+@pytest.mark.parametrize("h", [1, 2, 8])
+def test_balanced_16_layers(h):
+    for layer in range(0, W.NUM_LAYERS_W3, 1 if h == 1 else 5):
+        print(f"balanced: 16-layer workload, layer {layer}, heads together {h}", flush=True)
+        _bf16_case(W.make_workload(3, layer=layer, append=True), h=h)
+
+
+def test_balanced_rope_matches_oracle():
+    pa = _pa()
+    w = W.make_batch(EDGE, sum(W.pages_for(L) for L in EDGE) + 9, seed=8104, append=True)
+    cos, sin = W.rope_table()
+    plan = pa.balance_plan(w.seq_lens, w.num_pages)
+    f = DeviceBatch(w)
+    got = _run(f, plan, rope=(cos, sin))
+    q_rot, k_rot = oracle.rope.rope_new_token(w.q, w.k_new, w.seq_lens, cos, sin)
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, k_rot, w.v_new, w.block_tables,
+                                    w.seq_lens)
+    assert np.array_equal(host16(f.k_pool), k_ref) and np.array_equal(host16(f.v_pool), v_ref)
+    ref = oracle.decode_attention(q_rot, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got, ref, where="balanced rope")
+
+
+def test_balanced_wrong_length_and_bad_page_give_nan_rows_only():
+    pa = _pa()
+    lens = [40, 300, 17, 129, 2048, 5]
+    w = W.make_batch(lens, sum(W.pages_for(L) for L in lens) + 5, seed=8105, append=True)
+    plan = pa.balance_plan(w.seq_lens, w.num_pages)
+    dev_lens = w.seq_lens.copy()
+    dev_lens[1] = 299                                  # not the plan's length
+    bt = w.block_tables.copy()
+    bt[3, 2] = w.num_pages + 7                         # a used entry outside the pool
+    f = DeviceBatch(w)
+    f.lens, f.bt = dev32(dev_lens), dev32(bt)
+    got = _run(f, plan)
+    for b in (1, 3):
+        assert np.all(np.isnan(got[b])), b
+    # sequence 1 (length not the plan's) appends nothing; sequence 3 appends
+    # into its valid last page, as the separate append does
+    app = [0, 2, 3, 4, 5]
+    k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new[app], w.v_new[app],
+                                    w.block_tables[app], w.seq_lens[app])
+    assert np.array_equal(host16(f.k_pool), k_ref) and np.array_equal(host16(f.v_pool), v_ref)
+    keep = [0, 2, 4, 5]
+    ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
+    assert_close(got[keep], ref[keep], where="balanced others")
+
+
+# ---------------------------------------------------------------------------
+# INT8 and INT4 pages
+# ---------------------------------------------------------------------------
+def _dev_q(w):
+    return tuple(torch.from_numpy(np.ascontiguousarray(x)).cuda()
+                 for x in (w.k_codes, w.v_codes, w.kv_scales))
+
+
+@pytest.mark.parametrize("h", [1, 8])
+@pytest.mark.parametrize("nbits", [8, 4])
+@pytest.mark.parametrize("num_cus", [0, 7])
+def test_balanced_quantised_pages(nbits, num_cus, h):
+    pa = _pa()
+    w = W.make_q8_batch(EDGE, sum(W.pages_for(L) for L in EDGE) + 9, 8300 + nbits, append=True,
+                        nbits=nbits)
+    post = kvquant.append_kv_q8(w.k_codes, w.v_codes, w.kv_scales, w.k_new, w.v_new,
+                                w.block_tables, w.seq_lens, nbits=nbits)
+    ref = kvquant.decode_attention_q8(w.q, *post, w.block_tables, w.seq_lens, w.scale,
+                                      nbits=nbits)
+    plan = pa.balance_plan(w.seq_lens, w.num_pages, num_cus=num_cus, heads_together=h)
+    q, kn, vn = dev16(w.q), dev16(w.k_new), dev16(w.v_new)
+    bt, lens = dev32(w.block_tables), dev32(w.seq_lens)
+    f = _dev_q(w)
+    out = pa.decode_balanced(q, f[0], f[1], bt, lens, w.max_seq_len, plan, k_new=kn, v_new=vn,
+                             kv_scales=f[2], scale=w.scale)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in f]
+    assert np.array_equal(got[0], post[0]) and np.array_equal(got[1], post[1])
+    assert np.array_equal(got[2].view(np.uint32), post[2].view(np.uint32))
+    fused = out.cpu().numpy().astype(np.float64)
+    assert_close(fused, ref, where=f"balanced int{nbits}")
+    # attention only over the appended pools
+    a = _dev_q(w)
+    pa.append_kv_q8(kn, vn, *a, bt, lens, nbits=nbits)
+    only = pa.decode_balanced(q, a[0], a[1], bt, lens, w.max_seq_len, plan, kv_scales=a[2],
+                              scale=w.scale, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_close(only.float().cpu().numpy().astype(np.float64), ref, bf16_out=True,
+                 where=f"balanced int{nbits} bf16 out")
+
+
+@pytest.mark.parametrize("h", [1, 8])
+@pytest.mark.parametrize("nbits", [8, 4])
+@pytest.mark.parametrize("mode", ["ramp_up", "tail_max", "scale2"])
+def test_balanced_quantised_sharp_and_rope(nbits, mode, h):
+    """Sharp BF16 rows quantised on the GPU, then the fused step with RoPE."""
+    pa = _pa()
+    lens = [37, 100, 255, 1000, 2048, 17, 1, 0]
+    w = W.make_sharp_batch(lens, sum(W.pages_for(L) for L in lens) + 11, 8400, mode, append=True)
+    npg = w.num_pages
+    width, dt = (64, np.int8) if nbits == 8 else (32, np.uint8)
+    kc = np.zeros((npg, 8, 16, width), dt)
+    vc = np.zeros((npg, 8, 16, width), dt)
+    sc = np.full((npg, 8, 2, 16), np.nan, np.float32)
+    d = [torch.from_numpy(x.copy()).cuda() for x in (kc, vc, sc)]
+    for b, L in enumerate(w.seq_lens):
+        if L > 1:
+            kr = W.logical_rows(w.k_pool, w.block_tables[b], int(L) - 1)
+            vr = W.logical_rows(w.v_pool, w.block_tables[b], int(L) - 1)
+            pa.fill_kv_q8(dev16(kr), dev16(vr), dev32(w.block_tables[b]), 0, *d, nbits=nbits)
+            kc, vc, sc = kvquant.fill_kv_q8(kc, vc, sc, kr, vr, w.block_tables[b], 0, nbits=nbits)
+    cos, sin = W.rope_table()
+    q_rot, k_rot = oracle.rope.rope_new_token(w.q, w.k_new, w.seq_lens, cos, sin)
+    post = kvquant.append_kv_q8(kc, vc, sc, k_rot, w.v_new, w.block_tables, w.seq_lens,
+                                nbits=nbits)
+    ref = kvquant.decode_attention_q8(q_rot, *post, w.block_tables, w.seq_lens, w.scale,
+                                      nbits=nbits)
+    plan = pa.balance_plan(w.seq_lens, npg, heads_together=h)
+    out = pa.decode_balanced(dev16(w.q), d[0], d[1], dev32(w.block_tables), dev32(w.seq_lens),
+                             w.max_seq_len, plan, k_new=dev16(w.k_new), v_new=dev16(w.v_new),
+                             kv_scales=d[2], scale=w.scale, rope_cos=torch.from_numpy(cos).cuda(),
+                             rope_sin=torch.from_numpy(sin).cuda())
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in d]
+    assert np.array_equal(got[0], post[0]) and np.array_equal(got[1], post[1])
+    assert np.array_equal(got[2].view(np.uint32), post[2].view(np.uint32))
+    assert_close(out.cpu().numpy().astype(np.float64), ref,
+                 where=f"balanced int{nbits} {mode} rope")
+
+
+@pytest.mark.parametrize("nbits", [8, 4])
+def test_balanced_quantised_full_batch512_zipf(nbits):
+    pa = _pa()
+    lens = W.workload_seq_lens(5)
+    w = W.make_q8_batch(lens, sum(W.pages_for(L) for L in lens) + 50, 8500 + nbits, append=True,
+                        nbits=nbits)
+    post = kvquant.append_kv_q8(w.k_codes, w.v_codes, w.kv_scales, w.k_new, w.v_new,
+                                w.block_tables, w.seq_lens, nbits=nbits)
+    ref = kvquant.decode_attention_q8(w.q, *post, w.block_tables, w.seq_lens, w.scale,
+                                      nbits=nbits)
+    plan = pa.balance_plan(w.seq_lens, w.num_pages)
+    f = _dev_q(w)
+    out = pa.decode_balanced(dev16(w.q), f[0], f[1], dev32(w.block_tables), dev32(w.seq_lens),
+                             w.max_seq_len, plan, k_new=dev16(w.k_new), v_new=dev16(w.v_new),
+                             kv_scales=f[2], scale=w.scale)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), ref, where=f"balanced int{nbits} zipf")
