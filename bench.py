@@ -412,12 +412,26 @@ def run_sweep(args) -> int:
                               pa.append_decode_attention_worklist(
                                   q, kn, vn, kpool, vpool, bt, lens, msl, wd, wps, scale=w.scale,
                                   out=out, workspace=workspace, stream=stream, kv_scales=scales)))
+            for h in (8, 1):
+                try:
+                    plan = pa.balance_plan(w.seq_lens, npg, max_seq_len=msl, heads_together=h,
+                                           device=dev)
+                except RuntimeError:
+                    continue
+                cases.append((f"balanced, {h} KV head{'s' if h > 1 else ''} per lane", 0,
+                              plan.groups,
+                              lambda plan=plan, kpool=kpool, vpool=vpool, scales=scales:
+                              pa.decode_balanced(q, kpool, vpool, bt, lens, msl, plan,
+                                                 k_new=kn, v_new=vn, kv_scales=scales,
+                                                 scale=w.scale, out=out, stream=stream)))
             for launch, cps, units, fn in cases:
                 t = timed(fn, args.steps)
+                unit_key = ("items" if launch == "work list" else
+                            "work_groups" if launch.startswith("balanced") else "splits")
                 print(json.dumps({
                     "workload": wi, "desc": W.WORKLOADS[wi], "pages": fmt,
                     "launch": launch, "pages_per_split": int(cps),
-                    ("items" if launch == "work list" else "splits"): int(units),
+                    unit_key: int(units),
                     "step_us": round(t * 1e6, 2), "kv_bytes": int(kv),
                     "kv_gbps": round(kv / t / 1e9, 1),
                     "seq_per_s_per_layer": round(int(np.count_nonzero(w.seq_lens)) / t, 1)}),
@@ -513,6 +527,11 @@ def main() -> int:
     ap.add_argument("--only-config", type=int, default=0,
                     help="measure this one configuration's candidate launches only (no "
                          "headline passes, no oracle): for profiling runs")
+    ap.add_argument("--placement-probe", action="store_true",
+                    help="instead of the bench line: the decode kernel on batch 256 x 2048 with "
+                         "the same logical cache under several page placements (identity, "
+                         "per-sequence regions, random chunks of 4..64 pages, one random "
+                         "permutation), interleaved, cold caches; one JSON line per placement")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused step of every workload "
                          "(1-5), BF16 and INT8 pages, grid launch with the library plan and "
@@ -534,6 +553,8 @@ def main() -> int:
 
     if args.sweep:
         return run_sweep(args)
+    if args.placement_probe:
+        return run_placement_probe(args)
     if args.only_config:
         if args.only_config not in CONFIGS:
             print("--only-config takes 1..5", file=sys.stderr)
@@ -904,6 +925,87 @@ def main() -> int:
     return 0
 
 
+def placement_tables(B: int, per: int, scheme: str, seed: int = 77):
+    """Block tables [B][per] over a pool of exactly B * per pages for a placement scheme:
+    ``identity`` (sequence b on pages b*per ..), ``region`` (the same pages, shuffled within
+    the sequence), ``chunksN`` (random N-page chunks of the pool, pages shuffled within each
+    chunk), ``random`` (one random permutation of the pool)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    n = B * per
+    if scheme == "identity":
+        flat = np.arange(n)
+    elif scheme == "region":
+        flat = np.concatenate([b * per + rng.permutation(per) for b in range(B)])
+    elif scheme.startswith("chunks"):
+        c = int(scheme[6:])
+        chunks = rng.permutation(n // c)
+        flat = np.concatenate([k * c + rng.permutation(c) for k in chunks])
+    elif scheme == "random":
+        flat = rng.permutation(n)
+    else:
+        raise ValueError(scheme)
+    return flat.reshape(B, per).astype(np.int32)
+
+
+def run_placement_probe(args) -> int:
+    """The decode kernel over the 256 x 2048 cache under several page placements."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from paged_kv_decode_07_amd import accounting as A
+    from paged_kv_decode_07_amd import binding as pa
+
+    w = W.make_workload(4, append=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(2**28, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int32, device=dev)
+    B, per = w.batch, W.MAX_BLOCKS
+    kp = torch.from_numpy(w.k_pool.view(np.int16)).to(dev)
+    vp = torch.from_numpy(w.v_pool.view(np.int16)).to(dev)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    old = torch.from_numpy(w.block_tables[:, :per].reshape(-1).astype(np.int64)).to(dev)
+    schemes = ["identity", "region", "chunks4", "chunks16", "chunks32", "chunks64", "random"]
+    cases = {}
+    for sch in schemes:
+        bt = placement_tables(B, per, sch)
+        new = torch.from_numpy(bt.reshape(-1).astype(np.int64)).to(dev)
+        k2, v2 = torch.empty_like(kp), torch.empty_like(vp)
+        k2[new] = kp[old]                     # the same logical cache at the new places
+        v2[new] = vp[old]
+        cases[sch] = (k2, v2, torch.from_numpy(bt).to(dev),
+                      torch.empty((B, 32, 64), dtype=torch.float32, device=dev))
+    del kp, vp
+    ref = None
+    times = {s: [] for s in schemes}
+    for it in range(args.warmup + args.steps):
+        for sch in schemes:                    # interleaved: drift hits every placement alike
+            k2, v2, bt, out = cases[sch]
+            torch.amax(flush_buf, dim=None, out=flush_out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.decode_attention(q, k2, v2, bt, lens, w.max_seq_len, scale=w.scale, out=out,
+                                stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                times[sch].append(e0.elapsed_time(e1) * 1e3)
+    kv = A.step_bytes(w.seq_lens)["kv"]
+    for sch in schemes:
+        out = cases[sch][3].cpu().numpy()
+        ref = out if ref is None else ref
+        t = float(np.median(times[sch]))
+        print(json.dumps({"placement": sch, "decode_us_median": round(t, 2),
+                          "decode_us_min": round(float(np.min(times[sch])), 2),
+                          "kv_gbps": round(kv / t / 1e3, 1), "steps": args.steps,
+                          "same_output_as_identity": bool(np.array_equal(out, ref))}), flush=True)
+    return 0
+
+
 def run_one_config(args) -> int:
     """Only configuration ``--only-config``'s candidate launches (no oracle, no
     headline passes): one JSON line; for profiling runs."""
@@ -921,6 +1023,12 @@ def run_one_config(args) -> int:
     def flush():
         if not args.no_flush:
             torch.amax(flush_buf, dim=None, out=flush_out)
+    if args.calibration_copy:
+        # one 256 MiB device copy: the known-size reference for byte counters
+        src = torch.ones(2**26, dtype=torch.int32, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     line, _ = measure_config(ci, args, stream, dev, flush, None)
     print(json.dumps({"config": ci, **line}), flush=True)
     return 0

@@ -68,3 +68,18 @@ def test_oracle_rates_and_parity_on_the_host():
     bumped[0][0, 3, 5] += 1e-3
     err, rel = bench.parity(bumped, refs)
     assert abs(err - 1e-3) < 1e-12 and rel > 0
+
+
+def test_placement_probe_tables_hold_every_page_once():
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import bench
+    for scheme in ("identity", "region", "chunks4", "chunks16", "chunks32", "chunks64", "random"):
+        t = bench.placement_tables(16, 128, scheme)
+        assert t.shape == (16, 128)
+        assert np.array_equal(np.sort(t.reshape(-1)), np.arange(16 * 128)), scheme
+    assert np.array_equal(bench.placement_tables(4, 128, "identity")[2], np.arange(256, 384))
+    reg = bench.placement_tables(4, 128, "region")
+    assert all(set(reg[b]) == set(range(128 * b, 128 * b + 128)) for b in range(4))
+    ch = bench.placement_tables(4, 128, "chunks16").reshape(-1, 16)
+    assert all(len(set(c // 16)) == 1 for c in ch)     # each 16 logical pages: one chunk
