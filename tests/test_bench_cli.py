@@ -83,3 +83,55 @@ def test_placement_probe_tables_hold_every_page_once():
     assert all(set(reg[b]) == set(range(128 * b, 128 * b + 128)) for b in range(4))
     ch = bench.placement_tables(4, 128, "chunks16").reshape(-1, 16)
     assert all(len(set(c // 16)) == 1 for c in ch)     # each 16 logical pages: one chunk
+
+
+def test_profile_summaries_split_launches_and_calibrate(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench_profiles as P
+
+    def row(i, name, counter="FETCH_SIZE", value=1.0):
+        return {"Dispatch_Id": str(i), "Kernel_Name": name, "Counter_Name": counter,
+                "Counter_Value": str(value)}
+    dec, mer = "void pa::decode_kernel<0, false, true, false, 1>(pa::DecodeArgs)", \
+        "void pa::merge_kernel<false>(pa::MergeArgs)"
+    bal = "void pa::decode_balanced_kernel<0, false, true, false>(pa::BalancedArgs)"
+    # two launches, 2 steps of 2 layers each; the first has a merge after every decode
+    rows = [row(1, "torch fill")]
+    i = 2
+    for _ in range(4):
+        rows += [row(i, dec), row(i + 1, mer)]
+        i += 2
+    rows += [row(i + k, bal) for k in range(4)]
+    s = P.split_launches(rows, ["grid", "balanced"], 2)
+    assert [len(s["grid"]["decode"]), len(s["grid"]["merge"])] == [4, 4]
+    assert [len(s["balanced"]["decode"]), len(s["balanced"]["merge"])] == [4, 0]
+    try:
+        P.split_launches(rows, ["a", "b", "c"], 1)
+    except SystemExit:
+        pass
+    else:
+        raise AssertionError("8 decode launches over 3 candidates must be refused")
+    # calibration: the copy's FETCH_SIZE reads half its bytes, WRITE_SIZE all
+    copy = "__amd_rocclr_copyBuffer"
+    f = [row(7, copy, "FETCH_SIZE", 131072.0), row(8, copy, "FETCH_SIZE", 2.0)]
+    w = [row(7, copy, "WRITE_SIZE", 262144.0), row(8, copy, "WRITE_SIZE", 4.0)]
+    cf, cw, ff, wf = P.calibration(f, w)
+    assert (cf, cw) == (131072.0, 262144.0) and abs(ff - 2.0) < 1e-12 and abs(wf - 1.0) < 1e-12
+
+
+def test_profile_summary_refuses_a_run_of_other_sources(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench_profiles as P
+    line = tmp_path / "run.log"
+    line.write_text("[bench] noise\n" + json.dumps({"kernel_source_sha": "0" * 16,
+                                                   "int8_pages": {"kernel_source_sha": "1" * 16}})
+                    + "\n")
+    for d in ("t", "f", "w"):
+        (tmp_path / d).mkdir()
+    try:
+        P.main(["headline", "--line", str(line), "--trace", str(tmp_path / "t"),
+                "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w")])
+    except SystemExit as e:
+        assert "profile again" in str(e)
+    else:
+        raise AssertionError("a run of other kernel sources must be refused")
