@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
     va = slot0 + 1024 + 64 * (4 * G + jq) + 8 * jr;
     sa = slot0 + 2048 + 4 * (4 * G + (n & 3));
   } else if constexpr (Q4) {
-    ka = slot0 + 32 * n + 4 * G;
+    ka = slot0 + 32 * n + 8 * G;
     va = slot0 + 512 + 32 * (4 * G + jq) + 8 * jr;
     sa = slot0 + 1024 + 4 * (4 * G + (n & 3));
   } else {
@@ -345,13 +345,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
         rope_pairs8(lo, hi, cs, sn);
       }
       if constexpr (Q4) {
-        float sum = 0.f;
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) sum += bf16_lo(w[k]) + bf16_hi(w[k]);
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        pc.qbias = kNibbleBias4 * sum;
+        q4_relayout(lo, hi, lane);
+        float bias = q4_bias_part(lo, hi);
+        bias += __shfl_xor(bias, 16);
+        bias += __shfl_xor(bias, 32);
+        pc.qbias = bias;
         lo = interleave_halves8(lo);
         hi = interleave_halves8(hi);
       }
@@ -467,9 +465,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t] = st.acc[t][0] + st.acc[t][1];
     if constexpr (Q4) {
-      const float bias = kNibbleBias4 * of_head(head_sum(st.wsum));
+      const float ws = of_head(head_sum(st.wsum));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) o[t] -= bias;
+      for (int t = 0; t < 4; ++t) o[t] -= q4_value_bias(t) * ws;
     }
     float m_out = of_head(st.m), l_out = of_head(st.l);
     if (bad) {

@@ -183,7 +183,7 @@ struct PageQ8 {
   uint32_t ks, vs;    // K and V scales of this lane's token 4G + n % 4
 };
 struct PageQ4 {
-  uint32_t k0, k1;    // K codes of token n, dims 8G .. 8G+7 and 32+8G .. 32+8G+7
+  u32x2 k;            // K codes of token n, dims 16G .. 16G+7 and 16G+8 .. 16G+15
   u32x2 v;            // V codes: 4 tokens x dims 4n .. 4n+3 (transposed read)
   uint32_t ks, vs;    // K and V scales of this lane's token 4G + n % 4
 };
@@ -227,23 +227,25 @@ __device__ __forceinline__ void lds_page_ready(PageQ8& r) {
                : "+v"(r.k0), "+v"(r.k1), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ks), "+v"(r.vs)::"memory");
 }
 
-// kaddr: K codes of (token n, dims 8G..); vaddr: V chunk of this lane; saddr:
-// the K scale of token 4G + n % 4 (its V scale 64 bytes on).
+// kaddr: K codes of (token n, dims 16G..); vaddr: V chunk of this lane;
+// saddr: the K scale of token 4G + n % 4 (its V scale 64 bytes on); OFF: the
+// slot's offset from these addresses, as the reads' immediate offset.
+template <uint32_t OFF = 0>
 __device__ __forceinline__ void lds_page_issue(PageQ4& r, uint32_t kaddr, uint32_t vaddr,
                                          uint32_t saddr) {
+  static_assert(OFF + 64 <= 65535, "LDS read offsets are 16 bits");
   asm volatile(
-      "ds_read_b32 %0, %5\n\t"
-      "ds_read_b32 %1, %5 offset:16\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b32 %3, %7\n\t"
-      "ds_read_b32 %4, %7 offset:64"
-      : "=&v"(r.k0), "=&v"(r.k1), "=&v"(r.v), "=&v"(r.ks), "=&v"(r.vs)
-      : "v"(kaddr), "v"(vaddr), "v"(saddr)
+      "ds_read_b64 %0, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%7\n\t"
+      "ds_read_b32 %2, %6 offset:%7\n\t"
+      "ds_read_b32 %3, %6 offset:%8"
+      : "=&v"(r.k), "=&v"(r.v), "=&v"(r.ks), "=&v"(r.vs)
+      : "v"(kaddr), "v"(vaddr), "v"(saddr), "i"(OFF), "i"(OFF + 64)
       : "memory");
 }
 __device__ __forceinline__ void lds_page_ready(PageQ4& r) {
   asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(r.k0), "+v"(r.k1), "+v"(r.v), "+v"(r.ks), "+v"(r.vs)::"memory");
+               : "+v"(r.k), "+v"(r.v), "+v"(r.ks), "+v"(r.vs)::"memory");
 }
 
 // 4 INT8 codes (bytes b0..b3 of w) -> BF16 pairs (b0, b2) and (b1, b3): the
@@ -286,7 +288,7 @@ __device__ __forceinline__ f32x4_t page_scores(const Page& r, bf16x8_t qlo, bf16
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(r.k1), qhi, s, 0, 0, 0);
   } else if constexpr (FMT == kFmtINT4) {
     bf16x8_t k0, k1;
-    nibbles_to_bf16x8x2(r.k0, r.k1, pc.nib, k0, k1);
+    nibbles_to_bf16x8x2(r.k, pc.nib, k0, k1);
     const f32x4_t nb = {-pc.qbias, -pc.qbias, -pc.qbias, -pc.qbias};
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qlo, nb, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qhi, s, 0, 0, 0);
@@ -352,9 +354,15 @@ __device__ __forceinline__ void raise_max(LaneState& st, float mx, int G) {
 // weight and remainder into one word; a quad broadcast gives every lane of
 // the quad the four tokens' words, and v_perm keeps the halves of its row.
 // sel: 0x05040100 (q even, low halves) or 0x07060302 (q odd, high halves).
-__device__ __forceinline__ bf16x4_t weight_operand(float w, uint32_t sel) {
+// WSUM (INT4 pages): the two parts' sum, the weight the products actually
+// carry, is added to `wsum` (the code offsets are taken out with it, so that
+// the rounding of the remainder does not leave a multiple of the offset).
+template <bool WSUM = false>
+__device__ __forceinline__ bf16x4_t weight_operand(float w, uint32_t sel, float* wsum = nullptr) {
   const uint32_t h = pack_bf16_rne(w, 0.f);
-  const uint32_t hr = pack_bf16_rne(w, w - bf16_lo(h));     // [BF16(w) | BF16(remainder)]
+  const float whi = bf16_lo(h);
+  const uint32_t hr = pack_bf16_rne(w, w - whi);             // [BF16(w) | BF16(remainder)]
+  if constexpr (WSUM) *wsum += whi + bf16_hi(hr);
   // quad_perm [c,c,c,c] (control 0x55 c): every lane of the quad gets lane c's word
   const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hr, 0x00, 0xF, 0xF, false);
   const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hr, 0x55, 0xF, 0xF, false);
@@ -373,12 +381,12 @@ template <int FMT, typename Page>
 __device__ __forceinline__ void page_v_operands(const Page& r, const PageConsts& pc, u32x2* bv) {
   if constexpr (FMT == kFmtINT4) {
     // tile e: dim 4n + e of tokens 4G .. 4G+3 (nibble e of each 16-bit unit);
-    // dead slots hold finite values code + 24 and weight 0
+    // dead slots hold finite widened codes and weight 0
     uint32_t x[4], y[4];
-    nibble_pairs2<0>(r.v.x, r.v.y, pc.nib, x[0], y[0]);
-    nibble_pairs2<1>(r.v.x, r.v.y, pc.nib, x[1], y[1]);
-    nibble_pairs2<2>(r.v.x, r.v.y, pc.nib, x[2], y[2]);
-    nibble_pairs2<3>(r.v.x, r.v.y, pc.nib, x[3], y[3]);
+    nibble_pairs2<0>(r.v, pc.nib, x[0], y[0]);
+    nibble_pairs2<1>(r.v, pc.nib, x[1], y[1]);
+    nibble_pairs2<2>(r.v, pc.nib, x[2], y[2]);
+    nibble_pairs2<3>(r.v, pc.nib, x[3], y[3]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) bv[e] = u32x2{x[e], y[e]};
   } else if constexpr (FMT == kFmtINT8) {
@@ -420,7 +428,6 @@ __device__ __forceinline__ float page_weight(LaneState& st, const Page& r, float
     if (MASK) w = dead ? 0.f : w;                            // scale bits of a dead slot
   }
   st.l += p;
-  if constexpr (FMT == kFmtINT4) st.wsum += w;
   return w;
 }
 
@@ -435,7 +442,7 @@ __device__ __forceinline__ void consume_page(LaneState& st, Page& r, bf16x8_t ql
   if (MASK) x = dead ? -INFINITY : x;
   raise_max(st, x, G);
   const float w = page_weight<FMT, MASK>(st, r, x, dead);
-  const bf16x4_t A = weight_operand(w, pc.sel);
+  const bf16x4_t A = weight_operand<FMT == kFmtINT4>(w, pc.sel, &st.wsum);
   if constexpr (FMT == kFmtBF16) {
     if (MASK) {
       // tokens 4G .. 4G+3 sit in (lo, hi) halves of the two words
@@ -466,8 +473,8 @@ __device__ __forceinline__ void consume_pages2(LaneState& st, const Page& ra, co
   const float wb = page_weight<FMT, false>(st, rb, xb, false);
   // one product over 32 tokens per tile: k = 8G .. 8G+7 of this lane are
   // tokens 4G .. 4G+3 of page a, then of page b, in both operands
-  const bf16x4_t Aa = weight_operand(wa, pc.sel);
-  const bf16x4_t Ab = weight_operand(wb, pc.sel);
+  const bf16x4_t Aa = weight_operand<FMT == kFmtINT4>(wa, pc.sel, &st.wsum);
+  const bf16x4_t Ab = weight_operand<FMT == kFmtINT4>(wb, pc.sel, &st.wsum);
   const u32x4 A8 = {__builtin_bit_cast(u32x2, Aa).x, __builtin_bit_cast(u32x2, Aa).y,
                     __builtin_bit_cast(u32x2, Ab).x, __builtin_bit_cast(u32x2, Ab).y};
   u32x2 va[4], vb[4];
@@ -650,7 +657,16 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
 
   // ent[] (loaded above) holds the window's entries; only those up to
   // `last` are ever picked
-  bool bad_page = false;
+  // a used entry of the split outside the pool (one vote over the window:
+  // entry j of the row's window sits in lane j % 64 of ent[j / 64])
+  int bad_page = 0;
+  {
+    bool mine = false;
+#pragma unroll
+    for (int c = 0; c < kMaxSplitPages / 64; ++c)
+      mine |= p0 + c * 64 + lane < p1 && (unsigned)ent[c] >= (unsigned)a.num_pages;
+    bad_page = __builtin_amdgcn_ballot_w64(mine) != 0;
+  }
   auto raw_page_id = [&](int i) -> int {
     const int j = i - p0;
     int id = __builtin_amdgcn_readlane(ent[0], j & 63);
@@ -661,9 +677,7 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   };
   auto page_id = [&](int i) -> int64_t {
     const int id = raw_page_id(i);
-    const bool ok = (unsigned)id < (unsigned)a.num_pages;
-    bad_page |= !ok;
-    return ok ? id : 0;
+    return (unsigned)id < (unsigned)a.num_pages ? id : 0;   // a bad entry reads page 0 (outputs NaN)
   };
 
   __shared__ __attribute__((aligned(16))) char ring[F::kRingDepth][kWaves * WPH][F::kSlot];
@@ -723,9 +737,9 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
     va = slot0 + 1024 + 64 * (4 * G + jq) + 8 * jr;
     sa = slot0 + 2048 + 4 * (4 * G + (n & 3));
   } else if constexpr (Q4) {
-    // K: token n, bytes 4G (dims 8G ..) and 16 + 4G; V: dims 16 jr .. 16 jr + 15
-    // of token 4G + jq, so that lane n receives dims 4n .. 4n+3 of 4 tokens
-    ka = slot0 + 32 * n + 4 * G;
+    // K: token n, bytes 8G .. 8G+7 (dims 16G .. 16G+15); V: dims 16 jr .. 16 jr
+    // + 15 of token 4G + jq, so that lane n receives dims 4n .. 4n+3 of 4 tokens
+    ka = slot0 + 32 * n + 8 * G;
     va = slot0 + 512 + 32 * (4 * G + jq) + 8 * jr;
     sa = slot0 + 1024 + 4 * (4 * G + (n & 3));
   } else {
@@ -783,19 +797,19 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
     if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
     consume_page<FMT, MASK>(st, cur, qlo, qhi, pc, lane, MASK ? tail_valid : kPage);
   };
-  // pages i and i+1, both before the last page, in one pass; the ring keeps
-  // depth - 2 pages in flight while they are used
-  auto step2 = [&](int i) {
-    const int slot_a = (i - q0) % F::kRingDepth;
-    const int slot_b = (i + 1 - q0) % F::kRingDepth;
+  // pages i and i+1, both before the last page, in one pass, from ring slots
+  // SA and SB (compile-time, so that the LDS reads take the slot offsets as
+  // immediates); the ring keeps depth - 2 pages in flight while they are used
+  auto step2 = [&](int i, auto slot_a, auto slot_b) {
+    constexpr int SA = decltype(slot_a)::value, SB = decltype(slot_b)::value;
     wait_page<F::kLoads, F::kRingDepth>(min(last - i - 1, F::kRingDepth - 2));   // page i+1 landed
     PageT pa_, pb_;
-    lds_read(pa_, slot_a * kRingSlotBytes);
-    lds_read(pb_, slot_b * kRingSlotBytes);
+    lds_page_issue<SA * kRingSlotBytes>(pa_, ka, va, sa);
+    lds_page_issue<SB * kRingSlotBytes>(pb_, ka, va, sa);
     lds_page_ready(pa_);
     lds_page_ready(pb_);
-    if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot_a);
-    if (i + 1 + F::kRingDepth <= last) fetch(i + 1 + F::kRingDepth, slot_b);
+    if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, SA);
+    if (i + 1 + F::kRingDepth <= last) fetch(i + 1 + F::kRingDepth, SB);
     consume_pages2<FMT>(st, pa_, pb_, qlo, qhi, pc, lane);
   };
 
@@ -818,14 +832,14 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
       rope_pairs8(lo, hi, a.rope_cos + row, a.rope_sin + row);
     }
     if constexpr (Q4) {
-      // the row's sum (all 64 dims: this lane's 16, then the 4 token groups)
-      float sum = 0.f;
-      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) sum += bf16_lo(w[k]) + bf16_hi(w[k]);
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      pc.qbias = kNibbleBias4 * sum;
+      // lane G takes dims 16G .. 16G+15 (one 64-bit read of the K codes);
+      // the offset of the widened codes over the row's 64 dims: this lane's
+      // 16, then the 4 token groups
+      q4_relayout(lo, hi, lane);
+      float bias = q4_bias_part(lo, hi);
+      bias += __shfl_xor(bias, 16);
+      bias += __shfl_xor(bias, 32);
+      pc.qbias = bias;
       lo = interleave_halves8(lo);
       hi = interleave_halves8(hi);
     }
@@ -855,8 +869,24 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   }
   if (has_pages) {
     int i = q0;
-    if constexpr (F::kPairs)
-      for (; i + 1 < last; i += 2) step2(i);
+    if constexpr (F::kPairs) {
+      // page i sits in slot (i - q0) % 3: the pairs cycle through slots
+      // (0, 1), (2, 0), (1, 2)
+      static_assert(F::kRingDepth == 3, "the pair loop is unrolled for a ring of three slots");
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      while (i + 1 < last) {
+        step2(i, S0{}, S1{});
+        i += 2;
+        if (i + 1 >= last) break;
+        step2(i, S2{}, S0{});
+        i += 2;
+        if (i + 1 >= last) break;
+        step2(i, S1{}, S2{});
+        i += 2;
+      }
+    }
     for (; i < last; ++i) step(i, std::false_type{});
     step(last, std::true_type{});
   }
@@ -949,10 +979,11 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = st.acc[t][0] + st.acc[t][1];
   if constexpr (Q4) {
-    // the values were code + 24: take 24 x the head's weight sum back out
-    const float bias = kNibbleBias4 * of_head(head_sum(st.wsum));
+    // the values were code + 136 (tile 0) or code + 24: take that times the
+    // head's weight sum back out
+    const float ws = of_head(head_sum(st.wsum));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] -= bias;
+    for (int t = 0; t < 4; ++t) o[t] -= q4_value_bias(t) * ws;
   }
   float m_out = of_head(st.m), l_out = of_head(st.l);
   if (bad_page) {

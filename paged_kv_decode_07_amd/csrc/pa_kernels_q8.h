@@ -82,47 +82,64 @@ __device__ __forceinline__ bf16x8_t codes_to_bf16x8(u32x2 c) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-// INT4 widening without a conversion: the BF16 word 0x4180 | (u << 3) is
-// exactly 16 + u for a nibble u, i.e. code + 24.  The products of such values
-// with BF16 operands are exact, and the bias is taken out afterwards (24 x
-// the sum of the other operand).  kNibbleBias4 is that offset.
-constexpr float kNibbleBias4 = 24.f;
-// The two constants of the widening, held in registers the compiler cannot
-// see through, so that mask-and-bias is one v_and_or_b32 (a VALU instruction
-// here takes one scalar operand and no literal besides it).
+// INT4 widening without a conversion.  A nibble u at bits 3..6 of a 16-bit
+// unit becomes the BF16 word 0x4180 | (u << 3), exactly 16 + u = code + 24;
+// the first nibble of the unit (bits 0..3) becomes 0x4300 | u, exactly
+// 128 + u = code + 136, which needs no shift.  The products of such values
+// with BF16 operands are exact, and the offsets are taken out afterwards
+// (each times the sum of the other operand over the dims it applies to).
+constexpr float kNibbleBias4 = 24.f;        // nibbles 1, 2, 3 of a 16-bit unit
+constexpr float kNibbleBias4First = 136.f;  // nibble 0
+// The constants of the widening, held in registers the compiler cannot see
+// through (an empty asm statement hides their values; the compiler itself
+// materialises them), so that mask-and-bias is one v_and_or_b32 (a VALU
+// instruction here takes one scalar operand and no literal besides it).
 struct NibbleConsts {
-  uint32_t mask;   // 0x00780078: bits 3..6 of each half
-  uint32_t bias;   // 0x41804180: BF16 16.0 in each half
+  uint32_t mask;    // 0x00780078: bits 3..6 of each half
+  uint32_t bias;    // 0x41804180: BF16 16.0 in each half
+  uint32_t mask0;   // 0x000F000F: bits 0..3 of each half
+  uint32_t bias0;   // 0x43004300: BF16 128.0 in each half
 };
 __device__ __forceinline__ NibbleConsts nibble_consts() {
-  NibbleConsts c;
-  asm volatile("s_mov_b32 %0, 0x00780078" : "=s"(c.mask));
-  asm volatile("v_mov_b32 %0, 0x41804180" : "=v"(c.bias));
+  NibbleConsts c{0x00780078u, 0x41804180u, 0x000f000fu, 0x43004300u};
+  asm volatile("" : "+s"(c.mask), "+v"(c.bias), "+s"(c.mask0), "+v"(c.bias0));
   return c;
 }
-// Nibble pair at bits 4E .. 4E+3 and 16+4E .. 16+4E+3 of w0 and of w1 -> a
-// BF16 pair for each (code + 24 each; the first in the low half).  One 64-bit
-// shift serves both words: the bits it carries across them fall outside the
-// mask.
-template <int E>
-__device__ __forceinline__ void nibble_pairs2(uint32_t w0, uint32_t w1, const NibbleConsts& k,
-                                              uint32_t& o0, uint32_t& o1) {
-  const uint64_t w = ((uint64_t)w1 << 32) | w0;
-  uint64_t f;
-  if constexpr (E == 0) f = w << 3;
-  else f = w >> (4 * E - 3);
-  o0 = ((uint32_t)f & k.mask) | k.bias;
-  o1 = ((uint32_t)(f >> 32) & k.mask) | k.bias;
+// A right shift of a register pair as one 64-bit value (the compiler makes
+// it a funnel shift and a shift; an instruction written in inline asm would
+// escape its hazard tracking, e.g. against the accumulators of a matrix
+// product still in flight).
+template <int S>
+__device__ __forceinline__ u32x2 shr64(u32x2 w) {
+  const uint64_t v = (((uint64_t)w.y << 32) | w.x) >> S;
+  return u32x2{(uint32_t)v, (uint32_t)(v >> 32)};
 }
-// Two words of 8 INT4 codes each (dims 0..7 of a row piece) -> 8 BF16 values
-// code + 24 per word, in the dim order 0 4 1 5 2 6 3 7.
-__device__ __forceinline__ void nibbles_to_bf16x8x2(uint32_t w0, uint32_t w1, const NibbleConsts& k,
+// Nibble pair E (bits 4E .. 4E+3 and 16+4E .. 16+4E+3) of w.x and of w.y ->
+// a BF16 pair for each (the first in the low half).  Nibble 0 is masked in
+// place; nibbles 1..3 take one 64-bit shift for both words (the bits it
+// carries from w.y into w.x fall outside the mask).
+template <int E>
+__device__ __forceinline__ void nibble_pairs2(u32x2 w, const NibbleConsts& k, uint32_t& o0,
+                                              uint32_t& o1) {
+  if constexpr (E == 0) {
+    o0 = (w.x & k.mask0) | k.bias0;
+    o1 = (w.y & k.mask0) | k.bias0;
+  } else {
+    const u32x2 f = shr64<4 * E - 3>(w);
+    o0 = (f.x & k.mask) | k.bias;
+    o1 = (f.y & k.mask) | k.bias;
+  }
+}
+// Two words of 8 INT4 codes each (16 consecutive dims of a row) -> 8 BF16
+// values per word in the dim order 0 4 1 5 2 6 3 7 (dims 0 and 4 of each
+// word code + 136, the others code + 24).
+__device__ __forceinline__ void nibbles_to_bf16x8x2(u32x2 w, const NibbleConsts& k,
                                                     bf16x8_t& b0, bf16x8_t& b1) {
   uint32_t a[4], b[4];
-  nibble_pairs2<0>(w0, w1, k, a[0], b[0]);
-  nibble_pairs2<1>(w0, w1, k, a[1], b[1]);
-  nibble_pairs2<2>(w0, w1, k, a[2], b[2]);
-  nibble_pairs2<3>(w0, w1, k, a[3], b[3]);
+  nibble_pairs2<0>(w, k, a[0], b[0]);
+  nibble_pairs2<1>(w, k, a[1], b[1]);
+  nibble_pairs2<2>(w, k, a[2], b[2]);
+  nibble_pairs2<3>(w, k, a[3], b[3]);
   b0 = __builtin_bit_cast(bf16x8_t, u32x4{a[0], a[1], a[2], a[3]});
   b1 = __builtin_bit_cast(bf16x8_t, u32x4{b[0], b[1], b[2], b[3]});
 }
@@ -133,6 +150,46 @@ __device__ __forceinline__ uint4 interleave_halves8(uint4 q) {
                     __builtin_amdgcn_perm(q.z, q.x, 0x07060302u),
                     __builtin_amdgcn_perm(q.w, q.y, 0x05040100u),
                     __builtin_amdgcn_perm(q.w, q.y, 0x07060302u));
+}
+
+// INT4 pages: lane 16 G + n of the score product holds dims 16G .. 16G+15 of
+// its query row (lo: 16G .., hi: 16G+8 ..), one 64-bit LDS read of the
+// token's codes.  From the standard layout (lo: dims 8G .., hi: 32+8G ..)
+// the lanes of column n exchange their parts: dims 16G.. are the lo (G < 2)
+// or hi (G >= 2) part of lane G' = 2G mod 4, dims 16G+8.. that of lane
+// G' + 1.  All 64 lanes must be active.
+__device__ __forceinline__ void q4_relayout(uint4& lo, uint4& hi, int lane) {
+  const int G = lane >> 4, n = lane & 15;
+  const int src0 = 16 * ((2 * G) & 3) + n, src1 = src0 + 16;
+  const bool upper = G >= 2;
+  const uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w}, h[4] = {hi.x, hi.y, hi.z, hi.w};
+  uint32_t o0[4], o1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t a0 = (uint32_t)__shfl((int)l[k], src0), b0 = (uint32_t)__shfl((int)h[k], src0);
+    const uint32_t a1 = (uint32_t)__shfl((int)l[k], src1), b1 = (uint32_t)__shfl((int)h[k], src1);
+    o0[k] = upper ? b0 : a0;
+    o1[k] = upper ? b1 : a1;
+  }
+  lo = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+  hi = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+}
+// INT4 pages: this lane's part of the offset of the score product, in the
+// layout of q4_relayout: 24 x the sum of its 16 query values plus (136 - 24)
+// x those at dims 0, 4, 8, 12 of them (the first nibbles of the 16-bit
+// code units).  The column's offset is the sum over the 4 lanes G.
+__device__ __forceinline__ float q4_bias_part(uint4 lo, uint4 hi) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += bf16_lo(w[k]) + bf16_hi(w[k]);
+  const float first = (bf16_lo(lo.x) + bf16_lo(lo.z)) + (bf16_lo(hi.x) + bf16_lo(hi.z));
+  return kNibbleBias4 * sum + (kNibbleBias4First - kNibbleBias4) * first;
+}
+// INT4 pages: the value offset of output tile e (dims 4n + e: tile 0 holds
+// the first nibbles)
+__device__ __forceinline__ constexpr float q4_value_bias(int e) {
+  return e == 0 ? kNibbleBias4First : kNibbleBias4;
 }
 
 // One quantised row of 64 values is held by a quad of lanes: lane c (0..3)
