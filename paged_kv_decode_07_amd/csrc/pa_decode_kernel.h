@@ -68,19 +68,22 @@
 // to BF16 exactly and the V scale joins the weight (p * v_scale), while the
 // normaliser sums p alone.
 //
-// INT4 pages: a nibble u = code + 8 becomes the BF16 value 16 + u = code + 24
-// with a shift and one mask-and-or per pair (no conversion instruction); the
-// bias is removed around each product.  Scores: -24 x (the sum of the query
-// row) is the accumulator input of the score product.  Values: each lane also
-// sums its weights (p * v_scale), rescaled with the accumulators, and 24 x
-// that sum is subtracted from the output.  The packed K word gives its dims
-// in the order 0 4 1 5 2 6 3 7, and the query operand is permuted to match.
-// One transposed read gives a lane 4 tokens x 4 dims (the 16-bit unit is 4
-// codes), so tile e of the value product is dims 4n + e.  With its smaller
-// pages this format is bound by the arithmetic per page rather than by HBM:
-// its 3-deep ring lets full pages be consumed two at a time (one vote and
-// rescale for both, one 16x16x32 value product per tile over their 32
-// tokens).
+// INT4 pages: a nibble u = code + 8 becomes a BF16 value without a
+// conversion instruction: 128 + u = code + 136 for the first nibble of a
+// 16-bit unit (masked in place), 16 + u = code + 24 for the others (a shift
+// and one mask-and-or per pair).  The offsets are removed around each
+// product.  Scores: minus the offsets times the query row is the accumulator
+// input of the score product.  Values: each lane also sums the weights its
+// products carry (the BF16 weight plus its BF16 remainder), rescaled with the
+// accumulators, and each tile's offset times that sum is subtracted from the
+// output.  A lane reads dims 16G .. 16G+15 of a token's K codes in one 64-bit
+// LDS read; each word gives its dims in the order 0 4 1 5 2 6 3 7, and the
+// query operand is exchanged between lanes and permuted to match.  One
+// transposed read gives a lane 4 tokens x 4 dims (the 16-bit unit is 4
+// codes), so tile e of the value product is dims 4n + e.  The 3-deep ring
+// lets full pages be consumed two at a time (one vote and rescale for both,
+// one 16x16x32 value product per tile over their 32 tokens); with its small
+// pages this format is bound by its page stream's per-page requests.
 //
 // Masking: slots past the sequence in its last page may hold any bits.  Their
 // scores are selected to -inf, their weights to 0, and for BF16 pages their V

@@ -29,8 +29,8 @@ int plan_split(const pa_shape* s, int batch, int max_seq_len, int fixed, int* pa
 // The defaults were fitted to the BF16 kernel on MI355X over batch 8 .. 512
 // and split sizes 8 .. 128.
 // Up to `resident` work-groups may share a CU; a CU holding more than one
-// streams shared_gain times the pages of one work-group alone (a kernel
-// bound by its arithmetic hides more latency with more waves per SIMD).
+// streams shared_gain times the pages of one work-group alone (more waves
+// per SIMD hide more of each page's latency).
 struct PlanModel {
   double page_us = 0.6, group_us = 3.0, empty_us = 0.5, merge_us = 8.0;
   double hbm_bytes_per_us = 6.6e6;
