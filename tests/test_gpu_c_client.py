@@ -1,7 +1,8 @@
 """The library driven from C++ alone: a host program (tests/c_client) that
 allocates with hipMalloc, calls the header's pa_append_decode_attention (or
-its INT8 and INT4 forms) on the default stream and writes the results back to
-files.  No Python binding or torch tensor takes part in the step; the outputs
+its INT8 and INT4 forms, the balanced launch over a plan it builds from the
+host lengths, or the allocation-free step) on the default stream and writes
+the results back to files.  No Python binding or torch tensor takes part in the step; the outputs
 are checked against the oracle as in the binding's parity tests (pools
 bit-exact, attention within the FP32 bound)."""
 
@@ -24,9 +25,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CLIENT = os.path.join(ROOT, "paged_kv_decode_07_amd", "_lib", "decode_client")
 
 
-@pytest.mark.parametrize("lens,pps", [([37, 1, 200, 16, 0, 513], 0), ([2048] * 3, 8)],
-                         ids=["ragged-auto", "long-split8"])
-def test_c_client_step_matches_oracle(tmp_path, lens, pps):
+@pytest.mark.parametrize("lens,pps,launch,heads", [
+    ([37, 1, 200, 16, 0, 513], 0, 0, 8), ([2048] * 3, 8, 0, 8),
+    ([37, 1, 200, 16, 0, 513], 0, 1, 8), ([2048] * 3, 0, 1, 1),
+    ([37, 1, 200, 16, 0, 513], 4, 2, 8)],
+    ids=["ragged-auto", "long-split8", "balanced-ragged", "balanced-long-1-head-lanes",
+         "noalloc-ragged-split4"])
+def test_c_client_step_matches_oracle(tmp_path, lens, pps, launch, heads):
     if not os.path.exists(CLIENT):
         pytest.fail("decode_client is not built (build the library and the client first)")
     pages = sum(W.pages_for(L) for L in lens) + 5
@@ -38,8 +43,9 @@ def test_c_client_step_matches_oracle(tmp_path, lens, pps):
     for name, arr in (("q", w.q), ("k_new", k_new), ("v_new", v_new), ("k_pool", w.k_pool),
                       ("v_pool", w.v_pool), ("bt", w.block_tables), ("lens", w.seq_lens)):
         np.ascontiguousarray(arr).tofile(tmp_path / f"{name}.bin")
-    (tmp_path / "meta.txt").write_text(f"{B} {pages} {W.MAX_BLOCKS} {max_len} {pps}\n")
-    print(f"c_client: lens {lens} pps {pps}", flush=True)
+    (tmp_path / "meta.txt").write_text(
+        f"{B} {pages} {W.MAX_BLOCKS} {max_len} {pps} 16 {launch} {heads}\n")
+    print(f"c_client: lens {lens} pps {pps} launch {launch} heads {heads}", flush=True)
     res = subprocess.run([CLIENT, str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, f"client exit {res.returncode}: {res.stdout}{res.stderr}"
 
@@ -54,11 +60,14 @@ def test_c_client_step_matches_oracle(tmp_path, lens, pps):
     assert np.all(out[w.seq_lens == 0] == 0)          # an idle slot's rows are zero
 
 
-@pytest.mark.parametrize("bits,lens,pps", [(8, [37, 1, 200, 16, 0, 513], 0),
-                                           (4, [37, 1, 200, 16, 0, 513], 0),
-                                           (4, [2048] * 3, 64)],
-                         ids=["int8-ragged-auto", "int4-ragged-auto", "int4-long-split64"])
-def test_c_client_quantised_step_matches_oracle(tmp_path, bits, lens, pps):
+@pytest.mark.parametrize("bits,lens,pps,launch", [(8, [37, 1, 200, 16, 0, 513], 0, 0),
+                                                  (4, [37, 1, 200, 16, 0, 513], 0, 0),
+                                                  (4, [2048] * 3, 64, 0),
+                                                  (8, [37, 1, 200, 16, 0, 513], 0, 1),
+                                                  (4, [2048, 17, 1000], 0, 1)],
+                         ids=["int8-ragged-auto", "int4-ragged-auto", "int4-long-split64",
+                              "int8-balanced", "int4-balanced"])
+def test_c_client_quantised_step_matches_oracle(tmp_path, bits, lens, pps, launch):
     if not os.path.exists(CLIENT):
         pytest.fail("decode_client is not built (build the library and the client first)")
     pages = sum(W.pages_for(L) for L in lens) + 5
@@ -68,8 +77,9 @@ def test_c_client_quantised_step_matches_oracle(tmp_path, bits, lens, pps):
                       ("v_pool", w.v_codes), ("scales", w.kv_scales), ("bt", w.block_tables),
                       ("lens", w.seq_lens)):
         np.ascontiguousarray(arr).tofile(tmp_path / f"{name}.bin")
-    (tmp_path / "meta.txt").write_text(f"{B} {pages} {W.MAX_BLOCKS} {max(lens)} {pps} {bits}\n")
-    print(f"c_client: {bits}-bit pages, lens {lens} pps {pps}", flush=True)
+    (tmp_path / "meta.txt").write_text(
+        f"{B} {pages} {W.MAX_BLOCKS} {max(lens)} {pps} {bits} {launch}\n")
+    print(f"c_client: {bits}-bit pages, lens {lens} pps {pps} launch {launch}", flush=True)
     res = subprocess.run([CLIENT, str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, f"client exit {res.returncode}: {res.stdout}{res.stderr}"
 
