@@ -56,6 +56,7 @@ _CSRC = os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc")
 _DEVICE = ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_kernel.h", "pa_host.h")
 KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode.hip",)]
 KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_q8.hip",)]
+BALANCED_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_balanced.hip",)]
 
 
 def log(msg: str) -> None:
@@ -68,6 +69,15 @@ def kernel_source_hash(sources=None) -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def source_hashes() -> dict:
+    """sha256[:16] of each kernel family's sources, printed ahead of the tables of
+    the sweep, the placement probe and the one-configuration runs, so that a
+    summary can tell which sources it describes."""
+    return {"grid_bf16": kernel_source_hash(KERNEL_SOURCES),
+            "grid_quantised": kernel_source_hash(KERNEL_SOURCES_Q8),
+            "balanced": kernel_source_hash(BALANCED_SOURCES)}
 
 
 def measured_traffic(path: str = TRAFFIC_FILE, sources=None):
@@ -343,6 +353,7 @@ def run_sweep(args) -> int:
     from paged_kv_decode_07_amd import accounting as A
     from paged_kv_decode_07_amd import binding as pa
 
+    print(json.dumps({"kernel_sources": source_hashes()}), flush=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.load_library()
@@ -956,6 +967,7 @@ def run_placement_probe(args) -> int:
     from paged_kv_decode_07_amd import accounting as A
     from paged_kv_decode_07_amd import binding as pa
 
+    print(json.dumps({"kernel_sources": source_hashes()}), flush=True)
     w = W.make_workload(4, append=False)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -1030,7 +1042,7 @@ def run_one_config(args) -> int:
         torch.cuda.synchronize()
         del src
     line, _ = measure_config(ci, args, stream, dev, flush, None)
-    print(json.dumps({"config": ci, **line}), flush=True)
+    print(json.dumps({"config": ci, **line, "kernel_sources": source_hashes()}), flush=True)
     return 0
 
 

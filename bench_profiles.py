@@ -10,11 +10,19 @@ Two modes, each reading rocprofv3 output directories (``-f csv -d DIR``):
       by bench.py while the kernel sources are unchanged) and, with --util,
       utilisation counters (profiles/decode_kernel_utilisation_b256_l2048.md).
 
-  python bench_profiles.py config N --trace DIR --fetch DIR --write DIR --util DIR
+  python bench_profiles.py config N --line FILE --trace DIR --fetch DIR --write DIR --util DIR
       runs of ``bench.py --only-config N``: per candidate launch, the decode
       and merge kernels' average durations, HBM bytes over the algorithmic
-      bytes, and utilisation; prints a markdown table (the profile's prose is
-      written around it).
+      bytes, and utilisation (profiles/decode_step_trace_config*.md; the
+      hand-written notes after the notes marker are kept).
+
+  python bench_profiles.py sweep --json FILE --steps K --warmup W
+  python bench_profiles.py placement --json FILE --steps K --warmup W
+      the output of ``bench.py --sweep`` / ``--placement-probe`` as tables
+      (profiles/decode_step_sweep_workloads_1_5.md,
+      profiles/decode_kernel_placement_b256_l2048.md).
+
+Every mode refuses a run whose kernel sources are not the current ones.
 
 HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what they
 read for a 256 MiB device copy of the same run (``--calibration-copy``).
@@ -363,18 +371,48 @@ def split_launches(rows, names, layers):
     return out
 
 
+NOTES = "<!-- notes: kept when the tables above are regenerated -->"
+
+
+def write_keeping_notes(path: str, text: str) -> None:
+    """Write a generated summary, keeping whatever an existing file holds after
+    the notes marker (the hand-written reading of the tables)."""
+    notes = ""
+    if os.path.exists(path):
+        with open(path) as f:
+            old = f.read()
+        k = old.find(NOTES)
+        if k >= 0:
+            notes = old[k + len(NOTES):]
+    with open(path, "w") as o:
+        o.write(text.rstrip("\n") + "\n\n" + NOTES + (notes if notes else "\n"))
+
+
+def check_sources(found: dict, keys) -> None:
+    want = bench.source_hashes()
+    for k in keys:
+        if found.get(k) != want[k]:
+            raise SystemExit(f"the run's {k} kernel sources ({found.get(k)}) are not the current "
+                             f"ones ({want[k]}): run it again")
+
+
+CONFIG_FILES = {3: "decode_step_trace_config3_b64_16layers.md",
+                5: "decode_step_trace_config5_b512_zipf.md"}
+
+
 def config(a) -> int:
     import workloads as W
     from paged_kv_decode_07_amd import accounting as A
 
     ci = a.config
     line = _json_line(a.line)
+    check_sources(line.get("kernel_sources", {}), ("grid_bf16", "balanced"))
     names = list(line["launches"])
     layers = int(line["layers"])
     alg = A.step_bytes(W.workload_seq_lens(ci), append=True)
     trace = split_launches(_csv(a.trace, "kernel_trace"), names, layers)
     fetch_rows, write_rows = _csv(a.fetch, "counter_collection"), _csv(a.write, "counter_collection")
-    _, _, ff, wf = calibration(fetch_rows, write_rows)
+    cf, cw, ff, wf = calibration(fetch_rows, write_rows)
     fetch = split_launches(fetch_rows, names, layers)
     write = split_launches(write_rows, names, layers)
     util = split_launches(_csv(a.util, "counter_collection"), names, layers) if a.util else None
@@ -387,10 +425,34 @@ def config(a) -> int:
         v = [float(r["Counter_Value"]) for r in rs if r["Counter_Name"] == counter]
         return float(np.sum(v)) if v else 0.0
 
-    print(f"config {ci}: {layers} layer(s); per layer K/V {int(alg['kv']):,} B, every algorithmic "
-          f"byte {int(alg['total']):,} B\n")
-    print("| launch | work-groups | decode kernel avg us | merge kernel avg us | layer: kernels us "
-          "| HBM bytes / algorithmic |\n|---|---|---|---|---|---|")
+    box = lambda d: _box(d)                                   # noqa: E731
+    tag = os.path.basename(os.path.normpath(a.trace))
+    cmds = [f"rocprofv3 --kernel-trace --stats -f csv -d {box(a.trace)} -o c{ci} -- python -u "
+            f"/root/repo/bench.py --only-config {ci} --steps 10 --warmup 2"]
+    for d, ctr in ((a.fetch, "FETCH_SIZE"), (a.write, "WRITE_SIZE")):
+        cmds.append(f"rocprofv3 --pmc {ctr} -f csv -d {box(d)} -o c{ci} -- python -u "
+                    f"/root/repo/bench.py --only-config {ci} --steps 2 --warmup 1 --calibration-copy")
+    if a.util:
+        cmds.append(f"rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d {box(a.util)} -o c{ci} -- python -u "
+                    f"/root/repo/bench.py --only-config {ci} --steps 2 --warmup 1")
+    cmds.append(f"python bench_profiles.py config {ci} --line {_rel(a.line)} --trace {_rel(a.trace)} "
+                f"--fetch {_rel(a.fetch)} --write {_rel(a.write)}"
+                + (f" --util {_rel(a.util)}" if a.util else ""))
+    del tag
+    src = line["kernel_sources"]
+    out = [f"# Workload {ci}: {W.WORKLOADS[ci]}; fused step, BF16 pages, every launch\n",
+           "Commands (MI355X, ROCm 7.2; the profiler runs from /tmp with TMPDIR=/tmp, the summary "
+           "from the repository root; one pass each; `--calibration-copy` adds one 256 MiB device "
+           "copy as the byte counters' reference):\n",
+           "```\n" + "\n".join(cmds) + "\n```\n",
+           f"Kernel sources sha256[:16]: grid and work-list kernel `{src['grid_bf16']}`; balanced "
+           f"kernel `{src['balanced']}`.\n",
+           f"`--only-config {ci}` times the fused append + attention step of the workload's "
+           f"{layers} layer{'s' if layers > 1 else ''} back to back under every launch that can "
+           "plan it, in this order: " + "; ".join(names) + ". Per layer: K/V "
+           f"{int(alg['kv']):,} bytes; every algorithmic byte of the step {int(alg['total']):,}.\n",
+           "| launch | work-groups | decode kernel avg us | merge kernel avg us | layer: kernels us "
+           "| HBM bytes / algorithmic |\n|---|---|---|---|---|---|"]
     for n in names:
         d, m = trace[n]["decode"], trace[n]["merge"]
         wg = int(d[0]["Grid_Size_X"]) // int(d[0]["Workgroup_Size_X"])
@@ -399,15 +461,113 @@ def config(a) -> int:
                 + kib(write[n]["decode"] + write[n]["merge"], "WRITE_SIZE") * wf) * 1024 / nd)
         dm, mm = dur(d), dur(m)
         per_layer = dm + mm * len(m) / len(d)
-        print(f"| {n} | {wg} | {dm:.2f} | {mm:.2f} | {per_layer:.2f} | "
-              f"{hbm / float(alg['total']):.4f} |")
+        out.append(f"| {n} | {wg} | {dm:.2f} | {mm:.2f} | {per_layer:.2f} | "
+                   f"{hbm / float(alg['total']):.4f} |")
+    out.append(f"\nHBM bytes: FETCH_SIZE x {ff:.3f} + WRITE_SIZE x {wf:.3f} (KiB per dispatch x "
+               f"1024; the 256 MiB copy reads {cf:,.1f} KiB by FETCH_SIZE and writes {cw:,.1f} KiB "
+               "by WRITE_SIZE), decode and merge kernels together, per layer.\n")
     if util:
-        print("\n| launch | GUI-active us | VALU busy | MFMA busy | waves waiting | waves issuing |\n"
-              "|---|---|---|---|---|---|")
+        out.append("Utilisation (decode kernel; " + UTIL_NOTE.replace("\n", " ").strip() + "):\n")
+        out.append("| launch | GUI-active us | VALU busy | MFMA busy | waves waiting | waves issuing |\n"
+                   "|---|---|---|---|---|---|")
         for n in names:
             u = utilisation(util[n]["decode"])
-            print(f"| {n} | {u['gui_us']:.1f} | {100 * u['valu']:.1f}% | {100 * u['mfma']:.1f}% | "
-                  f"{100 * u['wait']:.1f}% | {100 * u['issue']:.1f}% |")
+            out.append(f"| {n} | {u['gui_us']:.1f} | {100 * u['valu']:.1f}% | "
+                       f"{100 * u['mfma']:.1f}% | {100 * u['wait']:.1f}% | {100 * u['issue']:.1f}% |")
+    text = "\n".join(out) + "\n"
+    path = os.path.join(PROFILES, CONFIG_FILES.get(ci, f"decode_step_trace_workload{ci}.md"))
+    write_keeping_notes(path, text)
+    print(text)
+    return 0
+
+
+def _lines(path: str):
+    with open(path) as f:
+        return [json.loads(x) for x in f if x.strip().startswith("{")]
+
+
+def sweep(a) -> int:
+    rows = _lines(a.json)
+    check_sources(rows[0].get("kernel_sources", {}), ("grid_bf16", "grid_quantised", "balanced"))
+    src = rows[0]["kernel_sources"]
+    rows = [r for r in rows if "workload" in r]
+    out = ["# Fused decode step on every workload: BF16, INT8 and INT4 pages, every launch\n",
+           "Commands (MI355X, ROCm 7.2, from the repository root):\n",
+           f"```\npython -u bench.py --sweep --steps {a.steps} --warmup {a.warmup} > "
+           f"{_rel(a.json)}\npython bench_profiles.py sweep --json {_rel(a.json)} --steps "
+           f"{a.steps} --warmup {a.warmup}\n```\n",
+           "One layer's fused append + attention step (workload 3: its first layer), caches "
+           f"flushed before every step, median of {a.steps} event-timed steps. `grid (lengths "
+           "plan)` is `pa_append_decode_attention[_q8|_q4]` with the split size from "
+           "`pa_decode_plan_lengths[_q8|_q4]`; `work list` is "
+           "`pa_append_decode_attention_worklist[_q8|_q4]` over `pa_decode_worklist`; `balanced, "
+           "h KV heads per lane` is `pa_decode_balanced` over `pa_balance_plan` with "
+           "`heads_together` = h (work-groups in the units column). K/V bytes: 2,048 per valid "
+           "token (BF16 pages), 1,088 (INT8 codes and scales), 576 (INT4). The last rows run "
+           "workload 3 as a model step: its 16 layers' fused steps back to back (one pool region "
+           "per layer; sequences/s counts the whole 16-layer step), launched as 16 calls and "
+           "replayed as one HIP graph. INT4 grid and work-list launches whose grid fits the CUs "
+           "with splits of 32 pages or more run two wavefronts per KV head. Kernel sources: grid "
+           f"and work list `{src['grid_bf16']}` (BF16) and `{src['grid_quantised']}` (INT8, "
+           f"INT4), balanced `{src['balanced']}`.\n",
+           "| workload | pages | launch | pages/split | splits, items or work-groups | step µs | "
+           "K/V GB/s | sequences/s |\n|---|---|---|---|---|---|---|---|"]
+    best = {}
+    for r in rows:
+        units = r.get("work_groups", r.get("splits", r.get("items", "")))
+        out.append(f"| {r['workload']} | {r['pages']} | {r['launch']} | {r['pages_per_split']} | "
+                   f"{units} | {r['step_us']} | {r['kv_gbps']:,.0f} | "
+                   f"{r['seq_per_s_per_layer']:,.0f} |")
+        if "16 calls" in r["launch"] or "graph" in r["launch"]:
+            continue
+        k = (r["workload"], r["pages"])
+        if k not in best or r["step_us"] < best[k]["step_us"]:
+            best[k] = r
+    out.append("\nFastest launch per workload and page format (one layer):\n")
+    out.append("| workload | BF16 | INT8 | INT4 |\n|---|---|---|---|")
+    for wi in sorted({k[0] for k in best}):
+        cells = []
+        for fmt in ("bf16", "int8", "int4"):
+            r = best.get((wi, fmt))
+            cells.append(f"{r['step_us']} µs, {r['launch']} ({r['kv_gbps']:,.0f} GB/s)" if r else "–")
+        out.append(f"| {wi} | " + " | ".join(cells) + " |")
+    text = "\n".join(out) + "\n"
+    write_keeping_notes(os.path.join(PROFILES, "decode_step_sweep_workloads_1_5.md"), text)
+    print(text)
+    return 0
+
+
+def placement(a) -> int:
+    rows = _lines(a.json)
+    check_sources(rows[0].get("kernel_sources", {}), ("grid_bf16",))
+    src = rows[0]["kernel_sources"]
+    rows = [r for r in rows if "placement" in r]
+    out = ["# Page placement: the decode kernel on batch 256 x 2048 under seven placements\n",
+           "Commands (MI355X, ROCm 7.2, from the repository root):\n",
+           f"```\npython -u bench.py --placement-probe --steps {a.steps} --warmup {a.warmup} > "
+           f"{_rel(a.json)}\npython bench_profiles.py placement --json {_rel(a.json)} --steps "
+           f"{a.steps} --warmup {a.warmup}\n```\n",
+           "The same logical cache (workload 4 without the append: 256 sequences of 2,048 tokens, "
+           "1 GiB of BF16 K/V in a pool of exactly 32,768 pages) is laid out under each placement, "
+           "then `pa_decode_attention` (one 128-page split per sequence) runs interleaved over the "
+           f"placements, caches flushed before every launch, {a.steps} timed rounds after "
+           f"{a.warmup} warm-up rounds; median and minimum of the event-timed launches. "
+           "Placements: `identity` (each sequence's pages consecutive, in order); `region` (the "
+           "same 128 pages per sequence, shuffled); `chunksN` (random N-page chunks of the pool, "
+           "pages shuffled within each chunk); `random` (one random permutation of the pool, the "
+           "workload's own placement). Kernel sources "
+           f"`{src['grid_bf16']}`.\n",
+           "| placement | median µs | min µs | K/V GB/s (median) | output bitwise = identity |\n"
+           "|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['placement']} | {r['decode_us_median']:.2f} | {r['decode_us_min']:.2f} | "
+                   f"{r['kv_gbps']:,.1f} | {r['same_output_as_identity']} |")
+    med = [r["decode_us_median"] for r in rows]
+    out.append(f"\nThe spread is {100 * (max(med) / min(med) - 1):.1f}% "
+               f"({min(med):.1f} to {max(med):.1f} µs).")
+    text = "\n".join(out) + "\n"
+    write_keeping_notes(os.path.join(PROFILES, "decode_kernel_placement_b256_l2048.md"), text)
+    print(text)
     return 0
 
 
@@ -427,8 +587,14 @@ def main(argv=None) -> int:
         p.add_argument("--fetch", required=True)
         p.add_argument("--write", required=True)
         p.add_argument("--util", default=None)
+    for name in ("sweep", "placement"):
+        p = sub.add_parser(name)
+        p.add_argument("--json", required=True, help=f"the output of bench.py --{name}"
+                       + ("" if name == "sweep" else "-probe"))
+        p.add_argument("--steps", type=int, required=True)
+        p.add_argument("--warmup", type=int, required=True)
     a = ap.parse_args(argv)
-    return headline(a) if a.mode == "headline" else config(a)
+    return {"headline": headline, "config": config, "sweep": sweep, "placement": placement}[a.mode](a)
 
 
 if __name__ == "__main__":

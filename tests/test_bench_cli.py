@@ -135,3 +135,25 @@ def test_profile_summary_refuses_a_run_of_other_sources(tmp_path):
         assert "profile again" in str(e)
     else:
         raise AssertionError("a run of other kernel sources must be refused")
+
+
+def test_profile_summaries_keep_the_notes_and_refuse_other_sources(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench_profiles as P
+    f = tmp_path / "p.md"
+    P.write_keeping_notes(str(f), "# tables v1\n")
+    assert f.read_text().startswith("# tables v1") and P.NOTES in f.read_text()
+    f.write_text(f.read_text() + "- a reading of the tables\n")
+    P.write_keeping_notes(str(f), "# tables v2\n")
+    text = f.read_text()
+    assert text.startswith("# tables v2") and "v1" not in text
+    assert text.endswith(P.NOTES + "\n- a reading of the tables\n")
+    j = tmp_path / "sweep.json"
+    j.write_text(json.dumps({"kernel_sources": {"grid_bf16": "0", "grid_quantised": "1",
+                                                "balanced": "2"}}) + "\n")
+    try:
+        P.main(["sweep", "--json", str(j), "--steps", "1", "--warmup", "1"])
+    except SystemExit as e:
+        assert "run it again" in str(e)
+    else:
+        raise AssertionError("a sweep of other kernel sources must be refused")
