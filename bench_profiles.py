@@ -515,9 +515,9 @@ def sweep(a) -> int:
     best = {}
     for r in rows:
         units = r.get("work_groups", r.get("splits", r.get("items", "")))
+        rate = r.get("seq_per_s_per_layer", r.get("seq_per_s"))
         out.append(f"| {r['workload']} | {r['pages']} | {r['launch']} | {r['pages_per_split']} | "
-                   f"{units} | {r['step_us']} | {r['kv_gbps']:,.0f} | "
-                   f"{r['seq_per_s_per_layer']:,.0f} |")
+                   f"{units} | {r['step_us']} | {r['kv_gbps']:,.0f} | {rate:,.0f} |")
         if "16 calls" in r["launch"] or "graph" in r["launch"]:
             continue
         k = (r["workload"], r["pages"])
