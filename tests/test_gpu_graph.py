@@ -6,7 +6,10 @@ and replayed with new inputs written into the same buffers.  Every replay is
 checked bit for bit against the same step run eagerly on a twin set of
 buffers, with eager work and synchronisations between the replays; the last
 step is also checked against the oracle.  BF16, INT8 and INT4 pages; the INT4
-step runs 32-page splits, the launch with two wavefronts per KV head.
+step runs 32-page splits, the launch with two wavefronts per KV head.  The
+allocation-free step (its partials in the library's own scratch, no
+workspace argument) is captured as well, and each of its replays must equal
+the ordinary fused step with a workspace bit for bit.
 """
 
 from __future__ import annotations
@@ -37,13 +40,13 @@ def _device():
 
 # split size per page format: INT4 pages at 32-page splits take the launch with
 # two wavefronts per KV head (the plan's grid fits the CUs)
-SPLIT = {"bf16": 8, "int8": 8, "int4": 32}
+SPLIT = {"bf16": 8, "int8": 8, "int4": 32, "bf16-noalloc": 8}
 
 
 def _state(fmt: str, seed: int):
     lens0 = np.array([5, 100, 250, 31, 0, 390 - STEPS], np.int32)
     pages = len(lens0) * W.pages_for(CAP) + 4
-    if fmt != "bf16":
+    if fmt not in ("bf16", "bf16-noalloc"):
         w = W.make_q8_batch(lens0, pages, seed, nbits=4 if fmt == "int4" else 8)
         pools = [torch.from_numpy(a.copy()).cuda() for a in (w.k_codes, w.v_codes, w.kv_scales)]
     else:
@@ -62,17 +65,21 @@ def _state(fmt: str, seed: int):
     return w, pools, bt, lens0
 
 
-def _run(fmt, pools, q, kn, vn, bt, lens, out, ws):
+def _run(fmt, pools, q, kn, vn, bt, lens, out, ws, eager=False):
     from paged_kv_decode_07_amd import binding as pa
-    fn = {"bf16": pa.append_decode_attention, "int8": pa.append_decode_attention_q8,
-          "int4": pa.append_decode_attention_q4}[fmt]
+    if fmt == "bf16-noalloc" and not eager:
+        pa.append_decode_attention_noalloc(q, kn, vn, *pools, bt, lens, CAP, out=out,
+                                           pages_per_split=SPLIT[fmt])
+        return
+    fn = {"bf16": pa.append_decode_attention, "bf16-noalloc": pa.append_decode_attention,
+          "int8": pa.append_decode_attention_q8, "int4": pa.append_decode_attention_q4}[fmt]
     fn(q, kn, vn, *pools, bt, lens, CAP, out=out, pages_per_split=SPLIT[fmt], workspace=ws)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4", "bf16-noalloc"])
 def test_graph_replays_match_eager_steps(fmt):
     from paged_kv_decode_07_amd import binding as pa
-    seed = {"bf16": 0, "int8": 1, "int4": 2}[fmt]
+    seed = {"bf16": 0, "int8": 1, "int4": 2, "bf16-noalloc": 3}[fmt]
     w, pools_g, bt_h, lens0 = _state(fmt, 1300 + seed)
     pools_e = [p.clone() for p in pools_g]
     B = len(lens0)
@@ -115,7 +122,8 @@ def test_graph_replays_match_eager_steps(fmt):
         graph.replay()
         torch.cuda.synchronize()
         # the same step, eagerly, on the twin buffers
-        _run(fmt, pools_e, dev16(qh), dev16(knh), dev16(vnh), bt, dev32(lens), out_e, ws_e)
+        _run(fmt, pools_e, dev16(qh), dev16(knh), dev16(vnh), bt, dev32(lens), out_e, ws_e,
+             eager=True)
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), f"replay {step}: output differs from the eager step"
         for pg, pe in zip(pools_g, pools_e):
@@ -126,7 +134,7 @@ def test_graph_replays_match_eager_steps(fmt):
 
     # the final state against the oracle (the cache holds every appended token)
     qh, lens = last
-    if fmt != "bf16":
+    if fmt not in ("bf16", "bf16-noalloc"):
         kc, vc, sc = (p.cpu().numpy() for p in pools_g)
         ref = kvquant.decode_attention_q8(qh, kc, vc, sc, bt_h, lens, W.SCALE,
                                           nbits=4 if fmt == "int4" else 8)
