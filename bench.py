@@ -378,7 +378,7 @@ def run_sweep(args) -> int:
         torch.cuda.synchronize()
         return float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
 
-    for wi in (1, 2, 3, 4, 5):
+    for wi in (1, 2, 3, 4, 5, 6):
         t0 = time.perf_counter()
         w = W.make_workload(wi, append=True)
         log(f"workload {wi}: {w.batch} sequences, {w.num_pages} pages "
@@ -545,8 +545,8 @@ def main() -> int:
                          "permutation), interleaved, cold caches; one JSON line per placement")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused step of every workload "
-                         "(1-5), BF16 and INT8 pages, grid launch with the library plan and "
-                         "work-list launch; one JSON line per case")
+                         "(1-6; 6 is the truncated reading of workload 5's Zipf lengths), BF16, "
+                         "INT8 and INT4 pages, under every launch; one JSON line per case")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -19,7 +19,7 @@ Two modes, each reading rocprofv3 output directories (``-f csv -d DIR``):
   python bench_profiles.py sweep --json FILE --steps K --warmup W
   python bench_profiles.py placement --json FILE --steps K --warmup W
       the output of ``bench.py --sweep`` / ``--placement-probe`` as tables
-      (profiles/decode_step_sweep_workloads_1_5.md,
+      (profiles/decode_step_sweep_workloads_1_6.md,
       profiles/decode_kernel_placement_b256_l2048.md).
 
 Every mode refuses a run whose kernel sources are not the current ones.
@@ -532,7 +532,7 @@ def sweep(a) -> int:
             cells.append(f"{r['step_us']} µs, {r['launch']} ({r['kv_gbps']:,.0f} GB/s)" if r else "–")
         out.append(f"| {wi} | " + " | ".join(cells) + " |")
     text = "\n".join(out) + "\n"
-    write_keeping_notes(os.path.join(PROFILES, "decode_step_sweep_workloads_1_5.md"), text)
+    write_keeping_notes(os.path.join(PROFILES, "decode_step_sweep_workloads_1_6.md"), text)
     print(text)
     return 0
 

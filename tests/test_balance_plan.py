@@ -91,7 +91,7 @@ def check_plan(lens, num_cus=256, max_blocks=128, h=8):
 
 
 @pytest.mark.parametrize("h", [1, 2, 4, 8])
-@pytest.mark.parametrize("wi", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("wi", [1, 2, 3, 4, 5, 6])
 def test_workload_plans_are_valid_and_balanced(wi, h):
     lens = W.workload_seq_lens(wi)
     groups, load = check_plan(lens, h=h)

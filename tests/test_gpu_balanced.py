@@ -110,7 +110,7 @@ def test_balanced_many_single_token_sequences():
 
 
 @pytest.mark.parametrize("h", [1, 8])
-@pytest.mark.parametrize("wi", [1, 2, 4, 5])
+@pytest.mark.parametrize("wi", [1, 2, 4, 5, 6])
 def test_balanced_full_workloads(wi, h):
     print(f"balanced: workload {wi}, heads together {h}", flush=True)
     w = W.make_workload(wi, append=True)

@@ -61,13 +61,14 @@ def test_fused_seq_len_one_returns_the_new_v_row():
             assert np.array_equal(got[b, h], vnew[h // 4])
 
 
-def test_fused_full_batch512_zipf():
-    w = W.make_workload(5)
+@pytest.mark.parametrize("wi", [5, 6], ids=["zipf-clipped", "zipf-truncated"])
+def test_fused_full_batch512_zipf(wi):
+    w = W.make_workload(wi)
     got = _two_call_vs_fused(w, 0)
     k_ref, v_ref = oracle.append_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.block_tables,
                                     w.seq_lens)
     ref = oracle.decode_attention(w.q, k_ref, v_ref, w.block_tables, w.seq_lens, w.scale)
-    assert_close(got, ref, where="fused batch512 every sequence")
+    assert_close(got, ref, where=f"fused batch512 (workload {wi}) every sequence")
 
 
 def test_fused_full_batch256_len2048_bench_configuration():

@@ -47,6 +47,15 @@ def test_workload_shapes_and_length_ranges():
     assert l5.shape == (512,) and l5.min() >= 1 and l5.max() == 2048
     # clipped Zipf(1.1): a large share at the clip, some single-token sequences
     assert 0.3 < np.mean(l5 == 2048) < 0.6 and np.mean(l5 == 1) > 0.03
+    # truncated Zipf(1.1): P(L = k) proportional to k^-1.1 on 1..2048 (mean of the law about
+    # 179, worked out here from the definition), so few sequences are long
+    k = np.arange(1, 2049, dtype=np.float64)
+    law_mean = float((k ** -0.1).sum() / (k ** -1.1).sum())
+    assert 175 < law_mean < 185
+    l6 = W.workload_seq_lens(6)
+    assert l6.shape == (512,) and l6.min() >= 1 and l6.max() <= 2048
+    assert abs(l6.mean() - law_mean) < 60 and np.mean(l6 == 1) > 0.1
+    assert np.array_equal(l6, W.workload_seq_lens(6))        # seeded
 
 
 def test_small_workload_layout():

@@ -222,7 +222,7 @@ def _seed_repr(seed):
 
 
 # ---------------------------------------------------------------------------
-# The five workloads: Llama-3.2-1B decode-step shapes (synthetic stand-ins; the
+# The workloads: Llama-3.2-1B decode-step shapes (synthetic stand-ins; the
 # pages name no public benchmark or dataset)
 # ---------------------------------------------------------------------------
 WORKLOADS = {
@@ -231,6 +231,8 @@ WORKLOADS = {
     3: "16 layers, batch 64, seq_len uniform in [16, 2048], q sigma 0.5, append then attend per layer",
     4: "batch 256, every seq_len 2048 (1 GiB of K/V), pool of exactly 32768 pages",
     5: "batch 512, seq_len Zipf(1.1) clipped to [1, 2048], append then attend, 10% poison slack",
+    6: "batch 512, seq_len Zipf(1.1) truncated to [1, 2048] (the law renormalised on 1..2048), "
+       "append then attend, 10% poison slack",
 }
 NUM_LAYERS_W3 = 16
 POOL_PAGES_W3 = 8192
@@ -250,6 +252,12 @@ def workload_seq_lens(index: int, seed: Optional[int] = None) -> np.ndarray:
         return np.full(256, MAX_CONTEXT, dtype=np.int32)
     if index == 5:
         return np.clip(rng.zipf(1.1, size=512), 1, MAX_CONTEXT).astype(np.int32)
+    if index == 6:
+        # the other reading of "Zipf (s=1.1, clipped to [1, 2048])": P(L = k) proportional
+        # to k^-1.1 on 1..2048 only (mean about 179, against about 1000 for the clipped draw)
+        k = np.arange(1, MAX_CONTEXT + 1, dtype=np.float64)
+        p = k ** -1.1
+        return rng.choice(MAX_CONTEXT, size=512, p=p / p.sum()).astype(np.int32) + 1
     raise ValueError(index)
 
 
@@ -258,13 +266,13 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
     """Inputs of workload ``index`` (for workload 3: of layer ``layer``).
 
     ``append`` overrides whether the last token of every sequence is held
-    back for an append (default: workloads 3 and 5 append, the others not).
+    back for an append (default: workloads 3, 5 and 6 append, the others not).
     """
     seed = index if seed is None else seed
     lens = workload_seq_lens(index, seed)
     name = f"w{index}"
     recipe = {"workload": WORKLOADS[index]}
-    app = (index in (3, 5)) if append is None else bool(append)
+    app = (index in (3, 5, 6)) if append is None else bool(append)
     if index == 1:
         return make_batch(lens, 64, [seed, 1], name=name, recipe=recipe, placement=placement,
                           append=app)
@@ -280,7 +288,7 @@ def make_workload(index: int, seed: Optional[int] = None, layer: int = 0,
     if index == 4:
         return make_batch(lens, 256 * MAX_BLOCKS, [seed, 1], name=name, recipe=recipe,
                           placement=placement, append=app)
-    if index == 5:
+    if index in (5, 6):
         need = int(sum(pages_for(L) for L in lens))
         pool = need + (need + 9) // 10
         return make_batch(lens, pool, [seed, 1], append=app, name=name, recipe=recipe,
