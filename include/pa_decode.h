@@ -24,7 +24,9 @@
  * request count never grows the pool): every buffer is allocated and owned
  * by the caller.  The library allocates no device memory and keeps no
  * mutable global state besides a per-device cache of the compute-unit
- * count.  All device pointers are HIP device addresses.  Calls only enqueue
+ * count and, for pa_append_decode_attention_noalloc, a static device array
+ * per GPU (part of the loaded code object) and its address.  All device
+ * pointers are HIP device addresses.  Calls only enqueue
  * work on `stream` (a hipStream_t; NULL means the default stream) and
  * return without synchronising, except pa_validate_metadata.
  *
