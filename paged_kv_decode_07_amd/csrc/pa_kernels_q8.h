@@ -33,6 +33,9 @@ constexpr int kFmtINT4 = 2;
 constexpr int kHeadCodes = kPage * kD;           // 1 KiB: one head's 16 rows in a page
 constexpr int kPageCodes = kHkv * kHeadCodes;    // 8 KiB per page (K or V)
 constexpr int kScalePageFloats = kHkv * 2 * kPage;   // 256 floats = 1 KiB per page
+// Ring depths (build-time; the measured best).  INT8 pages: 2 (a deeper ring
+// would turn on the two-page pass, which the grid kernel only has for INT4
+// pages).  INT4 pages: 3, the depth its two-page pass is unrolled for, or 2.
 #ifndef PA_Q8_RING_DEPTH
 #define PA_Q8_RING_DEPTH 2
 #endif
