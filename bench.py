@@ -40,6 +40,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -63,11 +64,17 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash(sources=None) -> str:
+    """sha256[:16] of the kernel sources' code: comments and blank lines are left
+    out, so that a summary keyed to it survives an edit of the prose alone."""
     h = hashlib.sha256()
     for p in sources or KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            code = _COMMENTS.sub("", f.read())
+        h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -157,3 +157,15 @@ def test_profile_summaries_keep_the_notes_and_refuse_other_sources(tmp_path):
         assert "run it again" in str(e)
     else:
         raise AssertionError("a sweep of other kernel sources must be refused")
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    a = tmp_path / "a.h"
+    a.write_text("// a kernel\nint f(int x) {\n  return x + 1;  /* one */\n}\n")
+    h0 = bench.kernel_source_hash([str(a)])
+    a.write_text("// the kernel, reworded\n\nint f(int x) {\n  return x + 1;  /* the one */\n}\n")
+    assert bench.kernel_source_hash([str(a)]) == h0
+    a.write_text("// a kernel\nint f(int x) {\n  return x + 2;  /* one */\n}\n")
+    assert bench.kernel_source_hash([str(a)]) != h0
