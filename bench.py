@@ -327,6 +327,7 @@ def measure_config(ci: int, args, stream, dev, flush, refs):
         outs = [L["out"].cpu().numpy().astype(np.float64) for L in layers]
         err, rel = parity(outs, refs) if refs is not None else (None, None)
         res[name] = {"pages_per_split": int(ps), "step_us": round(float(t.mean()) * 1e6, 2),
+                     "step_median_us": round(float(np.median(t)) * 1e6, 2),
                      "step_min_us": round(float(t.min()) * 1e6, 2),
                      "kv_gbps": round(kv / float(t.mean()) / 1e9, 1),
                      "max_abs_vs_oracle": err, "max_rel_vs_oracle": rel}
@@ -337,7 +338,8 @@ def measure_config(ci: int, args, stream, dev, flush, refs):
     line = {
         "workload": states[0][0].recipe.get("workload", ""), "layers": nl, "batch": B,
         "launch": name, "pages_per_split": res[name]["pages_per_split"],
-        "step_us": round(t_best * 1e6, 2), "per_layer_us": round(t_best / nl * 1e6, 2),
+        "step_us": round(t_best * 1e6, 2), "step_median_us": res[name]["step_median_us"],
+        "step_min_us": res[name]["step_min_us"], "per_layer_us": round(t_best / nl * 1e6, 2),
         "kv_bytes": int(kv), "kv_gbps": round(kv / t_best / 1e9, 1),
         "hbm_peak_frac": round(kv / t_best / 1e9 / HBM_PEAK_GBPS, 4),
         "seq_per_s_per_layer": round(int(np.count_nonzero(w0.seq_lens)) * nl / t_best, 1),
@@ -909,6 +911,8 @@ def main() -> int:
     configs["4"] = {
         "workload": W.WORKLOADS[4], "layers": 1, "batch": B, "launch": "grid, default plan "
         "(pages_per_split=0)", "pages_per_split": ps, "step_us": round(mean_step * 1e6, 2),
+        "step_median_us": round(float(np.median(t_step)) * 1e6, 2),
+        "step_min_us": round(float(t_step.min()) * 1e6, 2),
         "per_layer_us": round(mean_step * 1e6, 2), "kv_bytes": int(kv),
         "kv_gbps": round(value, 1), "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "seq_per_s_per_layer": round(B / mean_step, 1), "max_abs_vs_oracle": err4,
