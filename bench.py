@@ -58,6 +58,11 @@ _DEVICE = ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_kernel.h", "pa_host.h")
 KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode.hip",)]
 KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_q8.hip",)]
 BALANCED_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_balanced.hip",)]
+STREAM_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_measure.hip",)]
+# (wavefronts per KV head, LDS ring slots) of the decode kernels on the 256 x 2048
+# batch: BF16 and INT8 pages one wavefront per KV head and two slots; INT4 pages
+# two wavefronts per KV head (one 128-page split per sequence) and three slots
+STREAM_SHAPES = {"bf16": (1, 2), "int8": (1, 2), "int4": (2, 3)}
 
 
 def log(msg: str) -> None:
@@ -84,7 +89,8 @@ def source_hashes() -> dict:
     summary can tell which sources it describes."""
     return {"grid_bf16": kernel_source_hash(KERNEL_SOURCES),
             "grid_quantised": kernel_source_hash(KERNEL_SOURCES_Q8),
-            "balanced": kernel_source_hash(BALANCED_SOURCES)}
+            "balanced": kernel_source_hash(BALANCED_SOURCES),
+            "page_stream": kernel_source_hash(STREAM_SOURCES)}
 
 
 def measured_traffic(path: str = TRAFFIC_FILE, sources=None):
@@ -145,6 +151,18 @@ def config_layers(ci: int, placement: str = "random"):
         return [W.make_workload(3, layer=layer, placement=placement, append=True)
                 for layer in range(W.NUM_LAYERS_W3)]
     return [W.make_workload(ci, placement=placement, append=True)]
+
+
+def page_stream_entry(fmt: str, nbytes: int, t_stream, t_step) -> dict:
+    """One page format's stream time beside its fused step's (both medians)."""
+    import numpy as np
+    wph, ring = STREAM_SHAPES[fmt]
+    us, step_us = float(np.median(t_stream)) * 1e6, float(np.median(t_step)) * 1e6
+    return {"waves_per_head": wph, "ring": ring, "us": round(us, 2),
+            "gbps": round(nbytes / us / 1e3, 1),
+            "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "step_median_us": round(step_us, 2),
+            "step_over_stream": round(step_us / us, 4)}
 
 
 def prepare_states(configs, placement: str, headline=None):
@@ -556,6 +574,11 @@ def main() -> int:
                     help="instead of the bench line: time the fused step of every workload "
                          "(1-6; 6 is the truncated reading of workload 5's Zipf lengths), BF16, "
                          "INT8 and INT4 pages, under every launch; one JSON line per case")
+    ap.add_argument("--page-stream", action="store_true",
+                    help="instead of the bench line: the decode kernels' page reads alone "
+                         "(pa_page_stream) on batch 256 x 2048 for every page format, "
+                         "wavefronts per KV head and ring depth, beside each format's decode "
+                         "kernel, interleaved, cold caches; one JSON line per case")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -575,6 +598,8 @@ def main() -> int:
         return run_sweep(args)
     if args.placement_probe:
         return run_placement_probe(args)
+    if args.page_stream:
+        return run_page_stream(args)
     if args.only_config:
         if args.only_config not in CONFIGS:
             print("--only-config takes 1..5", file=sys.stderr)
@@ -759,7 +784,16 @@ def main() -> int:
         pre_step()
         q8_step()
     t_q8 = timed(q8_step, K)
-    log(f"{K} INT8-page steps done")
+    # the same pages read by the decode kernel's loads alone (no arithmetic)
+    ps_sink = torch.empty((B, 16), dtype=torch.int32, device=dev)
+
+    def page_stream_fn(kp, vp, sp, fmt):
+        wph, ring = STREAM_SHAPES[fmt]
+        return lambda: pa.page_stream(kp, vp, sp, bt, lens, wph, ring, sink=ps_sink, stream=stream)
+    q8_stream = page_stream_fn(q8_k, q8_v, q8_s, "int8")
+    q8_stream()
+    t_q8_stream = timed(q8_stream, K)
+    log(f"{K} INT8-page steps and page streams done")
     del q8_k, q8_v, q8_s
 
     # pass F: the same over INT4 pages (quantised on the GPU as for pass E)
@@ -780,7 +814,10 @@ def main() -> int:
         pre_step()
         q4_step()
     t_q4 = timed(q4_step, K)
-    log(f"{K} INT4-page steps done")
+    q4_stream = page_stream_fn(q4_k, q4_v, q4_s, "int4")
+    q4_stream()
+    t_q4_stream = timed(q4_stream, K)
+    log(f"{K} INT4-page steps and page streams done")
     del q4_k, q4_v, q4_s, ws4
 
     # diagnostic: the same step with the pages in identity order (each
@@ -797,6 +834,10 @@ def main() -> int:
     identity_step()
     t_identity = timed(identity_step, K)
     del k_id, v_id
+
+    bf_stream = page_stream_fn(k_pool, v_pool, None, "bf16")
+    bf_stream()
+    t_bf_stream = timed(bf_stream, K)
 
     # what a plain streaming read of 1 GiB achieves on this device
     sink = torch.zeros(65536, dtype=torch.int32, device=dev)
@@ -856,6 +897,15 @@ def main() -> int:
             "gbps": round(read_gbps, 1),
             "frac_of_peak": round(read_gbps / HBM_PEAK_GBPS, 4),
             "step_value_frac_of_achievable": round(value / read_gbps, 4),
+        },
+        "page_stream": {
+            "kernel": "pa_page_stream: each format's pages requested with the decode kernel's "
+                      "own loads, ring and waits and read back from LDS, no attention "
+                      "arithmetic (medians of the timed launches, cold caches)",
+            **{fmt: page_stream_entry(fmt, by_b, t_s, t_k)
+               for fmt, by_b, t_s, t_k in (("bf16", kv, t_bf_stream, t_step),
+                                           ("int8", by_q8, t_q8_stream, t_q8),
+                                           ("int4", by_q4, t_q4_stream, t_q4))},
         },
         "identity_placement_step_us": round(float(t_identity.mean()) * 1e6, 2),
         "int8_pages": {
@@ -1026,6 +1076,83 @@ def run_placement_probe(args) -> int:
                           "decode_us_min": round(float(np.min(times[sch])), 2),
                           "kv_gbps": round(kv / t / 1e3, 1), "steps": args.steps,
                           "same_output_as_identity": bool(np.array_equal(out, ref))}), flush=True)
+    return 0
+
+
+def run_page_stream(args) -> int:
+    """pa_page_stream on the 256 x 2048 cache for every page format, wavefronts per
+    KV head and ring depth, beside each format's decode kernel; interleaved,
+    cold caches; one JSON line per case."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from paged_kv_decode_07_amd import accounting as A
+    from paged_kv_decode_07_amd import binding as pa
+
+    print(json.dumps({"kernel_sources": source_hashes()}), flush=True)
+    w = W.make_workload(4, append=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(2**28, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int32, device=dev)
+    B, npg = w.batch, w.num_pages
+    kp = torch.from_numpy(w.k_pool.view(np.int16)).to(dev)
+    vp = torch.from_numpy(w.v_pool.view(np.int16)).to(dev)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    ident = torch.arange(npg, dtype=torch.int32, device=dev)
+    pools = {"bf16": (kp, vp, None)}
+    for fmt, new, fill in (("int8", pa.new_q8_pools, pa.fill_kv_q8),
+                           ("int4", pa.new_q4_pools, pa.fill_kv_q4)):
+        kc, vc, sc = new(npg, device=dev)
+        fill(kp.view(npg * 16, 8, 64), vp.view(npg * 16, 8, 64), ident, 0, kc, vc, sc,
+             stream=stream)
+        pools[fmt] = (kc, vc, sc)
+    nbytes = {"bf16": A.step_bytes(w.seq_lens)["kv"], "int8": A.step_bytes_q8(w.seq_lens)["kv"],
+              "int4": A.step_bytes_q4(w.seq_lens)["kv"]}
+    sink = torch.empty((B, 16), dtype=torch.int32, device=dev)
+    out = torch.empty((B, 32, 64), dtype=torch.float32, device=dev)
+    cases = {}
+    for fmt, (kc, vc, sc) in pools.items():
+        if fmt == "bf16":
+            cases[(fmt, "decode kernel", 0, 0)] = lambda: pa.decode_attention(
+                q, kp, vp, bt, lens, w.max_seq_len, scale=w.scale, out=out, stream=stream)
+        else:
+            cases[(fmt, "decode kernel", 0, 0)] = (
+                lambda kc=kc, vc=vc, sc=sc, nb=8 if fmt == "int8" else 4: pa.decode_attention_q8(
+                    q, kc, vc, sc, bt, lens, w.max_seq_len, scale=w.scale, out=out,
+                    stream=stream, nbits=nb))
+        for wph in (1, 2):
+            for ring in (1, 2, 3):
+                if (fmt, wph, ring) == ("bf16", 2, 3):
+                    continue                      # 192 KiB of LDS ring
+                cases[(fmt, "page stream", wph, ring)] = (
+                    lambda kc=kc, vc=vc, sc=sc, wph=wph, ring=ring: pa.page_stream(
+                        kc, vc, sc, bt, lens, wph, ring, sink=sink, stream=stream))
+    times = {c: [] for c in cases}
+    for it in range(args.warmup + args.steps):
+        for c, fn in cases.items():               # interleaved: drift hits every case alike
+            torch.amax(flush_buf, dim=None, out=flush_out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                times[c].append(e0.elapsed_time(e1) * 1e3)
+    for (fmt, what, wph, ring), t in times.items():
+        med = float(np.median(t))
+        line = {"format": fmt, "case": what, "us_median": round(med, 2),
+                "us_min": round(float(np.min(t)), 2), "gbps": round(nbytes[fmt] / med / 1e3, 1),
+                "frac_of_peak": round(nbytes[fmt] / med / 1e3 / HBM_PEAK_GBPS, 4),
+                "steps": args.steps}
+        if what == "page stream":
+            line.update({"waves_per_head": wph, "ring": ring,
+                         "decode_kernel_shape": STREAM_SHAPES[fmt] == (wph, ring)})
+        print(json.dumps(line), flush=True)
     return 0
 
 

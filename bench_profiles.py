@@ -1,6 +1,6 @@
 """Summaries under profiles/ from rocprofv3 runs of bench.py.
 
-Two modes, each reading rocprofv3 output directories (``-f csv -d DIR``):
+Modes (the first two read rocprofv3 output directories, ``-f csv -d DIR``):
 
   python bench_profiles.py headline --line FILE --trace DIR --fetch DIR --write DIR [--util DIR]
       runs of ``bench.py --no-cpu-baseline --configs ''`` (the batch 256 x 2048
@@ -18,9 +18,11 @@ Two modes, each reading rocprofv3 output directories (``-f csv -d DIR``):
 
   python bench_profiles.py sweep --json FILE --steps K --warmup W
   python bench_profiles.py placement --json FILE --steps K --warmup W
-      the output of ``bench.py --sweep`` / ``--placement-probe`` as tables
-      (profiles/decode_step_sweep_workloads_1_6.md,
-      profiles/decode_kernel_placement_b256_l2048.md).
+  python bench_profiles.py stream --json FILE --steps K --warmup W
+      the output of ``bench.py --sweep`` / ``--placement-probe`` / ``--page-stream``
+      as tables (profiles/decode_step_sweep_workloads_1_6.md,
+      profiles/decode_kernel_placement_b256_l2048.md,
+      profiles/page_stream_b256_l2048.md).
 
 Every mode refuses a run whose kernel sources are not the current ones.
 
@@ -571,6 +573,55 @@ def placement(a) -> int:
     return 0
 
 
+def stream(a) -> int:
+    rows = _lines(a.json)
+    check_sources(rows[0].get("kernel_sources", {}), ("grid_bf16", "grid_quantised", "page_stream"))
+    src = rows[0]["kernel_sources"]
+    rows = [r for r in rows if "case" in r]
+    out = ["# Page stream: each format's page reads alone, beside its decode kernel, batch 256 x 2048\n",
+           "Commands (MI355X, ROCm 7.2, from the repository root):\n",
+           f"```\npython -u bench.py --page-stream --steps {a.steps} --warmup {a.warmup} > "
+           f"{_rel(a.json)}\npython bench_profiles.py stream --json {_rel(a.json)} --steps "
+           f"{a.steps} --warmup {a.warmup}\n```\n",
+           "Workload 4 without the append (256 sequences of 2,048 tokens at random pool slots). "
+           "`decode kernel` is `pa_decode_attention[_q8|_q4]` with the library's default plan "
+           "(one 128-page split per sequence). `page stream` is `pa_page_stream`: the same pages "
+           "requested with the decode kernel's direct-to-LDS loads for that format (same "
+           "lane-to-address maps, non-temporal policy and ring waits), each landed page read back "
+           "from LDS and folded, nothing else computed, with h wavefronts per KV head and an LDS "
+           "ring of r slots per wavefront; `*` marks the decode kernel's own (h, r). All cases "
+           f"run interleaved, caches flushed before every launch, {a.steps} timed rounds after "
+           f"{a.warmup} warm-up rounds; median and minimum of the event-timed launches. Bytes: "
+           "the K/V (and scale) bytes of the batch, 1 GiB BF16, 544 MiB INT8, 288 MiB INT4. "
+           f"Kernel sources: decode `{src['grid_bf16']}` (BF16), `{src['grid_quantised']}` (INT8, "
+           f"INT4); page stream `{src['page_stream']}`.\n",
+           "| format | case | h | r | median µs | min µs | GB/s (median) | % of 8 TB/s |\n"
+           "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        own = "*" if r.get("decode_kernel_shape") else ""
+        h = r.get("waves_per_head", "")
+        rr = f"{r['ring']}{own}" if "ring" in r else ""
+        out.append(f"| {r['format']} | {r['case']} | {h} | {rr} | {r['us_median']:.2f} | "
+                   f"{r['us_min']:.2f} | {r['gbps']:,.1f} | {100 * r['frac_of_peak']:.1f} |")
+    out.append("\nEach decode kernel beside the stream of its own shape and the fastest stream:\n")
+    out.append("| format | decode µs | own stream µs | decode / own stream | fastest stream (h, r) µs "
+               "| decode / fastest |\n|---|---|---|---|---|---|")
+    for fmt in ("bf16", "int8", "int4"):
+        dec = [r for r in rows if r["format"] == fmt and r["case"] == "decode kernel"]
+        st = [r for r in rows if r["format"] == fmt and r["case"] == "page stream"]
+        own = [r for r in st if r.get("decode_kernel_shape")]
+        if not dec or not own:
+            continue
+        fast = min(st, key=lambda r: r["us_median"])
+        d, o = dec[0]["us_median"], own[0]["us_median"]
+        out.append(f"| {fmt} | {d:.2f} | {o:.2f} | {d / o:.3f} | ({fast['waves_per_head']}, "
+                   f"{fast['ring']}) {fast['us_median']:.2f} | {d / fast['us_median']:.3f} |")
+    text = "\n".join(out) + "\n"
+    write_keeping_notes(os.path.join(PROFILES, "page_stream_b256_l2048.md"), text)
+    print(text)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -587,14 +638,15 @@ def main(argv=None) -> int:
         p.add_argument("--fetch", required=True)
         p.add_argument("--write", required=True)
         p.add_argument("--util", default=None)
-    for name in ("sweep", "placement"):
+    for name, flag in (("sweep", "sweep"), ("placement", "placement-probe"),
+                       ("stream", "page-stream")):
         p = sub.add_parser(name)
-        p.add_argument("--json", required=True, help=f"the output of bench.py --{name}"
-                       + ("" if name == "sweep" else "-probe"))
+        p.add_argument("--json", required=True, help=f"the output of bench.py --{flag}")
         p.add_argument("--steps", type=int, required=True)
         p.add_argument("--warmup", type=int, required=True)
     a = ap.parse_args(argv)
-    return {"headline": headline, "config": config, "sweep": sweep, "placement": placement}[a.mode](a)
+    return {"headline": headline, "config": config, "sweep": sweep, "placement": placement,
+            "stream": stream}[a.mode](a)
 
 
 if __name__ == "__main__":

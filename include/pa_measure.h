@@ -1,18 +1,21 @@
 /*
- * pa_measure.h -- measurement helper of the paged GQA decode library (C ABI).
+ * pa_measure.h -- measurement helpers of the paged GQA decode library (C ABI).
  *
  * The decode path is bound by HBM bandwidth ("6 Hours of YouTube and 85
  * handtyped pages of notes on LLM Inference - Start here", samir-vllm README:
  * decode is memory-bound; "Building an LLM inference engine from scratch",
  * section 5.1: the KV cache grows with every token).  Beside the device's
  * published peak, a benchmark reports what a plain streaming read achieves on
- * the same device: this entry point is that read.
+ * the same device (pa_stream_read), and what the decode kernels' own page
+ * reads achieve when nothing else is computed (pa_page_stream).
  */
 #ifndef PA_MEASURE_H
 #define PA_MEASURE_H
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include "pa_decode.h"
 
 #ifdef __cplusplus
 extern "C" {
@@ -30,6 +33,42 @@ extern "C" {
  * PA_ERR_ALIGN, PA_ERR_VALUE, PA_ERR_DEVICE, PA_ERR_LAUNCH as in pa_decode.h).
  */
 int pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t groups, void* stream);
+
+/*
+ * Page stream: the page reads of the decode kernels without their
+ * arithmetic, so that a benchmark can set a kernel's time beside the time of
+ * its own access pattern.  The pages are those the decode attention reads
+ * through the block tables ("6 Hours of YouTube ...", samir-vllm README,
+ * features completed so far: a page map and an attention length per
+ * sequence), in the pools of pa_decode.h (page_format 0, BF16), pa_decode_q8.h
+ * (1, INT8 codes and scales) or pa_decode_q4.h (2, INT4 codes and scales).
+ *
+ * One work-group per sequence b < batch; for each of the 8 KV heads,
+ * waves_per_head wavefronts (1 or 2: the first and the second half of the
+ * pages) stream the head's blocks of the ceil(seq_lens[b] / 16) pages named
+ * by block_tables[b] through a ring of `ring` LDS slots per wavefront (1..3),
+ * with the decode kernel's direct-to-LDS loads, cache policy and waits for
+ * that format.  Each landed page is read back from LDS and every 32-bit word
+ * of the head's blocks (K, V and, for codes, the head's scale line) is folded
+ * by XOR into one word per wavefront, stored at
+ * sink[b * 8 * waves_per_head + head * waves_per_head + half].
+ * A length outside [0, 16 * max_blocks_per_seq] streams nothing (fold 0); a
+ * block-table entry outside [0, num_pages) reads page 0.
+ *
+ * shape: as for the decode entry points, max_blocks_per_seq <= 256.  Pools:
+ * device, 16-byte aligned (kv_scales may be NULL for BF16 pages);
+ * block_tables, seq_lens: device int32 [batch][max_blocks_per_seq], [batch];
+ * sink: device, batch * 8 * waves_per_head uint32 words.  The rings of a
+ * work-group (ring x 8 x waves_per_head slots of 4 KiB for BF16, 2304 B for
+ * INT8, 1280 B for INT4) must fit the 160 KiB of LDS of a CU, else
+ * PA_ERR_VALUE (BF16 pages with 2 wavefronts per head: ring <= 2).
+ * Enqueued on `stream`; returns PA_OK or a negative pa_status (PA_ERR_NULL,
+ * PA_ERR_SHAPE, PA_ERR_ALIGN, PA_ERR_VALUE, PA_ERR_LAUNCH as in pa_decode.h).
+ */
+int pa_page_stream(const pa_shape* shape, int32_t batch, const void* k_pool, const void* v_pool,
+                   const void* kv_scales, int32_t page_format, const int32_t* block_tables,
+                   const int32_t* seq_lens, int32_t waves_per_head, int32_t ring, uint32_t* sink,
+                   void* stream);
 
 #ifdef __cplusplus
 }

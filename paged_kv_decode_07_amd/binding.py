@@ -42,7 +42,7 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_append_decode_attention_q4", "pa_append_decode_attention_rope_q4",
            "pa_decode_plan_lengths_q4", "pa_append_decode_attention_worklist_q4",
            # include/pa_measure.h
-           "pa_stream_read",
+           "pa_stream_read", "pa_page_stream",
            # include/pa_kvpool.h
            "pa_kvpool_create", "pa_kvpool_destroy", "pa_kvpool_credit", "pa_kvpool_submit",
            "pa_kvpool_admit", "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
@@ -123,6 +123,7 @@ def load_library(path: str | None = None):
         lib.pa_decode_balanced.argtypes = [SP, I32, P, P, P, RP, P, P, P, I32, P, P, I32,
                                            ctypes.c_float, P, I32, P, I64_, I32, P]
         lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
+        lib.pa_page_stream.argtypes = [SP, I32, P, P, P, I32, P, P, I32, I32, P, P]
         lib.pa_decode_worklist.argtypes = [SP, I32, P, I32, I32, I32, I32, P, I32,
                                            ctypes.POINTER(I32), ctypes.POINTER(I32),
                                            ctypes.POINTER(I32)]
@@ -838,6 +839,42 @@ def stream_read(buf, sink, groups: int = 0, stream=None) -> None:
         raise ValueError("stream_read: sink smaller than the number of work-groups")
     _check(load_library().pa_stream_read(_ptr(buf), nbytes, _ptr(sink), int(groups),
                                          _stream_ptr(stream)), "pa_stream_read")
+
+
+def page_stream(k_pool, v_pool, kv_scales, block_tables, seq_lens, waves_per_head: int = 1,
+                ring: int = 2, sink=None, stream=None) -> torch.Tensor:
+    """The decode kernels' page reads without their arithmetic (``include/pa_measure.h``).
+
+    The page format follows the pools: BF16 ``[pages][16][8][64]`` (``kv_scales``
+    None), INT8 ``[pages][8][16][64]`` or INT4 ``[pages][8][16][32]`` codes with
+    their scales.  Returns ``sink``: int32 ``[B][8 * waves_per_head]``, the XOR of
+    every word each wavefront read."""
+    B = int(seq_lens.shape[0])
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    _same_batch(B, block_tables=block_tables)
+    if kv_scales is None:
+        _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
+        _same_pools(k_pool, v_pool)
+        num_pages, fmt = int(k_pool.shape[0]), 0
+    else:
+        nbits = 8 if k_pool.dtype == torch.int8 else 4     # _q8_pools refuses anything else
+        num_pages, fmt = _q8_pools(k_pool, v_pool, kv_scales, nbits), 1 if nbits == 8 else 2
+    if waves_per_head not in (1, 2) or ring not in (1, 2, 3):
+        raise ValueError("page_stream: waves_per_head must be 1 or 2 and ring 1, 2 or 3")
+    words = B * HKV * waves_per_head
+    if sink is None:
+        sink = torch.empty((B, HKV * waves_per_head), dtype=torch.int32, device=seq_lens.device)
+    elif sink.dtype != torch.int32 or not _is_device(sink) or not sink.is_contiguous() or \
+            sink.numel() < words:
+        raise ValueError("page_stream: sink must be a contiguous int32 device tensor of "
+                         "batch x 8 x waves_per_head words")
+    shape = make_shape(num_pages, int(block_tables.shape[1]))
+    _check(load_library().pa_page_stream(
+        ctypes.byref(shape), B, _ptr(k_pool), _ptr(v_pool),
+        _ptr(kv_scales) if kv_scales is not None else None, fmt, _ptr(block_tables),
+        _ptr(seq_lens), int(waves_per_head), int(ring), _ptr(sink), _stream_ptr(stream)),
+        "pa_page_stream")
+    return sink
 
 
 class KVPool:

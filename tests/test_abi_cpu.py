@@ -264,6 +264,29 @@ def test_stream_read_argument_errors(lib):
     assert lib.pa_stream_read(F, 1024, sink, 65537, None) == -6
 
 
+def test_page_stream_argument_errors(lib):
+    F, T, sink = FAKE, ctypes.c_void_p(0x30000), ctypes.c_void_p(0x20000)
+    good = pa.make_shape(64, 8)
+
+    def call(shape=good, batch=2, k=F, v=F, s=F, fmt=0, bt=T, lens=T, wph=1, ring=2, out=sink):
+        return lib.pa_page_stream(ctypes.byref(shape) if shape is not None else None, batch, k, v,
+                                  s, fmt, bt, lens, wph, ring, out, None)
+    assert call(batch=0) == 0                                  # nothing to stream, no launch
+    assert call(shape=None) == -1
+    assert call(shape=pa.make_shape(64, 8, head_dim=128)) == -2
+    assert call(shape=pa.make_shape(64, 257)) == -6            # beyond the 256-page window
+    for bad in (dict(fmt=3), dict(fmt=-1), dict(wph=0), dict(wph=3), dict(ring=0), dict(ring=4),
+                dict(batch=-1)):
+        assert call(**bad) == -6, bad
+    assert call(fmt=0, wph=2, ring=3) == -6                    # 192 KiB of LDS ring
+    for null in (dict(k=None), dict(v=None), dict(bt=None), dict(lens=None), dict(out=None),
+                 dict(fmt=1, s=None), dict(fmt=2, s=None)):
+        assert call(**null) == -1, null
+    assert call(k=ctypes.c_void_p(0x10008)) == -3
+    assert call(fmt=1, s=ctypes.c_void_p(0x10004)) == -3
+    assert call(lens=ctypes.c_void_p(0x30002)) == -3
+
+
 def test_worklist_covers_every_item_once_largest_first():
     import numpy as np
     lens = np.array([0, 1, 2048, 17, 300, 2049, 16, 33, 1000], np.int32)    # 2049: beyond the bound

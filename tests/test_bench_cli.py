@@ -169,3 +169,34 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path):
     assert bench.kernel_source_hash([str(a)]) == h0
     a.write_text("// a kernel\nint f(int x) {\n  return x + 2;  /* one */\n}\n")
     assert bench.kernel_source_hash([str(a)]) != h0
+
+
+def test_page_stream_summary_sets_each_kernel_beside_its_own_stream(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    import bench_profiles as P
+    monkeypatch.setattr(P, "PROFILES", str(tmp_path))
+    rows = [{"kernel_sources": bench.source_hashes()}]
+    for fmt, dec, own, fast in (("bf16", 160.0, 158.0, 157.0), ("int8", 88.0, 86.0, 85.0),
+                                ("int4", 52.0, 50.0, 47.0)):
+        rows.append({"format": fmt, "case": "decode kernel", "us_median": dec, "us_min": dec - 1,
+                     "gbps": 1.0, "frac_of_peak": 0.5, "steps": 3})
+        wph, ring = bench.STREAM_SHAPES[fmt]
+        for (h, r), t in (((wph, ring), own), ((2, 2), fast)):
+            rows.append({"format": fmt, "case": "page stream", "us_median": t, "us_min": t - 1,
+                         "gbps": 1.0, "frac_of_peak": 0.5, "steps": 3, "waves_per_head": h,
+                         "ring": r, "decode_kernel_shape": (h, r) == (wph, ring)})
+    j = tmp_path / "stream.json"
+    j.write_text("\n".join(json.dumps(r) for r in rows) + "\n")
+    assert P.main(["stream", "--json", str(j), "--steps", "3", "--warmup", "1"]) == 0
+    text = (tmp_path / "page_stream_b256_l2048.md").read_text()
+    assert "| int4 | 52.00 | 50.00 | 1.040 | (2, 2) 47.00 | 1.106 |" in text
+    assert "| bf16 | 160.00 | 158.00 | 1.013 | (2, 2) 157.00 | 1.019 |" in text
+    rows[0] = {"kernel_sources": {**bench.source_hashes(), "page_stream": "0" * 16}}
+    j.write_text("\n".join(json.dumps(r) for r in rows) + "\n")
+    try:
+        P.main(["stream", "--json", str(j), "--steps", "3", "--warmup", "1"])
+    except SystemExit as e:
+        assert "run it again" in str(e)
+    else:
+        raise AssertionError("a page-stream run of other sources must be refused")
