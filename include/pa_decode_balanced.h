@@ -84,7 +84,8 @@ int pa_balance_plan(const pa_shape* shape, int32_t batch, const int32_t* seq_len
  * outputs and no append; one longer than max_seq_len, or with a used
  * block-table entry outside the pool, gets NaN outputs, and its new row is
  * written as pa_append_kv would (when its target page id lies in the pool).
- * Enqueues one kernel on `stream`.
+ * A pool of more than 2^28 pages returns PA_ERR_VALUE (a page id travels
+ * with its KV head in one 32-bit word).  Enqueues one kernel on `stream`.
  */
 int pa_decode_balanced(const pa_shape* shape, int32_t batch, const void* q,
                        const void* k_new, const void* v_new, const pa_rope* rope,

@@ -287,6 +287,14 @@ def test_page_stream_argument_errors(lib):
     assert call(lens=ctypes.c_void_p(0x30002)) == -3
 
 
+def test_balanced_launch_refuses_page_ids_beyond_28_bits(lib):
+    F = FAKE
+    shape = pa.make_shape((1 << 28) + 1, 128)      # checked before the plan and any launch
+    rc = lib.pa_decode_balanced(ctypes.byref(shape), 1, F, None, None, None, F, F, None, 0,
+                                F, F, 16, ctypes.c_float(0.125), F, 0, F, 1 << 20, 1, None)
+    assert rc == -6
+
+
 def test_worklist_covers_every_item_once_largest_first():
     import numpy as np
     lens = np.array([0, 1, 2048, 17, 300, 2049, 16, 33, 1000], np.int32)    # 2049: beyond the bound
