@@ -311,6 +311,32 @@ def pin_append_positions(ora):
     assert not np.array_equal(pre.k_pool, post.k_pool)
 
 
+def pin_fill_positions(ora):
+    """Filling tokens start .. start+T-1 of each sequence into a pool that holds
+    tokens 0 .. start-1 gives, byte for byte, the pool the generator builds
+    directly with tokens 0 .. start+T-1 (same placement).
+
+    Spans start at a page's first slot, end on its last, cross page boundaries,
+    fill one token, and reach the last slot of a 2,048-token context.
+    """
+    spans = [(0, 37), (15, 2), (16, 16), (0, 1), (2000, 48), (33, 300), (7, 9)]
+    lens = [s + t for s, t in spans]
+    q, k, v = _rand_case(114, lens)
+    pages = _pool_pages(lens, slack=5)
+    pre = W.pack_logical(q, [x[:s] for x, (s, _) in zip(k, spans)],
+                         [x[:s] for x, (s, _) in zip(v, spans)], pages, seed=24, capacity=lens)
+    post = W.pack_logical(q, k, v, pages, seed=24, capacity=lens)
+    assert np.array_equal(pre.block_tables, post.block_tables)
+    k_out, v_out = pre.k_pool, pre.v_pool
+    for b, (s, t) in enumerate(spans):
+        k_out, v_out = ora.fill_kv(k_out, v_out, k[b][s:s + t], v[b][s:s + t],
+                                   pre.block_tables[b], s)
+    assert np.array_equal(k_out, post.k_pool)
+    assert np.array_equal(v_out, post.v_pool)
+    # inputs untouched
+    assert not np.array_equal(pre.k_pool, post.k_pool)
+
+
 ALL_PINS = [
     pin_seq_len_one,
     pin_identical_values,
@@ -325,4 +351,5 @@ ALL_PINS = [
     pin_split_merge,
     pin_idle_slot,
     pin_append_positions,
+    pin_fill_positions,
 ]

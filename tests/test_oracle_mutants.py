@@ -39,6 +39,11 @@ MUTANTS = {
                            "physical = int(block_tables[b][pos % page_size])"),
     "append_k_gets_v": ("k_out[physical, slot] = k_new_bits[b]",
                         "k_out[physical, slot] = v_new_bits[b]"),
+    "fill_slot_off_by_one": ("t = start + j", "t = start + j + 1"),
+    "fill_page_modulo": ("physical = int(block_table_row[t // page_size])",
+                         "physical = int(block_table_row[t % page_size])"),
+    "fill_v_gets_k": ("v_out[physical, t % page_size] = v_rows_bits[j]",
+                      "v_out[physical, t % page_size] = k_rows_bits[j]"),
 }
 
 
