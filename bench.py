@@ -60,9 +60,10 @@ KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_q8.hi
 BALANCED_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_balanced.hip",)]
 STREAM_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_measure.hip",)]
 # (wavefronts per KV head, LDS ring slots) of the decode kernels on the 256 x 2048
-# batch: BF16 and INT8 pages one wavefront per KV head and two slots; INT4 pages
-# two wavefronts per KV head (one 128-page split per sequence) and three slots
-STREAM_SHAPES = {"bf16": (1, 2), "int8": (1, 2), "int4": (2, 3)}
+# batch: BF16 pages one wavefront per KV head and one slot, INT8 pages one and
+# two; INT4 pages two wavefronts per KV head (one 128-page split per sequence)
+# and three slots
+STREAM_SHAPES = {"bf16": (1, 1), "int8": (1, 2), "int4": (2, 3)}
 
 
 def log(msg: str) -> None:

@@ -541,9 +541,18 @@ int decode_impl(const pa_shape* shape, int32_t batch, const void* q, const void*
   a.batch = batch;
   // a batch that fits the compute units merges with its partials requested up front
   int cu = 0;
-  const bool merge_preload = current_cu_count(&cu) == PA_OK && batch <= cu;
+  const bool have_cu = current_cu_count(&cu) == PA_OK;
+  const bool merge_preload = have_cu && batch <= cu;
+  // One slot per wavefront unless the launch leaves CUs idle, or every
+  // work-group runs at once on its own CU with a short split: a busy CU then
+  // needs more pages in flight, or the start of each short stream is
+  // exposed, and a second slot per wavefront covers it (page order and
+  // arithmetic are the same either way).
+  const int64_t groups = work ? (int64_t)num_work : (int64_t)batch * ns;
+  const bool two_slots =
+      have_cu && groups <= cu && (groups < cu || ps < pa_host::kOneSlotMinPages);
   const hipError_t e = pa::launch_decode<pa::kFmtBF16>(a, batch, out_dtype == PA_OUT_BF16, fused,
-                                                rope != nullptr, merge_preload, false,
+                                                rope != nullptr, merge_preload, false, two_slots,
                                                 (hipStream_t)stream,
                                                 (hipEvent_t)event_before_main,
                                                 (hipEvent_t)event_after_main);

@@ -81,7 +81,7 @@ __device__ __forceinline__ void lds_store4u(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE>
+template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE, int RING = 0>
 __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedArgs a) {
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   constexpr bool Q8 = FMT == kFmtINT8;
@@ -94,7 +94,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
   const int G = lane >> 4;
   const int n = lane & 15;
 
-  __shared__ __attribute__((aligned(16))) char ring[F::kRingDepth][kWaves][F::kSlot];
+  // RING: slots per wavefront for this launch (0: the format's default)
+  constexpr int kDepth = RING > 0 ? RING : F::kRingDepth;
+  constexpr bool kPairs = F::kPairs && kDepth >= 3;
+  __shared__ __attribute__((aligned(16))) char ring[kDepth][kWaves][F::kSlot];
   // per segment: [q rows of its 4 heads (512 B) | new K row, new V row (256 B)
   // | RoPE cos, sin rows (256 B)]; after its pages, its staged output
   __shared__ __attribute__((aligned(16))) char segblk[kWaves][8][kBalSegBlk];
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
     }
   };
 #pragma unroll
-  for (int r = 0; r < F::kRingDepth; ++r)
+  for (int r = 0; r < kDepth; ++r)
     if (r < U) fetch(r, r);
 
   // LDS read addresses of this lane in slot 0 (as in the grid kernel)
@@ -423,36 +426,36 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
     };
     auto step = [&](int i, auto masked) {
       constexpr bool MASK = decltype(masked)::value;
-      const int slot = u % F::kRingDepth;
+      const int slot = u % kDepth;
       const uint32_t off = slot * kRingSlotBytes;
-      wait_page<F::kLoads, F::kRingDepth>(min(U - 1 - u, F::kRingDepth - 1));
+      wait_page<F::kLoads, kDepth>(min(U - 1 - u, kDepth - 1));
       if (MASK && app) park(slot0 + off);
       PageT cur;
       lds_read(cur, off);
       lds_page_ready(cur);
-      if (u + F::kRingDepth < U) fetch(u + F::kRingDepth, slot);
+      if (u + kDepth < U) fetch(u + kDepth, slot);
       consume_page<FMT, MASK>(st, cur, qlo, qhi, pc, lane, MASK ? tail_valid : kPage);
       ++u;
       (void)i;
     };
     auto step2 = [&]() {
-      const int slot_a = u % F::kRingDepth;
-      const int slot_b = (u + 1) % F::kRingDepth;
-      wait_page<F::kLoads, F::kRingDepth>(min(U - 2 - u, F::kRingDepth - 2));
+      const int slot_a = u % kDepth;
+      const int slot_b = (u + 1) % kDepth;
+      wait_page<F::kLoads, kDepth>(min(U - 2 - u, kDepth - 2));
       PageT pa_, pb_;
       lds_read(pa_, slot_a * kRingSlotBytes);
       lds_read(pb_, slot_b * kRingSlotBytes);
       lds_page_ready(pa_);
       lds_page_ready(pb_);
-      if (u + F::kRingDepth < U) fetch(u + F::kRingDepth, slot_a);
-      if (u + 1 + F::kRingDepth < U) fetch(u + 1 + F::kRingDepth, slot_b);
+      if (u + kDepth < U) fetch(u + kDepth, slot_a);
+      if (u + 1 + kDepth < U) fetch(u + 1 + kDepth, slot_b);
       consume_pages2<FMT>(st, pa_, pb_, qlo, qhi, pc, lane);
       u += 2;
     };
     {
       int i = 0;
       const int full = ends ? npg - 1 : npg;     // pages before a masked last one
-      if constexpr (F::kPairs)
+      if constexpr (kPairs)
         for (; i + 1 < full; i += 2) step2();
       for (; i < full; ++i) step(i, std::false_type{});
       if (ends) step(i, std::true_type{});
@@ -592,18 +595,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
   }
 }
 
+template <int FMT, int RING>
+void launch_balanced_ring(const BalancedArgs& a, dim3 grid, bool out_bf16, bool fused, bool rope,
+                          hipStream_t st) {
+  const dim3 block(kThreads);
+  if (out_bf16) {
+    if (rope) hipLaunchKernelGGL((decode_balanced_kernel<FMT, true, true, true, RING>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_balanced_kernel<FMT, true, true, false, RING>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_balanced_kernel<FMT, true, false, false, RING>), grid, block, 0, st, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((decode_balanced_kernel<FMT, false, true, true, RING>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_balanced_kernel<FMT, false, true, false, RING>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_balanced_kernel<FMT, false, false, false, RING>), grid, block, 0, st, a);
+  }
+}
+
+// two_slots (BF16 pages only): a two-slot ring instead of the default one slot.
 template <int FMT>
 hipError_t launch_balanced(const BalancedArgs& a, int groups, bool out_bf16, bool fused, bool rope,
-                           hipStream_t st) {
-  const dim3 grid(groups), block(kThreads);
-  if (out_bf16) {
-    if (rope) hipLaunchKernelGGL((decode_balanced_kernel<FMT, true, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_balanced_kernel<FMT, true, true, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_balanced_kernel<FMT, true, false, false>), grid, block, 0, st, a);
+                           bool two_slots, hipStream_t st) {
+  const dim3 grid(groups);
+  if constexpr (FMT == kFmtBF16) {
+    if (two_slots) launch_balanced_ring<FMT, 2>(a, grid, out_bf16, fused, rope, st);
+    else launch_balanced_ring<FMT, 0>(a, grid, out_bf16, fused, rope, st);
   } else {
-    if (rope) hipLaunchKernelGGL((decode_balanced_kernel<FMT, false, true, true>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_balanced_kernel<FMT, false, true, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_balanced_kernel<FMT, false, false, false>), grid, block, 0, st, a);
+    launch_balanced_ring<FMT, 0>(a, grid, out_bf16, fused, rope, st);
   }
   return hipGetLastError();
 }
@@ -869,8 +885,12 @@ PA_API int pa_decode_balanced(const pa_shape* shape, int32_t batch, const void* 
   a.batch = batch;
   const bool bf = out_dtype == PA_OUT_BF16;
   hipError_t e;
-  if (page_format == 1) e = pa::launch_balanced<pa::kFmtINT8>(a, groups, bf, fused, rope != nullptr, (hipStream_t)stream);
-  else if (page_format == 2) e = pa::launch_balanced<pa::kFmtINT4>(a, groups, bf, fused, rope != nullptr, (hipStream_t)stream);
-  else e = pa::launch_balanced<pa::kFmtBF16>(a, groups, bf, fused, rope != nullptr, (hipStream_t)stream);
+  // BF16 pages: two slots per wavefront when the plan leaves CUs idle (each
+  // busy CU then needs more pages in flight), else one
+  int cu = 0;
+  const bool two_slots = current_cu_count(&cu) == PA_OK && groups < cu;
+  if (page_format == 1) e = pa::launch_balanced<pa::kFmtINT8>(a, groups, bf, fused, rope != nullptr, false, (hipStream_t)stream);
+  else if (page_format == 2) e = pa::launch_balanced<pa::kFmtINT4>(a, groups, bf, fused, rope != nullptr, false, (hipStream_t)stream);
+  else e = pa::launch_balanced<pa::kFmtBF16>(a, groups, bf, fused, rope != nullptr, two_slots, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -13,7 +13,8 @@
 // gfx950's direct-to-LDS loads (every lane's 4 or 16 bytes land at lane*size
 // of the destination, without passing through VGPRs).  A slot is refilled as
 // soon as its page has been read into registers, so while a page is used the
-// next ring-depth pages are in flight.  A wavefront only ever reads its own
+// next ring-depth pages are in flight (BF16 pages: one slot, INT8: two,
+// INT4: three).  A wavefront only ever reads its own
 // slots, so explicit vmcnt waits are the only synchronisation.  The split's
 // block-table entries are preloaded into VGPRs and picked with v_readlane.
 // Every load instruction requests whole 128-byte lines (BF16: 8 token rows
@@ -140,7 +141,7 @@ struct PageFormat;
 #endif
 template <>
 struct PageFormat<kFmtBF16> {
-  static constexpr int kRingDepth = kRing;      // 2 slots of 4 KiB
+  static constexpr int kRingDepth = kRing;      // slots of 4 KiB (one)
   static constexpr int kSlot = 4096;            // [K | V] x 16 token rows x 128 B (swizzled pieces)
   static constexpr int kLoads = 4;              // direct-to-LDS loads per page
   static constexpr bool kPairs = PA_PAIR_STEPS && kRingDepth >= 3;
@@ -542,7 +543,7 @@ __device__ __forceinline__ void append_row_direct(const DecodeArgs& a, uint4 lo,
 // ring, and merge their running states through LDS at the end: the
 // occupancy of two work-groups per CU without split partials or a merge
 // launch.
-template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE = false, int WPH = 1>
+template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE = false, int WPH = 1, int RING = 0>
 __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeArgs a) {
   static_assert(WPH == 1 || WPH == 2, "one or two wavefronts per KV head");
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
@@ -683,7 +684,13 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
     return (unsigned)id < (unsigned)a.num_pages ? id : 0;   // a bad entry reads page 0 (outputs NaN)
   };
 
-  __shared__ __attribute__((aligned(16))) char ring[F::kRingDepth][kWaves * WPH][F::kSlot];
+  // RING: slots per wavefront for this launch (0: the format's default).  A
+  // one-slot ring still holds two slots of LDS, so that no more work-groups
+  // share a CU than with two (more would put more pages in flight per CU than
+  // its page stream runs fastest with).
+  constexpr int kDepth = RING > 0 ? RING : F::kRingDepth;
+  constexpr bool kPairs = PA_PAIR_STEPS && kDepth >= 3 && F::kPairs;
+  __shared__ __attribute__((aligned(16))) char ring[kDepth < 2 ? 2 : kDepth][kWaves * WPH][F::kSlot];
   const char* k_base = reinterpret_cast<const char*>(a.k_pool);
   const char* v_base = reinterpret_cast<const char*>(a.v_pool);
   const char* s_base = reinterpret_cast<const char*>(a.kv_scales);
@@ -790,14 +797,14 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   };
   auto step = [&](int i, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    const int slot = (i - q0) % F::kRingDepth;
+    const int slot = (i - q0) % kDepth;
     const uint32_t off = slot * kRingSlotBytes;
-    wait_page<F::kLoads, F::kRingDepth>(min(last - i, F::kRingDepth - 1));   // page i landed
+    wait_page<F::kLoads, kDepth>(min(last - i, kDepth - 1));   // page i landed
     if (MASK && app_here) park_new_row(slot0 + off);
     PageT cur;
     lds_read(cur, off);
     lds_page_ready(cur);
-    if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, slot);
+    if (i + kDepth <= last) fetch(i + kDepth, slot);
     consume_page<FMT, MASK>(st, cur, qlo, qhi, pc, lane, MASK ? tail_valid : kPage);
   };
   // pages i and i+1, both before the last page, in one pass, from ring slots
@@ -805,14 +812,14 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   // immediates); the ring keeps depth - 2 pages in flight while they are used
   auto step2 = [&](int i, auto slot_a, auto slot_b) {
     constexpr int SA = decltype(slot_a)::value, SB = decltype(slot_b)::value;
-    wait_page<F::kLoads, F::kRingDepth>(min(last - i - 1, F::kRingDepth - 2));   // page i+1 landed
+    wait_page<F::kLoads, kDepth>(min(last - i - 1, kDepth - 2));   // page i+1 landed
     PageT pa_, pb_;
     lds_page_issue<SA * kRingSlotBytes>(pa_, ka, va, sa);
     lds_page_issue<SB * kRingSlotBytes>(pb_, ka, va, sa);
     lds_page_ready(pa_);
     lds_page_ready(pb_);
-    if (i + F::kRingDepth <= last) fetch(i + F::kRingDepth, SA);
-    if (i + 1 + F::kRingDepth <= last) fetch(i + 1 + F::kRingDepth, SB);
+    if (i + kDepth <= last) fetch(i + kDepth, SA);
+    if (i + 1 + kDepth <= last) fetch(i + 1 + kDepth, SB);
     consume_pages2<FMT>(st, pa_, pb_, qlo, qhi, pc, lane);
   };
 
@@ -822,7 +829,7 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   // keeps it from waiting on the page stream at their later uses.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-  for (int r = 0; r < F::kRingDepth; ++r)
+  for (int r = 0; r < kDepth; ++r)
     if (q0 + r <= last) fetch(q0 + r, r);
 
   // while the first pages are in flight: the query operand and the new rows
@@ -872,10 +879,10 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   }
   if (has_pages) {
     int i = q0;
-    if constexpr (F::kPairs) {
+    if constexpr (kPairs) {
       // page i sits in slot (i - q0) % 3: the pairs cycle through slots
       // (0, 1), (2, 0), (1, 2)
-      static_assert(F::kRingDepth == 3, "the pair loop is unrolled for a ring of three slots");
+      static_assert(kDepth == 3, "the pair loop is unrolled for a ring of three slots");
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
       using S2 = std::integral_constant<int, 2>;
@@ -1021,35 +1028,40 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
 
 namespace pa {
 
-template <int FMT, int WPH>
+template <int FMT, int WPH, int RING = 0>
 inline void launch_decode_kernel(const DecodeArgs& a, dim3 grid, bool out_bf16, bool fused,
                                  bool rope, hipStream_t st) {
   const dim3 block(kThreads * WPH);
   if (out_bf16) {
-    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, true, true, true, WPH>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, true, true, false, WPH>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<FMT, true, false, false, WPH>), grid, block, 0, st, a);
+    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, true, true, true, WPH, RING>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, true, true, false, WPH, RING>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<FMT, true, false, false, WPH, RING>), grid, block, 0, st, a);
   } else {
-    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, false, true, true, WPH>), grid, block, 0, st, a);
-    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, false, true, false, WPH>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<FMT, false, false, false, WPH>), grid, block, 0, st, a);
+    if (rope) hipLaunchKernelGGL((decode_kernel<FMT, false, true, true, WPH, RING>), grid, block, 0, st, a);
+    else if (fused) hipLaunchKernelGGL((decode_kernel<FMT, false, true, false, WPH, RING>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<FMT, false, false, false, WPH, RING>), grid, block, 0, st, a);
   }
 }
 
 // Host: enqueue the decode kernel for page format FMT (plus the split merge
 // when the plan has more than one split).  two_waves (INT4 pages only): two
 // wavefronts per KV head, for plans whose grid fits the CUs at once (and
-// whose splits are long; the caller decides).  event_before/after (may be NULL) are recorded right around the
-// decode kernel.  Returns a hipError_t.
+// whose splits are long; the caller decides).  two_slots (BF16 pages only):
+// a two-slot ring instead of the default one slot (the caller decides).
+// event_before/after (may be NULL) are recorded right around the decode
+// kernel.  Returns a hipError_t.
 template <int FMT>
 inline hipError_t launch_decode(const DecodeArgs& a, int batch, bool out_bf16, bool fused,
-                                bool rope, bool merge_preload, bool two_waves, hipStream_t st,
-                                hipEvent_t event_before, hipEvent_t event_after) {
+                                bool rope, bool merge_preload, bool two_waves, bool two_slots,
+                                hipStream_t st, hipEvent_t event_before, hipEvent_t event_after) {
   const dim3 grid = a.work ? dim3(a.num_work) : dim3(a.num_splits * batch);
   hipError_t e = hipSuccess;
   if (event_before && (e = hipEventRecord(event_before, st)) != hipSuccess) return e;
   if constexpr (FMT == kFmtINT4) {
     if (two_waves) launch_decode_kernel<FMT, 2>(a, grid, out_bf16, fused, rope, st);
+    else launch_decode_kernel<FMT, 1>(a, grid, out_bf16, fused, rope, st);
+  } else if constexpr (FMT == kFmtBF16) {
+    if (two_slots) launch_decode_kernel<FMT, 1, 2>(a, grid, out_bf16, fused, rope, st);
     else launch_decode_kernel<FMT, 1>(a, grid, out_bf16, fused, rope, st);
   } else {
     launch_decode_kernel<FMT, 1>(a, grid, out_bf16, fused, rope, st);

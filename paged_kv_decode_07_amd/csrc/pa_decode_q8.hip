@@ -282,7 +282,7 @@ int decode_quant_impl(const pa_shape* shape, int32_t batch, const void* q, const
   const bool two_waves = FMT == pa::kFmtINT4 && have_cu && (int64_t)batch * ns <= cu &&
                          ps >= pa_host::kTwoWaveMinPages;
   const hipError_t e = pa::launch_decode<FMT>(a, batch, out_dtype == PA_OUT_BF16, fused,
-                                               rope != nullptr, merge_preload, two_waves,
+                                               rope != nullptr, merge_preload, two_waves, false,
                                                (hipStream_t)stream, nullptr, nullptr);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

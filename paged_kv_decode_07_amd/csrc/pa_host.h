@@ -47,6 +47,13 @@ struct PlanModel {
 // pay for the larger work-group and the merge of the two states (3- and
 // 8-page splits measured 9% and 4% slower with two).
 constexpr int kTwoWaveMinPages = 32;
+// BF16 pages stream through one LDS slot per wavefront, except in a launch
+// of fewer work-groups than CUs, or of one per CU with splits shorter than
+// this: a two-slot ring then keeps enough pages in flight and hides the start
+// of each short stream (measured: 4- and 32-page splits of 256 work-groups 4%
+// faster with two slots, 64 balanced work-groups 13%; 128-page splits, and
+// launches of more work-groups than CUs, 1-5% faster with one).
+constexpr int kOneSlotMinPages = 64;
 // worklist: the work-groups run in pa_decode_worklist's order (largest
 // first, no empty slots) instead of the grid order.
 double simulate_plan(const int32_t* lens, int batch, int max_seq_len, int ps, int cu, int xcds,
