@@ -59,15 +59,16 @@ XCDS = 8
 HOST = "pa_kernels.h + pa_kernels_q8.h + pa_decode_kernel.h + pa_host.h + "
 
 # the fused decode kernel's instances in the headline run, by format
-# (template arguments: page format, BF16 out, append, RoPE, wavefronts per KV head)
+# (template arguments: page format, BF16 out, append, RoPE, wavefronts per KV
+# head, ring slots per wavefront with 0 for the format's default)
 HEADLINE_KERNELS = (
-    ("void pa::decode_kernel<0, false, true, false, 1>", "BF16",
+    ("void pa::decode_kernel<0, false, true, false, 1, 0>", "BF16",
      "pa::decode_kernel<BF16 pages, FP32 out, append fused>", "TRAFFIC_FILE", "KERNEL_SOURCES",
      "pa_decode.hip", "step_bytes", ""),
-    ("void pa::decode_kernel<1, false, true, false, 1>", "INT8",
+    ("void pa::decode_kernel<1, false, true, false, 1, 0>", "INT8",
      "pa::decode_kernel<INT8 pages, FP32 out, quantised append fused>", "TRAFFIC_FILE_Q8",
      "KERNEL_SOURCES_Q8", "pa_decode_q8.hip", "step_bytes_q8", ""),
-    ("void pa::decode_kernel<2, false, true, false, 2>", "INT4",
+    ("void pa::decode_kernel<2, false, true, false, 2, 0>", "INT4",
      "pa::decode_kernel<INT4 pages, FP32 out, quantised append fused, two wavefronts per KV head>",
      "TRAFFIC_FILE_Q4", "KERNEL_SOURCES_Q8", "pa_decode_q8.hip", "step_bytes_q4",
      "One 128-page split per sequence, two wavefronts per KV head (each streams 64 pages; the\n"
@@ -77,13 +78,23 @@ HEADLINE_KERNELS = (
 TRACE_LABELS = (
     ("void at::native::reduce_kernel<512, 1, at::native::ReduceOp<int, at::native::func_wrapper_t"
      "<int, at::native::MaxNanFunctor<int>", "flush (torch amax over 1 GiB)"),
-    ("void pa::decode_kernel<0, false, true, false, 1>", "pa::decode_kernel<BF16, append>"),
-    ("void pa::decode_kernel<0, false, false, false, 1>", "pa::decode_kernel<BF16, no append>"),
-    ("void pa::decode_kernel<0, false, true, true, 1>", "pa::decode_kernel<BF16, append, RoPE>"),
-    ("void pa::decode_kernel<1, false, true, false, 1>", "pa::decode_kernel<INT8, append>"),
-    ("void pa::decode_kernel<2, false, true, false, 2>",
+    ("void pa::decode_kernel<0, false, true, false, 1, 0>", "pa::decode_kernel<BF16, append>"),
+    ("void pa::decode_kernel<0, false, false, false, 1, 0>", "pa::decode_kernel<BF16, no append>"),
+    ("void pa::decode_kernel<0, false, true, true, 1, 0>", "pa::decode_kernel<BF16, append, RoPE>"),
+    ("void pa::decode_kernel<0, false, true, false, 1, 2>",
+     "pa::decode_kernel<BF16, append, two-slot ring>"),
+    ("void pa::decode_kernel<0, false, false, false, 1, 2>",
+     "pa::decode_kernel<BF16, no append, two-slot ring>"),
+    ("void pa::decode_kernel<1, false, true, false, 1, 0>", "pa::decode_kernel<INT8, append>"),
+    ("void pa::decode_kernel<2, false, true, false, 2, 0>",
      "pa::decode_kernel<INT4, append, two wavefronts per KV head>"),
     ("(anonymous namespace)::stream_read_kernel", "pa_stream_read (1 GiB, non-temporal loads)"),
+    ("void (anonymous namespace)::page_stream_kernel<0, 1, 1>",
+     "pa_page_stream (BF16 pages, decode kernel's shape)"),
+    ("void (anonymous namespace)::page_stream_kernel<1, 1, 2>",
+     "pa_page_stream (INT8 pages, decode kernel's shape)"),
+    ("void (anonymous namespace)::page_stream_kernel<2, 2, 3>",
+     "pa_page_stream (INT4 pages, decode kernel's shape)"),
     ("void pa::merge_kernel<false>", "pa::merge_kernel<FP32 out>"),
 )
 

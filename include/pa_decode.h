@@ -145,14 +145,14 @@ int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch,
  * whose lengths are near max_seq_len.  For a skewed batch it leaves a tail:
  * measured on MI355X, fused step, batch of 512 with lengths clipped
  * Zipf(1.1) in [1, 2048], BF16 pages, cold caches: this plan (one 128-page
- * split per sequence) 209-211 us; pa_decode_plan_lengths 198-206 us; the
- * work list (pa_append_decode_attention_worklist) 177 us; the balanced
- * launch (include/pa_decode_balanced.h, 8 heads per lane) 167 us.  With
+ * split per sequence) 206-210 us; pa_decode_plan_lengths 202-208 us; the
+ * work list (pa_append_decode_attention_worklist) 169-171 us; the balanced
+ * launch (include/pa_decode_balanced.h, 8 heads per lane) 164-166 us.  With
  * lengths at hand, use one of the latter.  For batch 256 x 2048 all four
  * take 163-166 us.  For a batch of a few long sequences among many short
  * ones (512 lengths from Zipf(1.1) truncated to [1, 2048]) the work list
- * is the one that splits the long ones finely enough: 49 us, against 96 us
- * for pa_decode_plan_lengths and 68-89 us for the balanced launch.
+ * is the one that splits the long ones finely enough: 49 us, against 97 us
+ * for pa_decode_plan_lengths and 66-100 us for the balanced launch.
  */
 int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_len,
                    int32_t pages_per_split, int32_t* pages_out,

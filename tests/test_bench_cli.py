@@ -92,9 +92,9 @@ def test_profile_summaries_split_launches_and_calibrate(tmp_path):
     def row(i, name, counter="FETCH_SIZE", value=1.0):
         return {"Dispatch_Id": str(i), "Kernel_Name": name, "Counter_Name": counter,
                 "Counter_Value": str(value)}
-    dec, mer = "void pa::decode_kernel<0, false, true, false, 1>(pa::DecodeArgs)", \
+    dec, mer = "void pa::decode_kernel<0, false, true, false, 1, 0>(pa::DecodeArgs)", \
         "void pa::merge_kernel<false>(pa::MergeArgs)"
-    bal = "void pa::decode_balanced_kernel<0, false, true, false>(pa::BalancedArgs)"
+    bal = "void pa::decode_balanced_kernel<0, false, true, false, 0>(pa::BalancedArgs)"
     # two launches, 2 steps of 2 layers each; the first has a merge after every decode
     rows = [row(1, "torch fill")]
     i = 2
