@@ -208,26 +208,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
   const char* k_base = reinterpret_cast<const char*>(a.k_pool);
   const char* v_base = reinterpret_cast<const char*>(a.v_pool);
   const char* s_base = reinterpret_cast<const char*>(a.kv_scales);
-  uint32_t dma_k, dma_k1 = 0, dma_s = 0;
-  const char* kv_base = k_base;
-  uint32_t g_step, g_step_s = 0;                  // bytes between KV heads in a page
-  if constexpr (Q8) {
-    dma_k = (uint32_t)(16 * lane);
-    dma_s = (uint32_t)((lane & 31) * 4);
-    g_step = kHeadCodes;
-    g_step_s = 2 * kPage * 4;
-  } else if constexpr (Q4) {
-    kv_base = lane < 32 ? k_base : v_base;
-    dma_k = (uint32_t)(16 * (lane & 31));
-    dma_s = (uint32_t)((lane & 31) * 4);
-    g_step = kHeadCodes4;
-    g_step_s = 2 * kPage * 4;
-  } else {
-    const int t0 = lane >> 3, t1 = 8 + (lane >> 3);
-    dma_k = 2u * (uint32_t)(t0 * kRowElems) + 16u * (uint32_t)((lane & 7) ^ (t0 >> 1));
-    dma_k1 = 2u * (uint32_t)(t1 * kRowElems) + 16u * (uint32_t)((lane & 7) ^ (t1 >> 1));
-    g_step = 2 * kD;
-  }
+  // the lane offsets of head 0; each stream entry names its head
+  const PageDma dma = page_dma<FMT>(0, lane, k_base, v_base);
+  // bytes between KV heads in a page: codes, scale lines
+  constexpr uint32_t g_step = Q8 ? kHeadCodes : Q4 ? kHeadCodes4 : 2 * kD;
+  constexpr uint32_t g_step_s = QUANT ? 2 * kPage * 4 : 0;
   auto packed = [&](int u) -> uint32_t {
     uint32_t v = (uint32_t)__builtin_amdgcn_readlane(ent[0], u & 63);
 #pragma unroll
@@ -239,25 +224,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
     const uint32_t v = packed(u);
     const int64_t id = (v >> 3) & 0x0FFFFFFFu;
     const uint32_t gg = v & 7u;
-    char* dst = &ring[slot][wave][0];
-    if constexpr (Q8) {
-      const int64_t off = id * (int64_t)kPageCodes + gg * g_step;
-      __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 1024, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + gg * g_step_s + dma_s,
-                                       dst + 2048, 4, 0, kStreamCpol);
-    } else if constexpr (Q4) {
-      __builtin_amdgcn_global_load_lds(kv_base + id * (int64_t)kPageCodes4 + gg * g_step + dma_k, dst,
-                                       16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + gg * g_step_s + dma_s,
-                                       dst + 1024, 4, 0, kStreamCpol);
-    } else {
-      const int64_t off = id * (int64_t)(kPageElems * 2) + gg * g_step;
-      __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(k_base + off + dma_k1, dst + 1024, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 2048, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(v_base + off + dma_k1, dst + 3072, 16, 0, kStreamCpol);
-    }
+    page_fetch<FMT>(dma, k_base, v_base, s_base, id, gg * g_step, gg * g_step_s,
+                    &ring[slot][wave][0]);
   };
 #pragma unroll
   for (int r = 0; r < kDepth; ++r)

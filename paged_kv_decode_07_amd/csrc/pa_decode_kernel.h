@@ -172,6 +172,73 @@ struct PageFormat<kFmtINT4> {
   static constexpr bool kPairs = PA_PAIR_STEPS && kRingDepth >= 3;
 };
 
+// Cache-policy bits of the page-stream loads: every page is read once, so
+// every page format stream with the non-temporal policy (nt = 2).
+#ifndef PA_STREAM_CPOL
+#define PA_STREAM_CPOL 2
+#endif
+constexpr int kStreamCpol = PA_STREAM_CPOL;
+
+// This lane's part of a page's direct-to-LDS loads for page format FMT and
+// KV head g: the byte offsets within a page of its code loads (BF16: two per
+// pool) and of its scale float, and its code pool (INT4: K for lanes 0..31,
+// V for 32..63).  BF16 load j (tokens 8j .. 8j+7) has lane l take token
+// t = 8j + l/8 and the piece whose swizzled position is l%8, so that lane l
+// lands at byte bf16_slot_offset(t, that piece) - 1024 j of its destination;
+// INT8 lane l takes bytes 16 l of the head's code block (token l/4, dims
+// 16 (l%4) ..) and float l%32 of its scale line; INT4 lane l takes bytes
+// 16 (l%32) of the head's K (l < 32) or V block, and the same scale float.
+// The decode kernels and the page-stream measurement share these maps.
+struct PageDma {
+  uint32_t k, k1, s;
+  const char* kv;
+};
+template <int FMT>
+__device__ __forceinline__ PageDma page_dma(int g, int lane, const char* k_base,
+                                            const char* v_base) {
+  PageDma d{0u, 0u, 0u, k_base};
+  if constexpr (FMT == kFmtINT8) {
+    d.k = (uint32_t)(g * kHeadCodes + 16 * lane);                   // the head's 1 KiB block
+    d.s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
+  } else if constexpr (FMT == kFmtINT4) {
+    d.kv = lane < 32 ? k_base : v_base;
+    d.k = (uint32_t)(g * kHeadCodes4 + 16 * (lane & 31));           // 512 B of K, 512 B of V
+    d.s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
+  } else {
+    const int t0 = lane >> 3, t1 = 8 + (lane >> 3);
+    d.k = 2u * (uint32_t)(t0 * kRowElems + g * kD) + 16u * (uint32_t)((lane & 7) ^ (t0 >> 1));
+    d.k1 = 2u * (uint32_t)(t1 * kRowElems + g * kD) + 16u * (uint32_t)((lane & 7) ^ (t1 >> 1));
+  }
+  return d;
+}
+
+// Request page `id` into the LDS slot `dst` (format FMT's slot layout), its
+// head's blocks head_off and scale_off bytes past the lane offsets of d, with
+// the streaming cache policy.
+template <int FMT>
+__device__ __forceinline__ void page_fetch(const PageDma& d, const char* k_base,
+                                           const char* v_base, const char* s_base, int64_t id,
+                                           uint32_t head_off, uint32_t scale_off, char* dst) {
+  if constexpr (FMT == kFmtINT8) {
+    const int64_t off = id * (int64_t)kPageCodes + head_off;
+    __builtin_amdgcn_global_load_lds(k_base + off + d.k, dst, 16, 0, kStreamCpol);
+    __builtin_amdgcn_global_load_lds(v_base + off + d.k, dst + 1024, 16, 0, kStreamCpol);
+    __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + scale_off + d.s,
+                                     dst + 2048, 4, 0, kStreamCpol);
+  } else if constexpr (FMT == kFmtINT4) {
+    __builtin_amdgcn_global_load_lds(d.kv + id * (int64_t)kPageCodes4 + head_off + d.k, dst, 16, 0,
+                                     kStreamCpol);
+    __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + scale_off + d.s,
+                                     dst + 1024, 4, 0, kStreamCpol);
+  } else {
+    const int64_t off = id * (int64_t)(kPageElems * 2) + head_off;
+    __builtin_amdgcn_global_load_lds(k_base + off + d.k, dst, 16, 0, kStreamCpol);
+    __builtin_amdgcn_global_load_lds(k_base + off + d.k1, dst + 1024, 16, 0, kStreamCpol);
+    __builtin_amdgcn_global_load_lds(v_base + off + d.k, dst + 2048, 16, 0, kStreamCpol);
+    __builtin_amdgcn_global_load_lds(v_base + off + d.k1, dst + 3072, 16, 0, kStreamCpol);
+  }
+}
+
 // Registers of one page for one lane.
 struct PageBF16 {
   u32x4 k0, k1;       // K[token][8G..8G+7], K[token][32+8G..32+8G+7]
@@ -501,13 +568,6 @@ __device__ __forceinline__ int out_dim(int b, int n) {
   return 16 * b + n;
 }
 
-// Cache-policy bits of the page-stream loads: every page is read once, so
-// both page formats stream with the non-temporal policy (nt = 2).
-#ifndef PA_STREAM_CPOL
-#define PA_STREAM_CPOL 2
-#endif
-constexpr int kStreamCpol = PA_STREAM_CPOL;
-
 // The new K/V row of KV head g straight into the pool (no LDS parking): lane
 // c (K) and 4 + c (V), c = 0..3, hold the row parts {8c..8c+7} (lo) and
 // {32+8c..} (hi); K is rotated first with RoPE at position `pos`, quantised
@@ -694,47 +754,9 @@ __global__ __launch_bounds__(kThreads * WPH, 2 * WPH) void decode_kernel(DecodeA
   const char* k_base = reinterpret_cast<const char*>(a.k_pool);
   const char* v_base = reinterpret_cast<const char*>(a.v_pool);
   const char* s_base = reinterpret_cast<const char*>(a.kv_scales);
-  // DMA lane offsets (bytes within a page): INT8 lane l takes bytes 16 l of
-  // the head's code block (token l/4, dims 16 (l%4) ..) and float l%32 of its
-  // scale line; INT4 lane l takes bytes 16 (l%32) of the head's K (l < 32) or
-  // V block, and the same scale float; BF16 load j (tokens 8j .. 8j+7) has lane l take token
-  // t = 8j + l/8 and the piece whose swizzled position is l%8, so that lane l
-  // lands at byte bf16_slot_offset(t, that piece) - 1024 j of its destination
-  uint32_t dma_k, dma_k1 = 0, dma_s = 0;
-  const char* kv_base = k_base;
-  if constexpr (Q8) {
-    dma_k = (uint32_t)(g * kHeadCodes + 16 * lane);                 // the head's 1 KiB block
-    dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
-  } else if constexpr (Q4) {
-    kv_base = lane < 32 ? k_base : v_base;
-    dma_k = (uint32_t)(g * kHeadCodes4 + 16 * (lane & 31));         // 512 B of K, 512 B of V
-    dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
-  } else {
-    const int t0 = lane >> 3, t1 = 8 + (lane >> 3);
-    dma_k = 2u * (uint32_t)(t0 * kRowElems + g * kD) + 16u * (uint32_t)((lane & 7) ^ (t0 >> 1));
-    dma_k1 = 2u * (uint32_t)(t1 * kRowElems + g * kD) + 16u * (uint32_t)((lane & 7) ^ (t1 >> 1));
-  }
+  const PageDma dma = page_dma<FMT>(g, lane, k_base, v_base);
   auto fetch = [&](int page, int slot) {
-    const int64_t id = page_id(page);
-    char* dst = &ring[slot][wave][0];
-    if constexpr (Q8) {
-      const int64_t off = id * (int64_t)kPageCodes;
-      __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 1024, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + dma_s,
-                                       dst + 2048, 4, 0, kStreamCpol);
-    } else if constexpr (Q4) {
-      __builtin_amdgcn_global_load_lds(kv_base + id * (int64_t)kPageCodes4 + dma_k, dst, 16, 0,
-                                       kStreamCpol);
-      __builtin_amdgcn_global_load_lds(s_base + id * (int64_t)(kScalePageFloats * 4) + dma_s,
-                                       dst + 1024, 4, 0, kStreamCpol);
-    } else {
-      const int64_t off = id * (int64_t)(kPageElems * 2);
-      __builtin_amdgcn_global_load_lds(k_base + off + dma_k, dst, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(k_base + off + dma_k1, dst + 1024, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(v_base + off + dma_k, dst + 2048, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(v_base + off + dma_k1, dst + 3072, 16, 0, kStreamCpol);
-    }
+    page_fetch<FMT>(dma, k_base, v_base, s_base, page_id(page), 0u, 0u, &ring[slot][wave][0]);
   };
   // LDS read addresses of this lane in slot 0 of its wavefront
   const uint32_t slot0 = lds_address(&ring[0][wave][0]);

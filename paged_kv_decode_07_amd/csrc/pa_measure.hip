@@ -49,10 +49,11 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4v* __restri
 // Page stream.  One work-group per sequence, WPH wavefronts per KV head (the
 // two of a head take the first and the second half of the sequence's pages),
 // RING page slots per wavefront.  Each page is requested with the decode
-// kernel's direct-to-LDS loads for page format FMT (the same lane-to-address
-// maps, cache policy and ring waits), read back from LDS in full once it has
-// landed, and folded into one XOR word per wavefront; the slot is then
-// refilled.  Nothing else is computed.
+// kernels' own direct-to-LDS loads for page format FMT (page_dma and
+// page_fetch: the same lane-to-address maps and cache policy; the same ring
+// waits), read back from LDS in full once it has landed, and folded into one
+// XOR word per wavefront; the slot is then refilled.  Nothing else is
+// computed.
 constexpr int kStreamWindow = 256;               // pages of one wavefront's block-table window
 
 struct PageStreamArgs {
@@ -106,46 +107,10 @@ __global__ __launch_bounds__(pa::kWaves * WPH * 64) void page_stream_kernel(Page
       if ((j >> 6) == c) id = __builtin_amdgcn_readlane(ent[c], j & 63);
     return (unsigned)id < (unsigned)a.num_pages ? id : 0;   // an id outside the pool reads page 0
   };
-  // byte offsets within a page, as in the decode kernel: INT8 lane l takes
-  // bytes 16 l of the head's 1 KiB code block and float l % 32 of its scale
-  // line; INT4 lane l takes bytes 16 (l % 32) of the head's 512-byte K (l < 32)
-  // or V block and the same scale float; BF16 load j takes token 8 j + l / 8
-  // and the piece at swizzled position l % 8
-  uint32_t dma_k, dma_k1 = 0, dma_s = 0;
-  const char* kv_base = a.k_pool;
-  if constexpr (FMT == kFmtINT8) {
-    dma_k = (uint32_t)(g * kHeadCodes + 16 * lane);
-    dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
-  } else if constexpr (FMT == kFmtINT4) {
-    kv_base = lane < 32 ? a.k_pool : a.v_pool;
-    dma_k = (uint32_t)(g * kHeadCodes4 + 16 * (lane & 31));
-    dma_s = (uint32_t)((g * 2 * kPage + (lane & 31)) * 4);
-  } else {
-    const int t0 = lane >> 3, t1 = 8 + (lane >> 3);
-    dma_k = 2u * (uint32_t)(t0 * kRowElems + g * kD) + 16u * (uint32_t)((lane & 7) ^ (t0 >> 1));
-    dma_k1 = 2u * (uint32_t)(t1 * kRowElems + g * kD) + 16u * (uint32_t)((lane & 7) ^ (t1 >> 1));
-  }
+  // the decode kernels' own lane maps and loads for this format
+  const PageDma dma = page_dma<FMT>(g, lane, a.k_pool, a.v_pool);
   auto fetch = [&](int i, int slot) {
-    const int64_t id = page_id(i);
-    char* dst = &ring[slot][wave][0];
-    if constexpr (FMT == kFmtINT8) {
-      const int64_t off = id * (int64_t)kPageCodes;
-      __builtin_amdgcn_global_load_lds(a.k_pool + off + dma_k, dst, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(a.v_pool + off + dma_k, dst + 1024, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(a.scales + id * (int64_t)(kScalePageFloats * 4) + dma_s,
-                                       dst + 2048, 4, 0, kStreamCpol);
-    } else if constexpr (FMT == kFmtINT4) {
-      __builtin_amdgcn_global_load_lds(kv_base + id * (int64_t)kPageCodes4 + dma_k, dst, 16, 0,
-                                       kStreamCpol);
-      __builtin_amdgcn_global_load_lds(a.scales + id * (int64_t)(kScalePageFloats * 4) + dma_s,
-                                       dst + 1024, 4, 0, kStreamCpol);
-    } else {
-      const int64_t off = id * (int64_t)(kPageElems * 2);
-      __builtin_amdgcn_global_load_lds(a.k_pool + off + dma_k, dst, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(a.k_pool + off + dma_k1, dst + 1024, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(a.v_pool + off + dma_k, dst + 2048, 16, 0, kStreamCpol);
-      __builtin_amdgcn_global_load_lds(a.v_pool + off + dma_k1, dst + 3072, 16, 0, kStreamCpol);
-    }
+    page_fetch<FMT>(dma, a.k_pool, a.v_pool, a.scales, page_id(i), 0u, 0u, &ring[slot][wave][0]);
   };
   // the slot read back: every code byte once; the scale line once (lanes 32..63
   // hold a second copy of it).  The outputs are early-clobber: a later read of
