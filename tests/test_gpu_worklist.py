@@ -79,3 +79,32 @@ def test_worklist_launch_matches_grid_launch(q8, fused, out_dtype):
     for a, b in zip(p0, p1):
         assert torch.equal(a, b), "pools differ"
     assert torch.all(o0[5] == 0)
+
+
+def test_ring_depth_leaves_results_bitwise_unchanged():
+    """BF16 pages stream through one LDS slot per wavefront or two, chosen per launch from
+    the plan (more work-groups than CUs: one slot; at most one per CU with short splits: two).
+    The depth changes when pages are requested, not the order they are used in: the grid
+    launch of this plan (40 sequences x 8 splits = 320 work-groups: one slot) and its work
+    list (40 non-empty 16-page items: two slots) give the same bits, and both match the
+    oracle."""
+    import oracle
+    from gpu_util import assert_close
+    from paged_kv_decode_07_amd import binding as pa
+    lens = np.random.default_rng(1700).integers(1, 257, size=40).astype(np.int32)
+    lens[0], lens[1] = 256, 1                        # a full 16-page split, a one-token one
+    w = W.make_batch(lens, int(sum(W.pages_for(L) for L in lens)) + 8, 1701)
+    msl, ps = 2048, 16                               # 8 splits per sequence on the grid
+    db = DeviceBatch(w)
+    work_h, ps_w, _ = pa.decode_worklist(lens, w.num_pages, max_seq_len=msl, pages_per_split=ps,
+                                         num_cus=256)
+    assert ps_w == ps and len(work_h) == len(lens)   # one item per sequence: 40 <= 256 CUs
+    grid = pa.decode_attention(db.q, db.k_pool, db.v_pool, db.bt, db.lens, msl, scale=w.scale,
+                               pages_per_split=ps)
+    listed = pa.append_decode_attention_worklist(db.q, None, None, db.k_pool, db.v_pool, db.bt,
+                                                 db.lens, msl, dev32(work_h), ps, scale=w.scale)
+    torch.cuda.synchronize()
+    a, b = grid.cpu().numpy(), listed.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ref = oracle.decode_attention(w.q, w.k_pool, w.v_pool, w.block_tables, w.seq_lens, w.scale)
+    assert_close(a.astype(np.float64), ref, where="ring depths")
