@@ -580,6 +580,11 @@ def main() -> int:
                          "(pa_page_stream) on batch 256 x 2048 for every page format, "
                          "wavefronts per KV head and ring depth, beside each format's decode "
                          "kernel, interleaved, cold caches; one JSON line per case")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the bench line: the balanced launch with per-wavefront "
+                         "real-time stamps (pa_decode_balanced_timeline) on workloads 3, 4 and 5, "
+                         "beside the plain launch, interleaved, cold caches; one JSON line per "
+                         "case with the phases of each launch")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -601,6 +606,8 @@ def main() -> int:
         return run_placement_probe(args)
     if args.page_stream:
         return run_page_stream(args)
+    if args.timeline:
+        return run_timeline(args)
     if args.only_config:
         if args.only_config not in CONFIGS:
             print("--only-config takes 1..5", file=sys.stderr)
@@ -1154,6 +1161,143 @@ def run_page_stream(args) -> int:
             line.update({"waves_per_head": wph, "ring": ring,
                          "decode_kernel_shape": STREAM_SHAPES[fmt] == (wph, ring)})
         print(json.dumps(line), flush=True)
+    return 0
+
+
+TIMELINE_CASES = ((3, 1), (4, 8), (5, 8))     # (workload, KV heads per lane)
+
+
+def timeline_phases(stamps, khz: float) -> dict:
+    """Phases of one launch from its timeline stamps (int64 [groups][8][8]):
+    medians over wavefronts, and the work-groups' end times."""
+    import numpy as np
+    us = 1e3 / khz
+    t = stamps[..., :7].astype(np.int64)
+    w7 = stamps[..., 7].astype(np.int64)
+    pages = (w7 >> 48) & 0xFFFF
+    xcc = ((w7 >> 32) & 0xFFFF)[:, 0]
+    base = t[..., 0].min()
+    busy = pages > 0
+    runs = pages >= 2
+    wg_end = (t[..., 6].max(axis=1) - base) * us
+    per_page = (t[..., 4] - t[..., 3])[runs] * us / (pages[runs] - 1)
+    out = {
+        "span_us": float((t[..., 6].max() - base) * us),
+        "dispatch_us": float((t[..., 0].max() - base) * us),
+        "descriptor_us": float(np.median(t[..., 1] - t[..., 0]) * us),
+        "metadata_us": float(np.median(t[..., 2] - t[..., 1]) * us),
+        "first_page_us": float(np.median((t[..., 3] - t[..., 2])[busy]) * us),
+        "first_page_at_us": float(np.median((t[..., 3] - base)[busy]) * us),
+        "stream_us": float(np.median((t[..., 4] - t[..., 3])[busy]) * us),
+        "us_per_page": float(np.median(per_page)) if per_page.size else None,
+        "tail_us": float(np.median(t[..., 6] - t[..., 4]) * us),
+        "wg_end_us": wg_end,
+        "xcc": xcc,
+        "per_page_by_wg": np.array([np.median((t[g, :, 4] - t[g, :, 3])[runs[g]] * us /
+                                              (pages[g][runs[g]] - 1)) if runs[g].any() else np.nan
+                                    for g in range(t.shape[0])]),
+        "base": int(base), "end": int(t[..., 6].max()),
+        "pages": pages,
+    }
+    return out
+
+
+def run_timeline(args) -> int:
+    """The balanced launch with per-wavefront timeline stamps on workloads 3 (16
+    layers, one KV head per lane), 4 and 5 (8 heads per lane): where each
+    launch's time goes.  One JSON line per case."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_07_amd import binding as pa
+
+    print(json.dumps({"kernel_sources": source_hashes()}), flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    khz = pa.wall_clock_khz()
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(2**28, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int32, device=dev)
+
+    def up16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    for ci, h in TIMELINE_CASES:
+        hosts = config_layers(ci, args.placement)
+        w0 = hosts[0]
+        B, msl = w0.batch, w0.max_seq_len
+        layers = [dict(q=up16(w.q), kp=up16(w.k_pool), vp=up16(w.v_pool), kn=up16(w.k_new),
+                       vn=up16(w.v_new), bt=torch.from_numpy(w.block_tables).to(dev),
+                       lens=torch.from_numpy(w.seq_lens).to(dev),
+                       out=torch.empty((B, 32, 64), dtype=torch.float32, device=dev))
+                  for w in hosts]
+        plan = pa.balance_plan(w0.seq_lens, w0.num_pages, max_seq_len=msl, heads_together=h,
+                               device=dev)
+        stamps = [torch.zeros((plan.groups, 8, 8), dtype=torch.int64, device=dev) for _ in layers]
+
+        def step(timed):
+            for L, st in zip(layers, stamps):
+                if timed:
+                    pa.decode_balanced_timeline(L["q"], L["kp"], L["vp"], L["bt"], L["lens"], msl,
+                                                plan, k_new=L["kn"], v_new=L["vn"], scale=w0.scale,
+                                                out=L["out"], stamps=st, stream=stream)
+                else:
+                    pa.decode_balanced(L["q"], L["kp"], L["vp"], L["bt"], L["lens"], msl, plan,
+                                       k_new=L["kn"], v_new=L["vn"], scale=w0.scale,
+                                       out=L["out"], stream=stream)
+        t_tl, t_plain, phases = [], [], []
+        for it in range(args.warmup + args.steps):
+            for timed in (True, False):            # interleaved: drift hits both alike
+                torch.amax(flush_buf, dim=None, out=flush_out)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step(timed)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if it < args.warmup:
+                    continue
+                (t_tl if timed else t_plain).append(e0.elapsed_time(e1) * 1e3)
+                if timed:
+                    phases.append([timeline_phases(st.cpu().numpy(), khz) for st in stamps])
+        nl = len(layers)
+        us = 1e3 / khz
+        keys = ("span_us", "dispatch_us", "descriptor_us", "metadata_us", "first_page_us",
+                "first_page_at_us", "stream_us", "us_per_page", "tail_us")
+        med = {k: round(float(np.median([p[k] for ps in phases for p in ps if p[k] is not None])),
+                        3) for k in keys}
+        gaps = [(ps[l]["base"] - ps[l - 1]["end"]) * us for ps in phases for l in range(1, nl)]
+        ends = np.concatenate([p["wg_end_us"] for ps in phases for p in ps])
+        # per die: the work-groups' end times and per-page times, over every launch
+        xcc = np.concatenate([p["xcc"] for ps in phases for p in ps])
+        ppg = np.concatenate([p["per_page_by_wg"] for ps in phases for p in ps])
+        by_xcc = {str(int(x)): {"wg_end_median_us": round(float(np.median(ends[xcc == x])), 2),
+                                "us_per_page": round(float(np.nanmedian(ppg[xcc == x])), 3),
+                                "work_groups": int((xcc == x).sum()) // len(phases)}
+                  for x in np.unique(xcc)}
+        # stamped time over event time: spans and gaps of the step against the events
+        cover = [(ps[-1]["end"] - ps[0]["base"]) * us / t for ps, t in zip(phases, t_tl)]
+        pg = phases[0][0]["pages"]
+        line = {
+            "case": f"workload {ci}, balanced, {h} KV head{'s' if h > 1 else ''} per lane",
+            "workload": ci, "layers": nl, "batch": B, "heads_together": h,
+            "groups": plan.groups, "steps": args.steps, "warmup": args.warmup,
+            "clock_khz": khz,
+            "step_us_timeline": round(float(np.median(t_tl)), 2),
+            "step_us_plain": round(float(np.median(t_plain)), 2),
+            "per_layer_us_plain": round(float(np.median(t_plain)) / nl, 2),
+            "gap_us": round(float(np.median(gaps)), 3) if gaps else None,
+            **med,
+            "wg_end_us": {q: round(float(np.percentile(ends, v)), 2)
+                          for q, v in (("min", 0), ("p10", 10), ("p50", 50), ("p90", 90),
+                                       ("max", 100))},
+            "by_xcc": by_xcc,
+            "pages_per_wave": {"min": int(pg.min()), "median": float(np.median(pg)),
+                               "max": int(pg.max())},
+            "stamped_over_event": round(float(np.median(cover)), 4),
+        }
+        print(json.dumps(line), flush=True)
+        del layers, stamps
+        torch.cuda.empty_cache()
     return 0
 
 

@@ -19,10 +19,12 @@ Modes (the first two read rocprofv3 output directories, ``-f csv -d DIR``):
   python bench_profiles.py sweep --json FILE --steps K --warmup W
   python bench_profiles.py placement --json FILE --steps K --warmup W
   python bench_profiles.py stream --json FILE --steps K --warmup W
+  python bench_profiles.py timeline --json FILE --steps K --warmup W
       the output of ``bench.py --sweep`` / ``--placement-probe`` / ``--page-stream``
-      as tables (profiles/decode_step_sweep_workloads_1_6.md,
+      / ``--timeline`` as tables (profiles/decode_step_sweep_workloads_1_6.md,
       profiles/decode_kernel_placement_b256_l2048.md,
-      profiles/page_stream_b256_l2048.md).
+      profiles/page_stream_b256_l2048.md,
+      profiles/decode_balanced_timeline_workloads_3_4_5.md).
 
 Every mode refuses a run whose kernel sources are not the current ones.
 
@@ -633,6 +635,67 @@ def stream(a) -> int:
     return 0
 
 
+def timeline(a) -> int:
+    rows = _lines(a.json)
+    check_sources(rows[0].get("kernel_sources", {}), ("balanced",))
+    src = rows[0]["kernel_sources"]
+    rows = [r for r in rows if "case" in r]
+    khz = rows[0]["clock_khz"]
+    out = ["# Timeline of the balanced launch: where a launch's time goes, workloads 3, 4 and 5\n",
+           "Commands (MI355X, ROCm 7.2, from the repository root):\n",
+           f"```\npython -u bench.py --timeline --steps {a.steps} --warmup {a.warmup} > "
+           f"{_rel(a.json)}\npython bench_profiles.py timeline --json {_rel(a.json)} --steps "
+           f"{a.steps} --warmup {a.warmup}\n```\n",
+           "`pa_decode_balanced_timeline` runs the balanced launch's own kernel body (the same "
+           "reads, arithmetic and writes, outputs equal bit for bit) and stamps every wavefront "
+           f"with the device's real-time counter ({khz / 1000:g} MHz by `pa_wall_clock_khz`) at "
+           "its start, when its plan descriptor is in, when the lengths, page ids and q rows are "
+           "in, when its first page is in LDS, when its last page is consumed, and when its output "
+           "stores are issued and acknowledged. Fused append + attention, FP32 out, each step's "
+           "layers back to back on one stream, caches flushed before every step; timeline and "
+           f"plain steps interleaved, {a.steps} of each after {a.warmup} warm-up rounds. Phases "
+           "are medians over every wavefront of every launch of the timed steps; `pages` are the "
+           "pages of one wavefront's KV-head stream (4 KiB of BF16 K and V each). Workload 4 runs "
+           "here with 8 heads per lane (one sequence per work-group), the same shape as its grid "
+           f"launch. Balanced kernel sources `{src['balanced']}`.\n",
+           "| case | work-groups | plain step µs (per layer) | timeline step µs | launch span µs "
+           "| gap to next layer µs | start spread µs | descriptor µs | lengths, ids, q µs "
+           "| then first page µs | first page at µs | stream µs | µs per page | tail µs |\n"
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    f = lambda v, d=2: "–" if v is None else f"{v:.{d}f}"
+    for r in rows:
+        out.append(f"| {r['case']} | {r['groups']} | {r['step_us_plain']:.1f} "
+                   f"({r['per_layer_us_plain']:.2f}) | {r['step_us_timeline']:.1f} | "
+                   f"{f(r['span_us'])} | {f(r['gap_us'])} | {f(r['dispatch_us'])} | "
+                   f"{f(r['descriptor_us'])} | {f(r['metadata_us'])} | {f(r['first_page_us'])} | "
+                   f"{f(r['first_page_at_us'])} | {f(r['stream_us'])} | {f(r['us_per_page'], 3)} | "
+                   f"{f(r['tail_us'])} |")
+    out.append("\nWork-group end times (µs after the launch's first wavefront started, every "
+               "work-group of every launch) and the pages per wavefront:\n")
+    out.append("| case | min | p10 | median | p90 | max | max - median | pages per wavefront "
+               "(min / median / max) | stamped / event time |\n|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        e = r["wg_end_us"]
+        pw = r["pages_per_wave"]
+        out.append(f"| {r['case']} | {e['min']:.2f} | {e['p10']:.2f} | {e['p50']:.2f} | "
+                   f"{e['p90']:.2f} | {e['max']:.2f} | {e['max'] - e['p50']:.2f} | {pw['min']} / "
+                   f"{pw['median']:g} / {pw['max']} | {r['stamped_over_event']:.3f} |")
+    out.append("\nBy die (the XCC_ID each work-group ran on): median work-group end µs / median "
+               "µs per page:\n")
+    ids = sorted({k for r in rows for k in r["by_xcc"]}, key=int)
+    out.append("| case | " + " | ".join(f"XCD {k}" for k in ids) + " |\n|---|" +
+               "---|" * len(ids))
+    for r in rows:
+        cells = [f"{r['by_xcc'][k]['wg_end_median_us']:.2f} / {r['by_xcc'][k]['us_per_page']:.3f}"
+                 if k in r["by_xcc"] else "–" for k in ids]
+        out.append(f"| {r['case']} | " + " | ".join(cells) + " |")
+    text = "\n".join(out) + "\n"
+    write_keeping_notes(os.path.join(PROFILES, "decode_balanced_timeline_workloads_3_4_5.md"),
+                        text)
+    print(text)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -650,14 +713,14 @@ def main(argv=None) -> int:
         p.add_argument("--write", required=True)
         p.add_argument("--util", default=None)
     for name, flag in (("sweep", "sweep"), ("placement", "placement-probe"),
-                       ("stream", "page-stream")):
+                       ("stream", "page-stream"), ("timeline", "timeline")):
         p = sub.add_parser(name)
         p.add_argument("--json", required=True, help=f"the output of bench.py --{flag}")
         p.add_argument("--steps", type=int, required=True)
         p.add_argument("--warmup", type=int, required=True)
     a = ap.parse_args(argv)
     return {"headline": headline, "config": config, "sweep": sweep, "placement": placement,
-            "stream": stream}[a.mode](a)
+            "stream": stream, "timeline": timeline}[a.mode](a)
 
 
 if __name__ == "__main__":

@@ -145,13 +145,13 @@ int pa_decode_workspace_bytes(const pa_shape* shape, int32_t batch,
  * whose lengths are near max_seq_len.  For a skewed batch it leaves a tail:
  * measured on MI355X, fused step, batch of 512 with lengths clipped
  * Zipf(1.1) in [1, 2048], BF16 pages, cold caches: this plan (one 128-page
- * split per sequence) 206-210 us; pa_decode_plan_lengths 201-208 us; the
+ * split per sequence) 205-210 us; pa_decode_plan_lengths 201-208 us; the
  * work list (pa_append_decode_attention_worklist) 166-171 us; the balanced
  * launch (include/pa_decode_balanced.h, 8 heads per lane) 163-166 us.  With
  * lengths at hand, use one of the latter.  For batch 256 x 2048 all four
  * take 163-166 us.  For a batch of a few long sequences among many short
  * ones (512 lengths from Zipf(1.1) truncated to [1, 2048]) the work list
- * is the one that splits the long ones finely enough: 49 us, against 97 us
+ * is the one that splits the long ones finely enough: 49-50 us, against 96-97 us
  * for pa_decode_plan_lengths and 66-100 us for the balanced launch.
  */
 int pa_decode_plan(const pa_shape* shape, int32_t batch, int32_t max_seq_len,

@@ -7,7 +7,8 @@
  * section 5.1: the KV cache grows with every token).  Beside the device's
  * published peak, a benchmark reports what a plain streaming read achieves on
  * the same device (pa_stream_read), and what the decode kernels' own page
- * reads achieve when nothing else is computed (pa_page_stream).
+ * reads achieve when nothing else is computed (pa_page_stream), and where the
+ * time of a balanced launch goes (pa_decode_balanced_timeline).
  */
 #ifndef PA_MEASURE_H
 #define PA_MEASURE_H
@@ -69,6 +70,46 @@ int pa_page_stream(const pa_shape* shape, int32_t batch, const void* k_pool, con
                    const void* kv_scales, int32_t page_format, const int32_t* block_tables,
                    const int32_t* seq_lens, int32_t waves_per_head, int32_t ring, uint32_t* sink,
                    void* stream);
+
+/*
+ * Timeline of a balanced launch: pa_decode_balanced (pa_decode_balanced.h)
+ * with FP32 output and no RoPE, the same reads, arithmetic and writes, which
+ * also records for every wavefront the device's constant-rate real-time
+ * counter (pa_wall_clock_khz ticks per millisecond) at seven points of its
+ * work.  A benchmark can then tell a launch's fixed costs (the memory round
+ * trips before the first page lands, the output stores at the end) from its
+ * page stream, and see how evenly its work-groups finish (the samir-vllm
+ * README's decode is memory-bound, so these are what a launch spends beside
+ * its reads).
+ *
+ * stamps: device uint64 [groups][8 wavefronts][8 words], 8-byte aligned,
+ * stamp_words >= groups * 64 (else PA_ERR_VALUE; NULL: PA_ERR_NULL).  Per
+ * wavefront:
+ *   [0] start            [1] its plan descriptor in
+ *   [2] lengths, page ids and q rows in
+ *   [3] first page in LDS (0 when the wavefront has no pages)
+ *   [4] last page consumed
+ *   [5] every output store issued   [6] every store acknowledged
+ *   [7] bits 0..31 the HW_ID hardware register as read, bits 32..47 the
+ *       XCC_ID register (which of the 8 dies the work-group ran on), bits
+ *       48..63 the wavefront's page count.
+ * The stamps are written once a wavefront's stores are acknowledged, so
+ * [6] - [0] covers the wavefront's whole life.  Other arguments, results and
+ * errors as for pa_decode_balanced (out: FP32).
+ */
+int pa_decode_balanced_timeline(const pa_shape* shape, int32_t batch, const void* q,
+                                const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                void* kv_scales, int32_t page_format, const int32_t* block_tables,
+                                const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                float* out, const int32_t* plan, int64_t plan_words,
+                                int32_t groups, uint64_t* stamps, int64_t stamp_words,
+                                void* stream);
+
+/*
+ * Rate of the real-time counter that pa_decode_balanced_timeline reads, in
+ * kHz, for the current device.  Returns PA_OK, PA_ERR_NULL or PA_ERR_DEVICE.
+ */
+int pa_wall_clock_khz(int32_t* khz);
 
 #ifdef __cplusplus
 }

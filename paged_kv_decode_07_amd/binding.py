@@ -42,7 +42,8 @@ EXPORTS = ("pa_append_kv", "pa_decode_workspace_bytes", "pa_decode_plan", "pa_de
            "pa_append_decode_attention_q4", "pa_append_decode_attention_rope_q4",
            "pa_decode_plan_lengths_q4", "pa_append_decode_attention_worklist_q4",
            # include/pa_measure.h
-           "pa_stream_read", "pa_page_stream",
+           "pa_stream_read", "pa_page_stream", "pa_decode_balanced_timeline",
+           "pa_wall_clock_khz",
            # include/pa_kvpool.h
            "pa_kvpool_create", "pa_kvpool_destroy", "pa_kvpool_credit", "pa_kvpool_submit",
            "pa_kvpool_admit", "pa_kvpool_grow", "pa_kvpool_step", "pa_kvpool_finish",
@@ -124,6 +125,9 @@ def load_library(path: str | None = None):
                                            ctypes.c_float, P, I32, P, I64_, I32, P]
         lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
         lib.pa_page_stream.argtypes = [SP, I32, P, P, P, I32, P, P, I32, I32, P, P]
+        lib.pa_decode_balanced_timeline.argtypes = [SP, I32, P, P, P, P, P, P, I32, P, P, I32,
+                                                    ctypes.c_float, P, P, I64_, I32, P, I64_, P]
+        lib.pa_wall_clock_khz.argtypes = [ctypes.POINTER(I32)]
         lib.pa_decode_worklist.argtypes = [SP, I32, P, I32, I32, I32, I32, P, I32,
                                            ctypes.POINTER(I32), ctypes.POINTER(I32),
                                            ctypes.POINTER(I32)]
@@ -784,13 +788,8 @@ def balance_plan(seq_lens_host, num_pages: int, max_blocks: int = 128,
     return BalancedPlan(torch.from_numpy(host).to(device), groups.value, lens)
 
 
-def decode_balanced(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int, plan,
-                    k_new=None, v_new=None, kv_scales=None, scale: float = 0.125, out=None,
-                    out_dtype=torch.float32, rope_cos=None, rope_sin=None, stream=None):
-    """Decode step over a ``BalancedPlan`` (optionally with the fused append and RoPE).
-
-    BF16 pools as ``decode_attention``; with ``kv_scales`` the pools are INT8
-    (int8) or INT4 (uint8) code pools.  Returns ``out``; no workspace."""
+def _balanced_checks(q, k_pool, v_pool, block_tables, seq_lens, plan, k_new, v_new, kv_scales):
+    """Argument checks of the balanced launches: (batch, page format, shape)."""
     B = int(seq_lens.shape[0])
     _bits16(q, "q", (HQ, D))
     if (k_new is None) != (v_new is None):
@@ -812,12 +811,23 @@ def decode_balanced(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int,
         _bits16(k_pool, "k_pool", (PAGE, HKV, D)); _bits16(v_pool, "v_pool", (PAGE, HKV, D))
         _same_pools(k_pool, v_pool)
         num_pages = int(k_pool.shape[0])
+    return B, fmt, make_shape(num_pages, int(block_tables.shape[1]))
+
+
+def decode_balanced(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int, plan,
+                    k_new=None, v_new=None, kv_scales=None, scale: float = 0.125, out=None,
+                    out_dtype=torch.float32, rope_cos=None, rope_sin=None, stream=None):
+    """Decode step over a ``BalancedPlan`` (optionally with the fused append and RoPE).
+
+    BF16 pools as ``decode_attention``; with ``kv_scales`` the pools are INT8
+    (int8) or INT4 (uint8) code pools.  Returns ``out``; no workspace."""
+    B, fmt, shape = _balanced_checks(q, k_pool, v_pool, block_tables, seq_lens, plan, k_new,
+                                     v_new, kv_scales)
     if (rope_cos is None) != (rope_sin is None):
         raise ValueError("give both rope_cos and rope_sin, or neither")
     rope = _rope(rope_cos, rope_sin) if rope_cos is not None else None
     code = _out_code(out_dtype)
     out = _out(out, B, out_dtype, q.device)
-    shape = make_shape(num_pages, int(block_tables.shape[1]))
     rc = load_library().pa_decode_balanced(
         ctypes.byref(shape), B, _ptr(q), _ptr(k_new) if k_new is not None else None,
         _ptr(v_new) if v_new is not None else None,
@@ -827,6 +837,45 @@ def decode_balanced(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int,
         plan.words, plan.groups, _stream_ptr(stream))
     _check(rc, "pa_decode_balanced")
     return out
+
+
+# words per wavefront of the timeline launch (include/pa_measure.h)
+STAMP_WORDS = 8
+
+
+def decode_balanced_timeline(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len: int, plan,
+                             k_new=None, v_new=None, kv_scales=None, scale: float = 0.125,
+                             out=None, stamps=None, stream=None):
+    """``decode_balanced`` (FP32 output, no RoPE) that also records each
+    wavefront's real-time counter at seven points of its work
+    (``include/pa_measure.h``).  Returns ``(out, stamps)``; ``stamps`` is int64
+    ``[groups][8][8]`` (words 0..6 counter ticks, word 7 hardware ids and the
+    wavefront's page count)."""
+    B, fmt, shape = _balanced_checks(q, k_pool, v_pool, block_tables, seq_lens, plan, k_new,
+                                     v_new, kv_scales)
+    out = _out(out, B, torch.float32, q.device)
+    words = plan.groups * 8 * STAMP_WORDS
+    if stamps is None:
+        stamps = torch.zeros((plan.groups, 8, STAMP_WORDS), dtype=torch.int64, device=q.device)
+    elif stamps.dtype != torch.int64 or not _is_device(stamps) or not stamps.is_contiguous() or \
+            stamps.numel() < words:
+        raise ValueError("decode_balanced_timeline: stamps must be a contiguous int64 device "
+                         "tensor of groups x 8 x 8 words")
+    rc = load_library().pa_decode_balanced_timeline(
+        ctypes.byref(shape), B, _ptr(q), _ptr(k_new) if k_new is not None else None,
+        _ptr(v_new) if v_new is not None else None, _ptr(k_pool), _ptr(v_pool),
+        _ptr(kv_scales) if kv_scales is not None else None, fmt, _ptr(block_tables),
+        _ptr(seq_lens), int(max_seq_len), float(scale), _ptr(out), _ptr(plan.plan), plan.words,
+        plan.groups, _ptr(stamps), int(stamps.numel()), _stream_ptr(stream))
+    _check(rc, "pa_decode_balanced_timeline")
+    return out, stamps
+
+
+def wall_clock_khz() -> int:
+    """Rate of the counter ``decode_balanced_timeline`` reads, in kHz."""
+    khz = ctypes.c_int32(0)
+    _check(load_library().pa_wall_clock_khz(ctypes.byref(khz)), "pa_wall_clock_khz")
+    return int(khz.value)
 
 
 def stream_read(buf, sink, groups: int = 0, stream=None) -> None:

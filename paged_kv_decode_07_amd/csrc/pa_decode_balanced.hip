@@ -14,6 +14,7 @@
 
 #include "pa_decode.h"
 #include "pa_decode_balanced.h"
+#include "pa_measure.h"
 #include "pa_host.h"
 #include "pa_decode_kernel.h"
 
@@ -61,6 +62,11 @@ struct BalancedArgs {
   int32_t batch;
 };
 
+// Timeline launch: per wavefront, the real-time counter at kStampTimes points
+// of its work, then one word naming where it ran and how much it read.
+constexpr int kStampWords = 8;
+constexpr int kStampTimes = 7;
+
 // LDS reads and writes that the compiler does not see as LDS accesses (it
 // would wait for every direct-to-LDS page load in flight before one); a read
 // waits for itself in the same instruction group.
@@ -81,8 +87,11 @@ __device__ __forceinline__ void lds_store4u(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE, int RING = 0>
-__global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedArgs a) {
+// The kernel body.  STAMPS: also read the real-time counter at the points of
+// a wavefront's work that the timeline launch reports (the page arithmetic
+// and every memory access are those of the plain launch).
+template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE, int RING, bool STAMPS>
+__device__ __forceinline__ void balanced_body(const BalancedArgs& a, uint64_t* stamps) {
   static_assert(!ROPE || APPEND, "RoPE is fused with the append");
   constexpr bool Q8 = FMT == kFmtINT8;
   constexpr bool Q4 = FMT == kFmtINT4;
@@ -93,6 +102,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4;
   const int n = lane & 15;
+  uint64_t stamp[kStampTimes] = {};
+  auto mark = [&stamp](int k) {
+    if constexpr (STAMPS) stamp[k] = __builtin_amdgcn_s_memrealtime();
+  };
+  mark(0);                                       // start
 
   // RING: slots per wavefront for this launch (0: the format's default)
   constexpr int kDepth = RING > 0 ? RING : F::kRingDepth;
@@ -109,6 +123,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
   const int32_t* desc = a.plan + kBalHeader + ((int64_t)blockIdx.x * kWaves + wave) * kBalDesc;
   const int dv = desc[lane];
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  mark(1);                                       // descriptor in
   auto dw = [&](int i) { return __builtin_amdgcn_readlane(dv, i); };
   int nseg = dw(0);
   int U = dw(1);
@@ -177,6 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
     __builtin_amdgcn_global_load_lds(src, &segblk[wave][j][0], 16, 0, 0);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  mark(2);                                       // lengths, page ids, q rows in
 
   // ---- segments a plan cannot hold: wrong device length, beyond the
   // declared bound or the table, or a used page id outside the pool
@@ -397,6 +413,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
       const int slot = u % kDepth;
       const uint32_t off = slot * kRingSlotBytes;
       wait_page<F::kLoads, kDepth>(min(U - 1 - u, kDepth - 1));
+      if (u == 0) mark(3);                         // first page in LDS
       if (MASK && app) park(slot0 + off);
       PageT cur;
       lds_read(cur, off);
@@ -410,6 +427,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
       const int slot_a = u % kDepth;
       const int slot_b = (u + 1) % kDepth;
       wait_page<F::kLoads, kDepth>(min(U - 2 - u, kDepth - 2));
+      if (u == 0) mark(3);
       PageT pa_, pb_;
       lds_read(pa_, slot_a * kRingSlotBytes);
       lds_read(pb_, slot_b * kRingSlotBytes);
@@ -459,6 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
     lds_store16(blk + 16 * lane, u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]),
                                         __float_as_uint(o[2]), __float_as_uint(o[3])});
   }
+  mark(4);                                       // last page consumed
   wait_vmem<0>();
   __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): the staged rows are in LDS
 
@@ -561,6 +580,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedAr
       store_out(b, g, o);
     }
   }
+  if constexpr (STAMPS) {
+    mark(5);                                     // every output store issued
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    mark(6);                                     // every store acknowledged
+    if (lane == 0) {
+      // hardware ids: HW_ID (CU, shader array, engine) and XCC_ID (die)
+      const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+      const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xFFFFu;
+      uint64_t* d = stamps + ((int64_t)blockIdx.x * kWaves + wave) * kStampWords;
+#pragma unroll
+      for (int k = 0; k < kStampTimes; ++k) d[k] = stamp[k];
+      d[kStampTimes] = (uint64_t)hw | ((uint64_t)xcc << 32) | ((uint64_t)(U & 0xFFFF) << 48);
+    }
+  }
+}
+
+template <int FMT, bool OUT_BF16, bool APPEND, bool ROPE, int RING = 0>
+__global__ __launch_bounds__(kThreads, 2) void decode_balanced_kernel(BalancedArgs a) {
+  balanced_body<FMT, OUT_BF16, APPEND, ROPE, RING, false>(a, nullptr);
+}
+
+// The same work with the timeline stamps (FP32 output, no RoPE): kStampWords
+// words per wavefront.
+template <int FMT, bool APPEND, int RING = 0>
+__global__ __launch_bounds__(kThreads, 2) void decode_balanced_timeline_kernel(BalancedArgs a,
+                                                                               uint64_t* stamps) {
+  balanced_body<FMT, false, APPEND, false, RING, true>(a, stamps);
 }
 
 template <int FMT, int RING>
@@ -578,16 +624,33 @@ void launch_balanced_ring(const BalancedArgs& a, dim3 grid, bool out_bf16, bool 
   }
 }
 
-// two_slots (BF16 pages only): a two-slot ring instead of the default one slot.
+template <int FMT, int RING>
+void launch_timeline_ring(const BalancedArgs& a, uint64_t* stamps, dim3 grid, bool fused,
+                          hipStream_t st) {
+  const dim3 block(kThreads);
+  if (fused) hipLaunchKernelGGL((decode_balanced_timeline_kernel<FMT, true, RING>), grid, block, 0, st, a, stamps);
+  else hipLaunchKernelGGL((decode_balanced_timeline_kernel<FMT, false, RING>), grid, block, 0, st, a, stamps);
+}
+
+// two_slots (BF16 pages only): a two-slot ring instead of the default one slot;
+// stamps: the kernel that also writes the timeline there (FP32 output, no
+// RoPE), or NULL.
 template <int FMT>
 hipError_t launch_balanced(const BalancedArgs& a, int groups, bool out_bf16, bool fused, bool rope,
-                           bool two_slots, hipStream_t st) {
+                           bool two_slots, uint64_t* stamps, hipStream_t st) {
   const dim3 grid(groups);
   if constexpr (FMT == kFmtBF16) {
-    if (two_slots) launch_balanced_ring<FMT, 2>(a, grid, out_bf16, fused, rope, st);
-    else launch_balanced_ring<FMT, 0>(a, grid, out_bf16, fused, rope, st);
+    if (stamps) {
+      if (two_slots) launch_timeline_ring<FMT, 2>(a, stamps, grid, fused, st);
+      else launch_timeline_ring<FMT, 0>(a, stamps, grid, fused, st);
+    } else if (two_slots) {
+      launch_balanced_ring<FMT, 2>(a, grid, out_bf16, fused, rope, st);
+    } else {
+      launch_balanced_ring<FMT, 0>(a, grid, out_bf16, fused, rope, st);
+    }
   } else {
-    launch_balanced_ring<FMT, 0>(a, grid, out_bf16, fused, rope, st);
+    if (stamps) launch_timeline_ring<FMT, 0>(a, stamps, grid, fused, st);
+    else launch_balanced_ring<FMT, 0>(a, grid, out_bf16, fused, rope, st);
   }
   return hipGetLastError();
 }
@@ -798,13 +861,14 @@ PA_API int pa_balance_plan(const pa_shape* shape, int32_t batch, const int32_t* 
   return PA_OK;
 }
 
-PA_API int pa_decode_balanced(const pa_shape* shape, int32_t batch, const void* q,
-                              const void* k_new, const void* v_new, const pa_rope* rope,
-                              void* k_pool, void* v_pool, void* kv_scales, int32_t page_format,
-                              const int32_t* block_tables, const int32_t* seq_lens,
-                              int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
-                              const int32_t* plan, int64_t plan_words, int32_t groups,
-                              void* stream) {
+// Both balanced entry points; stamps (the timeline launch) or NULL.
+static int decode_balanced_impl(const pa_shape* shape, int32_t batch, const void* q,
+                                const void* k_new, const void* v_new, const pa_rope* rope,
+                                void* k_pool, void* v_pool, void* kv_scales, int32_t page_format,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
+                                const int32_t* plan, int64_t plan_words, int32_t groups,
+                                uint64_t* stamps, void* stream) {
   int rc = check_decode_sizes(shape, batch, max_seq_len);
   if (rc != PA_OK) return rc;
   if (out_dtype != PA_OUT_F32 && out_dtype != PA_OUT_BF16) return PA_ERR_VALUE;
@@ -857,8 +921,46 @@ PA_API int pa_decode_balanced(const pa_shape* shape, int32_t batch, const void* 
   // busy CU then needs more pages in flight), else one
   int cu = 0;
   const bool two_slots = current_cu_count(&cu) == PA_OK && groups < cu;
-  if (page_format == 1) e = pa::launch_balanced<pa::kFmtINT8>(a, groups, bf, fused, rope != nullptr, false, (hipStream_t)stream);
-  else if (page_format == 2) e = pa::launch_balanced<pa::kFmtINT4>(a, groups, bf, fused, rope != nullptr, false, (hipStream_t)stream);
-  else e = pa::launch_balanced<pa::kFmtBF16>(a, groups, bf, fused, rope != nullptr, two_slots, (hipStream_t)stream);
+  if (page_format == 1) e = pa::launch_balanced<pa::kFmtINT8>(a, groups, bf, fused, rope != nullptr, false, stamps, (hipStream_t)stream);
+  else if (page_format == 2) e = pa::launch_balanced<pa::kFmtINT4>(a, groups, bf, fused, rope != nullptr, false, stamps, (hipStream_t)stream);
+  else e = pa::launch_balanced<pa::kFmtBF16>(a, groups, bf, fused, rope != nullptr, two_slots, stamps, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+PA_API int pa_decode_balanced(const pa_shape* shape, int32_t batch, const void* q,
+                              const void* k_new, const void* v_new, const pa_rope* rope,
+                              void* k_pool, void* v_pool, void* kv_scales, int32_t page_format,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              int32_t max_seq_len, float scale, void* out, int32_t out_dtype,
+                              const int32_t* plan, int64_t plan_words, int32_t groups,
+                              void* stream) {
+  return decode_balanced_impl(shape, batch, q, k_new, v_new, rope, k_pool, v_pool, kv_scales,
+                              page_format, block_tables, seq_lens, max_seq_len, scale, out,
+                              out_dtype, plan, plan_words, groups, nullptr, stream);
+}
+
+PA_API int pa_decode_balanced_timeline(const pa_shape* shape, int32_t batch, const void* q,
+                                       const void* k_new, const void* v_new, void* k_pool,
+                                       void* v_pool, void* kv_scales, int32_t page_format,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       int32_t max_seq_len, float scale, float* out,
+                                       const int32_t* plan, int64_t plan_words, int32_t groups,
+                                       uint64_t* stamps, int64_t stamp_words, void* stream) {
+  if (!stamps) return PA_ERR_NULL;
+  if (!aligned(stamps, 8)) return PA_ERR_ALIGN;
+  if (groups < 1 || stamp_words < (int64_t)groups * pa::kWaves * pa::kStampWords)
+    return PA_ERR_VALUE;
+  return decode_balanced_impl(shape, batch, q, k_new, v_new, nullptr, k_pool, v_pool, kv_scales,
+                              page_format, block_tables, seq_lens, max_seq_len, scale, out,
+                              PA_OUT_F32, plan, plan_words, groups, stamps, stream);
+}
+
+PA_API int pa_wall_clock_khz(int32_t* khz) {
+  if (!khz) return PA_ERR_NULL;
+  int dev = 0, rate = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return PA_ERR_DEVICE;
+  *khz = rate;
+  return PA_OK;
 }

@@ -287,6 +287,28 @@ def test_page_stream_argument_errors(lib):
     assert call(lens=ctypes.c_void_p(0x30002)) == -3
 
 
+def test_timeline_argument_errors(lib):
+    F, T = FAKE, ctypes.c_void_p(0x30000)
+    good = pa.make_shape(64, 8)
+
+    def call(shape=good, batch=2, fmt=0, s=None, groups=2, plan_words=1 << 20,
+             stamps=ctypes.c_void_p(0x40000), words=2 * 8 * 8):
+        return lib.pa_decode_balanced_timeline(
+            ctypes.byref(shape) if shape is not None else None, batch, F, None, None, F, F, s,
+            fmt, T, T, 16, ctypes.c_float(0.125), F, F, plan_words, groups, stamps, words, None)
+    assert call(stamps=None) == -1
+    assert call(stamps=ctypes.c_void_p(0x40004)) == -3         # 8-byte words
+    assert call(words=2 * 8 * 8 - 1) == -6                     # 8 words per wavefront
+    assert call(groups=0) == -6
+    assert call(batch=0) == 0                                  # nothing to launch
+    assert call(shape=None) == -1
+    assert call(shape=pa.make_shape(64, 8, head_dim=128)) == -2
+    assert call(fmt=3) == -6
+    assert call(fmt=1) == -1                                   # INT8 pages need their scales
+    assert call(plan_words=64) == -6                           # plan shorter than its groups
+    assert lib.pa_wall_clock_khz(None) == -1
+
+
 def test_balanced_launch_refuses_page_ids_beyond_28_bits(lib):
     F = FAKE
     shape = pa.make_shape((1 << 28) + 1, 128)      # checked before the plan and any launch

@@ -200,3 +200,77 @@ def test_page_stream_summary_sets_each_kernel_beside_its_own_stream(tmp_path, mo
         assert "run it again" in str(e)
     else:
         raise AssertionError("a page-stream run of other sources must be refused")
+
+
+def _hand_stamps():
+    """Two work-groups of 8 wavefronts, 100 ticks per µs: start 10 + g + w ticks,
+    then 0.3, 1.8, 1.4 µs, 1 µs per page over 11 pages, 0.5 and 1.2 µs; wavefront
+    (1, 7) has no pages."""
+    import numpy as np
+    st = np.zeros((2, 8, 8), np.int64)
+    for g in range(2):
+        for w in range(8):
+            pages = 0 if (g, w) == (1, 7) else 11
+            t0 = 10 + g + w
+            t1, t2 = t0 + 30, t0 + 210
+            t3 = t2 + 140 if pages else 0
+            t4 = t3 + 100 * (pages - 1) if pages else t2
+            t5 = t4 + 50
+            st[g, w, :7] = (t0, t1, t2, t3, t4, t5, t5 + 120)
+            st[g, w, 7] = (pages << 48) | (g << 32) | 0x1234
+    return st
+
+
+def test_timeline_phases_from_hand_made_stamps():
+    sys.path.insert(0, ROOT)
+    import bench
+    p = bench.timeline_phases(_hand_stamps(), 100_000.0)
+    assert abs(p["descriptor_us"] - 0.3) < 1e-9 and abs(p["metadata_us"] - 1.8) < 1e-9
+    assert abs(p["first_page_us"] - 1.4) < 1e-9 and abs(p["us_per_page"] - 1.0) < 1e-9
+    assert abs(p["stream_us"] - 10.0) < 1e-9 and abs(p["tail_us"] - 1.7) < 1e-9
+    assert abs(p["dispatch_us"] - 0.08) < 1e-9                 # starts 10 .. 18 ticks
+    assert abs(p["span_us"] - (17 + 210 + 140 + 1000 + 170 - 10) / 100) < 1e-9
+    assert abs(p["first_page_at_us"] - (p["descriptor_us"] + p["metadata_us"] + 1.4 + 0.035)) < 0.05
+    assert list(p["xcc"]) == [0, 1]
+    assert abs(p["wg_end_us"] - 15.27).max() < 1e-9            # both end with a 11-page wave at 17
+
+
+def test_timeline_summary_tables(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    import bench_profiles as P
+    monkeypatch.setattr(P, "PROFILES", str(tmp_path))
+    rows = [{"kernel_sources": bench.source_hashes()}]
+    for ci, h, nl in ((3, 1, 16), (4, 8, 1)):
+        rows.append({"case": f"workload {ci}, balanced, {h} KV heads per lane", "workload": ci,
+                     "layers": nl, "batch": 64, "heads_together": h, "groups": 256, "steps": 3,
+                     "warmup": 1, "clock_khz": 100000, "step_us_timeline": 441.0,
+                     "step_us_plain": 437.0, "per_layer_us_plain": 437.0 / nl,
+                     "gap_us": 1.4 if nl > 1 else None, "span_us": 25.7, "dispatch_us": 0.3,
+                     "descriptor_us": 0.28, "metadata_us": 1.76, "first_page_us": 1.44,
+                     "first_page_at_us": 3.66, "stream_us": 16.0, "us_per_page": 1.131,
+                     "tail_us": 1.72,
+                     "wg_end_us": {"min": 19.5, "p10": 21.1, "p50": 22.2, "p90": 24.4, "max": 25.7},
+                     "by_xcc": {"0": {"wg_end_median_us": 21.3, "us_per_page": 1.043,
+                                      "work_groups": 32},
+                                "3": {"wg_end_median_us": 24.8, "us_per_page": 1.337,
+                                      "work_groups": 32}},
+                     "pages_per_wave": {"min": 9, "median": 15.0, "max": 16},
+                     "stamped_over_event": 0.99})
+    j = tmp_path / "timeline.json"
+    j.write_text("\n".join(json.dumps(r) for r in rows) + "\n")
+    assert P.main(["timeline", "--json", str(j), "--steps", "3", "--warmup", "1"]) == 0
+    text = (tmp_path / "decode_balanced_timeline_workloads_3_4_5.md").read_text()
+    assert ("| workload 3, balanced, 1 KV heads per lane | 256 | 437.0 (27.31) | 441.0 | 25.70 | "
+            "1.40 | 0.30 | 0.28 | 1.76 | 1.44 | 3.66 | 16.00 | 1.131 | 1.72 |") in text
+    assert "| workload 4, balanced, 8 KV heads per lane | 256 | 437.0 (437.00) | 441.0 | 25.70 | – |" in text
+    assert "| 19.50 | 21.10 | 22.20 | 24.40 | 25.70 | 3.50 | 9 / 15 / 16 | 0.990 |" in text
+    assert "| XCD 0 | XCD 3 |" in text and "| 21.30 / 1.043 | 24.80 / 1.337 |" in text
+    rows[0] = {"kernel_sources": {**bench.source_hashes(), "balanced": "0" * 16}}
+    j.write_text("\n".join(json.dumps(r) for r in rows) + "\n")
+    try:
+        P.main(["timeline", "--json", str(j), "--steps", "3", "--warmup", "1"])
+    except SystemExit as e:
+        assert "run it again" in str(e)
+    else:
+        raise AssertionError("a timeline run of other sources must be refused")
