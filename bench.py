@@ -57,7 +57,8 @@ _CSRC = os.path.join(ROOT, "paged_kv_decode_07_amd", "csrc")
 _DEVICE = ("pa_kernels.h", "pa_kernels_q8.h", "pa_decode_kernel.h", "pa_host.h")
 KERNEL_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode.hip",)]
 KERNEL_SOURCES_Q8 = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_q8.hip",)]
-BALANCED_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_decode_balanced.hip",)]
+BALANCED_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_balance_plan.h",
+                                                             "pa_decode_balanced.hip")]
 STREAM_SOURCES = [os.path.join(_CSRC, n) for n in _DEVICE + ("pa_measure.hip",)]
 # (wavefronts per KV head, LDS ring slots) of the decode kernels on the 256 x 2048
 # batch: BF16 pages one wavefront per KV head and one slot, INT8 pages one and

@@ -309,6 +309,12 @@ int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
  *     exceeds capacity; batch * splits always suffices);
  *   pages_out, splits_out (may be NULL): the split size and the splits per
  *     sequence of the plan, to be passed with the list.
+ * Host cost: planning the split size simulates one launch per candidate
+ * size (8 .. 256 pages), about 0.2 ms for 64 sequences and 1 ms for 512 on
+ * this repository's build host; building the list for a given size takes
+ * tens of microseconds.  A serving loop, whose lengths grow by one token a
+ * step, can plan the size once for a batch and pass it (pages_per_split)
+ * on the steps that follow, replanning when the batch changes.
  */
 int pa_decode_worklist(const pa_shape* shape, int32_t batch, const int32_t* seq_lens_host,
                        int32_t max_seq_len, int32_t pages_per_split, int32_t page_format,

@@ -53,8 +53,18 @@ extern "C" {
  *                  wavefronts of a work-group (for batches of few, long
  *                  sequences)
  *   plan           HOST int32 buffer of capacity_words words, or NULL to
- *                  query the size; the caller copies the plan to the device
- *   *words_out     words the plan takes; *groups_out work-groups to launch
+ *                  query the size; the caller copies the plan to the device.
+ *                  Every word of the plan is written.
+ *   *words_out     words the plan takes, 64 + groups * 8 * 64;
+ *                  *groups_out work-groups to launch.  Both are set also
+ *                  when capacity_words is too small (PA_ERR_VALUE), so a
+ *                  caller can offer room for its usual plan (groups = the
+ *                  compute units) and call again only when it is short.
+ * Planning runs on the host once per batch of lengths, that is once per
+ * decode step of a serving loop; it reuses its buffers from call to call
+ * (one set per calling thread).  Measured on this repository's build host:
+ * 512 Zipf lengths, 8 heads per lane, 256 work-groups: about 70 us, half of
+ * it writing the 512 KiB plan; 1 head per lane: about 220 us.
  * Returns PA_ERR_VALUE when the batch cannot be planned this way (a
  * wavefront would hold more than 7 stream pieces or 256 pages even with
  * more work-groups; batches of very many one-page sequences, or sequences

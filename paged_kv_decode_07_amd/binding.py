@@ -750,6 +750,11 @@ def append_decode_attention_worklist(q, k_new, v_new, k_pool, v_pool, block_tabl
     return out
 
 
+# int32 words of a balanced plan's header and of one wavefront's descriptor
+# (include/pa_decode_balanced.h)
+BAL_HEADER, BAL_DESC = 64, 64
+
+
 class BalancedPlan:
     """A plan of ``pa_balance_plan`` on the device: ``plan`` (int32 device tensor),
     ``groups`` (work-groups to launch) and the host lengths it was built for."""
@@ -778,11 +783,18 @@ def balance_plan(seq_lens_host, num_pages: int, max_blocks: int = 128,
     words, groups = ctypes.c_int64(), ctypes.c_int32()
     args = (ctypes.byref(shape), int(lens.size), lens.ctypes.data_as(ctypes.c_void_p),
             int(max_seq_len), int(num_cus), int(heads_together))
-    _check(lib.pa_balance_plan(*args, None, 0, ctypes.byref(words), ctypes.byref(groups)),
-           "pa_balance_plan")
-    host = np.zeros(words.value, dtype=np.int32)
-    _check(lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
-                               ctypes.byref(words), ctypes.byref(groups)), "pa_balance_plan")
+    # one call into room for as many work-groups as compute units (the usual
+    # plan; the library writes every word of it), a second when it needs more
+    guess = BAL_HEADER + max(int(num_cus) if num_cus > 0 else 256, 1) * 8 * BAL_DESC
+    host = np.empty(guess, dtype=np.int32)
+    rc = lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
+                             ctypes.byref(words), ctypes.byref(groups))
+    if rc != 0 and words.value > host.size:
+        host = np.empty(words.value, dtype=np.int32)
+        rc = lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
+                                 ctypes.byref(words), ctypes.byref(groups))
+    _check(rc, "pa_balance_plan")
+    host = host[:words.value]
     if host_only:
         return host, groups.value
     return BalancedPlan(torch.from_numpy(host).to(device), groups.value, lens)

@@ -3,8 +3,9 @@
 ``python -m paged_kv_decode_07_amd.build`` compiles ``csrc/pa_decode.hip``
 (BF16 pages; device kernels in ``csrc/pa_kernels.h``), ``csrc/pa_decode_q8.hip``
 (INT8 pages; ``csrc/pa_kernels_q8.h``), ``csrc/pa_decode_balanced.hip`` (the balanced
-launch over a host plan, every page format), ``csrc/pa_measure.hip`` (streaming-read
-calibration) and ``csrc/pa_kvpool.cpp`` (host page allocator), against the
+launch over a host plan, every page format), ``csrc/pa_balance_plan.cpp`` (its host
+planner), ``csrc/pa_measure.hip`` (streaming-read calibration) and
+``csrc/pa_kvpool.cpp`` (host page allocator), against the
 headers in ``include/``, into
 ``paged_kv_decode_07_amd/_lib/libpa_decode.so``.
 """
@@ -20,7 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", n)
         for n in ("pa_decode.hip", "pa_decode_q8.hip", "pa_decode_balanced.hip", "pa_measure.hip",
-                  "pa_kvpool.cpp")]
+                  "pa_kvpool.cpp", "pa_balance_plan.cpp")]
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libpa_decode.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")

@@ -16,27 +16,16 @@
 #include "pa_decode_balanced.h"
 #include "pa_measure.h"
 #include "pa_host.h"
+#include "pa_balance_plan.h"
 #include "pa_decode_kernel.h"
 
 #define PA_API extern "C" __attribute__((visibility("default")))
 
 namespace pa {
 
-// Plan layout (int32 words): a header of kBalHeader words, then one
-// descriptor of kBalDesc words per wavefront, work-group by work-group.
-// Descriptor: [0] segments, [1] pages, [2..7] unused; segment j (j <
-// kBalMaxSeg) at 8 + 8 j: sequence b, KV head g (8: an idle sequence's zero
-// rows), first page p0, end page p1, length L, kind (0 whole stream, 1 first
-// piece of a split stream, 2 later piece), pieces (kind 1: how many), stride
-// (kind 1: the later pieces are in wavefronts wave + stride, wave + 2 stride,
-// ...).  A wavefront's first piece of a split stream is always its last
-// segment, a later piece always its first.
-constexpr int kBalHeader = 64;
-constexpr int kBalDesc = 64;
-constexpr int kBalMaxSeg = 7;
-constexpr int kBalMaxPages = 256;
 constexpr int kBalSegBlk = 1024;
-constexpr int32_t kBalMagic = 0x50414231;
+static_assert(kBalPageTokens == kPage && kBalKvHeads == kHkv && kBalWaves == kWaves,
+              "the planner's geometry is the kernel's");
 
 struct BalancedArgs {
   const uint16_t* q;
@@ -657,209 +646,9 @@ hipError_t launch_balanced(const BalancedArgs& a, int groups, bool out_bf16, boo
 
 }  // namespace pa
 
-namespace pa_host {
-
-// A wavefront does not split a stream below this many pages unless the
-// work-group's pages call for it (short pieces cost a merge each).
-constexpr int kBalMinChunk = 4;
-
-struct BalUnit {
-  int b, g0, pages;          // heads g0 .. g0 + h - 1 of sequence b, ceil(L/16) pages
-};
-struct BalSeg {
-  int b, g, p0, p1, L, kind, pieces, stride;
-};
-
-// One attempt at `groups` work-groups with units of h heads (h = 1, 2, 4 or
-// 8): false when a wavefront would hold more segments or pages than a
-// descriptor allows.  A work-group's 8 wavefronts form 8 / h lanes of h
-// wavefronts; a lane streams its units' heads in lockstep (wavefront i of the
-// lane takes head g0 + i), so the heads of a sequence that one lane holds are
-// read together.  With h = 8 units are whole sequences and are never cut;
-// otherwise a work-group's units are laid end to end and cut evenly over its
-// lanes, and the pieces of a unit are merged in LDS (stride h).
-static bool balance_attempt(const std::vector<BalUnit>& units, const std::vector<int>& idle,
-                            const int32_t* lens, int groups, int h,
-                            std::vector<std::vector<BalSeg>>& waves) {
-  const int lanes = pa::kWaves / h;
-  waves.assign((size_t)groups * pa::kWaves, {});
-  // largest unit first into the least-loaded work-group (ties: lowest index);
-  // with h = 8 a work-group takes at most kBalMaxSeg sequences
-  std::vector<std::vector<BalUnit>> bins(groups);
-  std::priority_queue<std::pair<int64_t, int>, std::vector<std::pair<int64_t, int>>,
-                      std::greater<std::pair<int64_t, int>>> heap;
-  for (int k = 0; k < groups; ++k) heap.push({0, k});
-  for (const BalUnit& u : units) {
-    if (heap.empty()) return false;
-    auto top = heap.top();
-    heap.pop();
-    bins[top.second].push_back(u);
-    if (h < pa::kWaves || (int)bins[top.second].size() < pa::kBalMaxSeg)
-      heap.push({top.first + u.pages, top.second});
-  }
-  auto add = [&](int k, int lane, const BalUnit& u, int p0, int p1) {
-    for (int i = 0; i < h; ++i)
-      waves[(size_t)k * pa::kWaves + lane * h + i].push_back(
-          {u.b, u.g0 + i, p0, p1, lens[u.b], 0, 0, 0});
-  };
-  for (int k = 0; k < groups; ++k) {
-    std::vector<BalUnit>& bin = bins[k];
-    int64_t load = 0;
-    for (const BalUnit& u : bin) load += u.pages;
-    if (load == 0) continue;
-    if (h == pa::kWaves) {
-      if (load > pa::kBalMaxPages) return false;
-      for (const BalUnit& u : bin) add(k, 0, u, 0, u.pages);
-      continue;
-    }
-    const int per = (int)std::max<int64_t>((load + lanes - 1) / lanes, kBalMinChunk);
-    if (per > pa::kBalMaxPages) return false;
-    // long units (more than half a lane's share) first, each followed by a
-    // turn of the short ones, so that the short ones spread over the lanes
-    // instead of piling into the last
-    std::vector<BalUnit> order;
-    std::vector<std::vector<BalUnit>> runs;
-    for (const BalUnit& u : bin)
-      if (2 * u.pages > per) runs.push_back({u});
-    if (runs.empty()) runs.push_back({});
-    size_t turn = 0;
-    for (const BalUnit& u : bin)
-      if (2 * u.pages <= per) runs[turn++ % runs.size()].push_back(u);
-    for (auto& r : runs) order.insert(order.end(), r.begin(), r.end());
-    int64_t cursor = 0;
-    for (const BalUnit& u : order) {
-      int p = 0;
-      const int first_lane = (int)(cursor / per);
-      while (p < u.pages) {
-        const int lane = (int)(cursor / per);
-        const int take = (int)std::min<int64_t>(u.pages - p, (int64_t)(lane + 1) * per - cursor);
-        add(k, lane, u, p, p + take);
-        p += take;
-        cursor += take;
-      }
-      const int last_lane = (int)((cursor - 1) / per);
-      if (last_lane > first_lane) {
-        for (int i = 0; i < h; ++i) {
-          BalSeg& f = waves[(size_t)k * pa::kWaves + first_lane * h + i].back();
-          f.kind = 1;
-          f.pieces = last_lane - first_lane + 1;
-          f.stride = h;
-          for (int l = first_lane + 1; l <= last_lane; ++l)
-            waves[(size_t)k * pa::kWaves + l * h + i].front().kind = 2;
-        }
-      }
-    }
-  }
-  // idle sequences: a zero-row segment each, on the wavefront with the fewest
-  // segments, after a later piece and before a first piece
-  for (int b : idle) {
-    size_t best = 0;
-    for (size_t w = 1; w < waves.size(); ++w)
-      if (waves[w].size() < waves[best].size()) best = w;
-    std::vector<BalSeg>& v = waves[best];
-    const BalSeg z{b, 8, 0, 0, 0, 0, 0, 0};
-    size_t at = v.size();
-    if (!v.empty() && v.back().kind == 1) at = v.size() - 1;
-    if (at == 0 && !v.empty() && v.front().kind == 2) at = 1;
-    v.insert(v.begin() + (int64_t)at, z);
-  }
-  for (const auto& v : waves) {
-    if ((int)v.size() > pa::kBalMaxSeg) return false;
-    int pages = 0;
-    for (const BalSeg& s : v) pages += s.p1 - s.p0;
-    if (pages > pa::kBalMaxPages) return false;
-  }
-  return true;
-}
-
-int balance_plan(const pa_shape* shape, int batch, const int32_t* lens, int max_seq_len, int cus,
-                 int h, std::vector<int32_t>& plan, int* groups_out) {
-  if (h != 1 && h != 2 && h != 4 && h != 8) return PA_ERR_VALUE;
-  std::vector<BalUnit> units;
-  std::vector<int> idle;
-  for (int b = 0; b < batch; ++b) {
-    const int L = lens[b];
-    if (L < 0 || L > max_seq_len) return PA_ERR_VALUE;
-    const int np = ceil_div(L, pa::kPage);
-    if (np > shape->max_blocks_per_seq) return PA_ERR_VALUE;
-    if (np == 0) {
-      idle.push_back(b);
-      continue;
-    }
-    for (int g = 0; g < pa::kHkv; g += h) units.push_back({b, g, np});
-  }
-  std::stable_sort(units.begin(), units.end(),
-                   [](const BalUnit& x, const BalUnit& y) { return x.pages > y.pages; });
-  int64_t total = 0;                                  // page-units over the lanes
-  for (const BalUnit& u : units) total += u.pages;
-  const int nunits = (int)units.size();
-  const int lanes = pa::kWaves / h;
-  int groups = std::max(1, std::min(cus, std::max(nunits, 1)));
-  const int64_t need = (total + (int64_t)lanes * pa::kBalMaxPages - 1) /
-                       ((int64_t)lanes * pa::kBalMaxPages);
-  groups = (int)std::max<int64_t>(groups, need);
-  std::vector<std::vector<BalSeg>> waves;
-  const int limit = std::max(nunits, (int)((idle.size() + pa::kBalMaxSeg - 1) / pa::kBalMaxSeg) + 1);
-  while (!balance_attempt(units, idle, lens, groups, h, waves)) {
-    if (groups >= limit || groups > (1 << 20)) return PA_ERR_VALUE;
-    groups = std::min<int64_t>((int64_t)groups * 2, limit);
-  }
-  plan.assign((size_t)pa::kBalHeader + (size_t)groups * pa::kWaves * pa::kBalDesc, 0);
-  plan[0] = pa::kBalMagic;
-  plan[1] = groups;
-  plan[2] = batch;
-  plan[3] = shape->max_blocks_per_seq;
-  plan[4] = pa::kBalMaxSeg;
-  plan[5] = h;
-  for (size_t w = 0; w < waves.size(); ++w) {
-    int32_t* d = plan.data() + pa::kBalHeader + w * pa::kBalDesc;
-    int pages = 0;
-    for (size_t j = 0; j < waves[w].size(); ++j) {
-      const BalSeg& s = waves[w][j];
-      int32_t* e = d + 8 + 8 * j;
-      e[0] = s.b;
-      e[1] = s.g;
-      e[2] = s.p0;
-      e[3] = s.p1;
-      e[4] = s.L;
-      e[5] = s.kind;
-      e[6] = s.pieces;
-      e[7] = s.stride;
-      pages += s.p1 - s.p0;
-    }
-    d[0] = (int32_t)waves[w].size();
-    d[1] = pages;
-  }
-  *groups_out = groups;
-  return PA_OK;
-}
-
-}  // namespace pa_host
 
 using namespace pa_host;
 
-PA_API int pa_balance_plan(const pa_shape* shape, int32_t batch, const int32_t* seq_lens_host,
-                           int32_t max_seq_len, int32_t num_cus, int32_t heads_together,
-                           int32_t* plan, int64_t capacity_words, int64_t* words_out,
-                           int32_t* groups_out) {
-  int rc = check_decode_sizes(shape, batch, max_seq_len);
-  if (rc != PA_OK) return rc;
-  if (!words_out || !groups_out || (batch > 0 && !seq_lens_host)) return PA_ERR_NULL;
-  if (num_cus < 0 || capacity_words < 0) return PA_ERR_VALUE;
-  int cu = num_cus;
-  if (cu == 0 && (rc = current_cu_count(&cu)) != PA_OK) return rc;
-  std::vector<int32_t> p;
-  int groups = 0;
-  rc = balance_plan(shape, batch, seq_lens_host, max_seq_len, cu, heads_together, p, &groups);
-  if (rc != PA_OK) return rc;
-  *words_out = (int64_t)p.size();
-  *groups_out = groups;
-  if (plan) {
-    if (capacity_words < (int64_t)p.size()) return PA_ERR_VALUE;
-    std::copy(p.begin(), p.end(), plan);
-  }
-  return PA_OK;
-}
 
 // Both balanced entry points; stamps (the timeline launch) or NULL.
 static int decode_balanced_impl(const pa_shape* shape, int32_t batch, const void* q,

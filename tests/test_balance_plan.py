@@ -146,3 +146,37 @@ def test_refusals():
     assert groups >= 1 and plan.size == HEADER + groups * 8 * DESC
     with pytest.raises(RuntimeError, match="VALUE"):
         pa.balance_plan([10], 10, num_cus=256, heads_together=3, host_only=True)
+
+
+def test_short_buffer_reports_the_size_and_every_word_is_written():
+    import ctypes
+    lib = pa.load_library()
+    rng = np.random.default_rng(5)
+    lens = np.ascontiguousarray(rng.integers(0, 2049, 300).astype(np.int32))
+    shape = pa.make_shape(1 << 20, 128)
+    words, groups = ctypes.c_int64(), ctypes.c_int32()
+    args = (ctypes.byref(shape), lens.size, lens.ctypes.data_as(ctypes.c_void_p), 2048, 256, 1)
+    short = np.zeros(HEADER + 8 * DESC, np.int32)
+    assert lib.pa_balance_plan(*args, short.ctypes.data_as(ctypes.c_void_p), short.size,
+                               ctypes.byref(words), ctypes.byref(groups)) == -6
+    assert words.value == HEADER + groups.value * 8 * DESC and groups.value > 1
+    assert (short == 0).all()                               # nothing written into a short buffer
+    plans = []
+    for fill in (0, -1, 0x5A5A5A5A):                        # whatever the buffer held before
+        buf = np.full(words.value, fill, np.int32)
+        assert lib.pa_balance_plan(*args, buf.ctypes.data_as(ctypes.c_void_p), buf.size,
+                                   ctypes.byref(words), ctypes.byref(groups)) == 0
+        plans.append(buf)
+    assert all(np.array_equal(plans[0], p) for p in plans[1:])
+    host, g = pa.balance_plan(lens, 1 << 20, max_seq_len=2048, num_cus=256, heads_together=1,
+                              host_only=True)
+    assert g == groups.value and np.array_equal(host, plans[0])
+
+
+def test_wrapper_plans_beyond_its_first_guess():
+    # many idle and one-page sequences need more work-groups than compute units
+    lens = np.array([0] * 40 + [1] * 3000, np.int32)
+    plan, groups = pa.balance_plan(lens, 1 << 20, max_seq_len=16, num_cus=8, heads_together=8,
+                                   host_only=True)
+    assert groups > 8 and plan.size == HEADER + groups * 8 * DESC
+    check_plan(lens, num_cus=8, h=8)
