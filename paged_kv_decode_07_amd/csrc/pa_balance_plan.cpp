@@ -225,6 +225,7 @@ int balance_plan(const pa_shape* shape, int batch, const int32_t* lens, int max_
   }
   int64_t total = 0;                                  // page-units over the lanes
   for (const BalUnit& u : units) total += u.pages;
+  if (total >= ((int64_t)1 << 31)) return PA_ERR_VALUE;   // loads are 32-bit tree keys
   const int nunits = (int)units.size();
   const int lanes = pa::kBalWaves / h;
   int groups = std::max(1, std::min(cus, std::max(nunits, 1)));
