@@ -313,6 +313,25 @@ def measure_config(ci: int, args, stream, dev, flush, refs):
         except RuntimeError:
             continue                       # this batch cannot be planned with such lanes
         cands.append((f"balanced, {h} KV head{'s' if h > 1 else ''} per lane", 0, plan))
+    # host time of the planning call each launch needs for this batch of
+    # lengths (a serving loop makes it once per step): median of 20 calls
+    def host_us(fn):
+        t = []
+        for _ in range(20):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+        return round(float(np.median(t)) * 1e6, 1)
+    plan_us = {"grid, host-lengths plan": host_us(
+        lambda: pa.decode_plan_lengths(w0.seq_lens, npg, max_seq_len=msl))}
+    if B > 1:
+        plan_us["work list"] = host_us(
+            lambda: pa.decode_worklist(w0.seq_lens, npg, max_seq_len=msl))
+    for name, _, work in cands:
+        if isinstance(work, pa.BalancedPlan):
+            h = int(name.split(", ")[1].split(" ")[0])
+            plan_us[name] = host_us(lambda h=h: pa.balance_plan(
+                w0.seq_lens, npg, max_seq_len=msl, heads_together=h, host_only=True))
     need = max(pa.decode_workspace_bytes(B, msl, npg, 128, ps) for _, ps, _ in cands)
     workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
@@ -350,6 +369,7 @@ def measure_config(ci: int, args, stream, dev, flush, refs):
                      "step_median_us": round(float(np.median(t)) * 1e6, 2),
                      "step_min_us": round(float(t.min()) * 1e6, 2),
                      "kv_gbps": round(kv / float(t.mean()) / 1e9, 1),
+                     "plan_host_us": plan_us.get(name, 0.0),
                      "max_abs_vs_oracle": err, "max_rel_vs_oracle": rel}
         if best is None or t.mean() < best[1]:
             best = (name, float(t.mean()), outs)
@@ -358,6 +378,7 @@ def measure_config(ci: int, args, stream, dev, flush, refs):
     line = {
         "workload": states[0][0].recipe.get("workload", ""), "layers": nl, "batch": B,
         "launch": name, "pages_per_split": res[name]["pages_per_split"],
+        "plan_host_us": res[name]["plan_host_us"],
         "step_us": round(t_best * 1e6, 2), "step_median_us": res[name]["step_median_us"],
         "step_min_us": res[name]["step_min_us"], "per_layer_us": round(t_best / nl * 1e6, 2),
         "kv_bytes": int(kv), "kv_gbps": round(kv / t_best / 1e9, 1),

@@ -310,9 +310,10 @@ int pa_decode_attention_profiled(const pa_shape* shape, int32_t batch,
  *   pages_out, splits_out (may be NULL): the split size and the splits per
  *     sequence of the plan, to be passed with the list.
  * Host cost: planning the split size simulates one launch per candidate
- * size (8 .. 256 pages), about 0.2 ms for 64 sequences and 1 ms for 512 on
- * this repository's build host; building the list for a given size takes
- * tens of microseconds.  A serving loop, whose lengths grow by one token a
+ * size (8 .. 256 pages): on the host of an MI355X machine 50 us for 64
+ * sequences of uniform lengths, 0.4 ms for 512 Zipf lengths (bench.py's
+ * plan_host_us); building the list for a given size takes tens of
+ * microseconds.  A serving loop, whose lengths grow by one token a
  * step, can plan the size once for a batch and pass it (pages_per_split)
  * on the steps that follow, replanning when the batch changes.
  */

@@ -62,9 +62,10 @@ extern "C" {
  *                  compute units) and call again only when it is short.
  * Planning runs on the host once per batch of lengths, that is once per
  * decode step of a serving loop; it reuses its buffers from call to call
- * (one set per calling thread).  Measured on this repository's build host:
- * 512 Zipf lengths, 8 heads per lane, 256 work-groups: about 70 us, half of
- * it writing the 512 KiB plan; 1 head per lane: about 220 us.
+ * (one set per calling thread).  Measured on the host of an MI355X machine
+ * (bench.py's plan_host_us): 512 Zipf lengths, 8 heads per lane, 256
+ * work-groups, 28 us (the GPU step: about 164 us); 64 uniform lengths, 1 head
+ * per lane, 29 us; 512 Zipf lengths, 1 head per lane, 84 us.
  * Returns PA_ERR_VALUE when the batch cannot be planned this way (a
  * wavefront would hold more than 7 stream pieces or 256 pages even with
  * more work-groups; batches of very many one-page sequences, or sequences
