@@ -180,3 +180,32 @@ def test_wrapper_plans_beyond_its_first_guess():
                                    host_only=True)
     assert groups > 8 and plan.size == HEADER + groups * 8 * DESC
     check_plan(lens, num_cus=8, h=8)
+
+
+def test_concurrent_planning_matches_sequential():
+    # the planner keeps its buffers per calling thread; ctypes drops the GIL
+    # during the call, so these plans are built concurrently
+    import threading
+    rng = np.random.default_rng(11)
+    batches = [rng.integers(0, 2049, int(rng.integers(1, 600))).astype(np.int32) for _ in range(16)]
+    hs = [1, 2, 4, 8]
+
+    def plan(i):
+        return pa.balance_plan(batches[i], 1 << 20, max_seq_len=2048, num_cus=256,
+                               heads_together=hs[i % 4], host_only=True)
+    want = [plan(i) for i in range(len(batches))]
+    got = [[None] * len(batches) for _ in range(8)]
+
+    def worker(t):
+        for rep in range(3):
+            for i in range(len(batches)):
+                j = (i + t) % len(batches)
+                got[t][j] = plan(j)
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for t in range(8):
+        for i in range(len(batches)):
+            assert got[t][i][1] == want[i][1] and np.array_equal(got[t][i][0], want[i][0])
