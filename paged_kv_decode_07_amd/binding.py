@@ -767,13 +767,45 @@ class BalancedPlan:
         return int(self.plan.numel())
 
 
+# Pinned host buffers that plans are built in and uploaded from, per device:
+# idle [buffer, event recorded after its last upload] pairs.  A caller takes a
+# buffer out while it plans into it and queues its upload, and gives it back
+# with the event recorded; a buffer is written again only once that event has
+# completed, so an upload never waits for the work queued before it.
+_STAGING_SLOTS = 4
+_staging: dict = {}
+
+
+def _staging_take(device: torch.device, words: int):
+    with _lock:
+        pool = _staging.setdefault(str(device), [])
+        for i, slot in enumerate(pool):
+            if slot[0].numel() >= words and slot[1].query():
+                return pool.pop(i)
+        if len(pool) < _STAGING_SLOTS:
+            return [torch.empty(words, dtype=torch.int32, pin_memory=True), torch.cuda.Event()]
+        slot = pool.pop(0)                     # the least recently given back
+    slot[1].synchronize()
+    if slot[0].numel() < words:
+        slot[0] = torch.empty(words, dtype=torch.int32, pin_memory=True)
+    return slot
+
+
+def _staging_give(device: torch.device, slot) -> None:
+    with _lock:
+        _staging.setdefault(str(device), []).append(slot)
+
+
 def balance_plan(seq_lens_host, num_pages: int, max_blocks: int = 128,
                  max_seq_len: int | None = None, num_cus: int = 0, heads_together: int = 8,
-                 device="cuda", host_only: bool = False):
+                 device="cuda", host_only: bool = False, stream=None):
     """Plan of the balanced launch for host lengths (``include/pa_decode_balanced.h``).
 
-    Returns a ``BalancedPlan`` with the plan copied to ``device`` (or, with
-    ``host_only``, the host int32 array and the work-group count)."""
+    Returns a ``BalancedPlan`` whose plan is uploaded to ``device`` on ``stream``
+    (default: the device's current stream) without waiting for the work queued
+    there: the plan is built in a pinned buffer and copied asynchronously, so a
+    serving loop can plan its next step while the GPU runs this one.  With
+    ``host_only``: the host int32 array and the work-group count."""
     import numpy as np
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     if max_seq_len is None:
@@ -786,18 +818,37 @@ def balance_plan(seq_lens_host, num_pages: int, max_blocks: int = 128,
     # one call into room for as many work-groups as compute units (the usual
     # plan; the library writes every word of it), a second when it needs more
     guess = BAL_HEADER + max(int(num_cus) if num_cus > 0 else 256, 1) * 8 * BAL_DESC
-    host = np.empty(guess, dtype=np.int32)
-    rc = lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
-                             ctypes.byref(words), ctypes.byref(groups))
-    if rc != 0 and words.value > host.size:
-        host = np.empty(words.value, dtype=np.int32)
+    if host_only:
+        host = np.empty(guess, dtype=np.int32)
         rc = lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
                                  ctypes.byref(words), ctypes.byref(groups))
-    _check(rc, "pa_balance_plan")
-    host = host[:words.value]
-    if host_only:
-        return host, groups.value
-    return BalancedPlan(torch.from_numpy(host).to(device), groups.value, lens)
+        if rc != 0 and words.value > host.size:
+            host = np.empty(words.value, dtype=np.int32)
+            rc = lib.pa_balance_plan(*args, host.ctypes.data_as(ctypes.c_void_p), host.size,
+                                     ctypes.byref(words), ctypes.byref(groups))
+        _check(rc, "pa_balance_plan")
+        return host[:words.value], groups.value
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    slot = _staging_take(device, guess)
+    try:
+        rc = lib.pa_balance_plan(*args, ctypes.c_void_p(slot[0].data_ptr()), slot[0].numel(),
+                                 ctypes.byref(words), ctypes.byref(groups))
+        if rc != 0 and words.value > slot[0].numel():
+            _staging_give(device, slot)
+            slot = _staging_take(device, words.value)
+            rc = lib.pa_balance_plan(*args, ctypes.c_void_p(slot[0].data_ptr()),
+                                     slot[0].numel(), ctypes.byref(words), ctypes.byref(groups))
+        _check(rc, "pa_balance_plan")
+        st = stream if stream is not None else torch.cuda.current_stream(device)
+        with torch.cuda.stream(st):
+            plan = torch.empty(words.value, dtype=torch.int32, device=device)
+            plan.copy_(slot[0][:words.value], non_blocking=True)
+            slot[1].record(st)
+    finally:
+        _staging_give(device, slot)
+    return BalancedPlan(plan, groups.value, lens)
 
 
 def _balanced_checks(q, k_pool, v_pool, block_tables, seq_lens, plan, k_new, v_new, kv_scales):

@@ -261,3 +261,38 @@ def test_balanced_quantised_full_batch512_zipf(nbits):
                              kv_scales=f[2], scale=w.scale)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy().astype(np.float64), ref, where=f"balanced int{nbits} zipf")
+
+
+@pytest.mark.parametrize("h", [1, 8])
+def test_async_plan_uploads_back_to_back(h):
+    # plans are built in pinned buffers and uploaded without waiting for the
+    # queued work: with the GPU kept busy, 12 plans in a row reuse the 4 staging
+    # buffers while earlier uploads may still be pending
+    pa = _pa()
+    rng = np.random.default_rng(8900 + h)
+    batches = []
+    for i in range(12):
+        lens = rng.integers(0, 700, size=int(rng.integers(3, 40))).tolist()
+        batches.append(W.make_batch(lens, sum(W.pages_for(L) for L in lens) + 3, seed=8910 + i,
+                                    append=False))
+    dbs = [DeviceBatch(w) for w in batches]
+    a = torch.randn(4096, 4096, device="cuda")
+    for _ in range(8):
+        a = torch.tanh(a @ a)                          # keep the GPU busy meanwhile
+    outs, plans = [], []
+    for w, db in zip(batches, dbs):
+        plan = pa.balance_plan(w.seq_lens, w.num_pages, max_seq_len=w.max_seq_len,
+                               heads_together=h)
+        plans.append(plan)
+        outs.append(pa.decode_balanced(db.q, db.k_pool, db.v_pool, db.bt, db.lens,
+                                       w.max_seq_len, plan, scale=w.scale))
+    torch.cuda.synchronize()
+    for w, db, plan, out in zip(batches, dbs, plans, outs):
+        host, groups = pa.balance_plan(w.seq_lens, w.num_pages, max_seq_len=w.max_seq_len,
+                                       heads_together=h, host_only=True)
+        assert groups == plan.groups and np.array_equal(plan.plan.cpu().numpy(), host)
+        sync_plan = pa.BalancedPlan(torch.from_numpy(host).cuda(), groups, w.seq_lens)
+        ref = pa.decode_balanced(db.q, db.k_pool, db.v_pool, db.bt, db.lens, w.max_seq_len,
+                                 sync_plan, scale=w.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
